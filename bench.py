@@ -1,0 +1,295 @@
+"""Benchmark: NVFP4 linear-layer step (fprop + dgrad + wgrad) on one MI355X.
+
+One step is the whole hot path over one batch: X 1D nearest-even, W 2D (16x16)
+nearest-even with W^T emitted, Y = X.W^T; dY 1D stochastic, dX = dY.W; dY^T and
+X^T with the 16-point random Hadamard transform (dY stochastic), dW = dY^T.X.
+Each quantize call includes its amax pass.  Inputs are seeded synthetic tensors
+(workloads/) already resident in HBM when the timed region starts.
+
+Prints one JSON line.  `value` is whole-step NVFP4 linear TFLOP/s (3 GEMMs of
+2*M*N*K flops each, divided by the step time including every quantization);
+`roofline` is that of the dominant kernel (the block-scaled GEMM, timed with HIP
+events on its launch stream); `cpu_baseline` is the oracle timed on host cores
+on a bounded sample of the same workload, extrapolated to the step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# published MI355X peaks (dense)
+PEAK_HBM_GBS = 8000.0
+PEAK_F16_MFMA_TFLOPS = 2500.0
+PEAK_FP4_MFMA_TFLOPS = 10100.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mlp_up_12b", choices=["mlp_up_12b", "fprop_8k", "wgrad_8k", "block_3b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    return ap.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_src):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it stands (same hash); else None."""
+    p = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.md")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    h = re.search(r"source sha256\[:16\]: (\w+)", txt)
+    t = re.search(r"bytes per step \(3 GEMM launches\): ([0-9.eE+]+)", txt)
+    if not h or not t or h.group(1) != source_hash(kernel_src):
+        return None
+    return float(t.group(1)) / 3.0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the NVFP4 path here is single-GPU; "
+              f"see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_bit_microscaled_amd as fp4
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fp4.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.WORKLOADS[args.workload]
+    t_gen = time.time()
+
+    layers = []
+    for li, lin in enumerate(wl.linears):
+        inp = workloads.make_linear_inputs(lin, seed=li, x_outliers=wl.x_outliers, with_dy="dgrad" in wl.passes
+                                           or "wgrad" in wl.passes)
+        x, w = inp.x.to(dev), inp.w.to(dev)
+        dy = inp.dy.to(dev) if inp.dy is not None else None
+        bufs = fp4.LinearBuffers(lin.M, lin.N, lin.K, device=dev)
+        outs = {
+            "y": torch.empty(lin.M, lin.N, dtype=torch.bfloat16, device=dev),
+            "dx": torch.empty(lin.M, lin.K, dtype=torch.bfloat16, device=dev) if dy is not None else None,
+            "dw": torch.empty(lin.N, lin.K, dtype=torch.float32, device=dev) if dy is not None else None,
+        }
+        layers.append((lin, inp, x, w, dy, bufs, outs))
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    Q = fp4
+
+    def step(record):
+        """One pass of the whole hot path; `record` collects (kind, bytes/flops, ev0, ev1)."""
+        for lin, inp, x, w, dy, b, o in layers:
+            M, N, K = lin.M, lin.N, lin.K
+
+            def quant(src, flags, signs, seed, offset, out, out_t=None, nbytes=0):
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                Q.fp4_quantize(src, flags, signs, seed, offset, out, out_t)
+                e1.record(stream)
+                record.append(("quant", nbytes, e0, e1))
+
+            def gemm(a, bq, c, flops):
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                Q.fp4_gemm(a, bq, c)
+                e1.record(stream)
+                record.append(("gemm", flops, e0, e1))
+
+            in_b = x.element_size()
+            if "fprop" in wl.passes:
+                quant(x, 0, 0, 0, 0, b.xq, nbytes=M * K * (in_b + 0.5 + 1 / 16))
+                quant(w, Q.Q_2D, 0, 0, 0, b.wq, b.wq_t, nbytes=N * K * (in_b + 2 * (0.5 + 1 / 256)))
+                gemm(b.xq, b.wq, o["y"], 2.0 * M * N * K)
+            if "dgrad" in wl.passes:
+                if "fprop" not in wl.passes:
+                    quant(w, Q.Q_2D, 0, 0, 0, b.wq, b.wq_t, nbytes=N * K * (in_b + 2 * (0.5 + 1 / 256)))
+                quant(dy, Q.Q_SR, 0, workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, b.dyq,
+                      nbytes=M * N * (in_b + 0.5 + 1 / 16))
+                gemm(b.dyq, b.wq_t, o["dx"], 2.0 * M * N * K)
+            if "wgrad" in wl.passes:
+                f_dy = Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR
+                f_x = Q.Q_COLWISE | Q.Q_RHT
+                quant(dy, f_dy, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_WGRAD, b.dyq_t,
+                      nbytes=M * N * (in_b + 0.5 + 1 / 16))
+                quant(x, f_x, inp.signs, 0, 0, b.xq_t, nbytes=M * K * (in_b + 0.5 + 1 / 16))
+                gemm(b.dyq_t, b.xq_t, o["dw"], 2.0 * M * N * K)
+
+    for _ in range(args.warmup):
+        step([])
+    torch.cuda.synchronize()
+    records = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(records)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    gemm_ms = sum(e0.elapsed_time(e1) for k, _, e0, e1 in records if k == "gemm")
+    gemm_flops = sum(f for k, f, _, _ in records if k == "gemm")
+    n_gemm = sum(1 for k, *_ in records if k == "gemm")
+    quant_ms = sum(e0.elapsed_time(e1) for k, _, e0, e1 in records if k == "quant")
+    quant_bytes = sum(f for k, f, _, _ in records if k == "quant")
+    step_flops = gemm_flops / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+
+    kernel_src = os.path.join(ROOT, "nvfp4_bit_microscaled_amd", "csrc", "gemm.hip")
+    traffic = measured_traffic(kernel_src)
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(gemm_tflops, 2),
+        "peak": PEAK_F16_MFMA_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": "nvfp4 block-scaled GEMM (f16 MFMA on exactly dequantized E2M1xE4M3 operands)",
+        "flops_per_launch": gemm_flops / n_gemm,
+        "avg_launch_ms": round(gemm_ms / n_gemm, 4),
+        "frac_of_fp4_dense_peak": round(gemm_tflops / PEAK_FP4_MFMA_TFLOPS, 4),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, wl, args.cpu_sample_rows, step_flops)
+
+    lin0 = wl.linears[0]
+    out = {
+        "metric": "NVFP4 linear TFLOPS (fprop/dgrad/wgrad) + quantize GB/s, % of roofline, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands (e2m1 x e4m3 block scale), f16 MFMA products, f32 accumulate",
+        "data": "synthetic (seeded: X~N(0,1), W~N(0,0.02^2), dY~Laplace(0,1e-3); bf16)",
+        "config": {
+            "workload": wl.description,
+            "name": wl.name,
+            "linears": [[l.name, l.M, l.N, l.K] for l in wl.linears],
+            "passes": list(wl.passes),
+            "global_batch": lin0.M,
+            "parallelism": "single GPU",
+        },
+        "quantize": {
+            "achieved_gbs": round(quant_gbs, 1),
+            "peak_gbs": PEAK_HBM_GBS,
+            "frac": round(quant_gbs / PEAK_HBM_GBS, 4),
+            "note": "algorithmic bytes (input read + codes + scales written) per quantize call, amax pass included",
+            "ms_per_step": round(quant_ms / args.steps, 4),
+        },
+        "gemm_ms_per_step": round(gemm_ms / args.steps, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "input_generation_s": round(t_gen, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layers, wl, sample_rows, step_flops):
+    """The oracle, untuned, on the host: full-tensor amax passes, quantization of a
+    sample of logical rows of every operand, and the binary64 GEMM reference on a
+    sample x sample block of each pass; each part extrapolated linearly to the step."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    threads = oracle.default_threads()
+    _ = np.ones((256, 256)) @ np.ones((256, 256))  # start the BLAS thread pool outside the timed parts
+    total_s = 0.0
+    parts = []
+    t_start = time.perf_counter()
+    for lin, inp, *_ in layers:
+        M, N, K = lin.M, lin.N, lin.K
+        xf = workloads.widen(inp.x)
+        wf = workloads.widen(inp.w)
+        dyf = workloads.widen(inp.dy) if inp.dy is not None else None
+        r = sample_rows
+        jobs = []  # (array, kwargs, logical rows)
+        if "fprop" in wl.passes:
+            jobs += [("X", xf, dict(), M), ("W", wf, dict(two_d=True), N)]
+        if "dgrad" in wl.passes:
+            jobs += [("dY", dyf, dict(sr=True, seed=0, offset=1), M), ("W^T", wf, dict(two_d=True, colwise=True), K)]
+        if "wgrad" in wl.passes:
+            jobs += [("dY^T", dyf, dict(colwise=True, rht=True, sr=True, signs=inp.signs, seed=0, offset=2), N),
+                     ("X^T", xf, dict(colwise=True, rht=True, signs=inp.signs), K)]
+        qs = {}
+        for name, arr, kw, rows in jobs:
+            t = time.perf_counter()
+            a = oracle.amax(arr, colwise=kw.get("colwise", False), rht=kw.get("rht", False), signs=kw.get("signs", 0),
+                            threads=threads)
+            t_amax = time.perf_counter() - t
+            n = min(r, rows)
+            t = time.perf_counter()
+            qs[name] = oracle.quantize(arr, amax_in=a, rows=(0, n), threads=threads, **kw)
+            t_q = time.perf_counter() - t
+            total_s += t_amax + t_q * rows / n
+        pairs = []
+        if "fprop" in wl.passes:
+            pairs.append(("X", "W", M, N))
+        if "dgrad" in wl.passes:
+            pairs.append(("dY", "W^T", M, K))
+        if "wgrad" in wl.passes:
+            pairs.append(("dY^T", "X^T", N, K))
+        for a, b, rows_a, rows_b in pairs:
+            # the oracle's GEMM reference is dequantize(A), dequantize(B), then the
+            # binary64 products y = A.B^T and bound = |A|.|B|^T: the dequantizations
+            # scale with the rows of each operand, the products with both
+            qa, qb = qs[a], qs[b]
+            t = time.perf_counter()
+            da = oracle.dequantize(qa, threads=threads)
+            t_da = time.perf_counter() - t
+            t = time.perf_counter()
+            db = oracle.dequantize(qb, threads=threads)
+            t_db = time.perf_counter() - t
+            t = time.perf_counter()
+            _ = da @ db.T, np.abs(da) @ np.abs(db).T
+            t_mm = time.perf_counter() - t
+            total_s += t_da * rows_a / qa.rows + t_db * rows_b / qb.rows + t_mm * (rows_a / qa.rows) * (
+                rows_b / qb.rows)
+        del xf, wf, dyf
+        parts.append(lin.name)
+    wall = time.perf_counter() - t_start
+    return {
+        "value": round(step_flops / total_s / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"per operand: full-tensor amax + quantization of the first {sample_rows} logical rows; per pass: "
+                   f"binary64 GEMM reference (dequantize both operands, y and sum|ab| products) on a "
+                   f"{sample_rows}x{sample_rows} output block; amax passes at full size, every other part scaled to "
+                   f"the full step by its own size law ({round(total_s, 1)} s extrapolated, {round(wall, 1)} s measured)"),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * nvfp4_amd.h -- C ABI of the MI355X (gfx950) NVFP4 linear-layer library.
+ *
+ * NVFP4, as the NVFP4-12B page describes it (q2bstudio blog, "NVIDIA ... 4-bit
+ * pretraining with NVFP4, 12B Mamba-Transformer", paragraph 2): 4-bit E2M1
+ * elements in blocks of 16, one E4M3 scale per block and one FP32 scale per
+ * tensor; NVFP4 is used only for the GEMMs of linear layers; the recipe adds 2D
+ * block scaling for weights, 16x16 random Hadamard transforms on the
+ * weight-gradient operands and stochastic rounding on gradients only.
+ *
+ * Numerical definition (the pages give no formulas; this is the reading the
+ * library implements, bit for bit):
+ *   amax     = max |v| over the tensor (v after the Hadamard transform if any)
+ *   s_enc    = 2688 / amax (1 if amax == 0; FLT_MAX if the quotient overflows)
+ *   per block: S = E4M3_rne_satfinite((amax_b / 6) * s_enc),
+ *              m = s_enc / decode(S) (0 when S == 0)
+ *   element  = E2M1(v * m), nearest-even or stochastic, saturating at 6;
+ *              zero is always the +0 code; two codes per byte, low nibble first
+ *   decode   = E2M1 * decode(S) * (amax / 2688)
+ * All of it in binary32, one IEEE operation per step.
+ * Stochastic rounding: element i (row-major index in the logical output) uses
+ * the 16 bits (16*(i&1)) of word ((i&7)>>1) of Philox4x32-10 with counter
+ * (i>>3 as two 32-bit words, offset as two words) and key (seed as two words);
+ * it rounds up when that 16-bit value is below 2^16 * (distance to the lower
+ * grid point / grid step).
+ * Random Hadamard transform: in each 16-block, negate the elements whose bit is
+ * set in the 16-bit sign mask, apply Sylvester's H16 (butterflies at distance
+ * 1, 2, 4, 8), multiply by 1/4.
+ *
+ * Memory: every pointer argument of the compute calls is a device pointer the
+ * caller owns (allocated on the current HIP device); the library allocates no
+ * device memory and keeps no per-call state.  All work is enqueued on the given
+ * stream in stream order; no call synchronizes with the host.  The tensor amax
+ * stays on the device.
+ *
+ * Errors: arguments are checked before anything is enqueued; a failed check
+ * returns a non-zero fp4_status and enqueues nothing.  A launch failure reports
+ * FP4_ERR_HIP.  Faults that occur later on the device surface at the caller's
+ * next synchronization.  Non-finite inputs are outside the contract: their
+ * results are unspecified.
+ */
+#ifndef NVFP4_AMD_H
+#define NVFP4_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Marks the library's exported entry points (everything else is hidden). */
+#define FP4_API __attribute__((visibility("default")))
+
+typedef enum fp4_status {
+  FP4_OK = 0,
+  FP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  FP4_ERR_SHAPE = 2,       /* a size is negative, or not a multiple of 16 where blocks need it */
+  FP4_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks the stated alignment */
+  FP4_ERR_DTYPE = 4,       /* unknown input or output dtype */
+  FP4_ERR_MODE = 5,        /* unsupported combination of quantization flags */
+  FP4_ERR_MISMATCH = 6,    /* descriptor sizes do not agree with the call */
+  FP4_ERR_HIP = 7          /* a HIP launch or runtime call failed */
+} fp4_status;
+
+typedef enum fp4_dtype {
+  FP4_BF16 = 0,
+  FP4_FP32 = 1
+} fp4_dtype;
+
+/* quantization flags (fp4_quantize, fp4_amax) */
+#define FP4_Q_2D (1u << 0)         /* one scale per 16x16 tile (weights), else per 16 elements */
+#define FP4_Q_COLWISE (1u << 1)    /* the logical tensor is x^T: blocks run down the columns of x */
+#define FP4_Q_RHT (1u << 2)        /* random Hadamard transform of every 16-block first */
+#define FP4_Q_SR (1u << 3)         /* stochastic rounding (Philox4x32-10), else nearest-even */
+#define FP4_Q_AMAX_GIVEN (1u << 4) /* *out->amax already holds the tensor amax: skip its pass */
+
+/* A quantized logical tensor of `rows` x `cols`; cols is the blocked (contraction) dimension.
+ *   codes : [rows][cols/2] bytes, element 2j in the low nibble of byte j
+ *   scales: E4M3 codes; 1D: [rows][cols/16]; 2D: [ceil(rows/16)][cols/16]
+ *   amax  : one float, the tensor amax (decode scale = amax / 2688)
+ * codes and scales may be NULL when rows or cols is 0; amax may not. */
+typedef struct fp4_tensor {
+  uint8_t *codes;
+  uint8_t *scales;
+  float *amax;
+  int64_t rows;
+  int64_t cols;
+  int32_t two_d;
+} fp4_tensor;
+
+/* Bytes needed for the codes and scales of a rows x cols quantized tensor. */
+FP4_API fp4_status fp4_tensor_bytes(int64_t rows, int64_t cols, int32_t two_d, size_t *codes_bytes, size_t *scales_bytes);
+
+/* Tensor amax of the logical tensor of x ([rows][cols] with row stride ld elements):
+ * x itself, or x^T with FP4_Q_COLWISE; with FP4_Q_RHT the amax is taken after the
+ * transform (blocks along the logical rows).  Writes one float at amax_out.
+ * Needs: the blocked dimension (cols, or rows with COLWISE) a multiple of 16 when
+ * FP4_Q_RHT is set; ld >= cols; x 16-byte aligned and ld a multiple of 8 elements. */
+FP4_API fp4_status fp4_amax(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
+                    uint32_t rht_signs, float *amax_out, hipStream_t stream);
+
+/* Quantize the logical tensor L of x (L = x, or x^T with FP4_Q_COLWISE) into *out
+ * (out->rows x out->cols must equal L's shape; out->two_d must match FP4_Q_2D).
+ * Without FP4_Q_AMAX_GIVEN the tensor amax is computed first into out->amax.
+ * out_t (FP4_Q_2D only, nullable) also receives L^T quantized with the same tile
+ * scales: its codes and scales are the exact transposes of out's.
+ * Modes: 1D with any of COLWISE, RHT, SR; 2D with COLWISE only (no RHT, no SR).
+ * Needs: L's cols a multiple of 16 (and L's rows too for 2D); x 16-byte aligned,
+ * ld a multiple of 8 elements; codes 16-byte and scales 8-byte aligned. */
+FP4_API fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
+                        uint32_t rht_signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
+                        const fp4_tensor *out_t, hipStream_t stream);
+
+/* Block-scaled GEMM with FP32 accumulation: C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k]
+ * for A [M][K] and B [N][K] (both K-major, M = a->rows, N = b->rows, K = a->cols =
+ * b->cols, K a multiple of 16), written as fp32 or bf16 (nearest-even) with row
+ * stride ldc elements.  The products of the dequantized operands are exact; the
+ * accumulation is FP32. */
+FP4_API fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
+                    hipStream_t stream);
+
+/* Linear layer y = x . w^T with x [M][K], w [N][K] (dtype), y [M][N] (y_dtype).
+ * Forward: x 1D nearest-even into xq ([M][K]); w 2D (16x16) nearest-even into wq
+ * ([N][K]); wq_t (nullable, [K][N]) receives w^T with the same tile scales, for the
+ * backward pass.  Then y = gemm(xq, wq).  M, N, K multiples of 16. */
+FP4_API fp4_status fp4_linear_fprop(const void *x, const void *w, fp4_dtype dtype, void *y, fp4_dtype y_dtype, int64_t M,
+                            int64_t N, int64_t K, const fp4_tensor *xq, const fp4_tensor *wq,
+                            const fp4_tensor *wq_t, hipStream_t stream);
+
+/* Input gradient dx = dy . w with dy [M][N] (dtype), dx [M][K] (dx_dtype): dy is
+ * quantized 1D with stochastic rounding (seed, offset) into dyq ([M][N]) and
+ * multiplied with the forward pass's 2D-quantized w^T (wq_t, [K][N]). */
+FP4_API fp4_status fp4_linear_dgrad(const void *dy, fp4_dtype dtype, const fp4_tensor *wq_t, void *dx, fp4_dtype dx_dtype,
+                            int64_t M, int64_t N, int64_t K, uint64_t seed, uint64_t offset,
+                            const fp4_tensor *dyq, hipStream_t stream);
+
+/* Weight gradient dw = dy^T . x with dy [M][N], x [M][K] (dtype), dw [N][K] (dw_dtype):
+ * both operands are quantized transposed (blocks along the M tokens) after the random
+ * Hadamard transform with the same signs; dy with stochastic rounding (seed, offset)
+ * into dyq_t ([N][M]), x nearest-even into xq_t ([K][M]). */
+FP4_API fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dtype, void *dw, fp4_dtype dw_dtype,
+                            int64_t M, int64_t N, int64_t K, uint32_t rht_signs, uint64_t seed, uint64_t offset,
+                            const fp4_tensor *dyq_t, const fp4_tensor *xq_t, hipStream_t stream);
+
+/* A short static description of a status code. */
+FP4_API const char *fp4_status_string(fp4_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_AMD_H */

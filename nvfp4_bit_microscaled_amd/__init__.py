@@ -1,0 +1,187 @@
+"""Python binding of libnvfp4_amd.so, the gfx950 NVFP4 linear-layer library.
+
+Argument marshalling only: every step runs in the library's HIP kernels.  Torch
+supplies device memory and the current stream.  There is no fallback: if the
+library is not built, load() raises.  The functions keep the C names and the
+C argument order (see include/nvfp4_amd.h for the definitions).
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4_amd.so")
+
+FP4_BF16 = 0
+FP4_FP32 = 1
+
+Q_2D = 1 << 0
+Q_COLWISE = 1 << 1
+Q_RHT = 1 << 2
+Q_SR = 1 << 3
+Q_AMAX_GIVEN = 1 << 4
+
+STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_ALIGN", 4: "FP4_ERR_DTYPE",
+          5: "FP4_ERR_MODE", 6: "FP4_ERR_MISMATCH", 7: "FP4_ERR_HIP"}
+
+# every symbol the header declares
+EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_gemm", "fp4_linear_fprop", "fp4_linear_dgrad",
+           "fp4_linear_wgrad", "fp4_status_string")
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({status_string(code)})")
+
+
+class fp4_tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("amax", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("two_d", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load():
+    """Load the built library (raises if it is missing: build it with
+    nvfp4_bit_microscaled_amd/build.py or __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, u32, u64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32
+    tp = ctypes.POINTER(fp4_tensor)
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    sigs = {
+        "fp4_tensor_bytes": [i64, i64, i32, sz, sz],
+        "fp4_amax": [vp, i32, i64, i64, i64, u32, u32, vp, vp],
+        "fp4_quantize": [vp, i32, i64, i64, i64, u32, u32, u64, u64, tp, tp, vp],
+        "fp4_gemm": [tp, tp, vp, i32, i64, vp],
+        "fp4_linear_fprop": [vp, vp, i32, vp, i32, i64, i64, i64, tp, tp, tp, vp],
+        "fp4_linear_dgrad": [vp, i32, tp, vp, i32, i64, i64, i64, u64, u64, tp, vp],
+        "fp4_linear_wgrad": [vp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, tp, tp, vp],
+    }
+    for name, args in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.fp4_status_string.argtypes = [ctypes.c_int]
+    L.fp4_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return load().fp4_status_string(code).decode()
+
+
+def _check(fn, code):
+    if code != 0:
+        raise Fp4Error(fn, code)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FP4_BF16
+    if t.dtype == torch.float32:
+        return FP4_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ld(x: torch.Tensor) -> int:
+    assert x.dim() == 2 and x.stride(1) == 1, "2D row-major input expected"
+    return x.stride(0)
+
+
+class QTensor:
+    """Device buffers of one quantized logical tensor (codes, scales, amax)."""
+
+    def __init__(self, rows: int, cols: int, two_d: bool = False, device="cuda"):
+        nc, ns = tensor_bytes(rows, cols, two_d)
+        self.rows, self.cols, self.two_d = rows, cols, bool(two_d)
+        self.codes = torch.empty(nc, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(ns, dtype=torch.uint8, device=device)
+        self.amax = torch.zeros(1, dtype=torch.float32, device=device)
+        self._desc = fp4_tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.amax.data_ptr(), rows, cols,
+                                int(self.two_d))
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    def codes_2d(self):
+        return self.codes.view(self.rows, self.cols // 2)
+
+    def scales_2d(self):
+        r = (self.rows + 15) // 16 if self.two_d else self.rows
+        return self.scales.view(r, self.cols // 16)
+
+
+def tensor_bytes(rows: int, cols: int, two_d: bool = False):
+    nc, ns = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("fp4_tensor_bytes", load().fp4_tensor_bytes(rows, cols, int(two_d), ctypes.byref(nc), ctypes.byref(ns)))
+    return nc.value, ns.value
+
+
+def fp4_amax(x: torch.Tensor, flags: int, rht_signs: int, amax_out: torch.Tensor, stream=None):
+    _check("fp4_amax", load().fp4_amax(x.data_ptr(), _dtype(x), x.shape[0], x.shape[1], _ld(x), flags, rht_signs,
+                                       amax_out.data_ptr(), _stream(stream)))
+
+
+def fp4_quantize(x: torch.Tensor, flags: int, rht_signs: int, seed: int, offset: int, out: QTensor,
+                 out_t: QTensor = None, stream=None):
+    _check("fp4_quantize", load().fp4_quantize(x.data_ptr(), _dtype(x), x.shape[0], x.shape[1], _ld(x), flags,
+                                               rht_signs, seed, offset, out.desc,
+                                               out_t.desc if out_t is not None else None, _stream(stream)))
+
+
+def fp4_gemm(a: QTensor, b: QTensor, c: torch.Tensor, stream=None):
+    _check("fp4_gemm", load().fp4_gemm(a.desc, b.desc, c.data_ptr(), _dtype(c), c.stride(0), _stream(stream)))
+
+
+def fp4_linear_fprop(x, w, y, xq: QTensor, wq: QTensor, wq_t: QTensor = None, stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    assert x.dtype == w.dtype and x.is_contiguous() and w.is_contiguous() and y.is_contiguous()
+    _check("fp4_linear_fprop", load().fp4_linear_fprop(x.data_ptr(), w.data_ptr(), _dtype(x), y.data_ptr(), _dtype(y),
+                                                       M, N, K, xq.desc, wq.desc,
+                                                       wq_t.desc if wq_t is not None else None, _stream(stream)))
+
+
+def fp4_linear_dgrad(dy, wq_t: QTensor, dx, seed: int, offset: int, dyq: QTensor, stream=None):
+    M, N = dy.shape
+    K = dx.shape[1]
+    assert dy.is_contiguous() and dx.is_contiguous()
+    _check("fp4_linear_dgrad", load().fp4_linear_dgrad(dy.data_ptr(), _dtype(dy), wq_t.desc, dx.data_ptr(),
+                                                       _dtype(dx), M, N, K, seed, offset, dyq.desc, _stream(stream)))
+
+
+def fp4_linear_wgrad(dy, x, dw, rht_signs: int, seed: int, offset: int, dyq_t: QTensor, xq_t: QTensor, stream=None):
+    M, N = dy.shape
+    K = x.shape[1]
+    assert dy.dtype == x.dtype and dy.is_contiguous() and x.is_contiguous() and dw.is_contiguous()
+    _check("fp4_linear_wgrad", load().fp4_linear_wgrad(dy.data_ptr(), x.data_ptr(), _dtype(dy), dw.data_ptr(),
+                                                       _dtype(dw), M, N, K, rht_signs, seed, offset, dyq_t.desc,
+                                                       xq_t.desc, _stream(stream)))
+
+
+class LinearBuffers:
+    """Caller-owned quantized buffers for one linear layer y = x . w^T (M tokens,
+    K in-features, N out-features)."""
+
+    def __init__(self, M: int, N: int, K: int, device="cuda"):
+        self.xq = QTensor(M, K, device=device)
+        self.wq = QTensor(N, K, two_d=True, device=device)
+        self.wq_t = QTensor(K, N, two_d=True, device=device)
+        self.dyq = QTensor(M, N, device=device)
+        self.dyq_t = QTensor(N, M, device=device)
+        self.xq_t = QTensor(K, M, device=device)

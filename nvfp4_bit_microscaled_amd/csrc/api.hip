@@ -1,0 +1,166 @@
+// api.hip -- the extern "C" surface declared in include/nvfp4_amd.h: argument
+// checks (all before any enqueue), then the launchers.  The linear-layer calls
+// compose quantize and gemm exactly as the NVFP4-12B page's recipe assigns the
+// roles (paragraph 2): weights 2D-scaled, weight-gradient operands Hadamard
+// transformed, gradients stochastically rounded, everything else nearest-even.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace {
+
+fp4_status from_hip(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fp4_status check_tensor(const fp4_tensor *t, int64_t rows, int64_t cols, int32_t two_d) {
+  if (!t || !t->amax) return FP4_ERR_NULL;
+  if ((!t->codes || !t->scales) && rows > 0 && cols > 0) return FP4_ERR_NULL;  // empty tensors need no storage
+  if (t->rows != rows || t->cols != cols || (t->two_d != 0) != (two_d != 0)) return FP4_ERR_MISMATCH;
+  if (!aligned(t->codes, 16) || !aligned(t->scales, 8) || !aligned(t->amax, 4)) return FP4_ERR_ALIGN;
+  return FP4_OK;
+}
+
+fp4_status check_input(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld) {
+  if (dtype != FP4_BF16 && dtype != FP4_FP32) return FP4_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || ld < cols) return FP4_ERR_SHAPE;
+  if (!x && rows > 0 && cols > 0) return FP4_ERR_NULL;
+  // vector loads: 8 elements of a row at a time
+  if (cols % 8 != 0 || ld % 8 != 0 || !aligned(x, 16)) return FP4_ERR_ALIGN;
+  return FP4_OK;
+}
+
+fp4_status check_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
+                          const fp4_tensor *out, const fp4_tensor *out_t) {
+  const uint32_t known = FP4_Q_2D | FP4_Q_COLWISE | FP4_Q_RHT | FP4_Q_SR | FP4_Q_AMAX_GIVEN;
+  if (flags & ~known) return FP4_ERR_MODE;
+  const bool two_d = flags & FP4_Q_2D;
+  if (two_d && (flags & (FP4_Q_RHT | FP4_Q_SR))) return FP4_ERR_MODE;
+  if (out_t && !two_d) return FP4_ERR_MODE;
+  fp4_status s = check_input(x, dtype, rows, cols, ld);
+  if (s != FP4_OK) return s;
+  const bool colwise = flags & FP4_Q_COLWISE;
+  const int64_t lrows = colwise ? cols : rows, lcols = colwise ? rows : cols;
+  if (lcols % 16 != 0) return FP4_ERR_SHAPE;
+  if (two_d && lrows % 16 != 0) return FP4_ERR_SHAPE;
+  if ((flags & FP4_Q_RHT) && colwise && rows % 16 != 0) return FP4_ERR_SHAPE;
+  if ((s = check_tensor(out, lrows, lcols, two_d)) != FP4_OK) return s;
+  if (out_t && (s = check_tensor(out_t, lcols, lrows, 1)) != FP4_OK) return s;
+  return FP4_OK;
+}
+
+fp4_status check_gemm(const fp4_tensor *a, const fp4_tensor *b, const void *c, fp4_dtype c_dtype, int64_t ldc) {
+  if (!a || !b) return FP4_ERR_NULL;
+  if (c_dtype != FP4_BF16 && c_dtype != FP4_FP32) return FP4_ERR_DTYPE;
+  if (a->rows < 0 || b->rows < 0 || a->cols < 0 || a->cols != b->cols) return FP4_ERR_MISMATCH;
+  if (a->cols % 16 != 0) return FP4_ERR_SHAPE;
+  fp4_status s;
+  if ((s = check_tensor(a, a->rows, a->cols, a->two_d)) != FP4_OK) return s;
+  if ((s = check_tensor(b, b->rows, b->cols, b->two_d)) != FP4_OK) return s;
+  if ((a->two_d && a->rows % 16 != 0) || (b->two_d && b->rows % 16 != 0)) return FP4_ERR_SHAPE;
+  if (ldc < b->rows) return FP4_ERR_SHAPE;
+  if (!c && a->rows > 0 && b->rows > 0) return FP4_ERR_NULL;
+  if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+  return FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4_status fp4_tensor_bytes(int64_t rows, int64_t cols, int32_t two_d, size_t *codes_bytes, size_t *scales_bytes) {
+  if (!codes_bytes || !scales_bytes) return FP4_ERR_NULL;
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return FP4_ERR_SHAPE;
+  *codes_bytes = size_t(rows) * size_t(cols / 2);
+  *scales_bytes = size_t(two_d ? (rows + 15) / 16 : rows) * size_t(cols / 16);
+  return FP4_OK;
+}
+
+fp4_status fp4_amax(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
+                    uint32_t rht_signs, float *amax_out, hipStream_t stream) {
+  if (flags & ~(FP4_Q_COLWISE | FP4_Q_RHT)) return FP4_ERR_MODE;
+  fp4_status s = check_input(x, dtype, rows, cols, ld);
+  if (s != FP4_OK) return s;
+  if (!amax_out) return FP4_ERR_NULL;
+  if (flags & FP4_Q_RHT) {
+    const int64_t blocked = (flags & FP4_Q_COLWISE) ? rows : cols;
+    if (blocked % 16 != 0) return FP4_ERR_SHAPE;
+  }
+  return from_hip(nvfp4::launch_amax(x, dtype, rows, cols, ld, flags, rht_signs & 0xFFFFu, amax_out, stream));
+}
+
+fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
+                        uint32_t rht_signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
+                        const fp4_tensor *out_t, hipStream_t stream) {
+  fp4_status s = check_quantize(x, dtype, rows, cols, ld, flags, out, out_t);
+  if (s != FP4_OK) return s;
+  return from_hip(
+      nvfp4::launch_quantize(x, dtype, rows, cols, ld, flags, rht_signs & 0xFFFFu, seed, offset, out, out_t, stream));
+}
+
+fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
+                    hipStream_t stream) {
+  fp4_status s = check_gemm(a, b, c, c_dtype, ldc);
+  if (s != FP4_OK) return s;
+  return from_hip(nvfp4::launch_gemm(a, b, c, c_dtype, ldc, stream));
+}
+
+fp4_status fp4_linear_fprop(const void *x, const void *w, fp4_dtype dtype, void *y, fp4_dtype y_dtype, int64_t M,
+                            int64_t N, int64_t K, const fp4_tensor *xq, const fp4_tensor *wq,
+                            const fp4_tensor *wq_t, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
+  fp4_status s;
+  if ((s = check_quantize(x, dtype, M, K, K, 0, xq, nullptr)) != FP4_OK) return s;
+  if ((s = check_quantize(w, dtype, N, K, K, FP4_Q_2D, wq, wq_t)) != FP4_OK) return s;
+  if ((s = check_gemm(xq, wq, y, y_dtype, N)) != FP4_OK) return s;
+  hipError_t e = nvfp4::launch_quantize(x, dtype, M, K, K, 0, 0, 0, 0, xq, nullptr, stream);
+  if (e == hipSuccess) e = nvfp4::launch_quantize(w, dtype, N, K, K, FP4_Q_2D, 0, 0, 0, wq, wq_t, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm(xq, wq, y, y_dtype, N, stream);
+  return from_hip(e);
+}
+
+fp4_status fp4_linear_dgrad(const void *dy, fp4_dtype dtype, const fp4_tensor *wq_t, void *dx, fp4_dtype dx_dtype,
+                            int64_t M, int64_t N, int64_t K, uint64_t seed, uint64_t offset,
+                            const fp4_tensor *dyq, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
+  fp4_status s;
+  if ((s = check_quantize(dy, dtype, M, N, N, FP4_Q_SR, dyq, nullptr)) != FP4_OK) return s;
+  if ((s = check_tensor(wq_t, K, N, 1)) != FP4_OK) return s;
+  if ((s = check_gemm(dyq, wq_t, dx, dx_dtype, K)) != FP4_OK) return s;
+  hipError_t e = nvfp4::launch_quantize(dy, dtype, M, N, N, FP4_Q_SR, 0, seed, offset, dyq, nullptr, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm(dyq, wq_t, dx, dx_dtype, K, stream);
+  return from_hip(e);
+}
+
+fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dtype, void *dw, fp4_dtype dw_dtype,
+                            int64_t M, int64_t N, int64_t K, uint32_t rht_signs, uint64_t seed, uint64_t offset,
+                            const fp4_tensor *dyq_t, const fp4_tensor *xq_t, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
+  const uint32_t fdy = FP4_Q_COLWISE | FP4_Q_RHT | FP4_Q_SR, fx = FP4_Q_COLWISE | FP4_Q_RHT;
+  fp4_status s;
+  if ((s = check_quantize(dy, dtype, M, N, N, fdy, dyq_t, nullptr)) != FP4_OK) return s;
+  if ((s = check_quantize(x, dtype, M, K, K, fx, xq_t, nullptr)) != FP4_OK) return s;
+  if ((s = check_gemm(dyq_t, xq_t, dw, dw_dtype, K)) != FP4_OK) return s;
+  const uint32_t signs = rht_signs & 0xFFFFu;
+  hipError_t e = nvfp4::launch_quantize(dy, dtype, M, N, N, fdy, signs, seed, offset, dyq_t, nullptr, stream);
+  if (e == hipSuccess) e = nvfp4::launch_quantize(x, dtype, M, K, K, fx, signs, 0, 0, xq_t, nullptr, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm(dyq_t, xq_t, dw, dw_dtype, K, stream);
+  return from_hip(e);
+}
+
+const char *fp4_status_string(fp4_status status) {
+  switch (status) {
+    case FP4_OK: return "ok";
+    case FP4_ERR_NULL: return "a required pointer is NULL";
+    case FP4_ERR_SHAPE: return "bad size: negative, or not a multiple of 16 where blocks need it";
+    case FP4_ERR_ALIGN: return "a pointer or leading dimension breaks the required alignment";
+    case FP4_ERR_DTYPE: return "unknown dtype";
+    case FP4_ERR_MODE: return "unsupported combination of quantization flags";
+    case FP4_ERR_MISMATCH: return "descriptor sizes do not agree with the call";
+    case FP4_ERR_HIP: return "a HIP launch or runtime call failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

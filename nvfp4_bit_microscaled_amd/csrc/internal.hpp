@@ -1,0 +1,22 @@
+// internal.hpp -- launchers shared between the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/nvfp4_amd.h"
+
+namespace nvfp4 {
+
+__global__ void copy_f32_kernel(const float *src, float *dst);
+
+hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
+                       uint32_t signs, float *out, hipStream_t stream);
+
+hipError_t launch_quantize(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
+                           uint32_t signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
+                           const fp4_tensor *out_t, hipStream_t stream);
+
+hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
+                       hipStream_t stream);
+
+}  // namespace nvfp4

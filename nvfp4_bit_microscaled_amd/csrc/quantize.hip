@@ -1,0 +1,396 @@
+// quantize.hip -- tensor amax and NVFP4 quantization kernels for gfx950.
+//
+// Layouts (NVFP4-12B page, paragraph 2: 16-element blocks with an E4M3 scale
+// each and an FP32 scale per tensor; 2D scaling for weights; 16x16 random
+// Hadamard transforms for the weight-gradient operands; stochastic rounding for
+// gradients):
+//   rowwise  : the logical tensor is x [R][C]; a block is 16 consecutive
+//              elements of a row.  One thread owns one block, so the block amax
+//              needs no cross-lane traffic; a wave reads 2 KiB (bf16) and writes
+//              512 B of codes contiguously.
+//   colwise  : the logical tensor is x^T [C][R]; a block is 16 consecutive rows
+//              of one column of x.  A thread owns 8 adjacent columns of a 16-row
+//              slab: every load is a 16-byte row segment (a wave reads 1 KiB
+//              contiguous per row) and the transform runs down the registers.
+//   2D       : 16x16 tiles of x; 16 lanes own one tile (a lane per row), the tile
+//              amax is a 16-lane butterfly reduction, and the transposed codes
+//              are regrouped through LDS.
+// The tensor amax is a separate reduction pass (atomicMax on the bit pattern of
+// the non-negative float), zeroed by a one-thread kernel: no memset node.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Load 8 consecutive elements (16 bytes of bf16, 32 bytes of fp32) as floats.
+template <typename T>
+__device__ __forceinline__ void load8(const T *p, float v[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float v[8]) {
+  const uint4 q = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide max, then one atomic per workgroup.
+__device__ __forceinline__ void block_max_to(float v, float *out) {
+  __shared__ float part[kThreads / 64];
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = part[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, part[i]);
+    atomicMax(reinterpret_cast<unsigned int *>(out), __float_as_uint(m));
+  }
+}
+
+__global__ void zero_f32_kernel(float *p) { *p = 0.0f; }
+
+// Plain |x| max over [R][C] (row stride ld); 8 elements per thread-step.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_plain_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                             int64_t ld, float *out) {
+  const int64_t chunks_per_row = C / 8;
+  const int64_t total = R * chunks_per_row;
+  float m = 0.0f;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads) {
+    const int64_t r = i / chunks_per_row, c = (i - r * chunks_per_row) * 8;
+    float v[8];
+    load8(x + r * ld + c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+  }
+  block_max_to(m, out);
+}
+
+// amax after the Hadamard transform along rows (16 contiguous elements).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                                int64_t ld, uint32_t signs, float *out) {
+  const int64_t nkb = C / 16;
+  const int64_t total = R * nkb;
+  float m = 0.0f;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads) {
+    const int64_t r = i / nkb, c = (i - r * nkb) * 16;
+    float v[16];
+    load8(x + r * ld + c, v);
+    load8(x + r * ld + c + 8, v + 8);
+    rht16(v, signs);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+  }
+  block_max_to(m, out);
+}
+
+// amax after the Hadamard transform down columns (16 consecutive rows of x).
+// A thread owns 8 adjacent columns of one 16-row slab.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                                int64_t ld, uint32_t signs, float *out) {
+  const int64_t cchunks = C / 8, slabs = R / 16;
+  const int64_t total = cchunks * slabs;
+  float m = 0.0f;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads) {
+    const int64_t s = i / cchunks, c = (i - s * cchunks) * 8;
+    float v[16][8];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load8(x + (s * 16 + r) * ld + c, v[r]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) col[r] = v[r][j];
+      rht16(col, signs);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, __builtin_fabsf(col[r]));
+    }
+  }
+  block_max_to(m, out);
+}
+
+// Rowwise 1D quantization: one thread per 16-block.  grid.x covers the blocks of a
+// row, grid.y strides over rows.
+template <typename T, bool RHT, bool SR>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                             int64_t ld, uint32_t signs, uint64_t seed,
+                                                             uint64_t offset, const float *__restrict__ amax_p,
+                                                             uint8_t *__restrict__ codes,
+                                                             uint8_t *__restrict__ scales) {
+  const int64_t nkb = C / 16;
+  const int64_t kb = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (kb >= nkb) return;
+  const float s_enc = encode_scale(*amax_p);
+  for (int64_t r = blockIdx.y; r < R; r += gridDim.y) {
+    float v[16];
+    load8(x + r * ld + kb * 16, v);
+    load8(x + r * ld + kb * 16 + 8, v + 8);
+    if (RHT) rht16(v, signs);
+    float amax_b = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, __builtin_fabsf(v[j]));
+    uint32_t sc;
+    float mult;
+    block_scale(amax_b, s_enc, sc, mult);
+    uint2 packed;
+    if (SR) {
+      uint32_t rb[8];
+      sr_bits16(uint64_t(r) * uint64_t(C) + uint64_t(kb) * 16u, seed, offset, rb);
+      packed = encode16_sr(v, mult, rb);
+    } else {
+      packed = encode16_rne(v, mult);
+    }
+    *reinterpret_cast<uint2 *>(codes + r * (C / 2) + kb * 8) = packed;
+    scales[r * nkb + kb] = uint8_t(sc);
+  }
+}
+
+// Columnwise 1D quantization (logical tensor x^T, blocks down the columns of x).
+// A workgroup covers 512 columns; each of its 4 waves takes one 16-row slab per
+// step, lane l owning columns 8l..8l+7, and walks kSlabsPerBlock slabs so that
+// each logical row receives kSlabsPerBlock*8 contiguous code bytes.
+constexpr int kSlabsPerBlock = 8;
+
+template <typename T, bool RHT, bool SR>
+__global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                             int64_t ld, uint32_t signs, uint64_t seed,
+                                                             uint64_t offset, const float *__restrict__ amax_p,
+                                                             uint8_t *__restrict__ codes,
+                                                             uint8_t *__restrict__ scales) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = int64_t(blockIdx.x) * 512 + lane * 8;
+  if (c0 >= C) return;
+  const int64_t nslab = R / 16;  // logical K = R, blocks per logical row = R/16
+  const float s_enc = encode_scale(*amax_p);
+  for (int64_t sb = int64_t(blockIdx.y) * kSlabsPerBlock; sb < nslab; sb += int64_t(gridDim.y) * kSlabsPerBlock) {
+    for (int it = wave; it < kSlabsPerBlock; it += kThreads / 64) {
+      const int64_t s = sb + it;
+      if (s >= nslab) break;
+      float v[16][8];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) load8(x + (s * 16 + r) * ld + c0, v[r]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float col[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) col[r] = v[r][j];
+        if (RHT) rht16(col, signs);
+        float amax_b = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) amax_b = fmaxf(amax_b, __builtin_fabsf(col[r]));
+        uint32_t sc;
+        float mult;
+        block_scale(amax_b, s_enc, sc, mult);
+        const int64_t lrow = c0 + j;  // logical row = column of x
+        uint2 packed;
+        if (SR) {
+          uint32_t rb[8];
+          sr_bits16(uint64_t(lrow) * uint64_t(R) + uint64_t(s) * 16u, seed, offset, rb);
+          packed = encode16_sr(col, mult, rb);
+        } else {
+          packed = encode16_rne(col, mult);
+        }
+        *reinterpret_cast<uint2 *>(codes + lrow * (R / 2) + s * 8) = packed;
+        scales[lrow * nslab + s] = uint8_t(sc);
+      }
+    }
+  }
+}
+
+// 2D (16x16 tile) nearest-even quantization of x [R][C] (R, C multiples of 16).
+// Writes the direct layout (codes [R][C/2], scales [R/16][C/16]) to d_* and/or the
+// transposed layout (codes [C][R/2], scales [C/16][R/16]) to t_*; either may be null.
+// A wave covers 4 tiles side by side; lane = 16 * tile + row-in-tile.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quant_2d_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                           int64_t ld, const float *__restrict__ amax_p,
+                                                           uint8_t *__restrict__ d_codes,
+                                                           uint8_t *__restrict__ d_scales,
+                                                           uint8_t *__restrict__ t_codes,
+                                                           uint8_t *__restrict__ t_scales) {
+  __shared__ uint8_t tcodes[kThreads / 16][16][17];  // per tile: [row][col] one code per byte (+1 pad)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile_in_wave = lane >> 4, row = lane & 15;
+  const int tile_slot = wave * 4 + tile_in_wave;
+  const int64_t tiles_c = C / 16, tiles_r = R / 16;
+  const int64_t tc = int64_t(blockIdx.x) * 16 + tile_slot;  // 16 tiles per workgroup along columns
+  const float s_enc = encode_scale(*amax_p);
+  for (int64_t tr = blockIdx.y; tr < tiles_r; tr += gridDim.y) {
+    const bool active = tc < tiles_c;
+    float v[16];
+    float m = 0.0f;
+    if (active) {
+      const T *p = x + (tr * 16 + row) * ld + tc * 16;
+      load8(p, v);
+      load8(p + 8, v + 8);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+    }
+    // amax over the 16 lanes of this tile (xor within the 16-lane group)
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    uint32_t sc = 0;
+    float mult = 0.0f;
+    block_scale(m, s_enc, sc, mult);
+    if (active) {
+      const uint2 packed = encode16_rne(v, mult);
+      if (d_codes) {
+        *reinterpret_cast<uint2 *>(d_codes + (tr * 16 + row) * (C / 2) + tc * 8) = packed;
+        if (row == 0) d_scales[tr * tiles_c + tc] = uint8_t(sc);
+      }
+      if (t_codes) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t w = j < 8 ? packed.x : packed.y;
+          tcodes[tile_slot][row][j] = uint8_t((w >> (4 * (j & 7))) & 15u);
+        }
+      }
+    }
+    if (t_codes) {
+      __syncthreads();
+      if (active) {
+        // lane `row` now assembles column `row` of the tile: logical row tc*16+row of x^T
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w0 |= uint32_t(tcodes[tile_slot][i][row]) << (4 * i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w1 |= uint32_t(tcodes[tile_slot][8 + i][row]) << (4 * i);
+        *reinterpret_cast<uint2 *>(t_codes + (tc * 16 + row) * (R / 2) + tr * 8) = make_uint2(w0, w1);
+        if (row == 0) t_scales[tc * tiles_r + tr] = uint8_t(sc);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return unsigned(g);
+}
+
+template <typename T>
+hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, float *out,
+                     hipStream_t stream) {
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, out);
+  const int64_t cap = 256 * 16;  // 16 workgroups per CU are plenty for a streaming reduction
+  if (R == 0 || C == 0) return hipGetLastError();
+  if (!(flags & FP4_Q_RHT)) {
+    hipLaunchKernelGGL(amax_plain_kernel<T>, dim3(grid_for(R * (C / 8), kThreads * 4, cap)), dim3(kThreads), 0,
+                       stream, x, R, C, ld, out);
+  } else if (flags & FP4_Q_COLWISE) {
+    hipLaunchKernelGGL(amax_rht_cols_kernel<T>, dim3(grid_for((R / 16) * (C / 8), kThreads, cap)), dim3(kThreads),
+                       0, stream, x, R, C, ld, signs, out);
+  } else {
+    hipLaunchKernelGGL(amax_rht_rows_kernel<T>, dim3(grid_for(R * (C / 16), kThreads * 2, cap)), dim3(kThreads),
+                       0, stream, x, R, C, ld, signs, out);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, bool RHT, bool SR>
+void launch_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
+                 const fp4_tensor *out, hipStream_t stream) {
+  const int64_t nkb = C / 16;
+  dim3 grid(unsigned((nkb + kThreads - 1) / kThreads), unsigned(R < 65535 ? R : 65535));
+  hipLaunchKernelGGL((quant_rows_kernel<T, RHT, SR>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, seed,
+                     offset, out->amax, out->codes, out->scales);
+}
+
+template <typename T, bool RHT, bool SR>
+void launch_cols(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
+                 const fp4_tensor *out, hipStream_t stream) {
+  const int64_t nslab = R / 16;
+  const int64_t ys = (nslab + kSlabsPerBlock - 1) / kSlabsPerBlock;
+  dim3 grid(unsigned((C + 511) / 512), unsigned(ys < 65535 ? ys : 65535));
+  hipLaunchKernelGGL((quant_cols_kernel<T, RHT, SR>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, seed,
+                     offset, out->amax, out->codes, out->scales);
+}
+
+template <typename T>
+hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, uint64_t seed,
+                         uint64_t offset, const fp4_tensor *out, const fp4_tensor *out_t, hipStream_t stream) {
+  if (!(flags & FP4_Q_AMAX_GIVEN)) {
+    hipError_t e = amax_impl(x, R, C, ld, flags, signs, out->amax, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (R == 0 || C == 0) return hipGetLastError();
+  const bool rht = flags & FP4_Q_RHT, sr = flags & FP4_Q_SR;
+  if (flags & FP4_Q_2D) {
+    // direct layout is x's; with COLWISE the logical tensor is x^T, so `out` takes
+    // the transposed layout and `out_t` the direct one.
+    uint8_t *dc = nullptr, *ds = nullptr, *tcp = nullptr, *tsp = nullptr;
+    const fp4_tensor *direct = (flags & FP4_Q_COLWISE) ? out_t : out;
+    const fp4_tensor *transp = (flags & FP4_Q_COLWISE) ? out : out_t;
+    if (direct) { dc = direct->codes; ds = direct->scales; }
+    if (transp) { tcp = transp->codes; tsp = transp->scales; }
+    const int64_t tiles_c = C / 16, tiles_r = R / 16;
+    dim3 grid(unsigned((tiles_c + 15) / 16), unsigned(tiles_r < 65535 ? tiles_r : 65535));
+    hipLaunchKernelGGL(quant_2d_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, out->amax, dc, ds, tcp,
+                       tsp);
+    if (out_t && out_t->amax != out->amax) {
+      hipLaunchKernelGGL(copy_f32_kernel, dim3(1), dim3(1), 0, stream, out->amax, out_t->amax);
+    }
+  } else if (flags & FP4_Q_COLWISE) {
+    if (rht && sr) launch_cols<T, true, true>(x, R, C, ld, signs, seed, offset, out, stream);
+    else if (rht) launch_cols<T, true, false>(x, R, C, ld, signs, seed, offset, out, stream);
+    else if (sr) launch_cols<T, false, true>(x, R, C, ld, signs, seed, offset, out, stream);
+    else launch_cols<T, false, false>(x, R, C, ld, signs, seed, offset, out, stream);
+  } else {
+    if (rht && sr) launch_rows<T, true, true>(x, R, C, ld, signs, seed, offset, out, stream);
+    else if (rht) launch_rows<T, true, false>(x, R, C, ld, signs, seed, offset, out, stream);
+    else if (sr) launch_rows<T, false, true>(x, R, C, ld, signs, seed, offset, out, stream);
+    else launch_rows<T, false, false>(x, R, C, ld, signs, seed, offset, out, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+__global__ void copy_f32_kernel(const float *src, float *dst) { *dst = *src; }
+
+hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
+                       uint32_t signs, float *out, hipStream_t stream) {
+  if (dtype == FP4_BF16)
+    return amax_impl(static_cast<const uint16_t *>(x), R, C, ld, flags, signs, out, stream);
+  return amax_impl(static_cast<const float *>(x), R, C, ld, flags, signs, out, stream);
+}
+
+hipError_t launch_quantize(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
+                           uint32_t signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
+                           const fp4_tensor *out_t, hipStream_t stream) {
+  if (dtype == FP4_BF16)
+    return quantize_impl(static_cast<const uint16_t *>(x), R, C, ld, flags, signs, seed, offset, out, out_t, stream);
+  return quantize_impl(static_cast<const float *>(x), R, C, ld, flags, signs, seed, offset, out, out_t, stream);
+}
+
+}  // namespace nvfp4

@@ -67,7 +67,8 @@ def lib():
 
 
 def default_threads() -> int:
-    return int(os.environ.get("NVO_THREADS", os.cpu_count() or 1))
+    n = os.environ.get("NVO_THREADS") or os.environ.get("OMP_NUM_THREADS")
+    return int(n) if n else min(16, os.cpu_count() or 1)
 
 
 def _ptr(a, ctype):

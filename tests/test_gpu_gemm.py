@@ -1,0 +1,114 @@
+"""GPU parity of fp4_gemm: operands quantized by the oracle are uploaded, the GPU
+GEMM runs through the C ABI, and every output is checked against the binary64
+product of the oracle's dequantized operands within 1e-5 * sum|a b|."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import check_gemm, upload_q
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_operands(oracle, M, N, K, seed, a2d=False, b2d=False, a_kind="normal", b_std=0.02):
+    rng = np.random.default_rng(seed)
+    if a_kind == "laplace":
+        xa = workloads.laplace(rng, (M, K))
+    else:
+        xa = workloads.normal(rng, (M, K), outlier_frac=0.001 if a_kind == "outliers" else 0.0)
+    xb = workloads.normal(rng, (N, K), std=b_std)
+    return oracle.quantize(xa, two_d=a2d), oracle.quantize(xb, two_d=b2d)
+
+
+def run_gemm(fp4, oracle, qa, qb, out_dtype):
+    a, b = upload_q(fp4, qa), upload_q(fp4, qb)
+    c = torch.full((qa.rows, qb.rows), float("nan"), dtype=out_dtype, device="cuda")
+    fp4.fp4_gemm(a, b, c)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy()
+
+
+CASES = [
+    # (M, N, K, a2d, b2d): tile multiples, ragged M/N, K % 128 != 0, K % 32 == 16
+    (256, 256, 256, False, False),
+    (300, 200, 272, False, False),
+    (512, 384, 1040, False, True),
+    (129, 256, 4096, False, True),
+    (129, 257, 4096, False, False),
+    (1024, 1024, 4096, True, True),
+    (64, 16, 16, False, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:3])) + ("_a2d" if c[3] else "") +
+                         ("_b2d" if c[4] else ""))
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_gemm_parity(fp4, oracle, case, out_dtype):
+    M, N, K, a2d, b2d = case
+    qa, qb = oracle_operands(oracle, M, N, K, seed=M + N + K, a2d=a2d, b2d=b2d, a_kind="outliers")
+    y = run_gemm(fp4, oracle, qa, qb, out_dtype)
+    y_ref, bound = oracle.gemm_ref(qa, qb)
+    check_gemm(y, y_ref, bound, out_dtype == torch.bfloat16, f"gemm {case}")
+
+
+def test_tiny_config(fp4, oracle):
+    """X, W 256x256 fp32 N(0,1) seed 0, both 1D nearest-even on the GPU (bit-exact
+    against the oracle), Y = X . W^T in fp32."""
+    from parity import assert_q_equal, dev, host_q
+    x, w = workloads.make_tiny(0)
+    qx, qw = fp4.QTensor(256, 256), fp4.QTensor(256, 256)
+    fp4.fp4_quantize(dev(x), 0, 0, 0, 0, qx)
+    fp4.fp4_quantize(dev(w), 0, 0, 0, 0, qw)
+    y = torch.empty(256, 256, dtype=torch.float32, device="cuda")
+    fp4.fp4_gemm(qx, qw, y)
+    ox, ow = oracle.quantize(x.numpy()), oracle.quantize(w.numpy())
+    assert_q_equal(host_q(qx), ox, "tiny X")
+    assert_q_equal(host_q(qw), ow, "tiny W")
+    y_ref, bound = oracle.gemm_ref(ox, ow)
+    check_gemm(y.cpu().numpy(), y_ref, bound, False, "tiny")
+
+
+def test_one_hot_and_exact_products(fp4, oracle):
+    """K = 16, one block, A rows one-hot: the accumulator holds one exact product,
+    so the only roundings are the epilogue's two (gA*gB, then acc*g): within 2 ulp."""
+    xb = np.random.default_rng(4).standard_normal((48, 16)).astype(np.float32)
+    xa = np.zeros((32, 16), dtype=np.float32)
+    for m in range(32):
+        xa[m, m % 16] = 6.0
+    qa, qb = oracle.quantize(xa), oracle.quantize(xb)
+    y = run_gemm(fp4, oracle, qa, qb, torch.float32)
+    y_ref, _ = oracle.gemm_ref(qa, qb)
+    assert np.all(np.abs(y - y_ref) <= 2.0**-22 * np.abs(y_ref))
+
+
+def test_zero_k_and_zero_operands(fp4, oracle):
+    qa, qb = oracle_operands(oracle, 64, 80, 128, seed=1)
+    qa.codes[:] = 0
+    y = run_gemm(fp4, oracle, qa, qb, torch.float32)
+    assert np.all(y == 0.0)
+    # K = 0: an empty sum
+    a, b = fp4.QTensor(32, 0), fp4.QTensor(48, 0)
+    c = torch.full((32, 48), 7.0, device="cuda")
+    fp4.fp4_gemm(a, b, c)
+    torch.cuda.synchronize()
+    assert torch.all(c == 0)
+    # M = 0: nothing to do
+    e = fp4.QTensor(0, 64)
+    c2 = torch.empty(0, 48, device="cuda")
+    fp4.fp4_gemm(e, fp4.QTensor(48, 64), c2)
+
+
+def test_ldc_larger_than_n(fp4, oracle):
+    qa, qb = oracle_operands(oracle, 100, 60, 256, seed=2)
+    a, b = upload_q(fp4, qa), upload_q(fp4, qb)
+    big = torch.full((100, 96), -1.0, device="cuda")
+    c = big[:, :60]
+    from nvfp4_bit_microscaled_amd import load
+    st = load().fp4_gemm(a.desc, b.desc, c.data_ptr(), 1, 96, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    y = big.cpu().numpy()
+    assert np.all(y[:, 60:] == -1.0)
+    y_ref, bound = oracle.gemm_ref(qa, qb)
+    check_gemm(y[:, :60], y_ref, bound, False, "ldc")

@@ -1,0 +1,168 @@
+"""GPU parity of the three linear-layer passes, end to end through the C ABI:
+every intermediate quantized operand bit-exact against the oracle, every output
+within the GEMM tolerance of the binary64 reference built from the oracle's own
+quantization.  Full-size workloads are checked on sampled output rows (and all
+of their quantized operand rows); smaller ones in full."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import assert_q_equal, check_gemm, dev, host_q
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fprop(fp4, x_cpu, w_cpu, y_dtype):
+    M, K = x_cpu.shape
+    N = w_cpu.shape[0]
+    bufs = fp4.LinearBuffers(M, N, K)
+    y = torch.empty(M, N, dtype=y_dtype, device="cuda")
+    fp4.fp4_linear_fprop(dev(x_cpu), dev(w_cpu), y, bufs.xq, bufs.wq, bufs.wq_t)
+    torch.cuda.synchronize()
+    return bufs, y
+
+
+def sample_rows(n, count, seed):
+    if n <= count:
+        return np.arange(n)
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(n, size=count, replace=False))
+
+
+def pick(oracle, q, rows):
+    """The given logical rows of an oracle-quantized 1D tensor."""
+    return oracle.QTensor(q.codes[rows], q.scales[rows], q.amax, len(rows), q.K, False)
+
+
+def check_rows(oracle, x_f32, gpu_q, rows, **kw):
+    """Quantize only the chosen logical rows with the oracle (with the whole-tensor
+    amax), compare them with the GPU's rows bit for bit, and return the oracle's."""
+    amax = oracle.amax(x_f32, colwise=kw.get("colwise", False), rht=kw.get("rht", False), signs=kw.get("signs", 0))
+    codes, scales, g_amax = gpu_q
+    assert g_amax == amax
+    parts = [oracle.quantize(x_f32, amax_in=amax, rows=(int(r), int(r) + 1), **kw) for r in rows]
+    o_codes = np.concatenate([o.codes for o in parts])
+    o_scales = np.concatenate([o.scales for o in parts])
+    bad = [int(r) for i, r in enumerate(rows)
+           if not (np.array_equal(codes[r], o_codes[i]) and np.array_equal(scales[r], o_scales[i]))]
+    assert not bad, f"rows differing from the oracle: {bad[:8]}"
+    return oracle.QTensor(o_codes, o_scales, amax, len(rows), parts[0].K, False)
+
+
+@pytest.mark.parametrize("shape", [(256, 128, 512), (1008, 272, 400)], ids=lambda s: "x".join(map(str, s)))
+def test_small_linear_all_passes(fp4, oracle, shape):
+    M, N, K = shape
+    inp = workloads.make_linear_inputs(workloads.Linear("t", M, N, K), seed=M + N + K)
+    xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
+    # fprop
+    bufs, y = run_fprop(fp4, inp.x, inp.w, torch.bfloat16)
+    oxq, owq = oracle.linear_fprop(xf, wf)
+    assert_q_equal(host_q(bufs.xq), oxq, "xq")
+    assert_q_equal(host_q(bufs.wq), owq, "wq")
+    y_ref, bound = oracle.gemm_ref(oxq, owq)
+    check_gemm(y.float().cpu().numpy(), y_ref, bound, True, "fprop")
+    # dgrad
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    fp4.fp4_linear_dgrad(dev(inp.dy), bufs.wq_t, dx, workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, bufs.dyq)
+    odyq, owtq = oracle.linear_dgrad(dyf, wf, workloads.SR_SEED, workloads.SR_OFFSET_DGRAD)
+    assert_q_equal(host_q(bufs.wq_t), owtq, "wq_t")
+    assert_q_equal(host_q(bufs.dyq), odyq, "dyq")
+    y_ref, bound = oracle.gemm_ref(odyq, owtq)
+    check_gemm(dx.float().cpu().numpy(), y_ref, bound, True, "dgrad")
+    # wgrad
+    dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    fp4.fp4_linear_wgrad(dev(inp.dy), dev(inp.x), dw, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_WGRAD,
+                         bufs.dyq_t, bufs.xq_t)
+    odytq, oxtq = oracle.linear_wgrad(dyf, xf, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_WGRAD)
+    assert_q_equal(host_q(bufs.dyq_t), odytq, "dyq_t")
+    assert_q_equal(host_q(bufs.xq_t), oxtq, "xq_t")
+    y_ref, bound = oracle.gemm_ref(odytq, oxtq)
+    check_gemm(dw.cpu().numpy(), y_ref, bound, False, "wgrad")
+    # the unquantized product, for the record (not a gate): relative Frobenius error
+    exact = dyf.astype(np.float64).T @ xf.astype(np.float64)
+    rel = np.linalg.norm(dw.cpu().numpy() - exact) / np.linalg.norm(exact)
+    assert rel < 0.3
+
+
+def test_fprop_8k_config(fp4, oracle):
+    """X 8192x4096 N(0,1) with 0.1% x50 outliers, W 4096x4096 N(0, 0.02^2) 2D, Y bf16.
+    Quantized operands in full; Y on 64 sampled rows."""
+    wl = workloads.WORKLOADS["fprop_8k"]
+    lin = wl.linears[0]
+    inp = workloads.make_linear_inputs(lin, seed=0, x_outliers=True, with_dy=False)
+    xf, wf = workloads.widen(inp.x), workloads.widen(inp.w)
+    bufs, y = run_fprop(fp4, inp.x, inp.w, torch.bfloat16)
+    oxq, owq = oracle.linear_fprop(xf, wf)
+    assert_q_equal(host_q(bufs.xq), oxq, "xq")
+    assert_q_equal(host_q(bufs.wq), owq, "wq")
+    rows = sample_rows(lin.M, 64, 1)
+    y_ref, bound = oracle.gemm_ref(pick(oracle, oxq, rows), owq)
+    check_gemm(y.float().cpu().numpy()[rows], y_ref, bound, True, "fprop 8k")
+
+
+def test_wgrad_8k_config(fp4, oracle):
+    """dY 8192x4096 Laplace(0, 1e-3), X 8192x4096 N(0,1), RHT along the 8192 tokens,
+    dY stochastically rounded, dW fp32 4096x4096; sampled dW rows."""
+    lin = workloads.WORKLOADS["wgrad_8k"].linears[0]
+    inp = workloads.make_linear_inputs(lin, seed=0)
+    xf, dyf = workloads.widen(inp.x), workloads.widen(inp.dy)
+    M, N, K = lin.M, lin.N, lin.K
+    bufs = fp4.LinearBuffers(M, N, K)
+    dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    fp4.fp4_linear_wgrad(dev(inp.dy), dev(inp.x), dw, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_WGRAD,
+                         bufs.dyq_t, bufs.xq_t)
+    torch.cuda.synchronize()
+    odytq, oxtq = oracle.linear_wgrad(dyf, xf, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_WGRAD)
+    assert_q_equal(host_q(bufs.dyq_t), odytq, "dyq_t")
+    assert_q_equal(host_q(bufs.xq_t), oxtq, "xq_t")
+    rows = sample_rows(N, 64, 2)
+    y_ref, bound = oracle.gemm_ref(pick(oracle, odytq, rows), oxtq)
+    check_gemm(dw.cpu().numpy()[rows], y_ref, bound, False, "wgrad 8k")
+
+
+def test_mlp_up_12b_sampled(fp4, oracle):
+    """The 12B-hybrid-like MLP up-projection at full size (X 16384x5120, W 20480x5120,
+    dY 16384x20480): all three passes in the launch configuration the benchmark
+    times; quantized operands and outputs checked on sampled rows."""
+    lin = workloads.WORKLOADS["mlp_up_12b"].linears[0]
+    M, N, K = lin.M, lin.N, lin.K
+    inp = workloads.make_linear_inputs(lin, seed=0)
+    x, w, dy = dev(inp.x), dev(inp.w), dev(inp.dy)
+    bufs = fp4.LinearBuffers(M, N, K)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    fp4.fp4_linear_fprop(x, w, y, bufs.xq, bufs.wq, bufs.wq_t)
+    fp4.fp4_linear_dgrad(dy, bufs.wq_t, dx, workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, bufs.dyq)
+    fp4.fp4_linear_wgrad(dy, x, dw, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_WGRAD, bufs.dyq_t, bufs.xq_t)
+    torch.cuda.synchronize()
+    del x, w, dy
+    xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
+    sr, off_d, off_w = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
+
+    # fprop: sampled rows of X's quantization; W (2D) in full; sampled rows of Y
+    rows = sample_rows(M, 24, 3)
+    oxs = check_rows(oracle, xf, host_q(bufs.xq), rows)
+    owq = oracle.quantize(wf, two_d=True)
+    assert_q_equal(host_q(bufs.wq), owq, "wq")
+    y_ref, bound = oracle.gemm_ref(oxs, owq)
+    check_gemm(y.float().cpu().numpy()[rows], y_ref, bound, True, "fprop 12B")
+    del owq, y
+
+    # dgrad: sampled rows of dY's SR quantization; W^T (2D) in full; sampled dX rows
+    ods = check_rows(oracle, dyf, host_q(bufs.dyq), rows, sr=True, seed=sr, offset=off_d)
+    owtq = oracle.quantize(wf, two_d=True, colwise=True)
+    assert_q_equal(host_q(bufs.wq_t), owtq, "wq_t")
+    y_ref, bound = oracle.gemm_ref(ods, owtq)
+    check_gemm(dx.float().cpu().numpy()[rows], y_ref, bound, True, "dgrad 12B")
+    del owtq, dx
+
+    # wgrad: sampled rows of dY^T (RHT+SR); X^T (RHT) in full; sampled dW rows
+    wrows = sample_rows(N, 16, 4)
+    odt = check_rows(oracle, dyf, host_q(bufs.dyq_t), wrows, colwise=True, rht=True, sr=True, signs=inp.signs,
+                     seed=sr, offset=off_w)
+    oxtq = oracle.quantize(xf, colwise=True, rht=True, signs=inp.signs)
+    assert_q_equal(host_q(bufs.xq_t), oxtq, "xq_t")
+    y_ref, bound = oracle.gemm_ref(odt, oxtq)
+    check_gemm(dw.cpu().numpy()[wrows], y_ref, bound, False, "wgrad 12B")

@@ -1,0 +1,126 @@
+"""GPU parity of the quantizer: fp4_amax / fp4_quantize through the C ABI against
+the oracle on the same seeded inputs, bit for bit (codes, E4M3 scales, amax)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import assert_q_equal, dev, host_q
+
+pytestmark = pytest.mark.gpu
+
+
+def make_x(shape, seed, kind="normal", std=1.0, dtype=torch.bfloat16):
+    return workloads.random_matrix(shape, seed, kind=kind, std=std, dtype=dtype)
+
+
+def run_case(fp4, oracle, x_cpu, flags, signs=0, seed=0, offset=0):
+    colwise = bool(flags & fp4.Q_COLWISE)
+    two_d = bool(flags & fp4.Q_2D)
+    R, C = x_cpu.shape
+    lrows, lcols = (C, R) if colwise else (R, C)
+    x = dev(x_cpu)
+    q = fp4.QTensor(lrows, lcols, two_d)
+    q_t = fp4.QTensor(lcols, lrows, True) if two_d else None
+    fp4.fp4_quantize(x, flags, signs, seed, offset, q, q_t)
+    xf = workloads.widen(x_cpu)
+    ora = oracle.quantize(xf, two_d=two_d, colwise=colwise, rht=bool(flags & fp4.Q_RHT), sr=bool(flags & fp4.Q_SR),
+                          signs=signs, seed=seed, offset=offset)
+    assert_q_equal(host_q(q), ora, f"flags={flags} shape={tuple(x_cpu.shape)}")
+    if two_d:
+        ora_t = oracle.quantize(xf, two_d=True, colwise=not colwise)
+        assert_q_equal(host_q(q_t), ora_t, f"transposed flags={flags} shape={tuple(x_cpu.shape)}")
+    return q
+
+
+ROW_SHAPES = [(1, 16), (333, 272), (64, 4096), (257, 1040)]
+COL_SHAPES = [(16, 8), (784, 1000), (4096, 64), (272, 520)]
+TILE_SHAPES = [(16, 16), (272, 400), (1024, 4096), (48, 2064)]
+
+
+@pytest.mark.parametrize("shape", ROW_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("mode", ["rne", "sr", "rht", "rht_sr"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_rowwise(fp4, oracle, shape, mode, dtype):
+    flags = {"rne": 0, "sr": fp4.Q_SR, "rht": fp4.Q_RHT, "rht_sr": fp4.Q_RHT | fp4.Q_SR}[mode]
+    x = make_x(shape, seed=shape[0] * 7 + shape[1], dtype=dtype)
+    run_case(fp4, oracle, x, flags, signs=0xA5C3, seed=0x1234_5678_9ABC_DEF0, offset=3)
+
+
+@pytest.mark.parametrize("shape", COL_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("mode", ["rne", "sr", "rht", "rht_sr"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_colwise(fp4, oracle, shape, mode, dtype):
+    flags = fp4.Q_COLWISE | {"rne": 0, "sr": fp4.Q_SR, "rht": fp4.Q_RHT, "rht_sr": fp4.Q_RHT | fp4.Q_SR}[mode]
+    x = make_x(shape, seed=shape[0] * 3 + shape[1], kind="laplace", std=1e-3, dtype=dtype)
+    run_case(fp4, oracle, x, flags, signs=0x5A3C, seed=7, offset=2)
+
+
+@pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("colwise", [False, True], ids=["direct", "colwise"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_two_d(fp4, oracle, shape, colwise, dtype):
+    flags = fp4.Q_2D | (fp4.Q_COLWISE if colwise else 0)
+    x = make_x(shape, seed=shape[0] + shape[1], std=0.02, dtype=dtype)
+    run_case(fp4, oracle, x, flags)
+
+
+@pytest.mark.parametrize("flags_name", ["plain", "rht_rows", "rht_cols"])
+def test_amax(fp4, oracle, flags_name):
+    flags = {"plain": 0, "rht_rows": fp4.Q_RHT, "rht_cols": fp4.Q_RHT | fp4.Q_COLWISE}[flags_name]
+    x_cpu = make_x((1008, 2064), seed=5, kind="outliers")
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    fp4.fp4_amax(dev(x_cpu), flags, 0x1357, out)
+    got = float(out.cpu()[0])
+    want = oracle.amax(workloads.widen(x_cpu), colwise=bool(flags & fp4.Q_COLWISE), rht=bool(flags & fp4.Q_RHT),
+                       signs=0x1357)
+    assert got == want
+
+
+def test_amax_given_skips_the_pass(fp4, oracle):
+    """With FP4_Q_AMAX_GIVEN the caller's amax is used as is (here: twice the true amax)."""
+    x_cpu = make_x((128, 256), seed=9)
+    xf = workloads.widen(x_cpu)
+    a = 2.0 * oracle.amax(xf)
+    q = fp4.QTensor(128, 256)
+    q.amax.fill_(a)
+    fp4.fp4_quantize(dev(x_cpu), fp4.Q_AMAX_GIVEN, 0, 0, 0, q)
+    assert_q_equal(host_q(q), oracle.quantize(xf, amax_in=a), "amax given")
+
+
+def test_zero_input(fp4, oracle):
+    x_cpu = torch.zeros(64, 256, dtype=torch.bfloat16)
+    for flags in (0, fp4.Q_SR, fp4.Q_COLWISE | fp4.Q_RHT | fp4.Q_SR, fp4.Q_2D):
+        run_case(fp4, oracle, x_cpu, flags, signs=0xFFFF, seed=1, offset=1)
+
+
+def test_scale_underflow_and_saturation(fp4, oracle):
+    """Rows spanning 40 binades: blocks whose scale underflows to 0 (all codes 0),
+    subnormal E4M3 scales, and the saturating tensor maximum."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((96, 512)).astype(np.float32)
+    x *= np.exp2(rng.uniform(-30, 10, (96, 32))).repeat(16, axis=1).astype(np.float32)
+    x[5, 7] = 3.0e4
+    x_cpu = torch.from_numpy(x)
+    qs = [run_case(fp4, oracle, x_cpu, flags, signs=0x0F0F, seed=2, offset=5)
+          for flags in (0, fp4.Q_SR, fp4.Q_RHT, fp4.Q_COLWISE | fp4.Q_RHT | fp4.Q_SR)]
+    codes, scales, _ = host_q(qs[0])  # the rowwise case holds both kinds of small block
+    assert (scales == 0).any() and ((scales > 0) & (scales < 8)).any()
+
+
+def test_empty(fp4):
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    q = fp4.QTensor(0, 64)
+    fp4.fp4_quantize(x, 0, 0, 0, 0, q)
+    torch.cuda.synchronize()
+    assert float(q.amax.cpu()[0]) == 0.0
+
+
+def test_sr_offsets_decorrelate_on_gpu(fp4):
+    x = dev(make_x((256, 1024), seed=3))
+    a, b = fp4.QTensor(256, 1024), fp4.QTensor(256, 1024)
+    fp4.fp4_quantize(x, fp4.Q_SR, 0, 11, 1, a)
+    fp4.fp4_quantize(x, fp4.Q_SR, 0, 11, 2, b)
+    torch.cuda.synchronize()
+    frac = (a.codes != b.codes).float().mean().item()
+    assert 0.2 < frac < 0.95

@@ -1,0 +1,116 @@
+"""CPU-side checks of the product library: it loads without a GPU, exports every
+symbol include/nvfp4_amd.h declares, and rejects bad arguments before enqueuing
+anything (argument checks run on the host, so they need no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "nvfp4_amd.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*FP4_API\s+(?:fp4_status|const char \*)\s*(fp4_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import nvfp4_bit_microscaled_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from nvfp4_bit_microscaled_amd import build
+        build.build()
+    return m.load()
+
+
+def test_header_lists_the_binding_exports():
+    import nvfp4_bit_microscaled_amd as m
+    assert header_functions() == sorted(m.EXPORTS)
+
+
+def test_library_exports_every_header_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_does_not_export_internals():
+    import nvfp4_bit_microscaled_amd as m
+    out = os.popen(f"nm -D --defined-only {m.LIB_PATH}").read()
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {n for n in exported if n.startswith("fp4_")} == set(m.EXPORTS)
+
+
+def test_status_strings(lib):
+    import nvfp4_bit_microscaled_amd as m
+    for code in range(8):
+        assert m.status_string(code)
+    assert m.status_string(0) == "ok"
+
+
+def test_tensor_bytes(lib):
+    import nvfp4_bit_microscaled_amd as m
+    assert m.tensor_bytes(8192, 4096) == (8192 * 2048, 8192 * 256)
+    assert m.tensor_bytes(4096, 4096, True) == (4096 * 2048, 256 * 256)
+    assert m.tensor_bytes(20, 32, True) == (20 * 16, 2 * 2)
+    with pytest.raises(m.Fp4Error):
+        m.tensor_bytes(16, 24)
+
+
+def desc(rows, cols, two_d=0, base=0x10000):
+    import nvfp4_bit_microscaled_amd as m
+    return m.fp4_tensor(base, base + 0x100000, base + 0x200000, rows, cols, two_d)
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    """Every call below fails its host-side checks, so no device pointer is touched."""
+    import nvfp4_bit_microscaled_amd as m
+    x = ctypes.c_void_p(0x1000)
+    q = desc(64, 128)
+    Q = ctypes.byref
+    # unknown dtype
+    assert lib.fp4_quantize(x, 7, 64, 128, 128, 0, 0, 0, 0, Q(q), None, None) == 4
+    # K not a multiple of 16
+    assert lib.fp4_quantize(x, 0, 64, 120, 120, 0, 0, 0, 0, Q(desc(64, 120)), None, None) in (2, 3)
+    # descriptor shape mismatch
+    assert lib.fp4_quantize(x, 0, 64, 128, 128, 0, 0, 0, 0, Q(desc(32, 128)), None, None) == 6
+    # 2D with stochastic rounding is not a mode of the recipe
+    assert lib.fp4_quantize(x, 0, 64, 128, 128, m.Q_2D | m.Q_SR, 0, 0, 0, Q(desc(64, 128, 1)), None, None) == 5
+    # transposed output requested without 2D
+    assert lib.fp4_quantize(x, 0, 64, 128, 128, 0, 0, 0, 0, Q(q), Q(desc(128, 64, 1)), None) == 5
+    # null input
+    assert lib.fp4_quantize(None, 0, 64, 128, 128, 0, 0, 0, 0, Q(q), None, None) == 1
+    # misaligned input
+    assert lib.fp4_quantize(ctypes.c_void_p(0x1002), 0, 64, 128, 128, 0, 0, 0, 0, Q(q), None, None) == 3
+    # ld smaller than the row
+    assert lib.fp4_quantize(x, 0, 64, 128, 64, 0, 0, 0, 0, Q(q), None, None) == 2
+    # unknown flag bit
+    assert lib.fp4_quantize(x, 0, 64, 128, 128, 1 << 9, 0, 0, 0, Q(q), None, None) == 5
+    # colwise: logical tensor is [128][64]
+    assert lib.fp4_quantize(x, 0, 64, 128, 128, m.Q_COLWISE, 0, 0, 0, Q(q), None, None) == 6
+
+
+def test_gemm_rejects_bad_arguments(lib):
+    c = ctypes.c_void_p(0x1000)
+    Q = ctypes.byref
+    a, b = desc(64, 128), desc(32, 128)
+    assert lib.fp4_gemm(Q(a), Q(desc(32, 96)), c, 1, 32, None) == 6  # K mismatch
+    assert lib.fp4_gemm(Q(a), Q(b), c, 9, 32, None) == 4  # dtype
+    assert lib.fp4_gemm(Q(a), Q(b), c, 1, 16, None) == 2  # ldc < N
+    assert lib.fp4_gemm(Q(a), Q(b), None, 1, 32, None) == 1
+    assert lib.fp4_gemm(Q(a), Q(b), ctypes.c_void_p(0x1002), 1, 32, None) == 3
+    assert lib.fp4_gemm(Q(a), Q(desc(24, 128, 1)), c, 1, 32, None) == 2  # 2D rows not tile multiple
+    assert lib.fp4_gemm(None, Q(b), c, 1, 32, None) == 1
+
+
+def test_linear_rejects_bad_arguments(lib):
+    Q = ctypes.byref
+    x, w, y = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    M, N, K = 64, 32, 48
+    ok = lib.fp4_linear_fprop
+    assert ok(x, w, 0, y, 0, M, N, 40, Q(desc(M, 40)), Q(desc(N, 40, 1)), None, None) == 2
+    assert ok(x, w, 0, y, 0, M, N, K, Q(desc(M, K)), Q(desc(N, K, 0)), None, None) == 6  # W must be 2D
+    assert ok(x, w, 0, y, 0, M, N, K, Q(desc(M, K)), Q(desc(N, K, 1)), Q(desc(N, K, 1)), None) == 6  # W^T shape
+    assert lib.fp4_linear_dgrad(x, 0, Q(desc(N, K, 1)), y, 0, M, N, K, 0, 1, Q(desc(M, N)), None) == 6
+    assert lib.fp4_linear_wgrad(x, w, 0, y, 1, M, N, K, 0, 0, 2, Q(desc(N, M)), Q(desc(M, K)), None) == 6
