@@ -10,33 +10,42 @@
 // E8M0 scale can hold; folding the mantissa into the elements needs 6
 // significant bits (e.g. 1.5 * 1.875), which FP8/FP6/FP4 element formats cannot
 // store.  Every such mapping therefore either loses accuracy far beyond the
-// 1e-5 acceptance bound or needs four or more passes.  This kernel instead
-// dequantizes in registers: an E2M1 value times an E4M3 scale has at most 6
+// 1e-5 acceptance bound or needs four or more passes.  These kernels instead
+// dequantize in registers: an E2M1 value times an E4M3 scale has at most 6
 // significant bits and lies in [2^-10, 2688], so it is exact in f16, every
 // product of two such values is exact in the f32 accumulator, and the per-tensor
 // FP32 scales are applied once in the epilogue.  The products run on
 // v_mfma_f32_32x32x16_f16.  FP4 stays FP4 in HBM and in LDS (a quarter of the
 // bytes of an f16 GEMM); the conversion is v_cvt_scalef32_pk_f16_fp4 followed by
-// a packed f16 multiply by the block scale.
+// a packed f16 multiply by the block scale (the converter's own f32 scale
+// operand applies only its exponent, so it is left at 1).
 //
-// Data flow per workgroup (256 threads, 4 waves in a WAVES_M x WAVES_N grid):
-//   K advances in stages of 128 elements = 64 code bytes + 8 scale bytes per row.
-//   Global -> registers (next stage, 16-byte loads) while the current stage is
-//   consumed from LDS; LDS is double-buffered with one barrier per stage.
-//   LDS rows are 64 bytes; the four 16-byte chunks of a row are XOR-swizzled by
-//   row bits 1..2 so that 8 consecutive lanes reading one chunk index of 8
-//   consecutive rows hit distinct bank groups.
-// MFMA operand mapping: a 32x32x16 MFMA takes 8 f16 per lane for A (row l%32) and
-// 8 for B (column l%32), lane half g = l/32 supplying one 8-element K group.  Any
-// assignment of K values to (g, slot) works as long as A and B use the same one;
-// here lane half g of sub-step s (of 4) in half-stage h takes the 8 codes
-// [32*(2h+g) + 8s, +8), i.e. one 16-byte chunk per lane serves four MFMAs and
-// each lane's 8 values share one block scale.
-// Workgroup -> tile order: consecutive workgroup ids go to different XCDs, so ids
-// are renumbered to give each XCD a contiguous range, then walked in groups of
-// 8 tile-rows so that neighbouring tiles share A rows and B columns in L2.
+// MFMA operand mapping (both kernels): a 32x32x16 MFMA takes 8 f16 per lane for A
+// (row l%32) and 8 for B (column l%32), lane half g = l/32 supplying one group of
+// 8 K values.  Any assignment of K values to (g, slot) is valid as long as A and
+// B use the same one.  Here a lane reads one 16-byte chunk (32 codes, two scale
+// blocks) per operand tile and feeds it to four consecutive MFMAs, 8 codes each,
+// so the 8 values of one MFMA slot always share one block scale.
+//
+// Two kernels:
+//   gemm_kernel       the main path (K a multiple of 256, aligned operands):
+//                     256x256 output tile, four waves of 128x128, K stages of 256
+//                     elements; global -> LDS by direct DMA loads
+//                     (global_load_lds_dwordx4) into a double buffer, one barrier
+//                     per stage.  Per wave and 16 K it dequantizes 8 operand tiles
+//                     (64 VALU ops) for 16 MFMAs, so the conversions fit under the
+//                     matrix-core time.
+//   gemm_edge_kernel  any K multiple of 16, any 8-byte-aligned operands: 128x128
+//                     tile, register-staged loads with zero fill.
+// Workgroup -> tile order (both): consecutive workgroup ids go to different XCDs,
+// so ids are renumbered to give each XCD a contiguous range, then walked in
+// groups of 8 tile-rows so that neighbouring tiles share A rows and B columns in
+// that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "device.hpp"
 #include "internal.hpp"
@@ -49,8 +58,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 128;       // K elements per stage
-constexpr int kRowBytes = 64;  // code bytes per row per stage
 constexpr int kGroupM = 8;
 
 struct GemmParams {
@@ -65,7 +72,8 @@ struct GemmParams {
 
 // 8 E2M1 codes (one 32-bit word, element 2j in the low nibble of byte j) times the
 // block scale, as 8 f16.  Exact: see the header comment.
-__device__ __forceinline__ half8 dequant8(uint32_t w, half2v sc) {
+__device__ __forceinline__ half8 dequant8(uint32_t w, _Float16 s) {
+  const half2v sc = half2v{s, s};
   const half2v h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
   const half2v h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
   const half2v h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
@@ -73,118 +81,360 @@ __device__ __forceinline__ half8 dequant8(uint32_t w, half2v sc) {
   return half8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-__device__ __forceinline__ half2v scale_h2(uint32_t code) {
-  const _Float16 h = _Float16(e4m3_to_f32(code));  // exact: E4M3 values are f16 values
-  return half2v{h, h};
-}
+// Two E4M3 scale codes (the low 16 bits of w) as two f16: every E4M3 value,
+// subnormals included, is an f16 value, so the conversion is exact.
+__device__ __forceinline__ half2v scales2(uint32_t w) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false); }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 1) & 3)) << 4); }
+__device__ __forceinline__ uint32_t word(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
-template <int BM, int BN, bool FAST>
-struct StageRegs {
-  uint4 a[BM / 64];
-  uint4 b[BN / 64];
-  uint2 s[(BM + BN + 255) / 256];
-};
-
-// Load the code chunk for (row, byte offset kbyte) of a [rows][kbytes] code matrix.
-template <bool FAST>
-__device__ __forceinline__ uint4 load_chunk(const uint8_t *base, int64_t row, int64_t rows, int64_t kbytes,
-                                            int64_t kbyte) {
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (row < rows) {
-    const uint8_t *p = base + row * kbytes + kbyte;
-    if (FAST) {
-      v = *reinterpret_cast<const uint4 *>(p);
-    } else {
-      // rows are only guaranteed 8-byte aligned (K a multiple of 16): two 8-byte loads
-      if (kbyte + 8 <= kbytes) {
-        const uint2 lo = *reinterpret_cast<const uint2 *>(p);
-        v.x = lo.x;
-        v.y = lo.y;
-      }
-      if (kbyte + 16 <= kbytes) {
-        const uint2 hi = *reinterpret_cast<const uint2 *>(p + 8);
-        v.z = hi.x;
-        v.w = hi.y;
-      }
-    }
-  }
-  return v;
-}
-
-template <bool FAST>
-__device__ __forceinline__ uint2 load_scales8(const uint8_t *base, int64_t row, int64_t rows, int shift,
-                                              int64_t nkb, int64_t kb0) {
-  uint2 v = make_uint2(0u, 0u);
-  if (row < rows) {
-    const uint8_t *p = base + (row >> shift) * nkb + kb0;
-    if (FAST) {
-      v = *reinterpret_cast<const uint2 *>(p);
-    } else {
-      uint32_t w[2] = {0u, 0u};
-      for (int j = 0; j < 8; ++j)
-        if (kb0 + j < nkb) w[j >> 2] |= uint32_t(p[j]) << (8 * (j & 3));
-      v = make_uint2(w[0], w[1]);
-    }
-  }
-  return v;
-}
-
-template <int BM, int BN, int WM, int WN, bool FAST>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
-  constexpr int WAVES_N = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves per workgroup");
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int NS = (BM + BN + 255) / 256;
-
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s[2][(BM + BN) * 8];
-
-  const int t = threadIdx.x;
-  const int64_t M = p.M, N = p.N, K = p.K;
-  const int num_m = int((M + BM - 1) / BM), num_n = int((N + BN - 1) / BN);
+// Tile coordinates of this workgroup (see the header comment).
+__device__ __forceinline__ void tile_of(int num_m, int num_n, int &tm, int &tn) {
   int pid = blockIdx.x;
   const int total = gridDim.x;
   if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
   const int per_group = kGroupM * num_n;
   const int grp = pid / per_group, first_m = grp * kGroupM;
   const int gsz = min(num_m - first_m, kGroupM);
-  const int tm = first_m + (pid % per_group) % gsz;
-  const int tn = (pid % per_group) / gsz;
-  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  tm = first_m + (pid % per_group) % gsz;
+  tn = (pid % per_group) / gsz;
+}
 
-  const int64_t kbytes = K / 2, nkb = K / 16;
-  const int nstages = int((K + kBK - 1) / kBK);
-
-  StageRegs<BM, BN, FAST> st;
-  auto gload = [&](int kt) {
-    const int64_t kbyte = int64_t(kt) * kRowBytes + 16 * (t & 3);
+// acc (one 32x32 MFMA tile per entry) times the product of the two tensor decode
+// scales, stored at C[m0 + wm + 32 i + ...][n0 + wn + 32 j + lr].
+template <int TM, int TN>
+__device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0, int64_t n0,
+                                            int lr, int g) {
+  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
 #pragma unroll
-    for (int i = 0; i < BM / 64; ++i) st.a[i] = load_chunk<FAST>(p.a_codes, m0 + (t >> 2) + 64 * i, M, kbytes, kbyte);
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < BN / 64; ++i) st.b[i] = load_chunk<FAST>(p.b_codes, n0 + (t >> 2) + 64 * i, N, kbytes, kbyte);
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = n0 + 32 * j + lr;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int r = t + 256 * i;
-      const int64_t kb0 = int64_t(kt) * (kBK / 16);
-      if (r < BM) st.s[i] = load_scales8<FAST>(p.a_scales, m0 + r, M, p.a_shift, nkb, kb0);
-      else if (r < BM + BN) st.s[i] = load_scales8<FAST>(p.b_scales, n0 + (r - BM), N, p.b_shift, nkb, kb0);
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m < p.M && n < p.N) {
+          const float v = acc[i][j][r] * gscale;
+          if (p.c_bf16)
+            reinterpret_cast<uint16_t *>(p.c)[m * p.ldc + n] = f32_to_bf16(v);
+          else
+            reinterpret_cast<float *>(p.c)[m * p.ldc + n] = v;
+        }
+      }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel.
+// LDS stage layout: A codes [BM][128 B], B codes [BN][128 B], then scales
+// [BM + BN][16 B] (A rows first).  A row's eight 16-byte chunks are stored at
+// chunk ^ swz(row): the 32 lanes that read one chunk index of 32 consecutive rows
+// then touch every 16-byte bank group once per 8 (or 16) lanes.
+
+__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 1)) & 7; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Buffer resource for `bytes` bytes at p (raw, untyped: dword 3 as for gfx9 raw
+// buffers).  Loads whose per-lane offset is at or past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, int(bytes), 0x00020000);
+}
+
+// 16-byte DMA from a buffer into LDS: lane l reads voffset + soffset and writes
+// dst + 16 l (dst is wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, voffset, soffset, 0, 0);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP>
+__global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams p) {
+  constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int TM = WM / 32, TN = WN / 32, T = TM + TN;
+  constexpr int kRow = 128;  // code bytes per row per stage (256 K)
+  constexpr int kSc = 16;    // scale bytes per row per stage (16 blocks)
+  constexpr int B_OFF = BM * kRow, S_OFF = (BM + BN) * kRow;
+  constexpr int STAGE = (BM + BN) * (kRow + kSc);
+  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "code DMA: whole instructions per wave");
+  static_assert((BM + BN) % 64 == 0, "scale DMA: whole instructions");
+  static_assert(STAGE % 1024 == 0, "stage alignment");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int64_t M = p.M, N = p.N;
+  int tm, tn;
+  tile_of(int((M + BM - 1) / BM), int((N + BN - 1) / BN), tm, tn);
+  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const uint32_t kbytes = uint32_t(p.K / 2), nkb = uint32_t(p.K / 16);
+  const int nst = int(p.K / 256);
+
+  // DMA sources.  Unit u (16 bytes) of a wave's instruction j sits at row
+  // (j*NW + wave)*8 + lane/8 of the tile, physical chunk lane%8, and holds that
+  // row's logical chunk (lane%8) ^ swz8(row); swz8 depends only on the row's low
+  // 4 bits, so it is the same for every j.  The loads are buffer loads whose
+  // range check (on the per-lane offset) returns zeros for rows past the matrix
+  // edge; those rows' outputs are not stored.  Offsets are 32-bit: the launcher
+  // checks (rows + 256) * K/2 < 2^32.  Without CLAMP (M, N multiples of the
+  // tile) the row step between instructions rides in the scalar offset.
+  constexpr int JA = BM * 8 / NT, JB = BN * 8 / NT;
+  constexpr int NSC = ((BM + BN) / 64 + NW - 1) / NW;
+  static_assert(JA % 4 == 0 && JB % 4 == 0, "DMA split over four substeps");
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy: LDS destinations stay scalar
+  const int row0 = wave * 8 + (lane >> 3);
+  const uint32_t lchunk = uint32_t(((lane & 7) ^ swz8(row0)) << 4);
+  const uint32_t rstride = uint32_t(NW * 8) * kbytes;  // bytes between instruction j and j+1
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.a_codes, uint32_t(M) * kbytes);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.b_codes, uint32_t(N) * kbytes);
+  const __amdgpu_buffer_rsrc_t rssa = make_rsrc(p.a_scales, uint32_t((M + (1 << p.a_shift) - 1) >> p.a_shift) * nkb);
+  const __amdgpu_buffer_rsrc_t rssb = make_rsrc(p.b_scales, uint32_t((N + (1 << p.b_shift) - 1) >> p.b_shift) * nkb);
+  uint32_t va[CLAMP ? JA : 1], vb[CLAMP ? JB : 1];
+#pragma unroll
+  for (int j = 0; j < (CLAMP ? JA : 1); ++j) va[j] = uint32_t(m0 + row0 + NW * 8 * j) * kbytes + lchunk;
+#pragma unroll
+  for (int j = 0; j < (CLAMP ? JB : 1); ++j) vb[j] = uint32_t(n0 + row0 + NW * 8 * j) * kbytes + lchunk;
+  uint32_t vs[NSC];
+#pragma unroll
+  for (int j = 0; j < NSC; ++j) {
+    const int u = (j * NW + wave) * 64 + lane;
+    vs[j] = u < BM ? uint32_t((m0 + u) >> p.a_shift) * nkb : uint32_t((n0 + (u - BM)) >> p.b_shift) * nkb;
+  }
+
+  // global -> LDS: DMA instruction d (0 .. NDMA-1) of stage kt into buffer buf:
+  // A code rows for d < JA, then B code rows, then the scale rows.  Asynchronous:
+  // completion is awaited with vmcnt before the barrier that precedes the first
+  // read.
+  constexpr int NDMA = JA + JB + NSC;
+  auto dma = [&](int kt, int buf, int d) {
+    uint8_t *base = lds + buf * STAGE;
+    const uint32_t kofs = uint32_t(kt) * kRow;
+    if (d < JA) {
+      dma16(rsa, base + (d * NW + wave_s) * 1024, CLAMP ? va[d] : va[0], CLAMP ? kofs : kofs + d * rstride);
+    } else if (d < JA + JB) {
+      const int j = d - JA;
+      dma16(rsb, base + B_OFF + (j * NW + wave_s) * 1024, CLAMP ? vb[j] : vb[0], CLAMP ? kofs : kofs + j * rstride);
+    } else {
+      const int j = d - JA - JB;
+      const int u0 = (j * NW + wave_s) * 64;  // scalar
+      if ((BM + BN) % (64 * NW) == 0 || u0 < BM + BN)
+        dma16(u0 < BM ? rssa : rssb, base + S_OFF + u0 * kSc, vs[j], uint32_t(kt) * kSc);
+    }
+  };
+  auto issue = [&](int kt, int buf) {
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d) dma(kt, buf, d);
+  };
+
+  const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
+  const int lr = lane & 31, g = lane >> 5;
+  const int sw = swz8(lr);  // = swz8(row) for every row this lane reads (rows differ by multiples of 32)
+  // LDS byte offsets of this lane's first A and B rows; tile i adds 32*i rows
+  const int rowa = (wm + lr) * kRow, rowb = B_OFF + (wn + lr) * kRow;
+  const int sca = S_OFF + (wm + lr) * kSc + 2 * g, scb = S_OFF + (BM + wn + lr) * kSc + 2 * g;
+
+  // A stage is 4 quarters of 64 K; in quarter q lane half g reads 32-element chunk
+  // 2q+g of each of its rows (16 bytes) and that chunk's two block scales.
+  // Registers hold two quarters (ring of 2) and the f16 operands of two 16-K
+  // substeps: the substep after the current one is dequantized while the current
+  // one's MFMAs run.  Tiles 0..TM-1 are A's, TM..T-1 are B's.
+  uint4 ch[2][T];
+  uint32_t scw[2][T];
+  half2v scd[2][T];
+  half8 op[2][T];
+  // LDS read r (0 .. 2T-1) of quarter q into ring slot `slot`: the chunk of tile r
+  // for r < T, else the two scale codes of tile r - T
+  auto lds_read = [&](int buf, int q, int slot, int r) {
+    const uint8_t *base = lds + buf * STAGE;
+    if (r < T) {
+      const int chunk = ((2 * q + g) ^ sw) << 4;
+      const int row = r < TM ? rowa + 32 * kRow * r : rowb + 32 * kRow * (r - TM);
+      ch[slot][r] = *reinterpret_cast<const uint4 *>(base + row + chunk);
+    } else {
+      const int i = r - T;
+      const int sc = i < TM ? sca + 32 * kSc * i : scb + 32 * kSc * (i - TM);
+      scw[slot][i] = *reinterpret_cast<const uint16_t *>(base + sc + 4 * q);
+    }
+  };
+  // half h (codes 4h..4h+3) of tile i of substep s, from ring slot `slot` into
+  // operand set dst: two conversions and two multiplies
+  auto dequant_half = [&](int slot, int s, int dst, int i, int h) {
+    const uint32_t w = word(ch[slot][i], s);
+    const _Float16 sv = scd[slot][i][s >> 1];
+    const half2v sc = half2v{sv, sv};
+    const half2v lo = (h == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)
+                              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)) * sc;
+    const half2v hi = (h == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)
+                              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)) * sc;
+    op[dst][i][4 * h + 0] = lo[0];
+    op[dst][i][4 * h + 1] = lo[1];
+    op[dst][i][4 * h + 2] = hi[0];
+    op[dst][i][4 * h + 3] = hi[1];
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Explicit issue order.  A substep is NMF slots; slot k issues MFMA k of the
+  // current operand set, half of one tile's conversions for the next substep
+  // (4 VALU: the MFMA's 32 cycles leave room for them), and at most one LDS read
+  // and one DMA load; sched_barrier keeps the compiler from regrouping slots.
+  constexpr int NMF = TM * TN;
+  static_assert(NMF == 2 * T, "one half-tile of conversions per MFMA");
+  static_assert(2 * T <= NMF && NDMA <= 2 * NMF, "memory instructions fit the slots");
+  constexpr int kDmaPerSubstep = (NDMA + 3) / 4;
+
+  // One stage.  Quarters 0..2 read the next quarter of this buffer during their
+  // first substep; quarter 3 waits for stage kt+1's DMA and for every read of this
+  // buffer, passes the barrier, reads stage kt+1's first quarter from the other
+  // buffer and spreads stage kt+2's DMA into this buffer over its substeps.  The
+  // last stage has none of that.
+  auto stage = [&](int kt, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const int buf = kt & 1;
+    // a stage past the end re-loads the last one into this buffer, which is not
+    // read again (the final wait below drains it before the kernel ends)
+    const int kt_dma = min(kt + 2, nst - 1);
+    static_for<4>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      constexpr int slot = q & 1;
+      constexpr bool next_q = q < 3 || !LAST;  // is there a quarter after this one?
+      if constexpr (q == 3 && !LAST) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+      static_for<4>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int cur = s & 1;  // 4 substeps per quarter: the parity runs on across quarters and stages
+        // the substep whose operands are built now
+        constexpr bool has_next = s < 3 || next_q;
+        constexpr int nslot = s < 3 ? slot : slot ^ 1, ns = s < 3 ? s + 1 : 0;
+        static_for<NMF>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          constexpr int i = k / TN, j = k % TN;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][i], op[cur][TM + j], acc[i][j], 0, 0, 0);
+          if constexpr (has_next) dequant_half(nslot, ns, cur ^ 1, k / 2, k % 2);
+          if constexpr (s == 0 && next_q && k < 2 * T)
+            lds_read(q < 3 ? buf : buf ^ 1, q < 3 ? q + 1 : 0, slot ^ 1, k);
+          if constexpr (s == 2 && next_q && k < T) scd[slot ^ 1][k] = scales2(scw[slot ^ 1][k]);
+          if constexpr (q == 3 && !LAST && k < kDmaPerSubstep && s * kDmaPerSubstep + k < NDMA)
+            dma(kt_dma, buf, s * kDmaPerSubstep + k);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+    });
+  };
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  issue(min(1, nst - 1), 1);
+  // quarter 0 of stage 0 and the operands of its first substep
+#pragma unroll
+  for (int r = 0; r < 2 * T; ++r) lds_read(0, 0, 0, r);
+#pragma unroll
+  for (int i = 0; i < T; ++i) scd[0][i] = scales2(scw[0][i]);
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    dequant_half(0, 0, 0, i, 0);
+    dequant_half(0, 0, 0, i, 1);
+  }
+  for (int kt = 0; kt + 1 < nst; ++kt) stage(kt, std::false_type{});
+  stage(nst - 1, std::true_type{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  store_tiles<TM, TN>(p, acc, m0 + wm, n0 + wn, lr, g);
+}
+
+// ---------------------------------------------------------------------------
+// Edge kernel: any K (multiple of 16), operands only 8-byte aligned.
+// K advances in stages of 128 elements = 64 code bytes + 8 scale bytes per row,
+// register-staged (zero-filled past the edges), LDS double-buffered.  LDS rows are
+// 64 bytes; the four 16-byte chunks of a row are XOR-swizzled by row bits 1..2.
+
+constexpr int kEdgeBK = 128;
+constexpr int kEdgeRow = 64;
+
+__device__ __forceinline__ int swz4(int row, int chunk) { return row * kEdgeRow + ((chunk ^ ((row >> 1) & 3)) << 4); }
+
+__device__ __forceinline__ uint4 load_chunk(const uint8_t *base, int64_t row, int64_t rows, int64_t kbytes,
+                                            int64_t kbyte) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < rows) {
+    const uint8_t *q = base + row * kbytes + kbyte;
+    if (kbyte + 8 <= kbytes) {
+      const uint2 lo = *reinterpret_cast<const uint2 *>(q);
+      v.x = lo.x;
+      v.y = lo.y;
+    }
+    if (kbyte + 16 <= kbytes) {
+      const uint2 hi = *reinterpret_cast<const uint2 *>(q + 8);
+      v.z = hi.x;
+      v.w = hi.y;
+    }
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint2 load_scales8(const uint8_t *base, int64_t row, int64_t rows, int shift, int64_t nkb,
+                                              int64_t kb0) {
+  uint32_t w[2] = {0u, 0u};
+  if (row < rows) {
+    const uint8_t *q = base + (row >> shift) * nkb + kb0;
+    for (int j = 0; j < 8; ++j)
+      if (kb0 + j < nkb) w[j >> 2] |= uint32_t(q[j]) << (8 * (j & 3));
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+__global__ __launch_bounds__(256) void gemm_edge_kernel(GemmParams p) {
+  constexpr int BM = 128, BN = 128, WM = 64, WN = 64, WAVES_N = BN / WN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kEdgeRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kEdgeRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s[2][(BM + BN) * 8];
+
+  const int t = threadIdx.x;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  tile_of(int((M + BM - 1) / BM), int((N + BN - 1) / BN), tm, tn);
+  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const int64_t kbytes = K / 2, nkb = K / 16;
+  const int nstages = int((K + kEdgeBK - 1) / kEdgeBK);
+
+  uint4 ra[BM / 64], rb[BN / 64];
+  uint2 rs;
+  auto gload = [&](int kt) {
+    const int64_t kbyte = int64_t(kt) * kEdgeRow + 16 * (t & 3);
+#pragma unroll
+    for (int i = 0; i < BM / 64; ++i) ra[i] = load_chunk(p.a_codes, m0 + (t >> 2) + 64 * i, M, kbytes, kbyte);
+#pragma unroll
+    for (int i = 0; i < BN / 64; ++i) rb[i] = load_chunk(p.b_codes, n0 + (t >> 2) + 64 * i, N, kbytes, kbyte);
+    const int64_t kb0 = int64_t(kt) * (kEdgeBK / 16);
+    if (t < BM) rs = load_scales8(p.a_scales, m0 + t, M, p.a_shift, nkb, kb0);
+    else rs = load_scales8(p.b_scales, n0 + (t - BM), N, p.b_shift, nkb, kb0);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < BM / 64; ++i)
-      *reinterpret_cast<uint4 *>(&lds_a[buf][swz((t >> 2) + 64 * i, t & 3)]) = st.a[i];
+    for (int i = 0; i < BM / 64; ++i) *reinterpret_cast<uint4 *>(&lds_a[buf][swz4((t >> 2) + 64 * i, t & 3)]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < BN / 64; ++i)
-      *reinterpret_cast<uint4 *>(&lds_b[buf][swz((t >> 2) + 64 * i, t & 3)]) = st.b[i];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int r = t + 256 * i;
-      if (r < BM + BN) *reinterpret_cast<uint2 *>(&lds_s[buf][r * 8]) = st.s[i];
-    }
+    for (int i = 0; i < BN / 64; ++i) *reinterpret_cast<uint4 *>(&lds_b[buf][swz4((t >> 2) + 64 * i, t & 3)]) = rb[i];
+    *reinterpret_cast<uint2 *>(&lds_s[buf][t * 8]) = rs;
   };
 
   const int wave = t >> 6, lane = t & 63;
@@ -212,79 +462,45 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) sa[i] = *reinterpret_cast<const uint2 *>(&lds_s[buf][(wm + 32 * i + lr) * 8]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      sb[j] = *reinterpret_cast<const uint2 *>(&lds_s[buf][(BM + wn + 32 * j + lr) * 8]);
+    for (int j = 0; j < TN; ++j) sb[j] = *reinterpret_cast<const uint2 *>(&lds_s[buf][(BM + wn + 32 * j + lr) * 8]);
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int chunk = 2 * h + g;
       uint4 qa[TM], qb[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) qa[i] = *reinterpret_cast<const uint4 *>(&lds_a[buf][swz(wm + 32 * i + lr, chunk)]);
+      for (int i = 0; i < TM; ++i) qa[i] = *reinterpret_cast<const uint4 *>(&lds_a[buf][swz4(wm + 32 * i + lr, chunk)]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) qb[j] = *reinterpret_cast<const uint4 *>(&lds_b[buf][swz(wn + 32 * j + lr, chunk)]);
+      for (int j = 0; j < TN; ++j) qb[j] = *reinterpret_cast<const uint4 *>(&lds_b[buf][swz4(wn + 32 * j + lr, chunk)]);
+      // blocks 2*chunk and 2*chunk+1 of this stage: bytes 4h+2g, +1 of the 8 scale bytes
+      half2v sca[TM], scb[TN];
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int blk = 2 * chunk + pr;  // block (0..7) of this stage
-        half2v sca[TM], scb[TN];
+      for (int i = 0; i < TM; ++i) sca[i] = scales2((h == 0 ? sa[i].x : sa[i].y) >> (16 * g));
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sca[i] = scale_h2(((blk < 4 ? sa[i].x : sa[i].y) >> (8 * (blk & 3))) & 0xFFu);
+      for (int j = 0; j < TN; ++j) scb[j] = scales2((h == 0 ? sb[j].x : sb[j].y) >> (16 * g));
 #pragma unroll
-        for (int j = 0; j < TN; ++j) scb[j] = scale_h2(((blk < 4 ? sb[j].x : sb[j].y) >> (8 * (blk & 3))) & 0xFFu);
+      for (int s = 0; s < 4; ++s) {
+        half8 fa[TM], fb[TN];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int s = 2 * pr + s2;
-          half8 fa[TM], fb[TN];
+        for (int i = 0; i < TM; ++i) fa[i] = dequant8(word(qa[i], s), sca[i][s >> 1]);
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const uint32_t w = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
-            fa[i] = dequant8(w, sca[i]);
-          }
+        for (int j = 0; j < TN; ++j) fb[j] = dequant8(word(qb[j], s), scb[j][s >> 1]);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const uint32_t w = s == 0 ? qb[j].x : s == 1 ? qb[j].y : s == 2 ? qb[j].z : qb[j].w;
-            fb[j] = dequant8(w, scb[j]);
-          }
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
+          for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
     }
     if (kt + 1 < nstages) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  // Epilogue: apply the two per-tensor decode scales and store.
-  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t n = n0 + wn + 32 * j + lr;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (m < M && n < N) {
-          const float v = acc[i][j][r] * gscale;
-          if (p.c_bf16)
-            reinterpret_cast<uint16_t *>(p.c)[m * p.ldc + n] = f32_to_bf16(v);
-          else
-            reinterpret_cast<float *>(p.c)[m * p.ldc + n] = v;
-        }
-      }
-    }
+  store_tiles<TM, TN>(p, acc, m0 + wm, n0 + wn, lr, g);
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const GemmParams &p, bool fast, hipStream_t stream) {
-  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (fast)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true>), dim3(unsigned(tiles)), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false>), dim3(unsigned(tiles)), dim3(256), 0, stream, p);
-  return hipGetLastError();
+template <int BM, int BN>
+unsigned tiles_for(const GemmParams &p) {
+  return unsigned(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
 }
 
 }  // namespace
@@ -307,11 +523,19 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
   p.ldc = ldc;
   p.c_bf16 = c_dtype == FP4_BF16;
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const bool fast = (p.K % kBK == 0) && (reinterpret_cast<uintptr_t>(a->codes) % 16 == 0) &&
-                    (reinterpret_cast<uintptr_t>(b->codes) % 16 == 0) &&
-                    (reinterpret_cast<uintptr_t>(a->scales) % 8 == 0) &&
-                    (reinterpret_cast<uintptr_t>(b->scales) % 8 == 0);
-  return launch_cfg<128, 128, 64, 64>(p, fast, stream);
+  auto al = [](const void *q, uintptr_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
+  // main path: whole 256-element K stages, 16-byte aligned codes and scale rows,
+  // and every DMA offset within 32 bits
+  const bool main_path = p.K >= 256 && p.K % 256 == 0 && al(a->codes, 16) && al(b->codes, 16) &&
+                         al(a->scales, 16) && al(b->scales, 16) && (p.M + 256) * (p.K / 2) < (int64_t(1) << 32) &&
+                         (p.N + 256) * (p.K / 2) < (int64_t(1) << 32);
+  if (main_path && p.M % 256 == 0 && p.N % 256 == 0)
+    hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false>), dim3(tiles_for<256, 256>(p)), dim3(256), 0, stream, p);
+  else if (main_path)
+    hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true>), dim3(tiles_for<256, 256>(p)), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_edge_kernel, dim3(tiles_for<128, 128>(p)), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4
