@@ -145,16 +145,28 @@ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Buffer resource for `bytes` bytes at p (raw, untyped: dword 3 as for gfx9 raw
-// buffers).  Loads whose per-lane offset is at or past `bytes` return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, int(bytes), 0x00020000);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for `bytes` bytes at p: raw and untyped (stride 0; dword 3 as
+// for gfx9 raw buffers).  Loads whose per-lane offset is at or past `bytes`
+// return zero.
+__device__ __forceinline__ u32x4 make_rsrc(const void *p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{uint32_t(a), uint32_t(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
 }
 
 // 16-byte DMA from a buffer into LDS: lane l reads voffset + soffset and writes
-// dst + 16 l (dst is wave-uniform).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, uint32_t voffset, uint32_t soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, voffset, soffset, 0, 0);
+// dst + 16 l (dst is wave-uniform).  Issued as inline assembly on purpose: the
+// compiler then keeps no count of these loads, so it does not stall later LDS
+// reads of the other stage buffer on them (it cannot tell the two buffers
+// apart).  The kernel orders them itself, with vmcnt(0) before every barrier
+// that precedes a read of the buffer they fill and before it exits.  M0 is a
+// reserved register (never allocated to values), so writing it here is safe.
+__device__ __forceinline__ void dma16(const u32x4 &rsrc, void *dst, uint32_t voffset, uint32_t soffset) {
+  const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(dst));  // low half of a flat LDS address = offset
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset));
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP>
@@ -194,10 +206,10 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   const int row0 = wave * 8 + (lane >> 3);
   const uint32_t lchunk = uint32_t(((lane & 7) ^ swz8(row0)) << 4);
   const uint32_t rstride = uint32_t(NW * 8) * kbytes;  // bytes between instruction j and j+1
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.a_codes, uint32_t(M) * kbytes);
-  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.b_codes, uint32_t(N) * kbytes);
-  const __amdgpu_buffer_rsrc_t rssa = make_rsrc(p.a_scales, uint32_t((M + (1 << p.a_shift) - 1) >> p.a_shift) * nkb);
-  const __amdgpu_buffer_rsrc_t rssb = make_rsrc(p.b_scales, uint32_t((N + (1 << p.b_shift) - 1) >> p.b_shift) * nkb);
+  const u32x4 rsa = make_rsrc(p.a_codes, uint32_t(M) * kbytes);
+  const u32x4 rsb = make_rsrc(p.b_codes, uint32_t(N) * kbytes);
+  const u32x4 rssa = make_rsrc(p.a_scales, uint32_t((M + (1 << p.a_shift) - 1) >> p.a_shift) * nkb);
+  const u32x4 rssb = make_rsrc(p.b_scales, uint32_t((N + (1 << p.b_shift) - 1) >> p.b_shift) * nkb);
   uint32_t va[CLAMP ? JA : 1], vb[CLAMP ? JB : 1];
 #pragma unroll
   for (int j = 0; j < (CLAMP ? JA : 1); ++j) va[j] = uint32_t(m0 + row0 + NW * 8 * j) * kbytes + lchunk;
