@@ -21,8 +21,9 @@
  * Stochastic rounding: element i (row-major index in the logical output) uses
  * the 16 bits (16*(i&1)) of word ((i&7)>>1) of Philox4x32-10 with counter
  * (i>>3 as two 32-bit words, offset as two words) and key (seed as two words);
- * it rounds up when that 16-bit value is below 2^16 * (distance to the lower
- * grid point / grid step).
+ * with F = floor(2^16 * (distance to the lower grid point / grid step)) it rounds
+ * up when that 16-bit value plus F reaches 2^16 (the random bits are added below
+ * the kept precision and the sum is truncated).
  * Random Hadamard transform: in each 16-block, negate the elements whose bit is
  * set in the 16-bit sign mask, apply Sylvester's H16 (butterflies at distance
  * 1, 2, 4, 8), multiply by 1/4.

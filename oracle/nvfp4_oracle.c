@@ -64,9 +64,11 @@ NVO_EXPORT double nvo_e2m1_value(unsigned code) {
 
 /* Encode one scaled value s.  Nearest-even: nearest grid point, a tie going to the
  * even code.  Stochastic: between the two neighbouring grid points lo <= |s| < hi,
- * go up when the 16-bit random number, read as a fraction u16 / 2^16, is below
- * (|s| - lo) / (hi - lo).  |s| >= 6 saturates to 6 in both modes.  Zero is
- * always written as the +0 code. */
+ * the position f = (|s| - lo) / (hi - lo) in [0, 1) is cut to 16 fraction bits,
+ * F = floor(f * 2^16), and the 16 random bits u16 are added to it: the value goes
+ * up when the sum carries out of 16 bits (u16 + F >= 2^16), i.e. with probability
+ * F / 2^16 -- within 2^-16 of a grid step of unbiased.  |s| >= 6 saturates to 6 in
+ * both modes.  Zero is always written as the +0 code. */
 NVO_EXPORT unsigned nvo_e2m1_encode(float s, int stochastic, uint32_t u16) {
   float a = fabsf(s);
   unsigned mag;
@@ -80,8 +82,10 @@ NVO_EXPORT unsigned nvo_e2m1_encode(float s, int stochastic, uint32_t u16) {
     int up;
     if (!stochastic)
       up = (frac > 0.5f) || (frac == 0.5f && (lo & 1u));
-    else
-      up = ((float)(u16 & 0xFFFFu) * 0x1p-16f) < frac;
+    else {
+      uint32_t F = (uint32_t)floorf(frac * 65536.0f); /* exact: frac < 1 scaled by a power of two */
+      up = (u16 & 0xFFFFu) + F >= 65536u;
+    }
     mag = lo + (unsigned)up;
   }
   if (mag == 0) return 0;

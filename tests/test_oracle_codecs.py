@@ -70,12 +70,12 @@ def test_e2m1_rne_sweep(oracle):
 def test_e2m1_zero_is_canonical(oracle):
     assert oracle.e2m1_encode(-0.0) == 0
     assert oracle.e2m1_encode(-0.2) == 0  # rounds to zero: +0 code
-    assert oracle.e2m1_encode(-0.2, True, 0xFFFF) == 0
+    assert oracle.e2m1_encode(-0.2, True, 0) == 0  # u16 = 0 never rounds up
 
 
 def test_e2m1_sr_exact_probabilities(oracle):
     """Stochastic rounding: over all 2^16 random values the number of "up" decisions
-    is exactly ceil(frac * 2^16), so the expectation is within 2^-16 of a step of
+    is exactly floor(frac * 2^16), so the expectation is within 2^-16 of a step of
     the input (unbiased up to the 16-bit resolution; Quartet II page, paragraph 1)."""
     rng = np.random.default_rng(7)
     vals = np.concatenate([rng.uniform(0, 6, 40), GRID[:-1] + 1e-3, GRID, [5.999, 0.0001]]).astype(np.float32)
@@ -92,11 +92,12 @@ def test_e2m1_sr_exact_probabilities(oracle):
         frac = (a - GRID[lo]) / step
         assert set(np.unique(mags)).issubset({lo, lo + 1})
         ups = int((mags == lo + 1).sum())
-        assert ups == int(np.ceil(frac * 65536)), (v, ups)
+        assert ups == int(np.floor(frac * 65536)), (v, ups)
         mean = GRID[mags].mean()
         assert abs(mean - a) <= step * 2.0**-16 + 1e-12
-        # the up decisions are exactly the random values below frac (a threshold rule)
-        assert np.all((mags == lo + 1) == (u < frac * 65536))
+        # the up decisions are exactly the random values whose sum with the 16-bit
+        # position carries (a threshold rule: the largest draws go up)
+        assert np.all((mags == lo + 1) == (u >= 65536 - np.floor(frac * 65536)))
 
 
 def test_e2m1_sr_grid_points_never_move(oracle):

@@ -277,8 +277,9 @@ def test_sr_random_bit_mapping(oracle):
     """Element i (row-major in the logical output) uses bits 16*(i&1)..+15 of word
     (i&7)>>1 of Philox4x32-10(counter = (i>>3 as two words, offset as two words),
     key = seed as two words).  Values exactly half-way between grid points reveal
-    the top bit of that 16-bit draw: they round up iff it is 0.  Each block holds a
-    6 so that its scale is 448 and its multiplier exactly 1."""
+    the top bit of that 16-bit draw: they round up iff it is 1 (2^15 + u16 carries
+    out of 16 bits).  Each block holds a 6 so that its scale is 448 and its
+    multiplier exactly 1."""
     R, K = 4, 64
     x = np.full((R, K), 0.25, dtype=np.float32)
     x[:, ::16] = 6.0
@@ -297,4 +298,4 @@ def test_sr_random_bit_mapping(oracle):
             w = oracle.philox4x32_10([g & 0xFFFFFFFF, g >> 32, offset & 0xFFFFFFFF, offset >> 32], key)
             u16 = (w[(i & 7) >> 1] >> (16 * (i & 1))) & 0xFFFF
             lo, hi = (6, 7) if x[r, k] == 5.0 else (0, 1)
-            assert codes[r, k] == (hi if u16 < 0x8000 else lo), (r, k)
+            assert codes[r, k] == (hi if u16 >= 0x8000 else lo), (r, k)
