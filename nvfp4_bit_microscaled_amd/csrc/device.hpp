@@ -51,34 +51,54 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 magnitude code by counting the midpoints below |s|; a value exactly on a
-// midpoint goes to the even code (so the comparisons alternate between > and >=).
-__device__ __forceinline__ uint32_t e2m1_rne(float s) {
-  float a = __builtin_fabsf(s);
-  uint32_t mag = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
-                 uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
-  uint32_t sign = (__float_as_uint(s) >> 31) & (mag != 0u);
-  return (sign << 3) | mag;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Canonical zero: clear the sign bit of every code whose magnitude is 0 (the
+// converters write -0 for negative values that round to zero).  Per nibble,
+// magnitude + 7 sets bit 3 exactly when the magnitude is non-zero.
+__device__ __forceinline__ uint32_t canon_zero(uint32_t w) {
+  const uint32_t mag = w & 0x77777777u;
+  return mag | (w & ((mag + 0x77777777u) & 0x88888888u));
 }
 
-// Stochastic E2M1: lower neighbour by counting the grid points <= |s|, then up when
-// r16 < 2^16 * (|s| - lower) / step.  Both sides of that comparison are exact.
-__device__ __forceinline__ uint32_t e2m1_sr(float s, uint32_t r16) {
-  float a = __builtin_fabsf(s);
-  uint32_t mag;
-  if (a >= 6.0f) {
-    mag = 7u;
-  } else {
-    uint32_t lo = uint32_t(a >= 0.5f) + uint32_t(a >= 1.0f) + uint32_t(a >= 1.5f) + uint32_t(a >= 2.0f) +
-                  uint32_t(a >= 3.0f) + uint32_t(a >= 4.0f);
-    // grid point and 2^16 / step for each lower neighbour (codes 0..6)
-    float base = lo < 4u ? 0.5f * float(lo) : (lo == 4u ? 2.0f : (lo == 5u ? 3.0f : 4.0f));
-    float inv_step_2p16 = lo < 4u ? 131072.0f : (lo < 6u ? 65536.0f : 32768.0f);
-    float thresh = (a - base) * inv_step_2p16;  // exact: Sterbenz difference times a power of two
-    mag = lo + uint32_t(float(r16) < thresh);
-  }
-  uint32_t sign = (__float_as_uint(s) >> 31) & (mag != 0u);
-  return (sign << 3) | mag;
+// 8 scaled values -> 8 E2M1 codes (element 2j in the low nibble of byte j),
+// nearest-even with ties to the even code, |s| >= 6 saturating to 6.  gfx950's
+// converter rounds exactly this way (checked against the oracle's encoder over
+// every grid midpoint +-64 ulps and a dense sweep of binary32 values); its scale
+// operand is 1, the block multiplier having been applied already.
+__device__ __forceinline__ uint32_t encode8_rne(const float s[8]) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s[0], s[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s[2], s[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s[4], s[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s[6], s[7], 1.0f, 3);
+  return canon_zero(w);
+}
+
+// Two stochastically rounded E2M1 codes (element a in bits 0..3, b in bits 4..7 of
+// the result; the bits above are not defined).  a uses the low 16 bits of r, b the
+// high 16 bits.  With F = floor(2^16 * position of |s| between its grid
+// neighbours), a value rounds up when u16 + F >= 2^16.  gfx950's SR converter adds
+// its random operand's top bits (bits 31..10 for the first element of a pair,
+// 30..9 for the second) below the kept precision and truncates; the two elements
+// of a pair would share random bits, so each element gets its own call, with its
+// 16 bits at the top of its window and zeros below, and the wanted nibbles are
+// kept.  (Written to byte 0: this converter does not keep the other bytes of its
+// destination operand.)
+__device__ __forceinline__ uint32_t encode2_sr(float a, float b, uint32_t r) {
+  const f32x2 p = {a, b};
+  const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r << 16, 1.0f, 0);
+  const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, (r >> 1) & 0x7FFF8000u, 1.0f, 0);
+  return (lo & 0x0Fu) | (hi & 0xF0u);
+}
+
+// 8 scaled values -> 8 stochastically rounded codes; elements 2j, 2j+1 use r[j].
+__device__ __forceinline__ uint32_t encode8_sr(const float s[8], const uint32_t r[4]) {
+  const uint32_t b0 = encode2_sr(s[0], s[1], r[0]), b1 = encode2_sr(s[2], s[3], r[1]);
+  const uint32_t b2 = encode2_sr(s[4], s[5], r[2]), b3 = encode2_sr(s[6], s[7], r[3]);
+  // byte 0 of b0..b3 into bytes 0..3 (selector 0x0c gives a zero byte)
+  const uint32_t w = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
+  return canon_zero(w);
 }
 
 // Philox4x32-10 (Salmon et al., SC'11): counter (c0..c3), key (k0, k1).
@@ -90,13 +110,12 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
                                                  uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    const uint64_t p0 = uint64_t(0xD2511F53u) * c0, p1 = uint64_t(0xCD9E8D57u) * c2;
+    const uint32_t n0 = uint32_t(p1 >> 32) ^ c1 ^ k0, n2 = uint32_t(p0 >> 32) ^ c3 ^ k1;
     c0 = n0;
-    c1 = lo1;
+    c1 = uint32_t(p1);
     c2 = n2;
-    c3 = lo0;
+    c3 = uint32_t(p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -143,23 +162,21 @@ __device__ __forceinline__ void block_scale(float amax_b, float s_enc, uint32_t 
   mult = sf > 0.0f ? s_enc / sf : 0.0f;
 }
 
-// Encode a 16-block into 8 bytes (two uint32 words), nearest-even.
+// Scale a 16-block by its multiplier (one binary32 product per element) and
+// encode it into 8 bytes (two words), nearest-even or stochastic (r: the 8
+// random words of sr_bits16).
 __device__ __forceinline__ uint2 encode16_rne(const float v[16], float mult) {
-  uint32_t w[2] = {0u, 0u};
+  float s[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) w[j >> 3] |= e2m1_rne(v[j] * mult) << (4 * (j & 7));
-  return make_uint2(w[0], w[1]);
+  for (int j = 0; j < 16; ++j) s[j] = v[j] * mult;
+  return make_uint2(encode8_rne(s), encode8_rne(s + 8));
 }
 
-// Encode a 16-block stochastically; r holds the 8 random words of sr_bits16.
 __device__ __forceinline__ uint2 encode16_sr(const float v[16], float mult, const uint32_t r[8]) {
-  uint32_t w[2] = {0u, 0u};
+  float s[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t r16 = (r[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    w[j >> 3] |= e2m1_sr(v[j] * mult, r16) << (4 * (j & 7));
-  }
-  return make_uint2(w[0], w[1]);
+  for (int j = 0; j < 16; ++j) s[j] = v[j] * mult;
+  return make_uint2(encode8_sr(s, r), encode8_sr(s + 8, r + 4));
 }
 
 }  // namespace nvfp4

@@ -6,15 +6,20 @@
 // gradients):
 //   rowwise  : the logical tensor is x [R][C]; a block is 16 consecutive
 //              elements of a row.  One thread owns one block, so the block amax
-//              needs no cross-lane traffic; a wave reads 2 KiB (bf16) and writes
-//              512 B of codes contiguously.
+//              needs no cross-lane traffic.  A contiguous tensor is walked as a
+//              flat array of blocks (two per thread in flight); a strided one row
+//              by row.
 //   colwise  : the logical tensor is x^T [C][R]; a block is 16 consecutive rows
-//              of one column of x.  A thread owns 8 adjacent columns of a 16-row
-//              slab: every load is a 16-byte row segment (a wave reads 1 KiB
-//              contiguous per row) and the transform runs down the registers.
+//              of one column of x.  A workgroup covers 256 columns x 256 rows: a
+//              thread owns 8 adjacent columns of a 16-row slab (every load is a
+//              16-byte row segment, a wave reads 2 x 512 contiguous bytes per row)
+//              and runs the transform down its registers; codes and scales are
+//              gathered in LDS and leave as 128-byte runs of each logical row.
 //   2D       : 16x16 tiles of x; 16 lanes own one tile (a lane per row), the tile
 //              amax is a 16-lane butterfly reduction, and the transposed codes
 //              are regrouped through LDS.
+// Elements are encoded by gfx950's FP4 converters (nearest-even, or stochastic
+// with 16 Philox bits per element), see device.hpp.
 // The tensor amax is a separate reduction pass (atomicMax on the bit pattern of
 // the non-negative float), zeroed by a one-thread kernel: no memset node.
 #include <hip/hip_runtime.h>
@@ -137,8 +142,62 @@ __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const T *__rest
   block_max_to(m, out);
 }
 
-// Rowwise 1D quantization: one thread per 16-block.  grid.x covers the blocks of a
-// row, grid.y strides over rows.
+// One rowwise block: (optional transform,) block amax, scale, encode.  i0 is the
+// block's first logical index (row * C + 16 * kb), which seeds its random bits.
+template <bool RHT, bool SR>
+__device__ __forceinline__ void quant_block_rows(float v[16], uint32_t signs, uint64_t i0, uint64_t seed,
+                                                 uint64_t offset, float s_enc, uint2 &codes, uint32_t &sc) {
+  if (RHT) rht16(v, signs);
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, __builtin_fabsf(v[j]));
+  float mult;
+  block_scale(amax_b, s_enc, sc, mult);
+  if (SR) {
+    uint32_t rb[8];
+    sr_bits16(i0, seed, offset, rb);
+    codes = encode16_sr(v, mult, rb);
+  } else {
+    codes = encode16_rne(v, mult);
+  }
+}
+
+// Rowwise 1D quantization of a contiguous tensor (row stride == C): block b covers
+// elements [16 b, 16 b + 16) of the flat array, its codes bytes [8 b, 8 b + 8) and
+// scale byte b, and its logical index is 16 b.  Each thread has two blocks in
+// flight per step of a grid-stride loop.
+template <typename T, bool RHT, bool SR>
+__global__ __launch_bounds__(kThreads) void quant_rows_flat_kernel(const T *__restrict__ x, int64_t nblocks,
+                                                                  uint32_t signs, uint64_t seed, uint64_t offset,
+                                                                  const float *__restrict__ amax_p,
+                                                                  uint8_t *__restrict__ codes,
+                                                                  uint8_t *__restrict__ scales) {
+  const float s_enc = encode_scale(*amax_p);
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t b0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; b0 < nblocks; b0 += 2 * stride) {
+    const int64_t b1 = b0 + stride;
+    float v0[16], v1[16];
+    load8(x + b0 * 16, v0);
+    load8(x + b0 * 16 + 8, v0 + 8);
+    if (b1 < nblocks) {
+      load8(x + b1 * 16, v1);
+      load8(x + b1 * 16 + 8, v1 + 8);
+    }
+    uint2 c;
+    uint32_t sc;
+    quant_block_rows<RHT, SR>(v0, signs, uint64_t(b0) * 16u, seed, offset, s_enc, c, sc);
+    *reinterpret_cast<uint2 *>(codes + b0 * 8) = c;
+    scales[b0] = uint8_t(sc);
+    if (b1 < nblocks) {
+      quant_block_rows<RHT, SR>(v1, signs, uint64_t(b1) * 16u, seed, offset, s_enc, c, sc);
+      *reinterpret_cast<uint2 *>(codes + b1 * 8) = c;
+      scales[b1] = uint8_t(sc);
+    }
+  }
+}
+
+// Rowwise 1D quantization of a strided tensor: one thread per 16-block.  grid.x
+// covers the blocks of a row, grid.y strides over rows.
 template <typename T, bool RHT, bool SR>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T *__restrict__ x, int64_t R, int64_t C,
                                                              int64_t ld, uint32_t signs, uint64_t seed,
@@ -153,31 +212,25 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T *__restric
     float v[16];
     load8(x + r * ld + kb * 16, v);
     load8(x + r * ld + kb * 16 + 8, v + 8);
-    if (RHT) rht16(v, signs);
-    float amax_b = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, __builtin_fabsf(v[j]));
-    uint32_t sc;
-    float mult;
-    block_scale(amax_b, s_enc, sc, mult);
     uint2 packed;
-    if (SR) {
-      uint32_t rb[8];
-      sr_bits16(uint64_t(r) * uint64_t(C) + uint64_t(kb) * 16u, seed, offset, rb);
-      packed = encode16_sr(v, mult, rb);
-    } else {
-      packed = encode16_rne(v, mult);
-    }
+    uint32_t sc;
+    quant_block_rows<RHT, SR>(v, signs, uint64_t(r) * uint64_t(C) + uint64_t(kb) * 16u, seed, offset, s_enc, packed,
+                              sc);
     *reinterpret_cast<uint2 *>(codes + r * (C / 2) + kb * 8) = packed;
     scales[r * nkb + kb] = uint8_t(sc);
   }
 }
 
 // Columnwise 1D quantization (logical tensor x^T, blocks down the columns of x).
-// A workgroup covers 512 columns; each of its 4 waves takes one 16-row slab per
-// step, lane l owning columns 8l..8l+7, and walks kSlabsPerBlock slabs so that
-// each logical row receives kSlabsPerBlock*8 contiguous code bytes.
-constexpr int kSlabsPerBlock = 8;
+// A workgroup covers kColTile columns of x and kColSlabs 16-row slabs of it.
+// Thread (wave w, lane l) owns columns 8 (l % 32) .. +7 of the tile and slabs
+// 2 w + l / 32 + 8 i (i < kColSlabs / 8).  Codes go to LDS as [column][slab]
+// (8 bytes each; the 16-byte slab pairs of a row XOR-swizzled by bits 3..5 of the
+// row), scales as [column][slab] bytes, then each logical row leaves as
+// contiguous 16-byte stores.
+constexpr int kColTile = 256;   // columns of x (logical rows) per workgroup
+constexpr int kColSlabs = 16;   // 16-row slabs of x (logical blocks) per workgroup
+constexpr int kColRowBytes = kColSlabs * 8;
 
 template <typename T, bool RHT, bool SR>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restrict__ x, int64_t R, int64_t C,
@@ -185,42 +238,83 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restric
                                                              uint64_t offset, const float *__restrict__ amax_p,
                                                              uint8_t *__restrict__ codes,
                                                              uint8_t *__restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint8_t lcodes[kColTile * kColRowBytes];
+  __shared__ uint8_t lscales[kColTile * kColSlabs];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t c0 = int64_t(blockIdx.x) * 512 + lane * 8;
-  if (c0 >= C) return;
-  const int64_t nslab = R / 16;  // logical K = R, blocks per logical row = R/16
+  const int cg = lane & 31;
+  const int64_t c0 = int64_t(blockIdx.x) * kColTile;          // first column of the tile
+  const int64_t slab0 = int64_t(blockIdx.y) * kColSlabs;      // first slab of the tile
+  const int64_t nslab = R / 16;                                // logical blocks per logical row
+  const int64_t cfirst = c0 + 8 * cg;                          // this thread's first column
   const float s_enc = encode_scale(*amax_p);
-  for (int64_t sb = int64_t(blockIdx.y) * kSlabsPerBlock; sb < nslab; sb += int64_t(gridDim.y) * kSlabsPerBlock) {
-    for (int it = wave; it < kSlabsPerBlock; it += kThreads / 64) {
-      const int64_t s = sb + it;
-      if (s >= nslab) break;
-      float v[16][8];
+
+#pragma unroll 1
+  for (int i = 0; i < kColSlabs / 8; ++i) {
+    const int sl = 2 * wave + (lane >> 5) + 8 * i;             // slab within the tile
+    const int64_t s = slab0 + sl;
+    if (s >= nslab || cfirst >= C) continue;
+    float v[16][8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) load8(x + (s * 16 + r) * ld + c0, v[r]);
+    for (int r = 0; r < 16; ++r) load8(x + (s * 16 + r) * ld + cfirst, v[r]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float col[16];
+    for (int j = 0; j < 8; ++j) {
+      float col[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) col[r] = v[r][j];
-        if (RHT) rht16(col, signs);
-        float amax_b = 0.0f;
+      for (int r = 0; r < 16; ++r) col[r] = v[r][j];
+      if (RHT) rht16(col, signs);
+      float amax_b = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) amax_b = fmaxf(amax_b, __builtin_fabsf(col[r]));
-        uint32_t sc;
-        float mult;
-        block_scale(amax_b, s_enc, sc, mult);
-        const int64_t lrow = c0 + j;  // logical row = column of x
-        uint2 packed;
-        if (SR) {
-          uint32_t rb[8];
-          sr_bits16(uint64_t(lrow) * uint64_t(R) + uint64_t(s) * 16u, seed, offset, rb);
-          packed = encode16_sr(col, mult, rb);
-        } else {
-          packed = encode16_rne(col, mult);
-        }
-        *reinterpret_cast<uint2 *>(codes + lrow * (R / 2) + s * 8) = packed;
-        scales[lrow * nslab + s] = uint8_t(sc);
+      for (int r = 0; r < 16; ++r) amax_b = fmaxf(amax_b, __builtin_fabsf(col[r]));
+      uint32_t sc;
+      float mult;
+      block_scale(amax_b, s_enc, sc, mult);
+      const int row = 8 * cg + j;  // logical row within the tile
+      uint2 packed;
+      if (SR) {
+        uint32_t rb[8];
+        sr_bits16(uint64_t(cfirst + j) * uint64_t(R) + uint64_t(s) * 16u, seed, offset, rb);
+        packed = encode16_sr(col, mult, rb);
+      } else {
+        packed = encode16_rne(col, mult);
       }
+      const int pair = (sl >> 1) ^ ((row >> 3) & 7);
+      *reinterpret_cast<uint2 *>(&lcodes[row * kColRowBytes + pair * 16 + (sl & 1) * 8]) = packed;
+      lscales[row * kColSlabs + sl] = uint8_t(sc);
+    }
+  }
+  __syncthreads();
+
+  // codes: row `row` of the tile is logical row c0 + row; its kColSlabs * 8 bytes
+  // start at byte slab0 * 8 of that row.  A 16-byte chunk holds two slabs.
+  const int64_t nvalid = min<int64_t>(int64_t(kColSlabs), nslab - slab0);  // slabs of this tile inside x
+  for (int idx = threadIdx.x; idx < kColTile * (kColRowBytes / 16); idx += kThreads) {
+    const int row = idx / (kColRowBytes / 16), part = idx % (kColRowBytes / 16);
+    const int64_t c = c0 + row;
+    if (c >= C || 2 * part >= nvalid) continue;
+    const int pair = part ^ ((row >> 3) & 7);
+    const uint4 v = *reinterpret_cast<const uint4 *>(&lcodes[row * kColRowBytes + pair * 16]);
+    uint8_t *dst = codes + c * (R / 2) + (slab0 + 2 * part) * 8;
+    if (2 * part + 1 < nvalid) {
+      if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2 *>(dst + 8) = make_uint2(v.z, v.w);
+      }
+    } else {
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+    }
+  }
+  // scales: kColSlabs bytes per logical row
+  for (int row = threadIdx.x; row < kColTile; row += kThreads) {
+    const int64_t c = c0 + row;
+    if (c >= C) continue;
+    uint8_t *dst = scales + c * nslab + slab0;
+    const uint8_t *src = &lscales[row * kColSlabs];
+    if (nvalid == kColSlabs && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    } else {
+      for (int k = 0; k < nvalid; ++k) dst[k] = src[k];
     }
   }
 }
@@ -321,6 +415,13 @@ template <typename T, bool RHT, bool SR>
 void launch_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
                  const fp4_tensor *out, hipStream_t stream) {
   const int64_t nkb = C / 16;
+  if (ld == C) {
+    const int64_t nblocks = R * nkb;
+    hipLaunchKernelGGL((quant_rows_flat_kernel<T, RHT, SR>), dim3(grid_for(nblocks, 2 * kThreads, 256 * 32)),
+                       dim3(kThreads), 0, stream, x, nblocks, signs, seed, offset, out->amax, out->codes,
+                       out->scales);
+    return;
+  }
   dim3 grid(unsigned((nkb + kThreads - 1) / kThreads), unsigned(R < 65535 ? R : 65535));
   hipLaunchKernelGGL((quant_rows_kernel<T, RHT, SR>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, seed,
                      offset, out->amax, out->codes, out->scales);
@@ -330,8 +431,7 @@ template <typename T, bool RHT, bool SR>
 void launch_cols(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
                  const fp4_tensor *out, hipStream_t stream) {
   const int64_t nslab = R / 16;
-  const int64_t ys = (nslab + kSlabsPerBlock - 1) / kSlabsPerBlock;
-  dim3 grid(unsigned((C + 511) / 512), unsigned(ys < 65535 ? ys : 65535));
+  dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
   hipLaunchKernelGGL((quant_cols_kernel<T, RHT, SR>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, seed,
                      offset, out->amax, out->codes, out->scales);
 }
