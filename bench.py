@@ -48,7 +48,7 @@ def source_hash(path):
 def measured_traffic(kernel_src):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it
     was taken on the kernel source as it stands (same hash); else None."""
-    p = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.md")
+    p = os.path.join(ROOT, "profiles", "mlp_up_12b_hbm_traffic.md")
     if not os.path.exists(p):
         return None
     txt = open(p).read()
