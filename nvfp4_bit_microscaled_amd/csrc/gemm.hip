@@ -87,6 +87,16 @@ __device__ __forceinline__ half2v scales2(uint32_t w) { return __builtin_amdgcn_
 
 __device__ __forceinline__ uint32_t word(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
+// Tile at position l of the grouped order: groups of kGroupM tile-rows, walked
+// column by column, so that neighbouring positions share A rows and B columns.
+__device__ __forceinline__ void tile_at(int l, int num_m, int num_n, int &tm, int &tn) {
+  const int per_group = kGroupM * num_n;
+  const int grp = l / per_group, first_m = grp * kGroupM;
+  const int gsz = min(num_m - first_m, kGroupM);
+  tm = first_m + (l % per_group) % gsz;
+  tn = (l % per_group) / gsz;
+}
+
 // Tile coordinates of this workgroup (see the header comment).
 __device__ __forceinline__ void tile_of(int num_m, int num_n, int &tm, int &tn) {
   int pid = blockIdx.x;
@@ -122,6 +132,108 @@ __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&
         }
       }
     }
+}
+
+// Epilogue of the main kernel, whose MFMAs take the B tile as first operand so
+// that acc[i][j] holds the 32x32 block C^T: lane l owns row m = 32 i + l % 32 of C
+// and, in register group q, the 4 consecutive columns n = 32 j + 8 q + 4 (l / 32)
+// .. +3.  Each group is scaled by the two tensor decode scales and leaves as one
+// 8-byte (bf16, rounded to nearest-even in pairs) or 16-byte (fp32) store.
+// CHECK: the tile may stick out of C (rows or columns past the edge are skipped;
+// the launcher guarantees N % 4 == 0, so a group is wholly inside or outside).
+// The launcher also guarantees a 16-byte aligned C and ldc % 4 == 0.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <int TM, int TN, bool CHECK>
+__device__ __forceinline__ void store_tiles_t(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
+                                              int64_t n0, int lr, int g) {
+  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + 32 * i + lr;
+    if (CHECK && m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + 32 * j + 8 * q + 4 * g;
+        if (CHECK && n >= p.N) continue;
+        const float v0 = acc[i][j][4 * q] * gscale, v1 = acc[i][j][4 * q + 1] * gscale;
+        const float v2 = acc[i][j][4 * q + 2] * gscale, v3 = acc[i][j][4 * q + 3] * gscale;
+        if (p.c_bf16) {
+          const bf16x4 h = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+          *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = h;
+        } else {
+          *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) = make_float4(v0, v1, v2, v3);
+        }
+      }
+  }
+}
+
+// Epilogue of the main kernel through LDS (free once the last stage is read): each
+// wave writes its 128x128 block (C^T layout as above, scaled and converted) into
+// a private 32 KB region, row-major with the 16-byte chunks of a row XOR-swizzled
+// by the row, then reads it back a chunk per lane so that every store instruction
+// writes whole 128-byte lines of C.  fp32 outputs go in two passes of 64 rows.
+// CHECK as for store_tiles_t (N % 4 == 0; C 16-byte aligned, ldc % 4 == 0).
+template <int TM, int TN, bool CHECK>
+__device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
+                                                int64_t n0, int lane, uint8_t *region) {
+  static_assert(TM == 4 && TN == 4, "a 128x128 block per wave");
+  const int lr = lane & 31, g = lane >> 5;
+  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
+  if (p.c_bf16) {
+    // 128 rows x 256 bytes; chunk c of row r stored at chunk c ^ (r & 15)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = 32 * i + lr;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x4 h = {(__bf16)(acc[i][j][4 * q] * gscale), (__bf16)(acc[i][j][4 * q + 1] * gscale),
+                            (__bf16)(acc[i][j][4 * q + 2] * gscale), (__bf16)(acc[i][j][4 * q + 3] * gscale)};
+          *reinterpret_cast<bf16x4 *>(region + r * 256 + (((4 * j + q) ^ (r & 15)) << 4) + 8 * g) = h;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int idx = 64 * k + lane, r = idx >> 4, c = idx & 15;
+      const uint4 v = *reinterpret_cast<const uint4 *>(region + r * 256 + ((c ^ (r & 15)) << 4));
+      const int64_t m = m0 + r, n = n0 + 8 * c;
+      uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n;
+      if (!CHECK || (m < p.M && n + 8 <= p.N)) *reinterpret_cast<uint4 *>(dst) = v;
+      else if (m < p.M && n < p.N) *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+    }
+  } else {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // 64 rows x 512 bytes; chunk c of row r stored at chunk c ^ (r & 31)
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * half + ii, r = 32 * ii + lr;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = make_float4(acc[i][j][4 * q] * gscale, acc[i][j][4 * q + 1] * gscale,
+                                         acc[i][j][4 * q + 2] * gscale, acc[i][j][4 * q + 3] * gscale);
+            *reinterpret_cast<float4 *>(region + r * 512 + (((8 * j + 2 * q + g) ^ (r & 31)) << 4)) = v;
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+      for (int k = 0; k < 32; ++k) {
+        const int idx = 64 * k + lane, r = idx >> 5, c = idx & 31;
+        const float4 v = *reinterpret_cast<const float4 *>(region + r * 512 + ((c ^ (r & 31)) << 4));
+        const int64_t m = m0 + 64 * half + r, n = n0 + 4 * c;
+        if (!CHECK || (m < p.M && n < p.N))
+          *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) = v;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next half
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -181,15 +293,34 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "code DMA: whole instructions per wave");
   static_assert((BM + BN) % 64 == 0, "scale DMA: whole instructions");
   static_assert(STAGE % 1024 == 0, "stage alignment");
+  static_assert(2 * STAGE >= NW * 32768, "epilogue staging fits in LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int64_t M = p.M, N = p.N;
-  int tm, tn;
-  tile_of(int((M + BM - 1) / BM), int((N + BN - 1) / BN), tm, tn);
-  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const uint32_t kbytes = uint32_t(p.K / 2), nkb = uint32_t(p.K / 16);
   const int nst = int(p.K / 256);
+
+  // Persistent tiles.  The grid has at most one workgroup per CU; with a grid that
+  // is a multiple of 8 and smaller than the tile count, workgroup w runs on XCD
+  // w % 8, which owns the contiguous eighth of the tile sequence; its j-th
+  // workgroup takes tiles j, j + G/8, ... of that range, so the XCD's workgroups
+  // always work on neighbouring tiles.  Otherwise workgroup w takes w, w + G, ...
+  const int num_m = int((M + BM - 1) / BM), num_n = int((N + BN - 1) / BN);
+  const int ntiles = num_m * num_n;
+  int L, Lend, Lstride;
+  if ((gridDim.x & 7) == 0 && int(gridDim.x) < ntiles) {
+    const int x = blockIdx.x & 7;
+    L = int(int64_t(ntiles) * x / 8) + int(blockIdx.x >> 3);
+    Lend = int(int64_t(ntiles) * (x + 1) / 8);
+    Lstride = int(gridDim.x >> 3);
+  } else {
+    L = blockIdx.x;
+    Lend = ntiles;
+    Lstride = gridDim.x;
+  }
+  if (L >= Lend) return;
+  int64_t m0, n0;
 
   // DMA sources.  Unit u (16 bytes) of a wave's instruction j sits at row
   // (j*NW + wave)*8 + lane/8 of the tile, physical chunk lane%8, and holds that
@@ -210,17 +341,23 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   const u32x4 rsb = make_rsrc(p.b_codes, uint32_t(N) * kbytes);
   const u32x4 rssa = make_rsrc(p.a_scales, uint32_t((M + (1 << p.a_shift) - 1) >> p.a_shift) * nkb);
   const u32x4 rssb = make_rsrc(p.b_scales, uint32_t((N + (1 << p.b_shift) - 1) >> p.b_shift) * nkb);
-  uint32_t va[CLAMP ? JA : 1], vb[CLAMP ? JB : 1];
+  uint32_t va[CLAMP ? JA : 1], vb[CLAMP ? JB : 1], vs[NSC];
+  // tile coordinates of sequence position l (groups of 8 tile-rows) and its DMA offsets
+  auto set_tile = [&](int l) {
+    int tm, tn;
+    tile_at(l, num_m, num_n, tm, tn);
+    m0 = int64_t(tm) * BM;
+    n0 = int64_t(tn) * BN;
 #pragma unroll
-  for (int j = 0; j < (CLAMP ? JA : 1); ++j) va[j] = uint32_t(m0 + row0 + NW * 8 * j) * kbytes + lchunk;
+    for (int j = 0; j < (CLAMP ? JA : 1); ++j) va[j] = uint32_t(m0 + row0 + NW * 8 * j) * kbytes + lchunk;
 #pragma unroll
-  for (int j = 0; j < (CLAMP ? JB : 1); ++j) vb[j] = uint32_t(n0 + row0 + NW * 8 * j) * kbytes + lchunk;
-  uint32_t vs[NSC];
+    for (int j = 0; j < (CLAMP ? JB : 1); ++j) vb[j] = uint32_t(n0 + row0 + NW * 8 * j) * kbytes + lchunk;
 #pragma unroll
-  for (int j = 0; j < NSC; ++j) {
-    const int u = (j * NW + wave) * 64 + lane;
-    vs[j] = u < BM ? uint32_t((m0 + u) >> p.a_shift) * nkb : uint32_t((n0 + (u - BM)) >> p.b_shift) * nkb;
-  }
+    for (int j = 0; j < NSC; ++j) {
+      const int u = (j * NW + wave) * 64 + lane;
+      vs[j] = u < BM ? uint32_t((m0 + u) >> p.a_shift) * nkb : uint32_t((n0 + (u - BM)) >> p.b_shift) * nkb;
+    }
+  };
 
   // global -> LDS: DMA instruction d (0 .. NDMA-1) of stage kt into buffer buf:
   // A code rows for d < JA, then B code rows, then the scale rows.  Asynchronous:
@@ -338,7 +475,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
         static_for<NMF>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
           constexpr int i = k / TN, j = k % TN;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][i], op[cur][TM + j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][TM + j], op[cur][i], acc[i][j], 0, 0, 0);
           if constexpr (has_next) dequant_half(nslot, ns, cur ^ 1, k / 2, k % 2);
           if constexpr (s == 0 && next_q && k < 2 * T)
             lds_read(q < 3 ? buf : buf ^ 1, q < 3 ? q + 1 : 0, slot ^ 1, k);
@@ -351,25 +488,49 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
     });
   };
 
+  // Tile loop.  The first two stages of a tile are in flight before its loop
+  // starts; after the last stage every wave passes a barrier (LDS free), the next
+  // tile's first two stages are issued, and only then are this tile's outputs
+  // stored, so store and load latencies overlap.
+  set_tile(L);
   issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   issue(min(1, nst - 1), 1);
-  // quarter 0 of stage 0 and the operands of its first substep
+  for (;;) {
+    // stage 0 (and 1) landed, and the previous tile's stores are done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // quarter 0 of stage 0 and the operands of its first substep
 #pragma unroll
-  for (int r = 0; r < 2 * T; ++r) lds_read(0, 0, 0, r);
+    for (int r = 0; r < 2 * T; ++r) lds_read(0, 0, 0, r);
 #pragma unroll
-  for (int i = 0; i < T; ++i) scd[0][i] = scales2(scw[0][i]);
+    for (int i = 0; i < T; ++i) scd[0][i] = scales2(scw[0][i]);
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    dequant_half(0, 0, 0, i, 0);
-    dequant_half(0, 0, 0, i, 1);
-  }
-  for (int kt = 0; kt + 1 < nst; ++kt) stage(kt, std::false_type{});
-  stage(nst - 1, std::true_type{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int i = 0; i < T; ++i) {
+      dequant_half(0, 0, 0, i, 0);
+      dequant_half(0, 0, 0, i, 1);
+    }
+    for (int kt = 0; kt + 1 < nst; ++kt) stage(kt, std::false_type{});
+    stage(nst - 1, std::true_type{});
 
-  store_tiles<TM, TN>(p, acc, m0 + wm, n0 + wn, lr, g);
+    const int Lnext = L + Lstride;
+    // the clamped DMA of the last stages has landed and no wave reads LDS any more
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    store_tiles_lds<TM, TN, CLAMP>(p, acc, m0 + wm, n0 + wn, lane, lds + wave * 32768);
+    // every wave is done with its staging region before the next tile's DMA lands
+    __syncthreads();
+    if (Lnext < Lend) {
+      set_tile(Lnext);
+      issue(0, 0);
+      issue(min(1, nst - 1), 1);
+    }
+    if (Lnext >= Lend) break;
+    L = Lnext;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -510,6 +671,19 @@ __global__ __launch_bounds__(256) void gemm_edge_kernel(GemmParams p) {
   store_tiles<TM, TN>(p, acc, m0 + wm, n0 + wn, lr, g);
 }
 
+// Compute units of the current device (queried once per device).
+unsigned compute_units() {
+  static unsigned cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = unsigned(n);
+  }
+  return cached[dev];
+}
+
 template <int BM, int BN>
 unsigned tiles_for(const GemmParams &p) {
   return unsigned(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
@@ -537,14 +711,20 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
   if (p.M == 0 || p.N == 0) return hipSuccess;
   auto al = [](const void *q, uintptr_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
   // main path: whole 256-element K stages, 16-byte aligned codes and scale rows,
-  // and every DMA offset within 32 bits
+  // every DMA offset within 32 bits, and an output the vector stores can write
   const bool main_path = p.K >= 256 && p.K % 256 == 0 && al(a->codes, 16) && al(b->codes, 16) &&
                          al(a->scales, 16) && al(b->scales, 16) && (p.M + 256) * (p.K / 2) < (int64_t(1) << 32) &&
-                         (p.N + 256) * (p.K / 2) < (int64_t(1) << 32);
-  if (main_path && p.M % 256 == 0 && p.N % 256 == 0)
-    hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false>), dim3(tiles_for<256, 256>(p)), dim3(256), 0, stream, p);
-  else if (main_path)
-    hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true>), dim3(tiles_for<256, 256>(p)), dim3(256), 0, stream, p);
+                         (p.N + 256) * (p.K / 2) < (int64_t(1) << 32) &&
+                         al(c, 16) && ldc % 4 == 0 && p.N % 4 == 0;
+  if (main_path) {
+    // persistent: one workgroup per CU (its 144 KB of LDS admit no second one)
+    const unsigned tiles = tiles_for<256, 256>(p), cus = compute_units();
+    const dim3 grid(tiles < cus ? tiles : cus);
+    if (p.M % 256 == 0 && p.N % 256 == 0)
+      hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true>), grid, dim3(256), 0, stream, p);
+  }
   else
     hipLaunchKernelGGL(gemm_edge_kernel, dim3(tiles_for<128, 128>(p)), dim3(256), 0, stream, p);
   return hipGetLastError();
