@@ -38,6 +38,13 @@ CASES = [
     (129, 257, 4096, False, False),
     (1024, 1024, 4096, True, True),
     (64, 16, 16, False, False),
+    # main path with ragged edges (rows/columns past M, N read as zeros, not stored)
+    (300, 272, 512, False, True),
+    (300, 260, 512, False, False),
+    # more 256x256 tiles than CUs: persistent loop; 17x16 = 272 tiles, 17x17 = 289
+    # (an XCD split that is not even), ragged in both dimensions
+    (4352, 4096, 256, False, True),
+    (4100, 4100, 256, False, False),
 ]
 
 
