@@ -115,6 +115,25 @@ FP4_API fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, in
                         uint32_t rht_signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
                         const fp4_tensor *out_t, hipStream_t stream);
 
+/* Both quantized layouts of one tensor x [rows][cols] in one call (the pair the
+ * backward pass needs of dy -- dgrad takes dy rowwise, wgrad takes dy^T -- and the
+ * pair fprop and wgrad need of x), with both tensor amaxes taken in one read of x:
+ *   out_rows: x quantized 1D along its rows ([rows][cols], as fp4_quantize with flags 0
+ *             or FP4_Q_SR, Philox offset offset_rows);
+ *   out_cols: x^T quantized 1D (blocks down the columns of x, [cols][rows]), after the
+ *             16-point Hadamard transform if FP4_Q_RHT is set (as fp4_quantize with
+ *             FP4_Q_COLWISE [| FP4_Q_RHT] [| FP4_Q_SR], Philox offset offset_cols).
+ * Codes, scales and amaxes are bit-identical to those two fp4_quantize calls.
+ * flags: FP4_Q_SR (both layouts stochastic), FP4_Q_RHT (columnwise layout
+ * transformed), FP4_Q_AMAX_GIVEN (out_rows->amax and out_cols->amax already hold the
+ * two tensor amaxes; otherwise both are computed first, in one read of x, then each
+ * layout is written by its own kernel).
+ * Needs: rows and cols multiples of 16; x 16-byte aligned, ld a multiple of 8. */
+FP4_API fp4_status fp4_quantize_dual(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                                     uint32_t flags, uint32_t rht_signs, uint64_t seed, uint64_t offset_rows,
+                                     uint64_t offset_cols, const fp4_tensor *out_rows, const fp4_tensor *out_cols,
+                                     hipStream_t stream);
+
 /* Block-scaled GEMM with FP32 accumulation: C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k]
  * for A [M][K] and B [N][K] (both K-major, M = a->rows, N = b->rows, K = a->cols =
  * b->cols, K a multiple of 16), written as fp32 or bf16 (nearest-even) with row

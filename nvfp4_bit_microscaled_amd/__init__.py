@@ -26,8 +26,8 @@ STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_ALIGN"
           5: "FP4_ERR_MODE", 6: "FP4_ERR_MISMATCH", 7: "FP4_ERR_HIP"}
 
 # every symbol the header declares
-EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_gemm", "fp4_linear_fprop", "fp4_linear_dgrad",
-           "fp4_linear_wgrad", "fp4_status_string")
+EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_gemm", "fp4_linear_fprop",
+           "fp4_linear_dgrad", "fp4_linear_wgrad", "fp4_status_string")
 
 
 class Fp4Error(RuntimeError):
@@ -60,6 +60,7 @@ def load():
         "fp4_tensor_bytes": [i64, i64, i32, sz, sz],
         "fp4_amax": [vp, i32, i64, i64, i64, u32, u32, vp, vp],
         "fp4_quantize": [vp, i32, i64, i64, i64, u32, u32, u64, u64, tp, tp, vp],
+        "fp4_quantize_dual": [vp, i32, i64, i64, i64, u32, u32, u64, u64, u64, tp, tp, vp],
         "fp4_gemm": [tp, tp, vp, i32, i64, vp],
         "fp4_linear_fprop": [vp, vp, i32, vp, i32, i64, i64, i64, tp, tp, tp, vp],
         "fp4_linear_dgrad": [vp, i32, tp, vp, i32, i64, i64, i64, u64, u64, tp, vp],
@@ -142,6 +143,13 @@ def fp4_quantize(x: torch.Tensor, flags: int, rht_signs: int, seed: int, offset:
     _check("fp4_quantize", load().fp4_quantize(x.data_ptr(), _dtype(x), x.shape[0], x.shape[1], _ld(x), flags,
                                                rht_signs, seed, offset, out.desc,
                                                out_t.desc if out_t is not None else None, _stream(stream)))
+
+
+def fp4_quantize_dual(x: torch.Tensor, flags: int, rht_signs: int, seed: int, offset_rows: int, offset_cols: int,
+                      out_rows: QTensor, out_cols: QTensor, stream=None):
+    _check("fp4_quantize_dual", load().fp4_quantize_dual(x.data_ptr(), _dtype(x), x.shape[0], x.shape[1], _ld(x), flags,
+                                                         rht_signs, seed, offset_rows, offset_cols, out_rows.desc,
+                                                         out_cols.desc, _stream(stream)))
 
 
 def fp4_gemm(a: QTensor, b: QTensor, c: torch.Tensor, stream=None):

@@ -99,6 +99,19 @@ fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t co
       nvfp4::launch_quantize(x, dtype, rows, cols, ld, flags, rht_signs & 0xFFFFu, seed, offset, out, out_t, stream));
 }
 
+fp4_status fp4_quantize_dual(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
+                             uint32_t rht_signs, uint64_t seed, uint64_t offset_rows, uint64_t offset_cols,
+                             const fp4_tensor *out_rows, const fp4_tensor *out_cols, hipStream_t stream) {
+  if (flags & ~(FP4_Q_SR | FP4_Q_RHT | FP4_Q_AMAX_GIVEN)) return FP4_ERR_MODE;
+  fp4_status s = check_input(x, dtype, rows, cols, ld);
+  if (s != FP4_OK) return s;
+  if (rows % 16 != 0 || cols % 16 != 0) return FP4_ERR_SHAPE;
+  if ((s = check_tensor(out_rows, rows, cols, 0)) != FP4_OK) return s;
+  if ((s = check_tensor(out_cols, cols, rows, 0)) != FP4_OK) return s;
+  return from_hip(nvfp4::launch_quantize_dual(x, dtype, rows, cols, ld, flags, rht_signs & 0xFFFFu, seed, offset_rows,
+                                              offset_cols, out_rows, out_cols, stream));
+}
+
 fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                     hipStream_t stream) {
   fp4_status s = check_gemm(a, b, c, c_dtype, ldc);

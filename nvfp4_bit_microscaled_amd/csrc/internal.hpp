@@ -16,6 +16,10 @@ hipError_t launch_quantize(const void *x, fp4_dtype dtype, int64_t R, int64_t C,
                            uint32_t signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
                            const fp4_tensor *out_t, hipStream_t stream);
 
+hipError_t launch_quantize_dual(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
+                                uint32_t signs, uint64_t seed, uint64_t off_rows, uint64_t off_cols,
+                                const fp4_tensor *rows, const fp4_tensor *cols, hipStream_t stream);
+
 hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                        hipStream_t stream);
 

@@ -97,6 +97,29 @@ __global__ __launch_bounds__(kThreads) void amax_plain_kernel(const T *__restric
   block_max_to(m, out);
 }
 
+// Plain |x| max of a contiguous tensor: four 16-byte loads in flight per thread.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict__ x, int64_t nchunks, float *out) {
+  float m = 0.0f;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nchunks; i += 4 * stride) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = i + u * stride;
+      if (j < nchunks) load8(x + j * 8, v[u]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf(v[u][e]));
+  }
+  block_max_to(m, out);
+}
+
 // amax after the Hadamard transform along rows (16 contiguous elements).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const T *__restrict__ x, int64_t R, int64_t C,
@@ -232,6 +255,46 @@ constexpr int kColTile = 256;   // columns of x (logical rows) per workgroup
 constexpr int kColSlabs = 16;   // 16-row slabs of x (logical blocks) per workgroup
 constexpr int kColRowBytes = kColSlabs * 8;
 
+// Store a columnwise tile gathered in LDS (see quant_cols_kernel): row `row` of the
+// tile is logical row c0 + row; its kColSlabs * 8 code bytes start at byte
+// slab0 * 8 of that row, a 16-byte chunk holding two slabs; its scales are
+// kColSlabs bytes from scale slab0.
+__device__ __forceinline__ void store_col_tile(const uint8_t *lcodes, const uint8_t *lscales, int64_t R, int64_t C,
+                                               int64_t c0, int64_t slab0, uint8_t *__restrict__ codes,
+                                               uint8_t *__restrict__ scales) {
+  const int64_t nslab = R / 16;
+  const int64_t nvalid = min<int64_t>(int64_t(kColSlabs), nslab - slab0);  // slabs of this tile inside x
+  for (int idx = threadIdx.x; idx < kColTile * (kColRowBytes / 16); idx += kThreads) {
+    const int row = idx / (kColRowBytes / 16), part = idx % (kColRowBytes / 16);
+    const int64_t c = c0 + row;
+    if (c >= C || 2 * part >= nvalid) continue;
+    const int pair = part ^ ((row >> 3) & 7);
+    const uint4 v = *reinterpret_cast<const uint4 *>(&lcodes[row * kColRowBytes + pair * 16]);
+    uint8_t *dst = codes + c * (R / 2) + (slab0 + 2 * part) * 8;
+    if (2 * part + 1 < nvalid) {
+      if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2 *>(dst + 8) = make_uint2(v.z, v.w);
+      }
+    } else {
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+    }
+  }
+  // scales: kColSlabs bytes per logical row
+  for (int row = threadIdx.x; row < kColTile; row += kThreads) {
+    const int64_t c = c0 + row;
+    if (c >= C) continue;
+    uint8_t *dst = scales + c * nslab + slab0;
+    const uint8_t *src = &lscales[row * kColSlabs];
+    if (nvalid == kColSlabs && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    } else {
+      for (int k = 0; k < nvalid; ++k) dst[k] = src[k];
+    }
+  }
+}
 template <typename T, bool RHT, bool SR>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restrict__ x, int64_t R, int64_t C,
                                                              int64_t ld, uint32_t signs, uint64_t seed,
@@ -284,39 +347,39 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restric
   }
   __syncthreads();
 
-  // codes: row `row` of the tile is logical row c0 + row; its kColSlabs * 8 bytes
-  // start at byte slab0 * 8 of that row.  A 16-byte chunk holds two slabs.
-  const int64_t nvalid = min<int64_t>(int64_t(kColSlabs), nslab - slab0);  // slabs of this tile inside x
-  for (int idx = threadIdx.x; idx < kColTile * (kColRowBytes / 16); idx += kThreads) {
-    const int row = idx / (kColRowBytes / 16), part = idx % (kColRowBytes / 16);
-    const int64_t c = c0 + row;
-    if (c >= C || 2 * part >= nvalid) continue;
-    const int pair = part ^ ((row >> 3) & 7);
-    const uint4 v = *reinterpret_cast<const uint4 *>(&lcodes[row * kColRowBytes + pair * 16]);
-    uint8_t *dst = codes + c * (R / 2) + (slab0 + 2 * part) * 8;
-    if (2 * part + 1 < nvalid) {
-      if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-        *reinterpret_cast<uint4 *>(dst) = v;
-      } else {
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
-        *reinterpret_cast<uint2 *>(dst + 8) = make_uint2(v.z, v.w);
+  store_col_tile(lcodes, lscales, R, C, c0, slab0, codes, scales);
+}
+
+
+// Both tensor amaxes of a dual quantization in one read: |x| (rowwise layout) and
+// |x| after the transform down 16-row slabs (columnwise layout).  A thread owns 8
+// adjacent columns of one slab.
+template <typename T, bool RHT>
+__global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict__ x, int64_t R, int64_t C, int64_t ld,
+                                                            uint32_t signs, float *out_rows, float *out_cols) {
+  const int64_t cchunks = C / 8, slabs = R / 16;
+  const int64_t total = cchunks * slabs;
+  float mr = 0.0f, mc = 0.0f;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads) {
+    const int64_t sl = i / cchunks, c = (i - sl * cchunks) * 8;
+    float v[16][8];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load8(x + (sl * 16 + r) * ld + c, v[r]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        col[r] = v[r][j];
+        mr = fmaxf(mr, __builtin_fabsf(col[r]));
       }
-    } else {
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+      if (RHT) rht16(col, signs);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mc = fmaxf(mc, __builtin_fabsf(col[r]));
     }
   }
-  // scales: kColSlabs bytes per logical row
-  for (int row = threadIdx.x; row < kColTile; row += kThreads) {
-    const int64_t c = c0 + row;
-    if (c >= C) continue;
-    uint8_t *dst = scales + c * nslab + slab0;
-    const uint8_t *src = &lscales[row * kColSlabs];
-    if (nvalid == kColSlabs && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
-    } else {
-      for (int k = 0; k < nvalid; ++k) dst[k] = src[k];
-    }
-  }
+  block_max_to(mr, out_rows);
+  block_max_to(mc, out_cols);
 }
 
 // 2D (16x16 tile) nearest-even quantization of x [R][C] (R, C multiples of 16).
@@ -398,7 +461,11 @@ hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
   hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, out);
   const int64_t cap = 256 * 16;  // 16 workgroups per CU are plenty for a streaming reduction
   if (R == 0 || C == 0) return hipGetLastError();
-  if (!(flags & FP4_Q_RHT)) {
+  if (!(flags & FP4_Q_RHT) && ld == C) {
+    // a read-only stream runs best with a moderate grid (measured on the MI355X)
+    hipLaunchKernelGGL(amax_flat_kernel<T>, dim3(grid_for(R * (C / 8), kThreads * 4, 2048)), dim3(kThreads), 0,
+                       stream, x, R * (C / 8), out);
+  } else if (!(flags & FP4_Q_RHT)) {
     hipLaunchKernelGGL(amax_plain_kernel<T>, dim3(grid_for(R * (C / 8), kThreads * 4, cap)), dim3(kThreads), 0,
                        stream, x, R, C, ld, out);
   } else if (flags & FP4_Q_COLWISE) {
@@ -417,7 +484,7 @@ void launch_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, u
   const int64_t nkb = C / 16;
   if (ld == C) {
     const int64_t nblocks = R * nkb;
-    hipLaunchKernelGGL((quant_rows_flat_kernel<T, RHT, SR>), dim3(grid_for(nblocks, 2 * kThreads, 256 * 32)),
+    hipLaunchKernelGGL((quant_rows_flat_kernel<T, RHT, SR>), dim3(grid_for(nblocks, 2 * kThreads, 1 << 20)),
                        dim3(kThreads), 0, stream, x, nblocks, signs, seed, offset, out->amax, out->codes,
                        out->scales);
     return;
@@ -474,7 +541,48 @@ hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t 
   return hipGetLastError();
 }
 
+// Dual quantization: both amaxes in one read of x (unless given), then the rowwise
+// and the columnwise kernels.  (A single kernel writing both layouts from one read
+// measured slower on the MI355X: the encoders are bound by vector-ALU work, which
+// fusion does not reduce, and the fused kernel's registers halve occupancy.)
+template <typename T>
+hipError_t dual_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, uint64_t seed,
+                     uint64_t off_rows, uint64_t off_cols, const fp4_tensor *rows, const fp4_tensor *cols,
+                     hipStream_t stream) {
+  const bool rht = flags & FP4_Q_RHT, sr = flags & FP4_Q_SR;
+  if (!(flags & FP4_Q_AMAX_GIVEN)) {
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, rows->amax);
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, cols->amax);
+    if (R > 0 && C > 0) {
+      const dim3 grid(grid_for((R / 16) * (C / 8), kThreads, 2048));
+      if (rht)
+        hipLaunchKernelGGL((amax_dual_kernel<T, true>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
+                           rows->amax, cols->amax);
+      else
+        hipLaunchKernelGGL((amax_dual_kernel<T, false>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
+                           rows->amax, cols->amax);
+    }
+  }
+  if (R == 0 || C == 0) return hipGetLastError();
+  const uint32_t given = flags | FP4_Q_AMAX_GIVEN;
+  hipError_t e = quantize_impl(x, R, C, ld, (given & FP4_Q_SR) | FP4_Q_AMAX_GIVEN, signs, seed, off_rows, rows,
+                               nullptr, stream);
+  if (e != hipSuccess) return e;
+  const uint32_t fc = FP4_Q_COLWISE | FP4_Q_AMAX_GIVEN | (rht ? FP4_Q_RHT : 0u) | (sr ? FP4_Q_SR : 0u);
+  return quantize_impl(x, R, C, ld, fc, signs, seed, off_cols, cols, nullptr, stream);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_dual(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
+                                uint32_t signs, uint64_t seed, uint64_t off_rows, uint64_t off_cols,
+                                const fp4_tensor *rows, const fp4_tensor *cols, hipStream_t stream) {
+  if (dtype == FP4_BF16)
+    return dual_impl(static_cast<const uint16_t *>(x), R, C, ld, flags, signs, seed, off_rows, off_cols, rows, cols,
+                     stream);
+  return dual_impl(static_cast<const float *>(x), R, C, ld, flags, signs, seed, off_rows, off_cols, rows, cols,
+                   stream);
+}
 
 __global__ void copy_f32_kernel(const float *src, float *dst) { *dst = *src; }
 

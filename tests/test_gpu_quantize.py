@@ -124,3 +124,42 @@ def test_sr_offsets_decorrelate_on_gpu(fp4):
     torch.cuda.synchronize()
     frac = (a.codes != b.codes).float().mean().item()
     assert 0.2 < frac < 0.95
+
+
+DUAL_CASES = [
+    # (R, C, flags): the dy pair (SR, transformed columns), the x pair (RNE, transformed
+    # columns), plain, ragged tiles (C not a multiple of 256, R not of 256)
+    (256, 512, "sr_rht"),
+    (512, 256, "rht"),
+    (272, 400, "sr"),
+    (48, 784, "none"),
+]
+
+
+@pytest.mark.parametrize("case", DUAL_CASES, ids=lambda c: f"{c[0]}x{c[1]}_{c[2]}")
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_quantize_dual_matches_two_single_quantizations(fp4, oracle, case, dtype):
+    """One read of x, two layouts: each bit-exact against the oracle's own
+    quantization of that layout (rowwise with offset_rows, columnwise with
+    offset_cols), amaxes included."""
+    R, C, mode = case
+    sr, rht = "sr" in mode, "rht" in mode
+    rng = np.random.default_rng(R * 7 + C)
+    x = workloads.laplace(rng, (R, C)) if sr else workloads.normal(rng, (R, C), outlier_frac=0.01)
+    xt = torch.from_numpy(x).to(dtype)
+    xf = xt.float().numpy()
+    signs, seed, o_r, o_c = 0xA5C3, 0x1234_5678_9ABC, 11, 12
+    flags = (fp4.Q_SR if sr else 0) | (fp4.Q_RHT if rht else 0)
+    qr, qc = fp4.QTensor(R, C), fp4.QTensor(C, R)
+    fp4.fp4_quantize_dual(dev(xt), flags, signs, seed, o_r, o_c, qr, qc)
+    ora_r = oracle.quantize(xf, sr=sr, seed=seed, offset=o_r)
+    ora_c = oracle.quantize(xf, colwise=True, rht=rht, sr=sr, signs=signs, seed=seed, offset=o_c)
+    assert_q_equal(host_q(qr), ora_r, f"dual rows {case}")
+    assert_q_equal(host_q(qc), ora_c, f"dual cols {case}")
+    # with the amaxes given, the same codes
+    qr2, qc2 = fp4.QTensor(R, C), fp4.QTensor(C, R)
+    qr2.amax.copy_(qr.amax)
+    qc2.amax.copy_(qc.amax)
+    fp4.fp4_quantize_dual(dev(xt), flags | fp4.Q_AMAX_GIVEN, signs, seed, o_r, o_c, qr2, qc2)
+    assert_q_equal(host_q(qr2), ora_r, f"dual rows, amax given {case}")
+    assert_q_equal(host_q(qc2), ora_c, f"dual cols, amax given {case}")

@@ -114,3 +114,19 @@ def test_linear_rejects_bad_arguments(lib):
     assert ok(x, w, 0, y, 0, M, N, K, Q(desc(M, K)), Q(desc(N, K, 1)), Q(desc(N, K, 1)), None) == 6  # W^T shape
     assert lib.fp4_linear_dgrad(x, 0, Q(desc(N, K, 1)), y, 0, M, N, K, 0, 1, Q(desc(M, N)), None) == 6
     assert lib.fp4_linear_wgrad(x, w, 0, y, 1, M, N, K, 0, 0, 2, Q(desc(N, M)), Q(desc(M, K)), None) == 6
+
+
+def test_quantize_dual_rejects_bad_arguments(lib):
+    import nvfp4_bit_microscaled_amd as m
+    x = ctypes.c_void_p(0x1000)
+    Q = ctypes.byref
+    R, C = 64, 128
+    rows, cols = desc(R, C), desc(C, R)
+    f = lib.fp4_quantize_dual
+    assert f(x, 0, R, C, C, 1 << 9, 0, 0, 0, 0, Q(rows), Q(cols), None) == 5  # unknown flag
+    assert f(x, 0, R, C, C, m.Q_2D, 0, 0, 0, 0, Q(rows), Q(cols), None) == 5  # no 2D mode
+    assert f(x, 0, 40, C, C, 0, 0, 0, 0, 0, Q(desc(40, C)), Q(desc(C, 40)), None) == 2  # rows % 16
+    assert f(x, 0, R, C, C, 0, 0, 0, 0, 0, Q(cols), Q(cols), None) == 6  # rowwise descriptor shape
+    assert f(x, 0, R, C, C, 0, 0, 0, 0, 0, Q(rows), Q(rows), None) == 6  # columnwise descriptor shape
+    assert f(None, 0, R, C, C, 0, 0, 0, 0, 0, Q(rows), Q(cols), None) == 1
+    assert f(x, 0, R, C, C, 0, 0, 0, 0, 0, None, Q(cols), None) == 1
