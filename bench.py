@@ -1,9 +1,10 @@
 """Benchmark: NVFP4 linear-layer step (fprop + dgrad + wgrad) on one MI355X.
 
-One step is the whole hot path over one batch: X 1D nearest-even, W 2D (16x16)
-nearest-even with W^T emitted, Y = X.W^T; dY 1D stochastic, dX = dY.W; dY^T and
-X^T with the 16-point random Hadamard transform (dY stochastic), dW = dY^T.X.
-Each quantize call includes its amax pass.  Inputs are seeded synthetic tensors
+One step is the whole hot path over one batch: X 1D nearest-even and X^T with the
+16-point random Hadamard transform (one dual quantization), W 2D (16x16)
+nearest-even with W^T emitted, Y = X.W^T; dY 1D stochastic and dY^T transformed
+and stochastic (one dual quantization), dX = dY.W, dW = dY^T.X.  Each quantize
+call includes its amax pass.  Inputs are seeded synthetic tensors
 (workloads/) already resident in HBM when the timed region starts.
 
 Prints one JSON line.  `value` is whole-step NVFP4 linear TFLOP/s (3 GEMMs of
@@ -100,42 +101,52 @@ def main():
     Q = fp4
 
     def step(record):
-        """One pass of the whole hot path; `record` collects (kind, bytes/flops, ev0, ev1)."""
+        """One pass of the whole hot path; `record` collects (kind, bytes/flops, ev0, ev1).
+        X's two layouts (rowwise for fprop, transformed columnwise for wgrad) come from
+        one dual quantization, and so do dY's (rowwise SR for dgrad, transformed
+        columnwise SR for wgrad); each dual call includes its one-read amax pass."""
         for lin, inp, x, w, dy, b, o in layers:
             M, N, K = lin.M, lin.N, lin.K
-
-            def quant(src, flags, signs, seed, offset, out, out_t=None, nbytes=0):
-                e0, e1 = ev(), ev()
-                e0.record(stream)
-                Q.fp4_quantize(src, flags, signs, seed, offset, out, out_t)
-                e1.record(stream)
-                record.append(("quant", nbytes, e0, e1))
-
-            def gemm(a, bq, c, flops):
-                e0, e1 = ev(), ev()
-                e0.record(stream)
-                Q.fp4_gemm(a, bq, c)
-                e1.record(stream)
-                record.append(("gemm", flops, e0, e1))
-
             in_b = x.element_size()
-            if "fprop" in wl.passes:
-                quant(x, 0, 0, 0, 0, b.xq, nbytes=M * K * (in_b + 0.5 + 1 / 16))
-                quant(w, Q.Q_2D, 0, 0, 0, b.wq, b.wq_t, nbytes=N * K * (in_b + 2 * (0.5 + 1 / 256)))
-                gemm(b.xq, b.wq, o["y"], 2.0 * M * N * K)
-            if "dgrad" in wl.passes:
-                if "fprop" not in wl.passes:
-                    quant(w, Q.Q_2D, 0, 0, 0, b.wq, b.wq_t, nbytes=N * K * (in_b + 2 * (0.5 + 1 / 256)))
-                quant(dy, Q.Q_SR, 0, workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, b.dyq,
-                      nbytes=M * N * (in_b + 0.5 + 1 / 16))
-                gemm(b.dyq, b.wq_t, o["dx"], 2.0 * M * N * K)
-            if "wgrad" in wl.passes:
-                f_dy = Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR
-                f_x = Q.Q_COLWISE | Q.Q_RHT
-                quant(dy, f_dy, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_WGRAD, b.dyq_t,
-                      nbytes=M * N * (in_b + 0.5 + 1 / 16))
-                quant(x, f_x, inp.signs, 0, 0, b.xq_t, nbytes=M * K * (in_b + 0.5 + 1 / 16))
-                gemm(b.dyq_t, b.xq_t, o["dw"], 2.0 * M * N * K)
+            one_d = 0.5 + 1 / 16  # code + scale bytes per element of a 1D layout
+
+            def timed(kind, amount, fn):
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                record.append((kind, amount, e0, e1))
+
+            fprop, dgrad, wgrad = ("fprop" in wl.passes), ("dgrad" in wl.passes), ("wgrad" in wl.passes)
+            # X: rowwise (fprop) and/or transformed columnwise (wgrad)
+            if fprop and wgrad:
+                timed("quant", M * K * (in_b + 2 * one_d),
+                      lambda: Q.fp4_quantize_dual(x, Q.Q_RHT, inp.signs, 0, 0, 0, b.xq, b.xq_t))
+            elif fprop:
+                timed("quant", M * K * (in_b + one_d), lambda: Q.fp4_quantize(x, 0, 0, 0, 0, b.xq))
+            elif wgrad:
+                timed("quant", M * K * (in_b + one_d),
+                      lambda: Q.fp4_quantize(x, Q.Q_COLWISE | Q.Q_RHT, inp.signs, 0, 0, b.xq_t))
+            # W: 16x16 tiles, W and W^T
+            if fprop or dgrad:
+                timed("quant", N * K * (in_b + 2 * (0.5 + 1 / 256)), lambda: Q.fp4_quantize(w, Q.Q_2D, 0, 0, 0, b.wq,
+                                                                                           b.wq_t))
+            if fprop:
+                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm(b.xq, b.wq, o["y"]))
+            # dY: rowwise SR (dgrad) and/or transformed columnwise SR (wgrad)
+            sd, od, ow = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
+            if dgrad and wgrad:
+                timed("quant", M * N * (in_b + 2 * one_d),
+                      lambda: Q.fp4_quantize_dual(dy, Q.Q_SR | Q.Q_RHT, inp.signs, sd, od, ow, b.dyq, b.dyq_t))
+            elif dgrad:
+                timed("quant", M * N * (in_b + one_d), lambda: Q.fp4_quantize(dy, Q.Q_SR, 0, sd, od, b.dyq))
+            elif wgrad:
+                timed("quant", M * N * (in_b + one_d),
+                      lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR, inp.signs, sd, ow, b.dyq_t))
+            if dgrad:
+                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm(b.dyq, b.wq_t, o["dx"]))
+            if wgrad:
+                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm(b.dyq_t, b.xq_t, o["dw"]))
 
     for _ in range(args.warmup):
         step([])
@@ -203,7 +214,7 @@ def main():
             "achieved_gbs": round(quant_gbs, 1),
             "peak_gbs": PEAK_HBM_GBS,
             "frac": round(quant_gbs / PEAK_HBM_GBS, 4),
-            "note": "algorithmic bytes (input read + codes + scales written) per quantize call, amax pass included",
+            "note": "algorithmic bytes (input read once + codes + scales of every layout written) per quantize call; the time includes the amax pass",
             "ms_per_step": round(quant_ms / args.steps, 4),
         },
         "gemm_ms_per_step": round(gemm_ms / args.steps, 4),

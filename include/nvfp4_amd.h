@@ -165,6 +165,23 @@ FP4_API fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dty
                             int64_t M, int64_t N, int64_t K, uint32_t rht_signs, uint64_t seed, uint64_t offset,
                             const fp4_tensor *dyq_t, const fp4_tensor *xq_t, hipStream_t stream);
 
+/* Backward pass of the linear layer y = x . w^T (x [M][K], w [N][K], dy [M][N]):
+ *   dx = dy . w    (dx [M][K], dx_dtype)   and   dw = dy^T . x   (dw [N][K], dw_dtype).
+ * dy is quantized once for both GEMMs (fp4_quantize_dual with FP4_Q_SR | FP4_Q_RHT):
+ * rowwise with stochastic rounding at offset_dgrad into dyq ([M][N]), and transposed
+ * with the 16-point transform (rht_signs) and stochastic rounding at offset_wgrad
+ * into dyq_t ([N][M]).  wq_t ([K][N], 2D) is the forward pass's transposed weight.
+ * x^T quantized with the same transform ([K][M], nearest-even) is read from xq_t;
+ * if x is not NULL it is first quantized from x (dtype) into xq_t, otherwise xq_t
+ * must already hold it (for instance from fp4_quantize_dual of x in the forward
+ * pass).  The results equal fp4_linear_dgrad and fp4_linear_wgrad with the same
+ * seeds, offsets and signs.  M, N, K multiples of 16. */
+FP4_API fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, const fp4_tensor *wq_t,
+                                       void *dx, fp4_dtype dx_dtype, void *dw, fp4_dtype dw_dtype, int64_t M, int64_t N,
+                                       int64_t K, uint32_t rht_signs, uint64_t seed, uint64_t offset_dgrad,
+                                       uint64_t offset_wgrad, const fp4_tensor *dyq, const fp4_tensor *dyq_t,
+                                       const fp4_tensor *xq_t, hipStream_t stream);
+
 /* A short static description of a status code. */
 FP4_API const char *fp4_status_string(fp4_status status);
 

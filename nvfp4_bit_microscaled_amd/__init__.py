@@ -27,7 +27,7 @@ STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_ALIGN"
 
 # every symbol the header declares
 EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_gemm", "fp4_linear_fprop",
-           "fp4_linear_dgrad", "fp4_linear_wgrad", "fp4_status_string")
+           "fp4_linear_dgrad", "fp4_linear_wgrad", "fp4_linear_backward", "fp4_status_string")
 
 
 class Fp4Error(RuntimeError):
@@ -65,6 +65,7 @@ def load():
         "fp4_linear_fprop": [vp, vp, i32, vp, i32, i64, i64, i64, tp, tp, tp, vp],
         "fp4_linear_dgrad": [vp, i32, tp, vp, i32, i64, i64, i64, u64, u64, tp, vp],
         "fp4_linear_wgrad": [vp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, tp, tp, vp],
+        "fp4_linear_backward": [vp, vp, i32, tp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, u64, tp, tp, tp, vp],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -180,6 +181,20 @@ def fp4_linear_wgrad(dy, x, dw, rht_signs: int, seed: int, offset: int, dyq_t: Q
     _check("fp4_linear_wgrad", load().fp4_linear_wgrad(dy.data_ptr(), x.data_ptr(), _dtype(dy), dw.data_ptr(),
                                                        _dtype(dw), M, N, K, rht_signs, seed, offset, dyq_t.desc,
                                                        xq_t.desc, _stream(stream)))
+
+
+def fp4_linear_backward(dy, x, wq_t: QTensor, dx, dw, rht_signs: int, seed: int, offset_dgrad: int,
+                        offset_wgrad: int, dyq: QTensor, dyq_t: QTensor, xq_t: QTensor, stream=None):
+    """x may be None when xq_t already holds the transformed, transposed x."""
+    M, N = dy.shape
+    K = dx.shape[1]
+    assert dy.is_contiguous() and dx.is_contiguous() and dw.is_contiguous()
+    if x is not None:
+        assert x.dtype == dy.dtype and x.is_contiguous()
+    _check("fp4_linear_backward", load().fp4_linear_backward(
+        dy.data_ptr(), x.data_ptr() if x is not None else None, _dtype(dy), wq_t.desc, dx.data_ptr(), _dtype(dx),
+        dw.data_ptr(), _dtype(dw), M, N, K, rht_signs, seed, offset_dgrad, offset_wgrad, dyq.desc, dyq_t.desc,
+        xq_t.desc, _stream(stream)))
 
 
 class LinearBuffers:

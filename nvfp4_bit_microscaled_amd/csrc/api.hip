@@ -162,6 +162,31 @@ fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dtype, void
   return from_hip(e);
 }
 
+fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, const fp4_tensor *wq_t, void *dx,
+                               fp4_dtype dx_dtype, void *dw, fp4_dtype dw_dtype, int64_t M, int64_t N, int64_t K,
+                               uint32_t rht_signs, uint64_t seed, uint64_t offset_dgrad, uint64_t offset_wgrad,
+                               const fp4_tensor *dyq, const fp4_tensor *dyq_t, const fp4_tensor *xq_t,
+                               hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
+  fp4_status s;
+  if ((s = check_input(dy, dtype, M, N, N)) != FP4_OK) return s;
+  if ((s = check_tensor(dyq, M, N, 0)) != FP4_OK) return s;
+  if ((s = check_tensor(dyq_t, N, M, 0)) != FP4_OK) return s;
+  if (x && (s = check_quantize(x, dtype, M, K, K, FP4_Q_COLWISE | FP4_Q_RHT, xq_t, nullptr)) != FP4_OK) return s;
+  if ((s = check_tensor(xq_t, K, M, 0)) != FP4_OK) return s;
+  if ((s = check_tensor(wq_t, K, N, 1)) != FP4_OK) return s;
+  if ((s = check_gemm(dyq, wq_t, dx, dx_dtype, K)) != FP4_OK) return s;
+  if ((s = check_gemm(dyq_t, xq_t, dw, dw_dtype, K)) != FP4_OK) return s;
+  const uint32_t signs = rht_signs & 0xFFFFu;
+  hipError_t e = nvfp4::launch_quantize_dual(dy, dtype, M, N, N, FP4_Q_SR | FP4_Q_RHT, signs, seed, offset_dgrad,
+                                             offset_wgrad, dyq, dyq_t, stream);
+  if (e == hipSuccess && x)
+    e = nvfp4::launch_quantize(x, dtype, M, K, K, FP4_Q_COLWISE | FP4_Q_RHT, signs, 0, 0, xq_t, nullptr, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm(dyq, wq_t, dx, dx_dtype, K, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm(dyq_t, xq_t, dw, dw_dtype, K, stream);
+  return from_hip(e);
+}
+
 const char *fp4_status_string(fp4_status status) {
   switch (status) {
     case FP4_OK: return "ok";

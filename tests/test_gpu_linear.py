@@ -124,7 +124,8 @@ def test_wgrad_8k_config(fp4, oracle):
 def test_mlp_up_12b_sampled(fp4, oracle):
     """The 12B-hybrid-like MLP up-projection at full size (X 16384x5120, W 20480x5120,
     dY 16384x20480): all three passes in the launch configuration the benchmark
-    times; quantized operands and outputs checked on sampled rows."""
+    times (dual quantization of X and dY, fp4_linear_backward); quantized operands
+    and outputs checked on sampled rows."""
     lin = workloads.WORKLOADS["mlp_up_12b"].linears[0]
     M, N, K = lin.M, lin.N, lin.K
     inp = workloads.make_linear_inputs(lin, seed=0)
@@ -133,9 +134,13 @@ def test_mlp_up_12b_sampled(fp4, oracle):
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
     dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
-    fp4.fp4_linear_fprop(x, w, y, bufs.xq, bufs.wq, bufs.wq_t)
-    fp4.fp4_linear_dgrad(dy, bufs.wq_t, dx, workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, bufs.dyq)
-    fp4.fp4_linear_wgrad(dy, x, dw, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_WGRAD, bufs.dyq_t, bufs.xq_t)
+    # the benchmark's step: X's two layouts at once, W 2D (+W^T), Y; then the backward
+    # pass with dY's two layouts at once and X^T from the forward pass
+    fp4.fp4_quantize_dual(x, fp4.Q_RHT, inp.signs, 0, 0, 0, bufs.xq, bufs.xq_t)
+    fp4.fp4_quantize(w, fp4.Q_2D, 0, 0, 0, bufs.wq, bufs.wq_t)
+    fp4.fp4_gemm(bufs.xq, bufs.wq, y)
+    fp4.fp4_linear_backward(dy, None, bufs.wq_t, dx, dw, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_DGRAD,
+                            workloads.SR_OFFSET_WGRAD, bufs.dyq, bufs.dyq_t, bufs.xq_t)
     torch.cuda.synchronize()
     del x, w, dy
     xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
@@ -166,3 +171,42 @@ def test_mlp_up_12b_sampled(fp4, oracle):
     assert_q_equal(host_q(bufs.xq_t), oxtq, "xq_t")
     y_ref, bound = oracle.gemm_ref(odt, oxtq)
     check_gemm(dw.cpu().numpy()[wrows], y_ref, bound, False, "wgrad 12B")
+
+
+@pytest.mark.parametrize("quantize_x", [True, False], ids=["x_given", "xq_t_from_forward"])
+def test_linear_backward_equals_dgrad_and_wgrad(fp4, oracle, quantize_x):
+    """fp4_linear_backward (dY quantized once for both GEMMs) gives bit for bit the
+    outputs and quantized operands of fp4_linear_dgrad + fp4_linear_wgrad, and both
+    match the oracle."""
+    M, N, K = 528, 272, 400
+    inp = workloads.make_linear_inputs(workloads.Linear("t", M, N, K), seed=5)
+    xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
+    x, w, dy = dev(inp.x), dev(inp.w), dev(inp.dy)
+    sr, off_d, off_w = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
+    a = fp4.LinearBuffers(M, N, K)
+    fp4.fp4_quantize(w, fp4.Q_2D, 0, 0, 0, a.wq, a.wq_t)
+    dx_a = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dw_a = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    fp4.fp4_linear_dgrad(dy, a.wq_t, dx_a, sr, off_d, a.dyq)
+    fp4.fp4_linear_wgrad(dy, x, dw_a, inp.signs, sr, off_w, a.dyq_t, a.xq_t)
+    b = fp4.LinearBuffers(M, N, K)
+    if not quantize_x:
+        fp4.fp4_quantize_dual(x, fp4.Q_RHT, inp.signs, 0, 0, 0, b.xq, b.xq_t)
+    dx_b = torch.empty_like(dx_a)
+    dw_b = torch.empty_like(dw_a)
+    fp4.fp4_linear_backward(dy, x if quantize_x else None, a.wq_t, dx_b, dw_b, inp.signs, sr, off_d, off_w, b.dyq,
+                            b.dyq_t, b.xq_t)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_a, dx_b) and torch.equal(dw_a, dw_b)
+    for name, qa, qb in (("dyq", a.dyq, b.dyq), ("dyq_t", a.dyq_t, b.dyq_t), ("xq_t", a.xq_t, b.xq_t)):
+        assert torch.equal(qa.codes, qb.codes) and torch.equal(qa.scales, qb.scales), name
+        assert torch.equal(qa.amax, qb.amax), name
+    odyq, owtq = oracle.linear_dgrad(dyf, wf, sr, off_d)
+    odytq, oxtq = oracle.linear_wgrad(dyf, xf, inp.signs, sr, off_w)
+    assert_q_equal(host_q(b.dyq), odyq, "dyq")
+    assert_q_equal(host_q(b.dyq_t), odytq, "dyq_t")
+    assert_q_equal(host_q(b.xq_t), oxtq, "xq_t")
+    y_ref, bound = oracle.gemm_ref(odyq, owtq)
+    check_gemm(dx_b.float().cpu().numpy(), y_ref, bound, True, "backward dgrad")
+    y_ref, bound = oracle.gemm_ref(odytq, oxtq)
+    check_gemm(dw_b.cpu().numpy(), y_ref, bound, False, "backward wgrad")

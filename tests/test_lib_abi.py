@@ -130,3 +130,16 @@ def test_quantize_dual_rejects_bad_arguments(lib):
     assert f(x, 0, R, C, C, 0, 0, 0, 0, 0, Q(rows), Q(rows), None) == 6  # columnwise descriptor shape
     assert f(None, 0, R, C, C, 0, 0, 0, 0, 0, Q(rows), Q(cols), None) == 1
     assert f(x, 0, R, C, C, 0, 0, 0, 0, 0, None, Q(cols), None) == 1
+
+
+def test_linear_backward_rejects_bad_arguments(lib):
+    Q = ctypes.byref
+    dy, x, dx, dw = (ctypes.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000))
+    M, N, K = 64, 32, 48
+    f = lib.fp4_linear_backward
+    good = (Q(desc(K, N, 1)), dx, 1, dw, 0, M, N, K, 0, 0, 1, 2, Q(desc(M, N)), Q(desc(N, M)), Q(desc(K, M)), None)
+    assert f(dy, x, 0, *good[:5], M, N, 40, *good[8:]) == 2  # K % 16
+    assert f(dy, x, 0, Q(desc(K, N, 0)), *good[1:]) == 6  # W^T must be 2D
+    assert f(dy, x, 0, *good[:12], Q(desc(N, M)), *good[13:]) == 6  # dY rowwise shape
+    assert f(dy, x, 0, *good[:14], Q(desc(M, K)), None) == 6  # X^T shape
+    assert f(None, x, 0, *good) == 1
