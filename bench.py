@@ -38,7 +38,23 @@ def parse():
     ap.add_argument("--workload", default="mlp_up_12b", choices=["mlp_up_12b", "fprop_8k", "wgrad_8k", "block_3b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy three times (the known-size reference that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters into bytes) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of known size, beyond the 256 MB Infinity Cache: each
+    launch reads and writes exactly 512 MiB, so the HBM counters of these launches
+    give the factor that turns counter readings into bytes."""
+    import torch
+    x = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": x.numel() * 4, "launches": 3}), flush=True)
 
 
 def source_hash(path):
@@ -63,9 +79,12 @@ def measured_traffic(kernel_src):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the NVFP4 path here is single-GPU; "
-              f"see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the NVFP4 linear path here is measured "
+              f"on one GPU's shard; sharding across GPUs is designed, not built", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
