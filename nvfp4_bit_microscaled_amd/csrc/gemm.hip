@@ -170,69 +170,73 @@ __device__ __forceinline__ void store_tiles_t(const GemmParams &p, const f32x16 
   }
 }
 
-// Epilogue of the main kernel through LDS (free once the last stage is read): each
-// wave writes its 128x128 block (C^T layout as above, scaled and converted) into
-// a private 32 KB region, row-major with the 16-byte chunks of a row XOR-swizzled
-// by the row, then reads it back a chunk per lane so that every store instruction
-// writes whole 128-byte lines of C.  fp32 outputs go in two passes of 64 rows.
-// CHECK as for store_tiles_t (N % 4 == 0; C 16-byte aligned, ldc % 4 == 0).
+// Epilogue of the main kernel through LDS: each wave stages its 128x128 block
+// (C^T layout as above, scaled and converted) in a private 4 KB region, 32 rows
+// of 128 bytes at a time (64 bf16 or 32 fp32 columns), with the 16-byte chunks
+// of a row XOR-swizzled by the row, and reads each piece back a chunk per lane,
+// so that every store instruction writes whole 128-byte lines of C.  The region
+// lies outside the two stage buffers, so the next tile's stages can land while
+// this runs.  CHECK as for store_tiles_t (N % 4 == 0; C 16-byte aligned,
+// ldc % 4 == 0).
+constexpr int kEpiBytes = 4096;
+
 template <int TM, int TN, bool CHECK>
 __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
                                                 int64_t n0, int lane, uint8_t *region) {
   static_assert(TM == 4 && TN == 4, "a 128x128 block per wave");
   const int lr = lane & 31, g = lane >> 5;
+  const int wsw = (lr >> 1) & 7;  // swizzle of the row this lane writes
   const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
+  // read-back: chunk 64 k + lane of the piece is row (64 k + lane) / 8, chunk lane % 8
+  const int rr = lane >> 3, rc = lane & 7;
   if (p.c_bf16) {
-    // 128 rows x 256 bytes; chunk c of row r stored at chunk c ^ (r & 15)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = 32 * i + lr;
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int jp = 0; jp < TN / 2; ++jp) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bf16x4 h = {(__bf16)(acc[i][j][4 * q] * gscale), (__bf16)(acc[i][j][4 * q + 1] * gscale),
-                            (__bf16)(acc[i][j][4 * q + 2] * gscale), (__bf16)(acc[i][j][4 * q + 3] * gscale)};
-          *reinterpret_cast<bf16x4 *>(region + r * 256 + (((4 * j + q) ^ (r & 15)) << 4) + 8 * g) = h;
-        }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll 4
-    for (int k = 0; k < 32; ++k) {
-      const int idx = 64 * k + lane, r = idx >> 4, c = idx & 15;
-      const uint4 v = *reinterpret_cast<const uint4 *>(region + r * 256 + ((c ^ (r & 15)) << 4));
-      const int64_t m = m0 + r, n = n0 + 8 * c;
-      uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n;
-      if (!CHECK || (m < p.M && n + 8 <= p.N)) *reinterpret_cast<uint4 *>(dst) = v;
-      else if (m < p.M && n < p.N) *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
-    }
-  } else {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // 64 rows x 512 bytes; chunk c of row r stored at chunk c ^ (r & 31)
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * half + ii, r = 32 * ii + lr;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 v = make_float4(acc[i][j][4 * q] * gscale, acc[i][j][4 * q + 1] * gscale,
-                                         acc[i][j][4 * q + 2] * gscale, acc[i][j][4 * q + 3] * gscale);
-            *reinterpret_cast<float4 *>(region + r * 512 + (((8 * j + 2 * q + g) ^ (r & 31)) << 4)) = v;
+            const int j = 2 * jp + jj, c = 4 * jj + q;  // columns 8c .. 8c+7 of the piece; this lane's half g
+            const bf16x4 h = {(__bf16)(acc[i][j][4 * q] * gscale), (__bf16)(acc[i][j][4 * q + 1] * gscale),
+                              (__bf16)(acc[i][j][4 * q + 2] * gscale), (__bf16)(acc[i][j][4 * q + 3] * gscale)};
+            *reinterpret_cast<bf16x4 *>(region + lr * 128 + ((c ^ wsw) << 4) + 8 * g) = h;
           }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int r = 8 * k + rr;
+          const uint4 v = *reinterpret_cast<const uint4 *>(region + r * 128 + ((rc ^ ((r >> 1) & 7)) << 4));
+          const int64_t m = m0 + 32 * i + r, n = n0 + 64 * jp + 8 * rc;
+          uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n;
+          if (!CHECK || (m < p.M && n + 8 <= p.N)) *reinterpret_cast<uint4 *>(dst) = v;
+          else if (m < p.M && n < p.N) *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next piece
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll 4
-      for (int k = 0; k < 32; ++k) {
-        const int idx = 64 * k + lane, r = idx >> 5, c = idx & 31;
-        const float4 v = *reinterpret_cast<const float4 *>(region + r * 512 + ((c ^ (r & 31)) << 4));
-        const int64_t m = m0 + 64 * half + r, n = n0 + 4 * c;
-        if (!CHECK || (m < p.M && n < p.N))
-          *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) = v;
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = make_float4(acc[i][j][4 * q] * gscale, acc[i][j][4 * q + 1] * gscale,
+                                       acc[i][j][4 * q + 2] * gscale, acc[i][j][4 * q + 3] * gscale);
+          *reinterpret_cast<float4 *>(region + lr * 128 + (((2 * q + g) ^ wsw) << 4)) = v;  // columns 4(2q+g) ..
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int r = 8 * k + rr;
+          const float4 v = *reinterpret_cast<const float4 *>(region + r * 128 + ((rc ^ ((r >> 1) & 7)) << 4));
+          const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 4 * rc;
+          if (!CHECK || (m < p.M && n < p.N))
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) = v;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next piece
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next half
-    }
   }
 }
 
@@ -293,8 +297,8 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "code DMA: whole instructions per wave");
   static_assert((BM + BN) % 64 == 0, "scale DMA: whole instructions");
   static_assert(STAGE % 1024 == 0, "stage alignment");
-  static_assert(2 * STAGE >= NW * 32768, "epilogue staging fits in LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  static_assert(2 * STAGE + NW * kEpiBytes <= 160 * 1024, "stage buffers and epilogue regions fit in LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE + NW * kEpiBytes];
 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int64_t M = p.M, N = p.N;
@@ -447,17 +451,15 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   static_assert(2 * T <= NMF && NDMA <= 2 * NMF, "memory instructions fit the slots");
   constexpr int kDmaPerSubstep = (NDMA + 3) / 4;
 
-  // One stage.  Quarters 0..2 read the next quarter of this buffer during their
-  // first substep; quarter 3 waits for stage kt+1's DMA and for every read of this
-  // buffer, passes the barrier, reads stage kt+1's first quarter from the other
-  // buffer and spreads stage kt+2's DMA into this buffer over its substeps.  The
-  // last stage has none of that.
-  auto stage = [&](int kt, auto last_tag) {
+  // One stage, in buffer (kt + par) & 1.  Quarters 0..2 read the next quarter of
+  // this buffer during their first substep; quarter 3 waits for stage kt+1's DMA
+  // and for every read of this buffer, passes the barrier, reads stage kt+1's
+  // first quarter from the other buffer and spreads the DMA of stage kt_dma (of
+  // the tile whose offsets va/vb/vs hold) into this buffer over its substeps.
+  // The last stage has none of that.
+  auto stage = [&](int kt, auto last_tag, int par, int kt_dma) {
     constexpr bool LAST = decltype(last_tag)::value;
-    const int buf = kt & 1;
-    // a stage past the end re-loads the last one into this buffer, which is not
-    // read again (the final wait below drains it before the kernel ends)
-    const int kt_dma = min(kt + 2, nst - 1);
+    const int buf = (kt + par) & 1;
     static_for<4>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       constexpr int slot = q & 1;
@@ -488,20 +490,26 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
     });
   };
 
-  // Tile loop.  The first two stages of a tile are in flight before its loop
-  // starts; after the last stage every wave passes a barrier (LDS free), the next
-  // tile's first two stages are issued, and only then are this tile's outputs
-  // stored, so store and load latencies overlap.
+  // Tile loop.  A tile's first stage lands before its loop starts (its DMA runs
+  // during the previous tile's stage before last, in place of a stage past the
+  // end) and its second is issued as the previous tile's epilogue starts; the
+  // epilogue stages through its own LDS regions, so it overlaps both.  Tile
+  // buffers alternate with par, the buffer of the tile's stage 0, when the stage
+  // count is odd.
   set_tile(L);
+  int par = 0;
   issue(0, 0);
   issue(min(1, nst - 1), 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   for (;;) {
-    // stage 0 (and 1) landed, and the previous tile's stores are done
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // stage 0 of this tile is in buffer par and visible to every wave
+    const int64_t mc = m0, nc = n0;
+    const int Lnext = L + Lstride;
+    const bool more = Lnext < Lend;
     // quarter 0 of stage 0 and the operands of its first substep
 #pragma unroll
-    for (int r = 0; r < 2 * T; ++r) lds_read(0, 0, 0, r);
+    for (int r = 0; r < 2 * T; ++r) lds_read(par, 0, 0, r);
 #pragma unroll
     for (int i = 0; i < T; ++i) scd[0][i] = scales2(scw[0][i]);
 #pragma unroll
@@ -509,23 +517,38 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       dequant_half(0, 0, 0, i, 0);
       dequant_half(0, 0, 0, i, 1);
     }
-    for (int kt = 0; kt + 1 < nst; ++kt) stage(kt, std::false_type{});
-    stage(nst - 1, std::true_type{});
+    for (int kt = 0; kt + 2 < nst; ++kt) stage(kt, std::false_type{}, par, kt + 2);
+    if (nst >= 2) {
+      // the stage before last loads the next tile's first stage; without a next
+      // tile it re-loads this tile's last stage into a buffer that is not read
+      // again (drained below)
+      if (more) set_tile(Lnext);
+      stage(nst - 2, std::false_type{}, par, more ? 0 : nst - 1);
+    }
+    stage(nst - 1, std::true_type{}, par, 0);
 
-    const int Lnext = L + Lstride;
-    // the clamped DMA of the last stages has landed and no wave reads LDS any more
+    // every wave is done with this tile's stage buffers, and the DMA issued in the
+    // stage before last has landed
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    store_tiles_lds<TM, TN, CLAMP>(p, acc, m0 + wm, n0 + wn, lane, lds + wave * 32768);
-    // every wave is done with its staging region before the next tile's DMA lands
-    __syncthreads();
-    if (Lnext < Lend) {
-      set_tile(Lnext);
-      issue(0, 0);
-      issue(min(1, nst - 1), 1);
+    const int par_next = (par + nst) & 1;
+    if (more) {
+      if (nst >= 2) {
+        issue(1, par_next ^ 1);
+      } else {
+        set_tile(Lnext);
+        issue(0, par_next);
+      }
     }
-    if (Lnext >= Lend) break;
+    store_tiles_lds<TM, TN, CLAMP>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes);
+    if (!more) break;
+    if (nst == 1) {
+      // a one-stage tile's first stage was only just issued
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
     L = Lnext;
+    par = par_next;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
