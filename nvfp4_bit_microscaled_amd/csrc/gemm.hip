@@ -35,6 +35,9 @@
 //                     per stage.  Per wave and 16 K it dequantizes 8 operand tiles
 //                     (64 VALU ops) for 16 MFMAs, so the conversions fit under the
 //                     matrix-core time.
+//                     A second instance with 128x128 tiles (four waves of 64x64)
+//                     takes, as quarters, the few 256x256 tiles that would
+//                     otherwise run as a mostly idle last round.
 //   gemm_edge_kernel  any K multiple of 16, any 8-byte-aligned operands: 128x128
 //                     tile, register-staged loads with zero fill.
 // Workgroup -> tile order (both): consecutive workgroup ids go to different XCDs,
@@ -68,6 +71,8 @@ struct GemmParams {
   void *c;
   int64_t ldc;
   int c_bf16;
+  int tiles_main;  // gemm_kernel, 256x256: tiles [0, tiles_main) of the grouped order
+  int tail_first;  // gemm_kernel, quarters: the quarters of 256x256 tiles tail_first .. last
 };
 
 // 8 E2M1 codes (one 32-bit word, element 2j in the low nibble of byte j) times the
@@ -170,7 +175,7 @@ __device__ __forceinline__ void store_tiles_t(const GemmParams &p, const f32x16 
   }
 }
 
-// Epilogue of the main kernel through LDS: each wave stages its 128x128 block
+// Epilogue of the main kernel through LDS: each wave stages its block
 // (C^T layout as above, scaled and converted) in a private 4 KB region, 32 rows
 // of 128 bytes at a time (64 bf16 or 32 fp32 columns), with the 16-byte chunks
 // of a row XOR-swizzled by the row, and reads each piece back a chunk per lane,
@@ -183,7 +188,7 @@ constexpr int kEpiBytes = 4096;
 template <int TM, int TN, bool CHECK>
 __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
                                                 int64_t n0, int lane, uint8_t *region) {
-  static_assert(TM == 4 && TN == 4, "a 128x128 block per wave");
+  static_assert(TN % 2 == 0, "bf16 pieces are 64 columns");
   const int lr = lane & 31, g = lane >> 5;
   const int wsw = (lr >> 1) & 7;  // swizzle of the row this lane writes
   const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
@@ -285,8 +290,9 @@ __device__ __forceinline__ void dma16(const u32x4 &rsrc, void *dst, uint32_t vof
                : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP, bool QUARTERS>
 __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams p) {
+  static_assert(!QUARTERS || (BM == 128 && BN == 128), "quarters of 256x256 tiles");
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32, T = TM + TN;
@@ -310,8 +316,10 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   // w % 8, which owns the contiguous eighth of the tile sequence; its j-th
   // workgroup takes tiles j, j + G/8, ... of that range, so the XCD's workgroups
   // always work on neighbouring tiles.  Otherwise workgroup w takes w, w + G, ...
-  const int num_m = int((M + BM - 1) / BM), num_n = int((N + BN - 1) / BN);
-  const int ntiles = num_m * num_n;
+  // 256x256 tiles: a prefix of the grouped order.  Quarters: the four 128x128
+  // quarters of each later 256x256 tile, in that order.
+  const int num_m = int((M + 255) / 256), num_n = int((N + 255) / 256);
+  const int ntiles = QUARTERS ? 4 * (num_m * num_n - p.tail_first) : p.tiles_main;
   int L, Lend, Lstride;
   if ((gridDim.x & 7) == 0 && int(gridDim.x) < ntiles) {
     const int x = blockIdx.x & 7;
@@ -349,9 +357,16 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   // tile coordinates of sequence position l (groups of 8 tile-rows) and its DMA offsets
   auto set_tile = [&](int l) {
     int tm, tn;
-    tile_at(l, num_m, num_n, tm, tn);
-    m0 = int64_t(tm) * BM;
-    n0 = int64_t(tn) * BN;
+    if constexpr (QUARTERS) {
+      tile_at(p.tail_first + (l >> 2), num_m, num_n, tm, tn);
+      m0 = int64_t(tm) * 256 + BM * ((l >> 1) & 1);
+      n0 = int64_t(tn) * 256 + BN * (l & 1);
+    } else {
+      static_assert(QUARTERS || (BM == 256 && BN == 256), "tile grid of 256x256");
+      tile_at(l, num_m, num_n, tm, tn);
+      m0 = int64_t(tm) * BM;
+      n0 = int64_t(tn) * BN;
+    }
 #pragma unroll
     for (int j = 0; j < (CLAMP ? JA : 1); ++j) va[j] = uint32_t(m0 + row0 + NW * 8 * j) * kbytes + lchunk;
 #pragma unroll
@@ -443,13 +458,24 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // Explicit issue order.  A substep is NMF slots; slot k issues MFMA k of the
-  // current operand set, half of one tile's conversions for the next substep
-  // (4 VALU: the MFMA's 32 cycles leave room for them), and at most one LDS read
-  // and one DMA load; sched_barrier keeps the compiler from regrouping slots.
+  // current operand set, its share of the 2T half-tile conversions for the next
+  // substep (4 VALU each: with 128x128 per wave, one per MFMA, whose 32 cycles
+  // leave room for them), of the LDS reads and of the DMA loads; sched_barrier
+  // keeps the compiler from regrouping slots.
   constexpr int NMF = TM * TN;
-  static_assert(NMF == 2 * T, "one half-tile of conversions per MFMA");
-  static_assert(2 * T <= NMF && NDMA <= 2 * NMF, "memory instructions fit the slots");
   constexpr int kDmaPerSubstep = (NDMA + 3) / 4;
+  static_assert(kDmaPerSubstep <= NMF, "DMA loads fit the slots");
+  // items [K * C, (K + 1) * C) of TOTAL, C = ceil(TOTAL / NMF), for slot K
+  auto slot_items = [&](auto kc, auto total_c, auto &&f) {
+    constexpr int K = decltype(kc)::value, TOTAL = decltype(total_c)::value;
+    constexpr int C = (TOTAL + NMF - 1) / NMF;
+    static_for<C>([&](auto ic) {
+      constexpr int x = K * C + decltype(ic)::value;
+      if constexpr (x < TOTAL) f(std::integral_constant<int, x>{});
+    });
+  };
+  using HalfTiles = std::integral_constant<int, 2 * T>;
+  using Tiles = std::integral_constant<int, T>;
 
   // One stage, in buffer (kt + par) & 1.  Quarters 0..2 read the next quarter of
   // this buffer during their first substep; quarter 3 waits for stage kt+1's DMA
@@ -478,10 +504,20 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
           constexpr int k = decltype(kc)::value;
           constexpr int i = k / TN, j = k % TN;
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][TM + j], op[cur][i], acc[i][j], 0, 0, 0);
-          if constexpr (has_next) dequant_half(nslot, ns, cur ^ 1, k / 2, k % 2);
-          if constexpr (s == 0 && next_q && k < 2 * T)
-            lds_read(q < 3 ? buf : buf ^ 1, q < 3 ? q + 1 : 0, slot ^ 1, k);
-          if constexpr (s == 2 && next_q && k < T) scd[slot ^ 1][k] = scales2(scw[slot ^ 1][k]);
+          if constexpr (has_next)
+            slot_items(kc, HalfTiles{}, [&](auto hc) {
+              constexpr int h = decltype(hc)::value;
+              dequant_half(nslot, ns, cur ^ 1, h / 2, h % 2);
+            });
+          if constexpr (s == 0 && next_q)
+            slot_items(kc, HalfTiles{}, [&](auto rc) {
+              lds_read(q < 3 ? buf : buf ^ 1, q < 3 ? q + 1 : 0, slot ^ 1, decltype(rc)::value);
+            });
+          if constexpr (s == 2 && next_q)
+            slot_items(kc, Tiles{}, [&](auto tc) {
+              constexpr int x = decltype(tc)::value;
+              scd[slot ^ 1][x] = scales2(scw[slot ^ 1][x]);
+            });
           if constexpr (q == 3 && !LAST && k < kDmaPerSubstep && s * kDmaPerSubstep + k < NDMA)
             dma(kt_dma, buf, s * kDmaPerSubstep + k);
           __builtin_amdgcn_sched_barrier(0);
@@ -731,6 +767,8 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
   p.c = c;
   p.ldc = ldc;
   p.c_bf16 = c_dtype == FP4_BF16;
+  p.tiles_main = 0;
+  p.tail_first = -1;
   if (p.M == 0 || p.N == 0) return hipSuccess;
   auto al = [](const void *q, uintptr_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
   // main path: whole 256-element K stages, 16-byte aligned codes and scale rows,
@@ -740,16 +778,31 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
                          (p.N + 256) * (p.K / 2) < (int64_t(1) << 32) &&
                          al(c, 16) && ldc % 4 == 0 && p.N % 4 == 0;
   if (main_path) {
-    // persistent: one workgroup per CU (its 144 KB of LDS admit no second one)
+    // persistent: one workgroup per CU (its 160 KB of LDS admit no second one).
+    // When the tiles overrun whole rounds of the CUs by at most a quarter round,
+    // those last tiles would keep a few CUs busy for a full tile time while the
+    // rest idle; they go instead, as four 128x128 quarters each (at most one
+    // workgroup per CU), to a second launch after the persistent one.
     const unsigned tiles = tiles_for<256, 256>(p), cus = compute_units();
+    const unsigned rest = tiles % cus;
+    const bool split = tiles > cus && rest > 0 && rest <= cus / 4;
+    p.tiles_main = int(split ? tiles - rest : tiles);
     const dim3 grid(tiles < cus ? tiles : cus);
-    if (p.M % 256 == 0 && p.N % 256 == 0)
-      hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false>), grid, dim3(256), 0, stream, p);
+    const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
+    if (exact)
+      hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false, false>), grid, dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true>), grid, dim3(256), 0, stream, p);
-  }
-  else
+      hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true, false>), grid, dim3(256), 0, stream, p);
+    if (split) {
+      p.tail_first = p.tiles_main;
+      if (exact)
+        hipLaunchKernelGGL((gemm_kernel<128, 128, 2, 2, false, true>), dim3(4 * rest), dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_kernel<128, 128, 2, 2, true, true>), dim3(4 * rest), dim3(256), 0, stream, p);
+    }
+  } else {
     hipLaunchKernelGGL(gemm_edge_kernel, dim3(tiles_for<128, 128>(p)), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
