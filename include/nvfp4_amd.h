@@ -110,7 +110,8 @@ FP4_API fp4_status fp4_amax(const void *x, fp4_dtype dtype, int64_t rows, int64_
  * scales: its codes and scales are the exact transposes of out's.
  * Modes: 1D with any of COLWISE, RHT, SR; 2D with COLWISE only (no RHT, no SR).
  * Needs: L's cols a multiple of 16 (and L's rows too for 2D); x 16-byte aligned,
- * ld a multiple of 8 elements; codes 16-byte and scales 8-byte aligned. */
+ * ld a multiple of 8 elements; codes 16-byte and scales 8-byte aligned; with
+ * COLWISE or 2D, x at most 16776960 rows (FP4_ERR_SHAPE otherwise). */
 FP4_API fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
                         uint32_t rht_signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
                         const fp4_tensor *out_t, hipStream_t stream);

@@ -45,6 +45,8 @@ fp4_status check_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t 
   if (lcols % 16 != 0) return FP4_ERR_SHAPE;
   if (two_d && lrows % 16 != 0) return FP4_ERR_SHAPE;
   if ((flags & FP4_Q_RHT) && colwise && rows % 16 != 0) return FP4_ERR_SHAPE;
+  // columnwise and 2D launches give each 256 rows of x one grid row (at most 65535)
+  if ((colwise || two_d) && (rows + 255) / 256 > 65535) return FP4_ERR_SHAPE;
   if ((s = check_tensor(out, lrows, lcols, two_d)) != FP4_OK) return s;
   if (out_t && (s = check_tensor(out_t, lcols, lrows, 1)) != FP4_OK) return s;
   return FP4_OK;

@@ -31,24 +31,50 @@ __device__ __forceinline__ float encode_scale(float amax) {
 __device__ __forceinline__ float decode_scale(float amax) { return amax / kTensorRange; }
 
 // E4M3 (OCP "FN": bias 7, max 448) from a non-negative binary32, nearest-even on
-// the bits, clamped to the largest finite code 0x7E.
+// the bits, clamped to the largest finite code 0x7E.  gfx950's converter rounds
+// exactly so for every binary32 in [0, 464) (checked bit for bit against a
+// software encoder over all of them); at 464 and above it gives NaN instead of
+// saturating, so the input is clamped to 448 first (every value in (448, 464)
+// rounds to 448 either way).
 __device__ __forceinline__ uint32_t e4m3_from_f32(float u) {
-  if (!(u > 0.0f)) return 0u;
-  if (u < 0.015625f) {                          // below 2^-6: subnormal spacing 2^-9
-    return uint32_t(__builtin_rintf(u * 512.0f));  // exact scaling; 8 means 2^-6 = code 0x08
-  }
-  uint32_t b = __float_as_uint(u);
-  // keep 3 fraction bits: add half an output ulp minus one, plus the kept lsb (ties to even)
-  b += 0x7FFFFu + ((b >> 20) & 1u);
-  int32_t e = int32_t(b >> 23) - 127 + 7;       // E4M3 exponent field
-  uint32_t code = (uint32_t(e) << 3) | ((b >> 20) & 7u);
-  return (e > 15 || code > 0x7Eu) ? 0x7Eu : code;
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(u, 448.0f), 0.0f, 0, false)) & 0xFFu;
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   uint32_t e = (code >> 3) & 15u, m = code & 7u;
   if (e == 0) return float(m) * 0.001953125f;  // m * 2^-9
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// x / 6 rounded to nearest-even.  For x >= 2^-125 the product with RN(1/6)
+// corrected by one fused residual step is that quotient (checked for every
+// binary32 in that range); below it the quotient is subnormal and the division
+// is done as such.
+__device__ __forceinline__ float div6(float x) {
+  if (__builtin_expect(x >= 0x1p-125f, 1)) {
+    const float r6 = 1.0f / 6.0f;
+    const float q0 = x * r6;
+    return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, x), r6, q0);
+  }
+  return x / 6.0f;
+}
+
+// Element multipliers by scale code: tab[c] = s_enc / decode(c), 0 for c = 0.
+// A workgroup fills its table once (threads 0..127) and reads it per block.
+constexpr int kMultTable = 128;
+
+__device__ __forceinline__ void fill_mult_table(float *tab, float s_enc) {
+  if (threadIdx.x < kMultTable) {
+    const float sf = e4m3_to_f32(threadIdx.x);
+    tab[threadIdx.x] = sf > 0.0f ? s_enc / sf : 0.0f;
+  }
+}
+
+// Scale code and element multiplier of one block from its amax:
+// code = E4M3(RN(amax_b / 6) * s_enc), mult = s_enc / decode(code).
+__device__ __forceinline__ void block_scale(float amax_b, float s_enc, const float *tab, uint32_t &code, float &mult) {
+  code = e4m3_from_f32(div6(amax_b) * s_enc);
+  mult = tab[code];
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -89,7 +115,7 @@ __device__ __forceinline__ uint32_t encode2_sr(float a, float b, uint32_t r) {
   const f32x2 p = {a, b};
   const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r << 16, 1.0f, 0);
   const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, (r >> 1) & 0x7FFF8000u, 1.0f, 0);
-  return (lo & 0x0Fu) | (hi & 0xF0u);
+  return (lo & 0x0Fu) | (hi & ~0x0Fu);  // one bit-field insert; hi is zero above byte 0
 }
 
 // 8 scaled values -> 8 stochastically rounded codes; elements 2j, 2j+1 use r[j].
@@ -111,7 +137,9 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = uint64_t(0xD2511F53u) * c0, p1 = uint64_t(0xCD9E8D57u) * c2;
-    const uint32_t n0 = uint32_t(p1 >> 32) ^ c1 ^ k0, n2 = uint32_t(p0 >> 32) ^ c3 ^ k1;
+    // three-input exclusive or (truth table 0x96) in one instruction
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(uint32_t(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(uint32_t(p0 >> 32), c3, k1, 0x96);
     c0 = n0;
     c1 = uint32_t(p1);
     c2 = n2;
@@ -135,10 +163,9 @@ __device__ __forceinline__ void sr_bits16(uint64_t i0, uint64_t seed, uint64_t o
   r[4] = b.v[0]; r[5] = b.v[1]; r[6] = b.v[2]; r[7] = b.v[3];
 }
 
-// In-place orthonormal random Hadamard transform of a 16-vector.
-__device__ __forceinline__ void rht16(float v[16], uint32_t signs) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = ((signs >> j) & 1u) ? -v[j] : v[j];
+// In-place orthonormal Hadamard transform of a 16-vector whose random signs have
+// already been applied: butterflies at distances 1, 2, 4, 8, then a factor 1/4.
+__device__ __forceinline__ void hadamard16(float v[16]) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -154,12 +181,12 @@ __device__ __forceinline__ void rht16(float v[16], uint32_t signs) {
   for (int j = 0; j < 16; ++j) v[j] *= 0.25f;
 }
 
-// Scale code and element multiplier of one block from its amax.
-__device__ __forceinline__ void block_scale(float amax_b, float s_enc, uint32_t &code, float &mult) {
-  const float t = amax_b / 6.0f;
-  code = e4m3_from_f32(t * s_enc);
-  const float sf = e4m3_to_f32(code);
-  mult = sf > 0.0f ? s_enc / sf : 0.0f;
+// In-place orthonormal random Hadamard transform of a 16-vector: element j is
+// negated when bit j of the sign mask is set, then transformed.
+__device__ __forceinline__ void rht16(float v[16], uint32_t signs) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = ((signs >> j) & 1u) ? -v[j] : v[j];
+  hadamard16(v);
 }
 
 // Scale a 16-block by its multiplier (one binary32 product per element) and

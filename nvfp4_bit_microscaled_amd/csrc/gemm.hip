@@ -779,13 +779,13 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
                          al(c, 16) && ldc % 4 == 0 && p.N % 4 == 0;
   if (main_path) {
     // persistent: one workgroup per CU (its 160 KB of LDS admit no second one).
-    // When the tiles overrun whole rounds of the CUs by at most a quarter round,
-    // those last tiles would keep a few CUs busy for a full tile time while the
-    // rest idle; they go instead, as four 128x128 quarters each (at most one
-    // workgroup per CU), to a second launch after the persistent one.
+    // When the tiles overrun whole rounds of the CUs by at most half a round,
+    // those last tiles would keep some CUs busy for a full tile time while the
+    // rest idle; they go instead, as four 128x128 quarters each (one or two per
+    // CU, a quarter of the time each), to a second persistent launch.
     const unsigned tiles = tiles_for<256, 256>(p), cus = compute_units();
     const unsigned rest = tiles % cus;
-    const bool split = tiles > cus && rest > 0 && rest <= cus / 4;
+    const bool split = tiles > cus && rest > 0 && rest <= cus / 2;
     p.tiles_main = int(split ? tiles - rest : tiles);
     const dim3 grid(tiles < cus ? tiles : cus);
     const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
@@ -795,10 +795,11 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
       hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true, false>), grid, dim3(256), 0, stream, p);
     if (split) {
       p.tail_first = p.tiles_main;
+      const dim3 qgrid(4 * rest < cus ? 4 * rest : cus);
       if (exact)
-        hipLaunchKernelGGL((gemm_kernel<128, 128, 2, 2, false, true>), dim3(4 * rest), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((gemm_kernel<128, 128, 2, 2, false, true>), qgrid, dim3(256), 0, stream, p);
       else
-        hipLaunchKernelGGL((gemm_kernel<128, 128, 2, 2, true, true>), dim3(4 * rest), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((gemm_kernel<128, 128, 2, 2, true, true>), qgrid, dim3(256), 0, stream, p);
     }
   } else {
     hipLaunchKernelGGL(gemm_edge_kernel, dim3(tiles_for<128, 128>(p)), dim3(256), 0, stream, p);

@@ -57,6 +57,65 @@ __device__ __forceinline__ void load8<float>(const float *p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// load8 with every element negated when `neg` (the row's random sign of the
+// Hadamard transform): one exclusive or per 32-bit word, i.e. per two bf16.
+template <typename T>
+__device__ __forceinline__ void load8_neg(const T *p, float v[8], bool neg);
+
+template <>
+__device__ __forceinline__ void load8_neg<uint16_t>(const uint16_t *p, float v[8], bool neg) {
+  const uint4 q = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t f = neg ? 0x80008000u : 0u;
+  const uint32_t w[4] = {q.x ^ f, q.y ^ f, q.z ^ f, q.w ^ f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8_neg<float>(const float *p, float v[8], bool neg) {
+  load8(p, v);
+  const uint32_t f = neg ? 0x80000000u : 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ f);
+}
+
+// 16 rows x 8 adjacent columns of x (one 16-row slab), loaded as 16-byte row
+// segments and kept as loaded; column j is widened to binary32 when it is used,
+// so bf16 data takes half the registers.  Row r is negated when bit r of `neg`
+// is set (the random signs of the Hadamard transform down the columns).
+template <typename T>
+struct Slab8;
+
+template <>
+struct Slab8<uint16_t> {
+  uint4 w[16];
+  __device__ __forceinline__ void load(const uint16_t *p, int64_t ld, uint32_t neg) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint4 q = *reinterpret_cast<const uint4 *>(p + r * ld);
+      const uint32_t f = ((neg >> r) & 1u) ? 0x80008000u : 0u;
+      w[r] = make_uint4(q.x ^ f, q.y ^ f, q.z ^ f, q.w ^ f);
+    }
+  }
+  __device__ __forceinline__ float at(int r, int j) const {
+    const uint32_t v = j >> 1 == 0 ? w[r].x : j >> 1 == 1 ? w[r].y : j >> 1 == 2 ? w[r].z : w[r].w;
+    return __uint_as_float((j & 1) ? (v & 0xFFFF0000u) : (v << 16));
+  }
+};
+
+template <>
+struct Slab8<float> {
+  float v[16][8];
+  __device__ __forceinline__ void load(const float *p, int64_t ld, uint32_t neg) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load8_neg(p + r * ld, v[r], (neg >> r) & 1u);
+  }
+  __device__ __forceinline__ float at(int r, int j) const { return v[r][j]; }
+};
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -79,6 +138,10 @@ __device__ __forceinline__ void block_max_to(float v, float *out) {
 }
 
 __global__ void zero_f32_kernel(float *p) { *p = 0.0f; }
+__global__ void zero2_f32_kernel(float *p, float *q) {
+  *p = 0.0f;
+  *q = 0.0f;
+}
 
 // Plain |x| max over [R][C] (row stride ld); 8 elements per thread-step.
 template <typename T>
@@ -149,15 +212,14 @@ __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const T *__rest
   float m = 0.0f;
   for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads) {
     const int64_t s = i / cchunks, c = (i - s * cchunks) * 8;
-    float v[16][8];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) load8(x + (s * 16 + r) * ld + c, v[r]);
+    Slab8<T> sl;
+    sl.load(x + s * 16 * ld + c, ld, signs);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float col[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) col[r] = v[r][j];
-      rht16(col, signs);
+      for (int r = 0; r < 16; ++r) col[r] = sl.at(r, j);
+      hadamard16(col);
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, __builtin_fabsf(col[r]));
     }
@@ -169,13 +231,14 @@ __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const T *__rest
 // block's first logical index (row * C + 16 * kb), which seeds its random bits.
 template <bool RHT, bool SR>
 __device__ __forceinline__ void quant_block_rows(float v[16], uint32_t signs, uint64_t i0, uint64_t seed,
-                                                 uint64_t offset, float s_enc, uint2 &codes, uint32_t &sc) {
+                                                 uint64_t offset, float s_enc, const float *tab, uint2 &codes,
+                                                 uint32_t &sc) {
   if (RHT) rht16(v, signs);
   float amax_b = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, __builtin_fabsf(v[j]));
   float mult;
-  block_scale(amax_b, s_enc, sc, mult);
+  block_scale(amax_b, s_enc, tab, sc, mult);
   if (SR) {
     uint32_t rb[8];
     sr_bits16(i0, seed, offset, rb);
@@ -195,7 +258,10 @@ __global__ __launch_bounds__(kThreads) void quant_rows_flat_kernel(const T *__re
                                                                   const float *__restrict__ amax_p,
                                                                   uint8_t *__restrict__ codes,
                                                                   uint8_t *__restrict__ scales) {
+  __shared__ float tab[kMultTable];
   const float s_enc = encode_scale(*amax_p);
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   for (int64_t b0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; b0 < nblocks; b0 += 2 * stride) {
     const int64_t b1 = b0 + stride;
@@ -208,11 +274,11 @@ __global__ __launch_bounds__(kThreads) void quant_rows_flat_kernel(const T *__re
     }
     uint2 c;
     uint32_t sc;
-    quant_block_rows<RHT, SR>(v0, signs, uint64_t(b0) * 16u, seed, offset, s_enc, c, sc);
+    quant_block_rows<RHT, SR>(v0, signs, uint64_t(b0) * 16u, seed, offset, s_enc, tab, c, sc);
     *reinterpret_cast<uint2 *>(codes + b0 * 8) = c;
     scales[b0] = uint8_t(sc);
     if (b1 < nblocks) {
-      quant_block_rows<RHT, SR>(v1, signs, uint64_t(b1) * 16u, seed, offset, s_enc, c, sc);
+      quant_block_rows<RHT, SR>(v1, signs, uint64_t(b1) * 16u, seed, offset, s_enc, tab, c, sc);
       *reinterpret_cast<uint2 *>(codes + b1 * 8) = c;
       scales[b1] = uint8_t(sc);
     }
@@ -227,18 +293,21 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T *__restric
                                                              uint64_t offset, const float *__restrict__ amax_p,
                                                              uint8_t *__restrict__ codes,
                                                              uint8_t *__restrict__ scales) {
+  __shared__ float tab[kMultTable];
+  const float s_enc = encode_scale(*amax_p);
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
   const int64_t nkb = C / 16;
   const int64_t kb = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (kb >= nkb) return;
-  const float s_enc = encode_scale(*amax_p);
   for (int64_t r = blockIdx.y; r < R; r += gridDim.y) {
     float v[16];
     load8(x + r * ld + kb * 16, v);
     load8(x + r * ld + kb * 16 + 8, v + 8);
     uint2 packed;
     uint32_t sc;
-    quant_block_rows<RHT, SR>(v, signs, uint64_t(r) * uint64_t(C) + uint64_t(kb) * 16u, seed, offset, s_enc, packed,
-                              sc);
+    quant_block_rows<RHT, SR>(v, signs, uint64_t(r) * uint64_t(C) + uint64_t(kb) * 16u, seed, offset, s_enc, tab,
+                              packed, sc);
     *reinterpret_cast<uint2 *>(codes + r * (C / 2) + kb * 8) = packed;
     scales[r * nkb + kb] = uint8_t(sc);
   }
@@ -309,28 +378,30 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restric
   const int64_t slab0 = int64_t(blockIdx.y) * kColSlabs;      // first slab of the tile
   const int64_t nslab = R / 16;                                // logical blocks per logical row
   const int64_t cfirst = c0 + 8 * cg;                          // this thread's first column
+  __shared__ float tab[kMultTable];
   const float s_enc = encode_scale(*amax_p);
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
 
 #pragma unroll 1
   for (int i = 0; i < kColSlabs / 8; ++i) {
     const int sl = 2 * wave + (lane >> 5) + 8 * i;             // slab within the tile
     const int64_t s = slab0 + sl;
     if (s >= nslab || cfirst >= C) continue;
-    float v[16][8];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) load8(x + (s * 16 + r) * ld + cfirst, v[r]);
+    Slab8<T> slab;
+    slab.load(x + s * 16 * ld + cfirst, ld, RHT ? signs : 0u);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float col[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) col[r] = v[r][j];
-      if (RHT) rht16(col, signs);
+      for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
+      if (RHT) hadamard16(col);
       float amax_b = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax_b = fmaxf(amax_b, __builtin_fabsf(col[r]));
       uint32_t sc;
       float mult;
-      block_scale(amax_b, s_enc, sc, mult);
+      block_scale(amax_b, s_enc, tab, sc, mult);
       const int row = 8 * cg + j;  // logical row within the tile
       uint2 packed;
       if (SR) {
@@ -362,18 +433,17 @@ __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict
   float mr = 0.0f, mc = 0.0f;
   for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads) {
     const int64_t sl = i / cchunks, c = (i - sl * cchunks) * 8;
-    float v[16][8];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) load8(x + (sl * 16 + r) * ld + c, v[r]);
+    Slab8<T> slab;
+    slab.load(x + sl * 16 * ld + c, ld, RHT ? signs : 0u);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float col[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        col[r] = v[r][j];
-        mr = fmaxf(mr, __builtin_fabsf(col[r]));
+        col[r] = slab.at(r, j);
+        mr = fmaxf(mr, __builtin_fabsf(col[r]));  // the signs do not change |x|
       }
-      if (RHT) rht16(col, signs);
+      if (RHT) hadamard16(col);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mc = fmaxf(mc, __builtin_fabsf(col[r]));
     }
@@ -385,7 +455,15 @@ __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict
 // 2D (16x16 tile) nearest-even quantization of x [R][C] (R, C multiples of 16).
 // Writes the direct layout (codes [R][C/2], scales [R/16][C/16]) to d_* and/or the
 // transposed layout (codes [C][R/2], scales [C/16][R/16]) to t_*; either may be null.
-// A wave covers 4 tiles side by side; lane = 16 * tile + row-in-tile.
+// A workgroup covers a 256x256 block of x (16x16 tiles); wave w takes the block's
+// tile-rows w, w + 4, w + 8, w + 12.  Lane l owns tile-column l % 16 and rows
+// 4 (l / 16) .. +3 of the current tile-row, so a tile's amax is a reduction over
+// its four lanes.  Each element is encoded twice by the converter: paired along
+// its row (the direct codes, stored at once as 128-byte runs of each row) and
+// paired down its column (the transposed codes, gathered in LDS and stored as
+// 128-byte runs of each row of x^T when the block is done).
+constexpr int k2dBlock = 256;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void quant_2d_kernel(const T *__restrict__ x, int64_t R, int64_t C,
                                                            int64_t ld, const float *__restrict__ amax_p,
@@ -393,57 +471,107 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(const T *__restrict_
                                                            uint8_t *__restrict__ d_scales,
                                                            uint8_t *__restrict__ t_codes,
                                                            uint8_t *__restrict__ t_scales) {
-  __shared__ uint8_t tcodes[kThreads / 16][16][17];  // per tile: [row][col] one code per byte (+1 pad)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile_in_wave = lane >> 4, row = lane & 15;
-  const int tile_slot = wave * 4 + tile_in_wave;
-  const int64_t tiles_c = C / 16, tiles_r = R / 16;
-  const int64_t tc = int64_t(blockIdx.x) * 16 + tile_slot;  // 16 tiles per workgroup along columns
+  // transposed codes: [row of x^T in the block][16 tile-rows x 8 bytes]; the 8-byte
+  // slot of tile-row t in row q sits at t ^ (q / 16 % 16), which spreads the 16
+  // lanes that write one slot index over distinct banks
+  __shared__ __attribute__((aligned(16))) uint8_t tcodes[k2dBlock * 128];
+  __shared__ uint8_t tscales[16 * 16];  // [tile-column][tile-row]
+  __shared__ float tab[kMultTable];
   const float s_enc = encode_scale(*amax_p);
-  for (int64_t tr = blockIdx.y; tr < tiles_r; tr += gridDim.y) {
-    const bool active = tc < tiles_c;
-    float v[16];
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tcl = lane & 15, rq = lane >> 4;
+  const int64_t tiles_r = R / 16, tiles_c = C / 16;
+  const int64_t tr0 = int64_t(blockIdx.y) * 16, tc0 = int64_t(blockIdx.x) * 16;  // the block's first tile-row, -column
+  const int64_t tc = tc0 + tcl;
+#pragma unroll 1
+  for (int it = 0; it < 4; ++it) {
+    const int trl = wave + 4 * it;  // tile-row within the block
+    const int64_t tr = tr0 + trl;
+    const bool active = tc < tiles_c && tr < tiles_r;
+    float v[4][16];
     float m = 0.0f;
     if (active) {
-      const T *p = x + (tr * 16 + row) * ld + tc * 16;
-      load8(p, v);
-      load8(p + 8, v + 8);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+      for (int k = 0; k < 4; ++k) {
+        const T *p = x + (tr * 16 + 4 * rq + k) * ld + tc * 16;
+        load8(p, v[k]);
+        load8(p + 8, v[k] + 8);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[k][j]));
+      }
     }
-    // amax over the 16 lanes of this tile (xor within the 16-lane group)
+    // tile amax over the four lanes of this tile-column (lanes l, l ^ 16, l ^ 32, l ^ 48)
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    uint32_t sc;
+    float mult;
+    block_scale(m, s_enc, tab, sc, mult);
+    if (!active) continue;
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    uint32_t sc = 0;
-    float mult = 0.0f;
-    block_scale(m, s_enc, sc, mult);
-    if (active) {
-      const uint2 packed = encode16_rne(v, mult);
-      if (d_codes) {
-        *reinterpret_cast<uint2 *>(d_codes + (tr * 16 + row) * (C / 2) + tc * 8) = packed;
-        if (row == 0) d_scales[tr * tiles_c + tc] = uint8_t(sc);
-      }
-      if (t_codes) {
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t w = j < 8 ? packed.x : packed.y;
-          tcodes[tile_slot][row][j] = uint8_t((w >> (4 * (j & 7))) & 15u);
-        }
+      for (int j = 0; j < 16; ++j) v[k][j] *= mult;
+    if (d_codes) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint2 c = make_uint2(encode8_rne(v[k]), encode8_rne(v[k] + 8));
+        *reinterpret_cast<uint2 *>(d_codes + (tr * 16 + 4 * rq + k) * (C / 2) + tc * 8) = c;
       }
+      if (rq == 0) d_scales[tr * tiles_c + tc] = uint8_t(sc);
     }
     if (t_codes) {
-      __syncthreads();
-      if (active) {
-        // lane `row` now assembles column `row` of the tile: logical row tc*16+row of x^T
-        uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w0 |= uint32_t(tcodes[tile_slot][i][row]) << (4 * i);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w1 |= uint32_t(tcodes[tile_slot][8 + i][row]) << (4 * i);
-        *reinterpret_cast<uint2 *>(t_codes + (tc * 16 + row) * (R / 2) + tr * 8) = make_uint2(w0, w1);
-        if (row == 0) t_scales[tc * tiles_r + tr] = uint8_t(sc);
+      for (int j = 0; j < 16; j += 2) {
+        // columns j, j + 1 of the tile: rows 4rq, 4rq+1 -> byte 2rq of the column's
+        // 8 code bytes, rows 4rq+2, 4rq+3 -> byte 2rq+1
+        uint32_t w = 0u;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0][j], v[1][j], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2][j], v[3][j], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0][j + 1], v[1][j + 1], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2][j + 1], v[3][j + 1], 1.0f, 3);
+        w = canon_zero(w);
+        const int q = tcl * 16 + j;  // row of x^T within the block; q / 16 % 16 == tcl
+        const int slot = (trl ^ tcl) * 8 + 2 * rq;
+        *reinterpret_cast<uint16_t *>(&tcodes[q * 128 + slot]) = uint16_t(w);
+        *reinterpret_cast<uint16_t *>(&tcodes[(q + 1) * 128 + slot]) = uint16_t(w >> 16);
       }
-      __syncthreads();
+      if (rq == 0) tscales[tcl * 16 + trl] = uint8_t(sc);
+    }
+  }
+  if (!t_codes) return;
+  __syncthreads();
+  // 256 rows of x^T x 128 bytes: thread chunk i * 256 + tid is row (i*256 + tid) / 8,
+  // 16-byte chunk (tile-rows 2 ch, 2 ch + 1) (i*256 + tid) % 8
+  const int64_t nrows_t = min<int64_t>(k2dBlock, C - tc0 * 16);  // rows of x^T in this block
+  const int64_t ntr = min<int64_t>(16, tiles_r - tr0);             // tile-rows in this block
+#pragma unroll 2
+  for (int i = 0; i < 8; ++i) {
+    const int q = i * kThreads + threadIdx.x, row = q >> 3, ch = q & 7;
+    if (row >= nrows_t || 2 * ch >= ntr) continue;
+    const int g = (row >> 4) & 15;
+    uint4 v = *reinterpret_cast<const uint4 *>(&tcodes[row * 128 + ((2 * ch) ^ (g & ~1)) * 8]);
+    if (g & 1) v = make_uint4(v.z, v.w, v.x, v.y);  // the two slots sit swapped
+    uint8_t *dst = t_codes + (tc0 * 16 + row) * (R / 2) + (tr0 + 2 * ch) * 8;
+    if (2 * ch + 1 < ntr) {
+      if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2 *>(dst + 8) = make_uint2(v.z, v.w);
+      }
+    } else {
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+    }
+  }
+  if (threadIdx.x < 16 && tc0 + threadIdx.x < tiles_c) {
+    uint8_t *dst = t_scales + (tc0 + threadIdx.x) * tiles_r + tr0;
+    const uint8_t *src = &tscales[threadIdx.x * 16];
+    if (ntr == 16 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    } else {
+      for (int k = 0; k < ntr; ++k) dst[k] = src[k];
     }
   }
 }
@@ -462,8 +590,8 @@ hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
   const int64_t cap = 256 * 16;  // 16 workgroups per CU are plenty for a streaming reduction
   if (R == 0 || C == 0) return hipGetLastError();
   if (!(flags & FP4_Q_RHT) && ld == C) {
-    // a read-only stream runs best with a moderate grid (measured on the MI355X)
-    hipLaunchKernelGGL(amax_flat_kernel<T>, dim3(grid_for(R * (C / 8), kThreads * 4, 2048)), dim3(kThreads), 0,
+    // a read-only stream runs best with two workgroups per CU (measured on the MI355X)
+    hipLaunchKernelGGL(amax_flat_kernel<T>, dim3(grid_for(R * (C / 8), kThreads * 4, 512)), dim3(kThreads), 0,
                        stream, x, R * (C / 8), out);
   } else if (!(flags & FP4_Q_RHT)) {
     hipLaunchKernelGGL(amax_plain_kernel<T>, dim3(grid_for(R * (C / 8), kThreads * 4, cap)), dim3(kThreads), 0,
@@ -521,7 +649,7 @@ hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t 
     if (direct) { dc = direct->codes; ds = direct->scales; }
     if (transp) { tcp = transp->codes; tsp = transp->scales; }
     const int64_t tiles_c = C / 16, tiles_r = R / 16;
-    dim3 grid(unsigned((tiles_c + 15) / 16), unsigned(tiles_r < 65535 ? tiles_r : 65535));
+    const dim3 grid(unsigned((tiles_c + 15) / 16), unsigned((tiles_r + 15) / 16));
     hipLaunchKernelGGL(quant_2d_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, out->amax, dc, ds, tcp,
                        tsp);
     if (out_t && out_t->amax != out->amax) {
@@ -551,10 +679,10 @@ hipError_t dual_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
                      hipStream_t stream) {
   const bool rht = flags & FP4_Q_RHT, sr = flags & FP4_Q_SR;
   if (!(flags & FP4_Q_AMAX_GIVEN)) {
-    hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, rows->amax);
-    hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, cols->amax);
+    hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(1), 0, stream, rows->amax, cols->amax);
     if (R > 0 && C > 0) {
-      const dim3 grid(grid_for((R / 16) * (C / 8), kThreads, 2048));
+      // four workgroups per CU: the kernel's registers allow four waves per SIMD
+      const dim3 grid(grid_for((R / 16) * (C / 8), kThreads, 1024));
       if (rht)
         hipLaunchKernelGGL((amax_dual_kernel<T, true>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
                            rows->amax, cols->amax);

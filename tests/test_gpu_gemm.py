@@ -42,9 +42,14 @@ CASES = [
     (300, 272, 512, False, True),
     (300, 260, 512, False, False),
     # more 256x256 tiles than CUs: persistent loop; 17x16 = 272 tiles, 17x17 = 289
-    # (an XCD split that is not even), ragged in both dimensions
+    # (an XCD split that is not even), ragged in both dimensions; on a 256-CU GPU
+    # the tiles past the first 256 run as 128x128 quarters in a second launch
+    # (64 and 132 quarters, one per workgroup; the ragged case has quarters wholly
+    # past the edge)
     (4352, 4096, 256, False, True),
     (4100, 4100, 256, False, False),
+    # 89x4 = 356 tiles: 100 past one round, 400 quarters, more than one per CU
+    (22784, 1000, 256, False, False),
 ]
 
 

@@ -14,20 +14,20 @@ def make_x(shape, seed, kind="normal", std=1.0, dtype=torch.bfloat16):
     return workloads.random_matrix(shape, seed, kind=kind, std=std, dtype=dtype)
 
 
-def run_case(fp4, oracle, x_cpu, flags, signs=0, seed=0, offset=0):
+def run_case(fp4, oracle, x_cpu, flags, signs=0, seed=0, offset=0, with_t=True):
     colwise = bool(flags & fp4.Q_COLWISE)
     two_d = bool(flags & fp4.Q_2D)
     R, C = x_cpu.shape
     lrows, lcols = (C, R) if colwise else (R, C)
     x = dev(x_cpu)
     q = fp4.QTensor(lrows, lcols, two_d)
-    q_t = fp4.QTensor(lcols, lrows, True) if two_d else None
+    q_t = fp4.QTensor(lcols, lrows, True) if two_d and with_t else None
     fp4.fp4_quantize(x, flags, signs, seed, offset, q, q_t)
     xf = workloads.widen(x_cpu)
     ora = oracle.quantize(xf, two_d=two_d, colwise=colwise, rht=bool(flags & fp4.Q_RHT), sr=bool(flags & fp4.Q_SR),
                           signs=signs, seed=seed, offset=offset)
     assert_q_equal(host_q(q), ora, f"flags={flags} shape={tuple(x_cpu.shape)}")
-    if two_d:
+    if q_t is not None:
         ora_t = oracle.quantize(xf, two_d=True, colwise=not colwise)
         assert_q_equal(host_q(q_t), ora_t, f"transposed flags={flags} shape={tuple(x_cpu.shape)}")
     return q
@@ -63,6 +63,14 @@ def test_two_d(fp4, oracle, shape, colwise, dtype):
     flags = fp4.Q_2D | (fp4.Q_COLWISE if colwise else 0)
     x = make_x(shape, seed=shape[0] + shape[1], std=0.02, dtype=dtype)
     run_case(fp4, oracle, x, flags)
+
+
+@pytest.mark.parametrize("colwise", [False, True], ids=["direct", "colwise"])
+def test_two_d_single_layout(fp4, oracle, colwise):
+    """2D without the second layout: the kernel writes only the direct codes, or
+    (COLWISE) only the transposed ones; ragged against its 256x256 blocks."""
+    x = make_x((272, 528), seed=11, std=0.02)
+    run_case(fp4, oracle, x, fp4.Q_2D | (fp4.Q_COLWISE if colwise else 0), with_t=False)
 
 
 @pytest.mark.parametrize("flags_name", ["plain", "rht_rows", "rht_cols"])
