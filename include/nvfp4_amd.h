@@ -13,7 +13,8 @@
  *   amax     = max |v| over the tensor (v after the Hadamard transform if any)
  *   s_enc    = 2688 / amax (1 if amax == 0; FLT_MAX if the quotient overflows)
  *   per block: S = E4M3_rne_satfinite((amax_b / 6) * s_enc),
- *              m = s_enc / decode(S) (0 when S == 0)
+ *              m = s_enc / decode(S) (0 when S == 0; FLT_MAX if the quotient
+ *              overflows, as only a tensor amax below about 1e-35 can make it)
  *   element  = E2M1(v * m), nearest-even or stochastic, saturating at 6;
  *              zero is always the +0 code; two codes per byte, low nibble first
  *   decode   = E2M1 * decode(S) * (amax / 2688)

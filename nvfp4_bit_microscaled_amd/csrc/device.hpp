@@ -59,14 +59,17 @@ __device__ __forceinline__ float div6(float x) {
   return x / 6.0f;
 }
 
-// Element multipliers by scale code: tab[c] = s_enc / decode(c), 0 for c = 0.
-// A workgroup fills its table once (threads 0..127) and reads it per block.
+// Element multipliers by scale code: tab[c] = s_enc / decode(c), saturated at
+// the largest finite float (as the encode scale is: for a tensor amax below about
+// 1e-35 the quotient can overflow while the block's elements are tiny), 0 for
+// c = 0.  A workgroup fills its table once (threads 0..127) and reads it per block.
 constexpr int kMultTable = 128;
 
 __device__ __forceinline__ void fill_mult_table(float *tab, float s_enc) {
   if (threadIdx.x < kMultTable) {
     const float sf = e4m3_to_f32(threadIdx.x);
-    tab[threadIdx.x] = sf > 0.0f ? s_enc / sf : 0.0f;
+    const float m = sf > 0.0f ? s_enc / sf : 0.0f;
+    tab[threadIdx.x] = __builtin_isinf(m) ? 3.402823466e38f : m;
   }
 }
 

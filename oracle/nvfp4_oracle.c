@@ -241,14 +241,20 @@ NVO_EXPORT float nvo_decode_scale(float amax) { return amax / 2688.0f; }
 
 /* Block scale: the block amax divided by 6 (the largest element), times the
  * tensor encode scale, rounded to E4M3; the per-block multiplier is the tensor
- * encode scale divided by the decoded block scale (0 when the scale is 0). */
+ * encode scale divided by the decoded block scale (0 when the scale is 0).
+ * Like the encode scale, the multiplier saturates at the largest finite float:
+ * for a tensor whose amax is below about 1e-35 the quotient can overflow while
+ * the block's elements are tiny, and the scaled values must stay finite (an
+ * infinite multiplier would turn a zero element into NaN). */
 static void block_scale(float amax_b, float s_enc, unsigned *code, float *mult) {
   float t = amax_b / 6.0f;
   float u = t * s_enc;
   unsigned c = nvo_e4m3_encode(u);
   float sf = (float)nvo_e4m3_value(c);
   *code = c;
-  *mult = (sf > 0.0f) ? s_enc / sf : 0.0f;
+  float m = (sf > 0.0f) ? s_enc / sf : 0.0f;
+  if (isinf(m)) m = FLT_MAX;
+  *mult = m;
 }
 
 static void encode_block(const float v[16], float mult, int sr, int64_t i0, uint64_t seed, uint64_t offset,

@@ -116,6 +116,23 @@ def test_scale_underflow_and_saturation(fp4, oracle):
     assert (scales == 0).any() and ((scales > 0) & (scales < 8)).any()
 
 
+@pytest.mark.parametrize("top", [-110, -121], ids=["tiny", "scale_clamped"])
+def test_tiny_and_subnormal_blocks(fp4, oracle, top):
+    """fp32 tensors of tiny values: block amaxes log-uniform over [2^-149, 2^top],
+    so many blocks sit below 2^-125 (their amax / 6 is subnormal) and, with
+    top = -110, every E4M3 scale code occurs.  With top = -121 the tensor amax is
+    so small that 2688 / amax overflows and the encode scale takes its clamped
+    value."""
+    rng = np.random.default_rng(-top)
+    x = rng.uniform(-1.0, 1.0, (128, 1024)).astype(np.float64)
+    x *= np.exp2(rng.uniform(-149, top, (128, 64))).repeat(16, axis=1)
+    x_cpu = torch.from_numpy(x.astype(np.float32))
+    for flags in (fp4.Q_SR, fp4.Q_COLWISE | fp4.Q_RHT | fp4.Q_SR, fp4.Q_2D):
+        run_case(fp4, oracle, x_cpu, flags, signs=0x3C5A, seed=9, offset=4)
+    codes, scales, _ = host_q(run_case(fp4, oracle, x_cpu, 0))
+    assert len(np.unique(scales)) > (100 if top == -110 else 50)
+
+
 def test_empty(fp4):
     x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
     q = fp4.QTensor(0, 64)

@@ -76,6 +76,27 @@ def test_worked_block_rounding(oracle):
     assert deq[16] == 6 * 72 * g and deq[17] == 2 * 72 * g
 
 
+def test_worked_block_saturated_multiplier(oracle):
+    """Block [2^-129, 0, ...]: amax 2^-129 makes 2688 / amax overflow, so s_enc =
+    FLT_MAX = (1 - 2^-24) 2^128; t = fl(2^-129 / 6) = 174763 * 2^-149 (subnormal,
+    174762.67 rounded), u = t * FLT_MAX = 0.08333 rounds to the E4M3 value
+    1.375 * 2^-4 (code 3<<3 | 3 = 0x1B); s_enc / 0.0859375 overflows, so the
+    multiplier saturates at FLT_MAX as well: 2^-129 * FLT_MAX = 0.5 - 2^-25 rounds
+    to 0.5 (code 1) and the zeros stay 0.  (An infinite multiplier would give
+    code 7 and turn the zeros into NaN.)"""
+    row = np.zeros(16, dtype=np.float32)
+    row[0] = np.float32(2.0**-129)
+    q = oracle.quantize(row[None, :])
+    assert q.amax == np.float32(2.0**-129)
+    assert q.scales[0, 0] == 0x1B
+    codes = unpack(q.codes)[0]
+    assert codes[0] == 1 and np.all(codes[1:] == 0)
+    # stochastic: 0.5 - 2^-25 sits 2^-24 of a step below 0.5, so it rounds up for
+    # every 16-bit draw but 0; the zeros stay 0
+    c = unpack(oracle.quantize(row[None, :], sr=True, seed=1, offset=0).codes)[0]
+    assert c[0] in (0, 1) and np.all(c[1:] == 0)
+
+
 def test_zero_tensor(oracle):
     x = np.zeros((32, 64), dtype=np.float32)
     for kw in (dict(), dict(two_d=True), dict(colwise=True, rht=True, sr=True, signs=0x1234, seed=5, offset=9)):
