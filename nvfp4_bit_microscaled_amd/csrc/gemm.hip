@@ -142,107 +142,74 @@ __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&
 // Epilogue of the main kernel, whose MFMAs take the B tile as first operand so
 // that acc[i][j] holds the 32x32 block C^T: lane l owns row m = 32 i + l % 32 of C
 // and, in register group q, the 4 consecutive columns n = 32 j + 8 q + 4 (l / 32)
-// .. +3.  Each group is scaled by the two tensor decode scales and leaves as one
-// 8-byte (bf16, rounded to nearest-even in pairs) or 16-byte (fp32) store.
-// CHECK: the tile may stick out of C (rows or columns past the edge are skipped;
-// the launcher guarantees N % 4 == 0, so a group is wholly inside or outside).
-// The launcher also guarantees a 16-byte aligned C and ldc % 4 == 0.
+// .. +3.
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int TM, int TN, bool CHECK>
-__device__ __forceinline__ void store_tiles_t(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
-                                              int64_t n0, int lr, int g) {
-  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + 32 * i + lr;
-    if (CHECK && m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + 32 * j + 8 * q + 4 * g;
-        if (CHECK && n >= p.N) continue;
-        const float v0 = acc[i][j][4 * q] * gscale, v1 = acc[i][j][4 * q + 1] * gscale;
-        const float v2 = acc[i][j][4 * q + 2] * gscale, v3 = acc[i][j][4 * q + 3] * gscale;
-        if (p.c_bf16) {
-          const bf16x4 h = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-          *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = h;
-        } else {
-          *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) = make_float4(v0, v1, v2, v3);
-        }
-      }
-  }
-}
-
-// Epilogue of the main kernel through LDS: each wave stages its block
-// (C^T layout as above, scaled and converted) in a private 4 KB region, 32 rows
-// of 128 bytes at a time (64 bf16 or 32 fp32 columns), with the 16-byte chunks
-// of a row XOR-swizzled by the row, and reads each piece back a chunk per lane,
-// so that every store instruction writes whole 128-byte lines of C.  The region
-// lies outside the two stage buffers, so the next tile's stages can land while
-// this runs.  CHECK as for store_tiles_t (N % 4 == 0; C 16-byte aligned,
-// ldc % 4 == 0).
+// Epilogue of the main kernel through LDS, one 32x32 accumulator block at a
+// time: the block goes raw (fp32, C^T layout as above) from the accumulator
+// registers into a private 4 KB region, 32 rows of 128 bytes with the 16-byte
+// chunks of a row XOR-swizzled by the row; each lane then reads back whole
+// chunks of rows, scales them (gscale: the product of the two tensor decode
+// scales), converts and stores them, so every store writes whole row runs of C
+// (128 bytes fp32, 64 bytes bf16).  The region lies outside the two stage
+// buffers, so the next tile's stages can land while this runs, and only one
+// block's values pass through vector registers at a time.  CHECK: the tile may
+// stick out of C (rows or columns past the edge are skipped; the launcher
+// guarantees N % 4 == 0, a 16-byte aligned C and ldc % 4 == 0).
 constexpr int kEpiBytes = 4096;
 
 template <int TM, int TN, bool CHECK>
 __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
-                                                int64_t n0, int lane, uint8_t *region) {
-  static_assert(TN % 2 == 0, "bf16 pieces are 64 columns");
+                                                int64_t n0, int lane, uint8_t *region, float gscale) {
   const int lr = lane & 31, g = lane >> 5;
   const int wsw = (lr >> 1) & 7;  // swizzle of the row this lane writes
-  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
-  // read-back: chunk 64 k + lane of the piece is row (64 k + lane) / 8, chunk lane % 8
-  const int rr = lane >> 3, rc = lane & 7;
-  if (p.c_bf16) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int jp = 0; jp < TN / 2; ++jp) {
+    for (int j = 0; j < TN; ++j) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+      for (int q = 0; q < 4; ++q) {  // columns 8q + 4g .. +3 of the block: chunk 2q + g
+        const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]);
+        *reinterpret_cast<float4 *>(region + lr * 128 + (((2 * q + g) ^ wsw) << 4)) = v;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (p.c_bf16) {
+        // lane: rows 16k + lane / 4 (k = 0, 1), chunks 2 (lane % 4), +1 (8 columns)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int j = 2 * jp + jj, c = 4 * jj + q;  // columns 8c .. 8c+7 of the piece; this lane's half g
-            const bf16x4 h = {(__bf16)(acc[i][j][4 * q] * gscale), (__bf16)(acc[i][j][4 * q + 1] * gscale),
-                              (__bf16)(acc[i][j][4 * q + 2] * gscale), (__bf16)(acc[i][j][4 * q + 3] * gscale)};
-            *reinterpret_cast<bf16x4 *>(region + lr * 128 + ((c ^ wsw) << 4) + 8 * g) = h;
-          }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int r = 8 * k + rr;
-          const uint4 v = *reinterpret_cast<const uint4 *>(region + r * 128 + ((rc ^ ((r >> 1) & 7)) << 4));
-          const int64_t m = m0 + 32 * i + r, n = n0 + 64 * jp + 8 * rc;
+        for (int k = 0; k < 2; ++k) {
+          const int r = 16 * k + (lane >> 2), c = 2 * (lane & 3);
+          const int rs = (r >> 1) & 7;
+          const float4 x0 = *reinterpret_cast<const float4 *>(region + r * 128 + ((c ^ rs) << 4));
+          const float4 x1 = *reinterpret_cast<const float4 *>(region + r * 128 + (((c + 1) ^ rs) << 4));
+          const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 4 * c;
+          typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+          const bf16x8 h = {(__bf16)(x0.x * gscale), (__bf16)(x0.y * gscale), (__bf16)(x0.z * gscale),
+                            (__bf16)(x0.w * gscale), (__bf16)(x1.x * gscale), (__bf16)(x1.y * gscale),
+                            (__bf16)(x1.z * gscale), (__bf16)(x1.w * gscale)};
           uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n;
-          if (!CHECK || (m < p.M && n + 8 <= p.N)) *reinterpret_cast<uint4 *>(dst) = v;
-          else if (m < p.M && n < p.N) *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+          if (!CHECK || (m < p.M && n + 8 <= p.N)) {
+            *reinterpret_cast<bf16x8 *>(dst) = h;
+          } else if (m < p.M && n < p.N) {
+            const bf16x4 lo = {h[0], h[1], h[2], h[3]};
+            *reinterpret_cast<bf16x4 *>(dst) = lo;
+          }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next piece
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = make_float4(acc[i][j][4 * q] * gscale, acc[i][j][4 * q + 1] * gscale,
-                                       acc[i][j][4 * q + 2] * gscale, acc[i][j][4 * q + 3] * gscale);
-          *reinterpret_cast<float4 *>(region + lr * 128 + (((2 * q + g) ^ wsw) << 4)) = v;  // columns 4(2q+g) ..
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      } else {
+        // lane: rows 8k + lane / 8 (k = 0..3), chunk lane % 8 (4 columns)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int r = 8 * k + rr;
-          const float4 v = *reinterpret_cast<const float4 *>(region + r * 128 + ((rc ^ ((r >> 1) & 7)) << 4));
-          const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 4 * rc;
+          const int r = 8 * k + (lane >> 3), c = lane & 7;
+          const float4 x = *reinterpret_cast<const float4 *>(region + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+          const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 4 * c;
           if (!CHECK || (m < p.M && n < p.N))
-            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) = v;
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
+                make_float4(x.x * gscale, x.y * gscale, x.z * gscale, x.w * gscale);
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next piece
       }
-  }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next block
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -332,6 +299,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
     Lstride = gridDim.x;
   }
   if (L >= Lend) return;
+  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);  // loaded before any DMA is in flight
   int64_t m0, n0;
 
   // DMA sources.  Unit u (16 bytes) of a wave's instruction j sits at row
@@ -483,7 +451,14 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   // first quarter from the other buffer and spreads the DMA of stage kt_dma (of
   // the tile whose offsets va/vb/vs hold) into this buffer over its substeps.
   // The last stage has none of that.
-  auto stage = [&](int kt, auto last_tag, int par, int kt_dma) {
+  // after_epi: the previous tile's epilogue stores were issued after this tile's
+  // second-stage DMA.  Vector memory operations retire in issue order on this
+  // chip, so waiting until no more than that many stores are outstanding waits
+  // for the DMA alone.  Without CLAMP every store is issued: per 32x32 block, 2
+  // (bf16) or 4 (fp32) per lane; with CLAMP some may be skipped, so everything
+  // is drained.
+  constexpr int kStoresBf16 = TM * TN * 2, kStoresF32 = TM * TN * 4;
+  auto stage = [&](int kt, auto last_tag, int par, int kt_dma, bool after_epi) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int buf = (kt + par) & 1;
     static_for<4>([&](auto qc) {
@@ -491,7 +466,12 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       constexpr int slot = q & 1;
       constexpr bool next_q = q < 3 || !LAST;  // is there a quarter after this one?
       if constexpr (q == 3 && !LAST) {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        if (!CLAMP && after_epi && p.c_bf16)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStoresBf16) : "memory");
+        else if (!CLAMP && after_epi)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStoresF32 < 63 ? kStoresF32 : 63) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
       }
       static_for<4>([&](auto sc) {
@@ -534,6 +514,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   // count is odd.
   set_tile(L);
   int par = 0;
+  bool first = true;  // no epilogue stores in flight yet
   issue(0, 0);
   issue(min(1, nst - 1), 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -553,15 +534,15 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       dequant_half(0, 0, 0, i, 0);
       dequant_half(0, 0, 0, i, 1);
     }
-    for (int kt = 0; kt + 2 < nst; ++kt) stage(kt, std::false_type{}, par, kt + 2);
+    for (int kt = 0; kt + 2 < nst; ++kt) stage(kt, std::false_type{}, par, kt + 2, kt == 0 && !first);
     if (nst >= 2) {
       // the stage before last loads the next tile's first stage; without a next
       // tile it re-loads this tile's last stage into a buffer that is not read
       // again (drained below)
       if (more) set_tile(Lnext);
-      stage(nst - 2, std::false_type{}, par, more ? 0 : nst - 1);
+      stage(nst - 2, std::false_type{}, par, more ? 0 : nst - 1, nst == 2 && !first);
     }
-    stage(nst - 1, std::true_type{}, par, 0);
+    stage(nst - 1, std::true_type{}, par, 0, false);
 
     // every wave is done with this tile's stage buffers, and the DMA issued in the
     // stage before last has landed
@@ -576,7 +557,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
         issue(0, par_next);
       }
     }
-    store_tiles_lds<TM, TN, CLAMP>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes);
+    store_tiles_lds<TM, TN, CLAMP>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes, gscale);
     if (!more) break;
     if (nst == 1) {
       // a one-stage tile's first stage was only just issued
@@ -585,6 +566,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
     }
     L = Lnext;
     par = par_next;
+    first = false;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -772,11 +754,12 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
   if (p.M == 0 || p.N == 0) return hipSuccess;
   auto al = [](const void *q, uintptr_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
   // main path: whole 256-element K stages, 16-byte aligned codes and scale rows,
-  // every DMA offset within 32 bits, and an output the vector stores can write
+  // every DMA offset within 32 bits, and an output whose rows the 16-byte stores
+  // can write (16-byte aligned C and rows)
   const bool main_path = p.K >= 256 && p.K % 256 == 0 && al(a->codes, 16) && al(b->codes, 16) &&
                          al(a->scales, 16) && al(b->scales, 16) && (p.M + 256) * (p.K / 2) < (int64_t(1) << 32) &&
                          (p.N + 256) * (p.K / 2) < (int64_t(1) << 32) &&
-                         al(c, 16) && ldc % 4 == 0 && p.N % 4 == 0;
+                         al(c, 16) && ldc % (p.c_bf16 ? 8 : 4) == 0 && p.N % 4 == 0;
   if (main_path) {
     // persistent: one workgroup per CU (its 160 KB of LDS admit no second one).
     // When the tiles overrun whole rounds of the CUs by at most half a round,

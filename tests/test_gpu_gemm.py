@@ -111,6 +111,26 @@ def test_zero_k_and_zero_operands(fp4, oracle):
     fp4.fp4_gemm(e, fp4.QTensor(48, 64), c2)
 
 
+@pytest.mark.parametrize("ldc", [260, 264])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_row_stride_of_c(fp4, oracle, ldc, out_dtype):
+    """C with a row stride beyond N on a main-path shape: rows of 260 bf16 are not
+    16-byte multiples (the edge kernel takes that case), 264 are; the columns past
+    N keep their contents."""
+    M, N, K = 300, 256, 512
+    qa, qb = oracle_operands(oracle, M, N, K, seed=5)
+    a, b = upload_q(fp4, qa), upload_q(fp4, qb)
+    big = torch.full((M, ldc), -1.0, dtype=out_dtype, device="cuda")
+    from nvfp4_bit_microscaled_amd import load
+    dt = 1 if out_dtype == torch.float32 else 0
+    assert load().fp4_gemm(a.desc, b.desc, big.data_ptr(), dt, ldc, None) == 0
+    torch.cuda.synchronize()
+    y = big.float().cpu().numpy()
+    assert np.all(y[:, N:] == -1.0)
+    y_ref, bound = oracle.gemm_ref(qa, qb)
+    check_gemm(y[:, :N], y_ref, bound, out_dtype == torch.bfloat16, f"ldc {ldc}")
+
+
 def test_ldc_larger_than_n(fp4, oracle):
     qa, qb = oracle_operands(oracle, 100, 60, 256, seed=2)
     a, b = upload_q(fp4, qa), upload_q(fp4, qb)
