@@ -63,14 +63,15 @@ def source_hash(path):
 
 
 def measured_traffic(kernel_src):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it
-    was taken on the kernel source as it stands (same hash); else None."""
+    """HBM bytes per fp4_gemm call (its launches together) from the committed
+    rocprofv3 counter summary, if it was taken on the kernel source as it stands
+    (same hash); else None."""
     p = os.path.join(ROOT, "profiles", "mlp_up_12b_hbm_traffic.md")
     if not os.path.exists(p):
         return None
     txt = open(p).read()
     h = re.search(r"source sha256\[:16\]: (\w+)", txt)
-    t = re.search(r"bytes per step \(3 GEMM launches\): ([0-9.eE+]+)", txt)
+    t = re.search(r"bytes per step \(3 fp4_gemm calls\): ([0-9.eE+]+)", txt)
     if not h or not t or h.group(1) != source_hash(kernel_src):
         return None
     return float(t.group(1)) / 3.0
@@ -197,9 +198,11 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4),
         "traffic": traffic,
-        "kernel": "nvfp4 block-scaled GEMM (f16 MFMA on exactly dequantized E2M1xE4M3 operands)",
-        "flops_per_launch": gemm_flops / n_gemm,
-        "avg_launch_ms": round(gemm_ms / n_gemm, 4),
+        "kernel": "nvfp4 block-scaled GEMM (f16 MFMA on exactly dequantized E2M1xE4M3 operands); one fp4_gemm call "
+                  "per pass: a persistent 256x256-tile launch, plus a 128x128-quarters launch when the tiles overrun "
+                  "whole rounds of the CUs (wgrad here)",
+        "flops_per_call": gemm_flops / n_gemm,
+        "avg_call_ms": round(gemm_ms / n_gemm, 4),
         "frac_of_fp4_dense_peak": round(gemm_tflops / PEAK_FP4_MFMA_TFLOPS, 4),
     }
 
