@@ -38,10 +38,68 @@ def parse():
     ap.add_argument("--workload", default="mlp_up_12b", choices=["mlp_up_12b", "fprop_8k", "wgrad_8k", "block_3b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
+    ap.add_argument("--error-vs-k", action="store_true",
+                    help="instead of the benchmark: relative error of the NVFP4 GEMM against the unquantized binary64 "
+                         "product for K from 256 to 32768, per quantization mode (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (the known-size reference that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters into bytes) and exit")
     return ap.parse_args()
+
+
+ERROR_MODES = {  # operand A (activation- or gradient-like), operand B (weight-like)
+    "rne": (0, 0),
+    "rht": ("rht", "rht"),
+    "sr": ("sr", 0),
+    "rht_sr": ("rht_sr", "rht"),
+}
+
+
+def quantized_gemm_error(fp4, a, b, mode, signs, seed=0, offset=1):
+    """Relative Frobenius error ||C_q - C|| / ||C|| of the NVFP4 GEMM of bf16 device
+    tensors a [M, K], b [N, K] against their unquantized binary64 product.  Both
+    operands are quantized 1D along K (rowwise); `mode` picks the random Hadamard
+    transform (same signs on both operands, so the product is unchanged up to
+    quantization) and stochastic rounding of A.  Returns (error, C_q)."""
+    import torch
+    fa, fb = ERROR_MODES[mode]
+    flag = {0: 0, "rht": fp4.Q_RHT, "sr": fp4.Q_SR, "rht_sr": fp4.Q_RHT | fp4.Q_SR}
+    M, K = a.shape
+    N = b.shape[0]
+    qa, qb = fp4.QTensor(M, K), fp4.QTensor(N, K)
+    fp4.fp4_quantize(a, flag[fa], signs, seed, offset, qa)
+    fp4.fp4_quantize(b, flag[fb], signs, seed, offset, qb)
+    c = torch.empty(M, N, dtype=torch.float32, device=a.device)
+    fp4.fp4_gemm(qa, qb, c)
+    ref = a.double() @ b.double().T.contiguous()
+    err = float(torch.linalg.norm(c.double() - ref) / torch.linalg.norm(ref))
+    return err, c
+
+
+def error_vs_k():
+    """Error accumulation of the NVFP4 GEMM versus K (the pages discuss how FP4
+    errors grow along the reduction; they give no figures)."""
+    import torch
+
+    import nvfp4_bit_microscaled_amd as fp4
+    import workloads
+
+    fp4.load()
+    M = N = 512
+    rows = []
+    for outliers in (False, True):
+        for K in (256, 1024, 4096, 16384, 32768):
+            a, b, signs = workloads.error_operands(M, N, K, seed=K, outliers=outliers)
+            a, b = a.cuda(), b.cuda()
+            for mode in ERROR_MODES:
+                err, _ = quantized_gemm_error(fp4, a, b, mode, signs)
+                rows.append({"K": K, "data": "outliers" if outliers else "gaussian", "mode": mode,
+                             "rel_fro_error": round(err, 6)})
+    torch.cuda.synchronize()
+    print(json.dumps({"analysis": "NVFP4 GEMM relative Frobenius error vs K against the unquantized binary64 product",
+                      "M": M, "N": N, "operands": "A ~ N(0,1) (optionally 0.1% x50 outliers), B ~ N(0, 0.02^2); bf16",
+                      "modes": {k: f"A {v[0] or 'rne'}, B {v[1] or 'rne'}" for k, v in ERROR_MODES.items()},
+                      "rows": rows}), flush=True)
 
 
 def copy_calibration():
@@ -85,6 +143,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.error_vs_k:
+        error_vs_k()
         return
 
     import numpy as np

@@ -173,6 +173,52 @@ def test_mlp_up_12b_sampled(fp4, oracle):
     check_gemm(dw.cpu().numpy()[wrows], y_ref, bound, False, "wgrad 12B")
 
 
+def test_block_3b_sampled(fp4, oracle):
+    """The 3B-like block at 32768 tokens: QKV, O, up and down projections, each with
+    all three passes as the benchmark times them; every operand checked on sampled
+    rows (codes and scales bit-exact with the whole-tensor amax), every output on a
+    sampled block of rows and columns."""
+    wl = workloads.WORKLOADS["block_3b"]
+    sr, off_d, off_w = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
+    for li, lin in enumerate(wl.linears):
+        M, N, K = lin.M, lin.N, lin.K
+        inp = workloads.make_linear_inputs(lin, seed=li)
+        x, w, dy = dev(inp.x), dev(inp.w), dev(inp.dy)
+        bufs = fp4.LinearBuffers(M, N, K)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
+        fp4.fp4_quantize_dual(x, fp4.Q_RHT, inp.signs, 0, 0, 0, bufs.xq, bufs.xq_t)
+        fp4.fp4_quantize(w, fp4.Q_2D, 0, 0, 0, bufs.wq, bufs.wq_t)
+        fp4.fp4_gemm(bufs.xq, bufs.wq, y)
+        fp4.fp4_linear_backward(dy, None, bufs.wq_t, dx, dw, inp.signs, sr, off_d, off_w, bufs.dyq, bufs.dyq_t,
+                                bufs.xq_t)
+        torch.cuda.synchronize()
+        del x, w, dy
+        xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
+        owq = oracle.quantize(wf, two_d=True)
+        assert_q_equal(host_q(bufs.wq), owq, f"{lin.name} wq")
+        owtq = oracle.quantize(wf, two_d=True, colwise=True)
+        assert_q_equal(host_q(bufs.wq_t), owtq, f"{lin.name} wq_t")
+        rows = sample_rows(M, 12, 10 + li)
+        # fprop: Y rows, all columns
+        oxs = check_rows(oracle, xf, host_q(bufs.xq), rows)
+        y_ref, bound = oracle.gemm_ref(oxs, owq)
+        check_gemm(y.float().cpu().numpy()[rows], y_ref, bound, True, f"{lin.name} fprop")
+        # dgrad: dX rows, all columns
+        ods = check_rows(oracle, dyf, host_q(bufs.dyq), rows, sr=True, seed=sr, offset=off_d)
+        y_ref, bound = oracle.gemm_ref(ods, owtq)
+        check_gemm(dx.float().cpu().numpy()[rows], y_ref, bound, True, f"{lin.name} dgrad")
+        # wgrad: a sampled block of dW (rows of dY^T, rows of X^T)
+        nrows, kcols = sample_rows(N, 8, 20 + li), sample_rows(K, 48, 30 + li)
+        odt = check_rows(oracle, dyf, host_q(bufs.dyq_t), nrows, colwise=True, rht=True, sr=True,
+                         signs=inp.signs, seed=sr, offset=off_w)
+        oxt = check_rows(oracle, xf, host_q(bufs.xq_t), kcols, colwise=True, rht=True, signs=inp.signs)
+        y_ref, bound = oracle.gemm_ref(odt, oxt)
+        check_gemm(dw.cpu().numpy()[np.ix_(nrows, kcols)], y_ref, bound, False, f"{lin.name} wgrad")
+        del y, dx, dw, bufs
+
+
 @pytest.mark.parametrize("quantize_x", [True, False], ids=["x_given", "xq_t_from_forward"])
 def test_linear_backward_equals_dgrad_and_wgrad(fp4, oracle, quantize_x):
     """fp4_linear_backward (dY quantized once for both GEMMs) gives bit for bit the

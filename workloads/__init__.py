@@ -41,6 +41,18 @@ def normal(rng: np.random.Generator, shape, std=1.0, outlier_frac=0.0, outlier_s
     return x
 
 
+def error_operands(M: int, N: int, K: int, seed: int, outliers: bool):
+    """Operands of the error-versus-K analysis, drawn in this order: A [M, K] like
+    activations (N(0, 1), with 0.1% of the entries x50 when `outliers`), B [N, K]
+    like weights (N(0, 0.02^2)), then the 16-bit Hadamard sign mask; both rounded
+    to bf16."""
+    rng = np.random.default_rng(seed)
+    a = normal(rng, (M, K), outlier_frac=0.001 if outliers else 0.0)
+    b = normal(rng, (N, K), std=0.02)
+    signs = int(rng.integers(0, 2**32, dtype=np.uint64)) & 0xFFFF
+    return to_bf16(a), to_bf16(b), signs
+
+
 def laplace(rng: np.random.Generator, shape, scale=1e-3) -> np.ndarray:
     return rng.laplace(0.0, scale, size=shape).astype(np.float32)
 
