@@ -166,6 +166,24 @@ __device__ __forceinline__ void sr_bits16(uint64_t i0, uint64_t seed, uint64_t o
   r[4] = b.v[0]; r[5] = b.v[1]; r[6] = b.v[2]; r[7] = b.v[3];
 }
 
+// Butterflies of the 16-point Hadamard transform (distances 1, 2, 4, 8), without
+// its factor 1/4: for a maximum of |v| the factor is applied once to the result,
+// which gives the same value (multiplying by 1/4 and rounding is monotone, so the
+// largest element stays the largest).
+__device__ __forceinline__ void hadamard16_unscaled(float v[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
 // In-place orthonormal Hadamard transform of a 16-vector whose random signs have
 // already been applied: butterflies at distances 1, 2, 4, 8, then a factor 1/4.
 __device__ __forceinline__ void hadamard16(float v[16]) {

@@ -195,11 +195,13 @@ __global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const T *__rest
     float v[16];
     load8(x + r * ld + c, v);
     load8(x + r * ld + c + 8, v + 8);
-    rht16(v, signs);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = ((signs >> j) & 1u) ? -v[j] : v[j];
+    hadamard16_unscaled(v);
 #pragma unroll
     for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
   }
-  block_max_to(m, out);
+  block_max_to(m * 0.25f, out);  // the transform's factor, once (see hadamard16_unscaled)
 }
 
 // amax after the Hadamard transform down columns (16 consecutive rows of x).
@@ -219,12 +221,12 @@ __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const T *__rest
       float col[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) col[r] = sl.at(r, j);
-      hadamard16(col);
+      hadamard16_unscaled(col);
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, __builtin_fabsf(col[r]));
     }
   }
-  block_max_to(m, out);
+  block_max_to(m * 0.25f, out);  // the transform's factor, once (see hadamard16_unscaled)
 }
 
 // One rowwise block: (optional transform,) block amax, scale, encode.  i0 is the
@@ -443,13 +445,13 @@ __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict
         col[r] = slab.at(r, j);
         mr = fmaxf(mr, __builtin_fabsf(col[r]));  // the signs do not change |x|
       }
-      if (RHT) hadamard16(col);
+      if (RHT) hadamard16_unscaled(col);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mc = fmaxf(mc, __builtin_fabsf(col[r]));
     }
   }
   block_max_to(mr, out_rows);
-  block_max_to(mc, out_cols);
+  block_max_to(RHT ? mc * 0.25f : mc, out_cols);  // the transform's factor, once (see hadamard16_unscaled)
 }
 
 // 2D (16x16 tile) nearest-even quantization of x [R][C] (R, C multiples of 16).
