@@ -31,7 +31,7 @@
 //   gemm_kernel       the main path (K a multiple of 256, aligned operands):
 //                     256x256 output tile, four waves of 128x128, K stages of 256
 //                     elements; global -> LDS by direct DMA loads
-//                     (global_load_lds_dwordx4) into a double buffer, one barrier
+//                     (global_load_lds_dwordx4) into a double buffer, two barriers
 //                     per stage.  Per wave and 16 K it dequantizes 8 operand tiles
 //                     (64 VALU ops) for 16 MFMAs, so the conversions fit under the
 //                     matrix-core time.
@@ -431,8 +431,6 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   // leave room for them), of the LDS reads and of the DMA loads; sched_barrier
   // keeps the compiler from regrouping slots.
   constexpr int NMF = TM * TN;
-  constexpr int kDmaPerSubstep = (NDMA + 3) / 4;
-  static_assert(kDmaPerSubstep <= NMF, "DMA loads fit the slots");
   // items [K * C, (K + 1) * C) of TOTAL, C = ceil(TOTAL / NMF), for slot K
   auto slot_items = [&](auto kc, auto total_c, auto &&f) {
     constexpr int K = decltype(kc)::value, TOTAL = decltype(total_c)::value;
@@ -445,19 +443,25 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   using HalfTiles = std::integral_constant<int, 2 * T>;
   using Tiles = std::integral_constant<int, T>;
 
-  // One stage, in buffer (kt + par) & 1.  Quarters 0..2 read the next quarter of
-  // this buffer during their first substep; quarter 3 waits for stage kt+1's DMA
-  // and for every read of this buffer, passes the barrier, reads stage kt+1's
-  // first quarter from the other buffer and spreads the DMA of stage kt_dma (of
-  // the tile whose offsets va/vb/vs hold) into this buffer over its substeps.
-  // The last stage has none of that.
   // after_epi: the previous tile's epilogue stores were issued after this tile's
   // second-stage DMA.  Vector memory operations retire in issue order on this
-  // chip, so waiting until no more than that many stores are outstanding waits
-  // for the DMA alone.  Without CLAMP every store is issued: per 32x32 block, 2
-  // (bf16) or 4 (fp32) per lane; with CLAMP some may be skipped, so everything
-  // is drained.
+  // chip, so a wait that leaves that many stores (plus any newer DMA) outstanding
+  // still waits for the second-stage DMA.  Without CLAMP every store is issued:
+  // per 32x32 block, 2 (bf16) or 4 (fp32) per lane; with CLAMP some may be
+  // skipped, so the stores are not counted.
   constexpr int kStoresBf16 = TM * TN * 2, kStoresF32 = TM * TN * 4;
+  // One stage, in buffer (kt + par) & 1.  Quarters 0..2 read the next quarter of
+  // this buffer during their first substep, so after quarter 2's first substep no
+  // wave reads this buffer again: there every wave passes a first barrier, and the
+  // DMA of stage kt_dma (of the tile whose offsets va/vb/vs hold) into this buffer
+  // is spread over the next four substeps.  At quarter 3 every wave waits for stage
+  // kt+1's DMA (issued one stage earlier) and passes a second barrier, then reads
+  // stage kt+1's first quarter from the other buffer.  The last stage has none of
+  // that.  The wait at quarter 3 lets the newer operations stay in flight: this
+  // stage's DMA issued so far and, after a tile change, the epilogue stores.
+  constexpr int kDmaPer = (NDMA + 3) / 4;
+  static_assert(kDmaPer <= NMF, "DMA loads fit the slots");
+  constexpr int kDmaBeforeB = (3 * kDmaPer < NDMA) ? 3 * kDmaPer : NDMA;  // issued before the second barrier
   auto stage = [&](int kt, auto last_tag, int par, int kt_dma, bool after_epi) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int buf = (kt + par) & 1;
@@ -465,21 +469,28 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       constexpr int q = decltype(qc)::value;
       constexpr int slot = q & 1;
       constexpr bool next_q = q < 3 || !LAST;  // is there a quarter after this one?
-      if constexpr (q == 3 && !LAST) {
-        if (!CLAMP && after_epi && p.c_bf16)
-          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStoresBf16) : "memory");
-        else if (!CLAMP && after_epi)
-          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStoresF32 < 63 ? kStoresF32 : 63) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        __syncthreads();
-      }
       static_for<4>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
-        constexpr int cur = s & 1;  // 4 substeps per quarter: the parity runs on across quarters and stages
-        // the substep whose operands are built now
+        constexpr int cur = s & 1;
+        if constexpr (q == 2 && s == 1 && !LAST) {
+          // every wave has read all of this buffer (quarter 3 was read at quarter 2, substep 0)
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __syncthreads();
+        }
+        if constexpr (q == 3 && s == 0 && !LAST) {
+          // stage kt+1's DMA has landed: the newer operations (this stage's DMA issued so
+          // far, and the previous tile's epilogue stores) may stay in flight
+          if (!CLAMP && after_epi && p.c_bf16)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStoresBf16 + kDmaBeforeB < 63 ? kStoresBf16 + kDmaBeforeB : 63) : "memory");
+          else if (!CLAMP && after_epi)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStoresF32 + kDmaBeforeB < 63 ? kStoresF32 + kDmaBeforeB : 63) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kDmaBeforeB) : "memory");
+          __syncthreads();
+        }
         constexpr bool has_next = s < 3 || next_q;
         constexpr int nslot = s < 3 ? slot : slot ^ 1, ns = s < 3 ? s + 1 : 0;
+        constexpr int dslot = (q == 2 && s >= 1) ? s - 1 : (q == 3 && s == 0) ? 3 : -1;
         static_for<NMF>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
           constexpr int i = k / TN, j = k % TN;
@@ -498,8 +509,8 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
               constexpr int x = decltype(tc)::value;
               scd[slot ^ 1][x] = scales2(scw[slot ^ 1][x]);
             });
-          if constexpr (q == 3 && !LAST && k < kDmaPerSubstep && s * kDmaPerSubstep + k < NDMA)
-            dma(kt_dma, buf, s * kDmaPerSubstep + k);
+          if constexpr (!LAST && dslot >= 0 && k < kDmaPer && dslot * kDmaPer + k < NDMA)
+            dma(kt_dma, buf, dslot * kDmaPer + k);
           __builtin_amdgcn_sched_barrier(0);
         });
       });
