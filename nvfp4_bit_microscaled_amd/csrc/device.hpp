@@ -80,6 +80,30 @@ __device__ __forceinline__ void block_scale(float amax_b, float s_enc, const flo
   mult = tab[code];
 }
 
+// Block scale and multiplier of a 16-block transformed without the Hadamard
+// factor 1/4 (u = 4 v, see hadamard16_unscaled).  The block amax RN(max|u| / 4) is
+// the maximum of the rounded v (rounding is monotone).  When max|u| >= 2^-90 and
+// the multiplier is at least 2^-120, RN(u * (mult / 4)) equals RN(RN(u / 4) * mult)
+// for every element: mult / 4 is exact; u / 4 is exact unless |u| < 2^-124, and
+// such an element scales below 2^-30 either way (the multiplier is at most 12 over
+// the block amax), which encodes to zero under nearest-even and under stochastic
+// rounding with 16 random bits.  So the factor joins the multiplier, one product
+// per element fewer.  Otherwise (tiny blocks) the factor is applied to the
+// elements first, the arithmetic as defined.
+__device__ __forceinline__ void block_scale_quarter(float u[16], float s_enc, const float *tab, uint32_t &code,
+                                                    float &mult) {
+  float amax_u = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) amax_u = fmaxf(amax_u, __builtin_fabsf(u[j]));
+  block_scale(amax_u * 0.25f, s_enc, tab, code, mult);
+  if (__builtin_expect(amax_u >= 0x1p-90f && mult >= 0x1p-120f, 1)) {
+    mult *= 0.25f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) u[j] *= 0.25f;
+  }
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Canonical zero: clear the sign bit of every code whose magnitude is 0 (the
@@ -182,32 +206,6 @@ __device__ __forceinline__ void hadamard16_unscaled(float v[16]) {
       }
     }
   }
-}
-
-// In-place orthonormal Hadamard transform of a 16-vector whose random signs have
-// already been applied: butterflies at distances 1, 2, 4, 8, then a factor 1/4.
-__device__ __forceinline__ void hadamard16(float v[16]) {
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if ((i & h) == 0) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] *= 0.25f;
-}
-
-// In-place orthonormal random Hadamard transform of a 16-vector: element j is
-// negated when bit j of the sign mask is set, then transformed.
-__device__ __forceinline__ void rht16(float v[16], uint32_t signs) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = ((signs >> j) & 1u) ? -v[j] : v[j];
-  hadamard16(v);
 }
 
 // Scale a 16-block by its multiplier (one binary32 product per element) and

