@@ -10,8 +10,11 @@ call includes its amax pass.  Inputs are seeded synthetic tensors
 Prints one JSON line.  `value` is whole-step NVFP4 linear TFLOP/s (3 GEMMs of
 2*M*N*K flops each, divided by the step time including every quantization);
 `roofline` is that of the dominant kernel (the block-scaled GEMM, timed with HIP
-events on its launch stream); `cpu_baseline` is the oracle timed on host cores
-on a bounded sample of the same workload, extrapolated to the step.
+events on its launch stream); `quantize.kernels` times each quantizer kernel on
+its own after the timed steps (input read from HBM, amax passes separate), with
+its algorithmic bytes and its bound (HBM, or the vector ALU for the stochastic
+encoders); `cpu_baseline` is the oracle timed on host cores on a bounded sample
+of the same workload, extrapolated to the step.
 """
 import argparse
 import hashlib
@@ -37,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mlp_up_12b", choices=["mlp_up_12b", "fprop_8k", "wgrad_8k", "block_3b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel quantize breakdown (profiler runs that look at the steps only)")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
     ap.add_argument("--error-vs-k", action="store_true",
                     help="instead of the benchmark: relative error of the NVFP4 GEMM against the unquantized binary64 "
@@ -267,6 +272,9 @@ def main():
         "frac_of_fp4_dense_peak": round(gemm_tflops / PEAK_FP4_MFMA_TFLOPS, 4),
     }
 
+    breakdown = [] if args.no_breakdown else quantize_breakdown(layers, wl)
+    hbm_rows = [r for r in breakdown if r["bound"] == "hbm"]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers, wl, args.cpu_sample_rows, step_flops)
@@ -299,6 +307,10 @@ def main():
             "frac": round(quant_gbs / PEAK_HBM_GBS, 4),
             "note": "algorithmic bytes (input read once + codes + scales of every layout written) per quantize call; the time includes the amax pass",
             "ms_per_step": round(quant_ms / args.steps, 4),
+            "kernels": breakdown,
+            "hbm_bound_kernels_frac": round(sum(r["bytes"] for r in hbm_rows) / (sum(r["us"] for r in hbm_rows)
+                                                                                 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+            if hbm_rows else None,
         },
         "gemm_ms_per_step": round(gemm_ms / args.steps, 4),
         "roofline": roofline,
@@ -306,6 +318,83 @@ def main():
         "input_generation_s": round(t_gen, 1),
     }
     print(json.dumps(out), flush=True)
+
+
+def quantize_breakdown(layers, wl, reps=5):
+    """Each quantizer kernel of the step on its own: the layout kernels through
+    their entry points with the amax given (the step's own amax is in place), the
+    amax passes as fp4_amax (contiguous W) or as the difference between a dual call
+    with and without its amax pass.  A 512 MiB read runs before every timed call,
+    so each call reads its input from HBM, not from the 256 MB Infinity Cache.
+    Rates are algorithmic bytes (input read once, this kernel's outputs written
+    once) over the median of `reps` calls."""
+    import torch
+
+    import nvfp4_bit_microscaled_amd as Q
+    import workloads
+
+    stream = torch.cuda.current_stream()
+    flush = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def med_ms(fn):
+        ts = []
+        for _ in range(reps):
+            torch.sum(flush, dim=0, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    G = Q.Q_AMAX_GIVEN
+    one_d = 0.5 + 1 / 16
+    rows = []
+
+    def add(name, kernel, nbytes, ms, bound):
+        rows.append({"call": name, "kernel": kernel, "us": round(ms * 1e3, 1), "bytes": int(nbytes),
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9
+                                                                                    / PEAK_HBM_GBS, 3),
+                     "bound": bound})
+
+    for lin, inp, x, w, dy, b, o in layers:
+        M, N, K = lin.M, lin.N, lin.K
+        in_b = x.element_size()
+        sd, od, ow = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
+        fprop, dgrad, wgrad = ("fprop" in wl.passes), ("dgrad" in wl.passes), ("wgrad" in wl.passes)
+        if fprop and wgrad:
+            full = med_ms(lambda: Q.fp4_quantize_dual(x, Q.Q_RHT, inp.signs, 0, 0, 0, b.xq, b.xq_t))
+            given = med_ms(lambda: Q.fp4_quantize_dual(x, Q.Q_RHT | G, inp.signs, 0, 0, 0, b.xq, b.xq_t))
+            add(f"{lin.name} X dual amax (plain + transformed; dual call minus the same call with amax given)",
+                "amax_dual_kernel", M * K * in_b, full - given, "hbm")
+        if fprop:
+            add(f"{lin.name} X rowwise nearest-even", "quant_rows_flat_kernel", M * K * (in_b + one_d),
+                med_ms(lambda: Q.fp4_quantize(x, G, 0, 0, 0, b.xq)), "hbm")
+        if wgrad:
+            add(f"{lin.name} X^T columnwise transformed nearest-even", "quant_cols_kernel", M * K * (in_b + one_d),
+                med_ms(lambda: Q.fp4_quantize(x, Q.Q_COLWISE | Q.Q_RHT | G, inp.signs, 0, 0, b.xq_t)), "hbm")
+        if fprop or dgrad:
+            add(f"{lin.name} W amax", "amax_flat_kernel", N * K * in_b,
+                med_ms(lambda: Q.fp4_amax(w, 0, 0, b.wq.amax)), "hbm")
+            add(f"{lin.name} W 2D + W^T nearest-even", "quant_2d_kernel", N * K * (in_b + 2 * (0.5 + 1 / 256)),
+                med_ms(lambda: Q.fp4_quantize(w, Q.Q_2D | G, 0, 0, 0, b.wq, b.wq_t)), "hbm")
+        if dgrad and wgrad:
+            full = med_ms(lambda: Q.fp4_quantize_dual(dy, Q.Q_SR | Q.Q_RHT, inp.signs, sd, od, ow, b.dyq, b.dyq_t))
+            given = med_ms(lambda: Q.fp4_quantize_dual(dy, Q.Q_SR | Q.Q_RHT | G, inp.signs, sd, od, ow, b.dyq,
+                                                       b.dyq_t))
+            add(f"{lin.name} dY dual amax (plain + transformed; dual call minus the same call with amax given)",
+                "amax_dual_kernel", M * N * in_b, full - given, "hbm")
+        if dgrad:
+            add(f"{lin.name} dY rowwise stochastic", "quant_rows_flat_kernel", M * N * (in_b + one_d),
+                med_ms(lambda: Q.fp4_quantize(dy, Q.Q_SR | G, 0, sd, od, b.dyq)), "valu")
+        if wgrad:
+            add(f"{lin.name} dY^T columnwise transformed stochastic", "quant_cols_kernel", M * N * (in_b + one_d),
+                med_ms(lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR | G, inp.signs, sd, ow, b.dyq_t)),
+                "valu")
+    del flush
+    return rows
 
 
 def cpu_baseline(layers, wl, sample_rows, step_flops):
