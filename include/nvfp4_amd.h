@@ -106,7 +106,9 @@ FP4_API fp4_status fp4_amax(const void *x, fp4_dtype dtype, int64_t rows, int64_
 
 /* Quantize the logical tensor L of x (L = x, or x^T with FP4_Q_COLWISE) into *out
  * (out->rows x out->cols must equal L's shape; out->two_d must match FP4_Q_2D).
- * Without FP4_Q_AMAX_GIVEN the tensor amax is computed first into out->amax.
+ * Without FP4_Q_AMAX_GIVEN the tensor amax is computed first into out->amax (the
+ * amax pass keeps its per-workgroup maxima in out->codes, at most 8 KB, before the
+ * codes are written; x must not overlap out->codes, as for any output).
  * out_t (FP4_Q_2D only, nullable) also receives L^T quantized with the same tile
  * scales: its codes and scales are the exact transposes of out's.
  * Modes: 1D with any of COLWISE, RHT, SR; 2D with COLWISE only (no RHT, no SR).
@@ -129,7 +131,8 @@ FP4_API fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, in
  * flags: FP4_Q_SR (both layouts stochastic), FP4_Q_RHT (columnwise layout
  * transformed), FP4_Q_AMAX_GIVEN (out_rows->amax and out_cols->amax already hold the
  * two tensor amaxes; otherwise both are computed first, in one read of x, then each
- * layout is written by its own kernel).
+ * layout is written by its own kernel; the amax pass keeps its per-workgroup
+ * maxima in out_rows->codes before the codes are written).
  * Needs: rows and cols multiples of 16; x 16-byte aligned, ld a multiple of 8. */
 FP4_API fp4_status fp4_quantize_dual(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
                                      uint32_t flags, uint32_t rht_signs, uint64_t seed, uint64_t offset_rows,

@@ -20,8 +20,11 @@
 //              are regrouped through LDS.
 // Elements are encoded by gfx950's FP4 converters (nearest-even, or stochastic
 // with 16 Philox bits per element), see device.hpp.
-// The tensor amax is a separate reduction pass (atomicMax on the bit pattern of
-// the non-negative float), zeroed by a one-thread kernel: no memset node.
+// The tensor amax is a separate reduction pass.  Each workgroup's maximum goes to
+// the codes buffer of the tensor being quantized and a one-workgroup kernel
+// reduces them (fp4_amax alone, or a tensor under 8 KB of codes: an atomicMax on
+// the bit pattern of the non-negative float into an output zeroed by a one-thread
+// kernel).  No memset node either way.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -122,8 +125,12 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Block-wide max, then one atomic per workgroup.
-__device__ __forceinline__ void block_max_to(float v, float *out) {
+// Block-wide max of non-negative values.  With `partial`, workgroup b stores it
+// at partial[b] (amax_finish_kernel reduces those); otherwise it is folded into
+// *out with one atomic (its bit pattern orders like the value).  The atomics of
+// all workgroups serialise on one cache line, about 10 ns each on the MI355X, so
+// the partial form is used wherever the caller's output gives room for it.
+__device__ __forceinline__ void block_max_to(float v, float *out, float *partial) {
   __shared__ float part[kThreads / 64];
   v = wave_max(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -133,7 +140,27 @@ __device__ __forceinline__ void block_max_to(float v, float *out) {
     float m = part[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, part[i]);
-    atomicMax(reinterpret_cast<unsigned int *>(out), __float_as_uint(m));
+    if (partial) partial[blockIdx.x] = m;
+    else atomicMax(reinterpret_cast<unsigned int *>(out), __float_as_uint(m));
+  }
+  __syncthreads();  // part[] is reused by a second reduction in the same kernel
+}
+
+// out[t] = max of partial[t * n .. t * n + n) for t < nout (one workgroup).
+__global__ __launch_bounds__(kThreads) void amax_finish_kernel(const float *__restrict__ partial, int n, int nout,
+                                                               float *out0, float *out1) {
+  __shared__ float part[kThreads / 64];
+  for (int t = 0; t < nout; ++t) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, partial[t * n + i]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, part[i]);
+      *(t == 0 ? out0 : out1) = m;
+    }
+    __syncthreads();
   }
 }
 
@@ -146,7 +173,7 @@ __global__ void zero2_f32_kernel(float *p, float *q) {
 // Plain |x| max over [R][C] (row stride ld); 8 elements per thread-step.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_plain_kernel(const T *__restrict__ x, int64_t R, int64_t C,
-                                                             int64_t ld, float *out) {
+                                                             int64_t ld, float *out, float *partial) {
   const int64_t chunks_per_row = C / 8;
   const int64_t total = R * chunks_per_row;
   float m = 0.0f;
@@ -157,12 +184,13 @@ __global__ __launch_bounds__(kThreads) void amax_plain_kernel(const T *__restric
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
   }
-  block_max_to(m, out);
+  block_max_to(m, out, partial);
 }
 
 // Plain |x| max of a contiguous tensor: four 16-byte loads in flight per thread.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict__ x, int64_t nchunks, float *out) {
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict__ x, int64_t nchunks, float *out,
+                                                            float *partial) {
   float m = 0.0f;
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nchunks; i += 4 * stride) {
@@ -180,13 +208,14 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf(v[u][e]));
   }
-  block_max_to(m, out);
+  block_max_to(m, out, partial);
 }
 
 // amax after the Hadamard transform along rows (16 contiguous elements).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const T *__restrict__ x, int64_t R, int64_t C,
-                                                                int64_t ld, uint32_t signs, float *out) {
+                                                                int64_t ld, uint32_t signs, float *out,
+                                                                float *partial) {
   const int64_t nkb = C / 16;
   const int64_t total = R * nkb;
   float m = 0.0f;
@@ -201,14 +230,15 @@ __global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const T *__rest
 #pragma unroll
     for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
   }
-  block_max_to(m * 0.25f, out);  // the transform's factor, once (see hadamard16_unscaled)
+  block_max_to(m * 0.25f, out, partial);  // the transform's factor, once (see hadamard16_unscaled)
 }
 
 // amax after the Hadamard transform down columns (16 consecutive rows of x).
 // A thread owns 8 adjacent columns of one 16-row slab.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const T *__restrict__ x, int64_t R, int64_t C,
-                                                                int64_t ld, uint32_t signs, float *out) {
+                                                                int64_t ld, uint32_t signs, float *out,
+                                                                float *partial) {
   const int64_t cchunks = C / 8, slabs = R / 16;
   const int64_t total = cchunks * slabs;
   float m = 0.0f;
@@ -226,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const T *__rest
       for (int r = 0; r < 16; ++r) m = fmaxf(m, __builtin_fabsf(col[r]));
     }
   }
-  block_max_to(m * 0.25f, out);  // the transform's factor, once (see hadamard16_unscaled)
+  block_max_to(m * 0.25f, out, partial);  // the transform's factor, once (see hadamard16_unscaled)
 }
 
 // One rowwise block: (optional transform,) block amax, scale, encode.  i0 is the
@@ -439,7 +469,8 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restric
 // adjacent columns of one slab.
 template <typename T, bool RHT>
 __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict__ x, int64_t R, int64_t C, int64_t ld,
-                                                            uint32_t signs, float *out_rows, float *out_cols) {
+                                                            uint32_t signs, float *out_rows, float *out_cols,
+                                                            float *partial) {
   const int64_t cchunks = C / 8, slabs = R / 16;
   const int64_t total = cchunks * slabs;
   float mr = 0.0f, mc = 0.0f;
@@ -460,8 +491,10 @@ __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict
       for (int r = 0; r < 16; ++r) mc = fmaxf(mc, __builtin_fabsf(col[r]));
     }
   }
-  block_max_to(mr, out_rows);
-  block_max_to(RHT ? mc * 0.25f : mc, out_cols);  // the transform's factor, once (see hadamard16_unscaled)
+  // partials: rows at [0, grid), columns at [grid, 2 grid)
+  block_max_to(mr, out_rows, partial);
+  block_max_to(RHT ? mc * 0.25f : mc, out_cols, partial ? partial + gridDim.x : nullptr);  // the transform's
+                                                                                            // factor, once
 }
 
 // 2D (16x16 tile) nearest-even quantization of x [R][C] (R, C multiples of 16).
@@ -595,27 +628,45 @@ unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
   return unsigned(g);
 }
 
+// Partial maxima need one float per workgroup (two for the dual amax).  They are
+// stored in the codes buffer of the tensor the call is about to quantize, which
+// the encoding kernels overwrite afterwards (stream order keeps the reduction
+// before them); a codes buffer smaller than this takes the atomic form instead.
+constexpr size_t kPartialBytes = 2 * 1024 * sizeof(float);
+
+float *partial_room(const fp4_tensor *t) {
+  if (!t || !t->codes) return nullptr;
+  const size_t bytes = size_t(t->rows) * size_t(t->cols / 2);
+  return bytes >= kPartialBytes ? reinterpret_cast<float *>(t->codes) : nullptr;
+}
+
+// Tensor amax into *out.  With `partial` (room for 1024 floats), every workgroup
+// stores its maximum there and amax_finish_kernel reduces them; without it, *out
+// is zeroed and every workgroup folds its maximum in with an atomic.
 template <typename T>
 hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, float *out,
-                     hipStream_t stream) {
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, out);
-  const int64_t cap = 256 * 16;  // 16 workgroups per CU are plenty for a streaming reduction
+                     float *partial, hipStream_t stream) {
+  if (R == 0 || C == 0 || !partial) hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, out);
   if (R == 0 || C == 0) return hipGetLastError();
+  const int64_t cap = partial ? 1024 : 256 * 16;  // 16 workgroups per CU are plenty for a streaming reduction
+  dim3 grid;
   if (!(flags & FP4_Q_RHT) && ld == C) {
-    // four workgroups per CU: on the MI355X a 200 MB read-only stream took 45 us with
-    // 1024 workgroups, 54 us with 512 and 68 us with 4096 (one atomic per workgroup)
-    hipLaunchKernelGGL(amax_flat_kernel<T>, dim3(grid_for(R * (C / 8), kThreads * 4, 1024)), dim3(kThreads), 0,
-                       stream, x, R * (C / 8), out);
+    // four workgroups per CU: on the MI355X a 200 MB read-only stream took 37 us with
+    // 1024 workgroups, 52 us with 512 (kernel time without the atomics)
+    grid = dim3(grid_for(R * (C / 8), kThreads * 4, 1024));
+    hipLaunchKernelGGL(amax_flat_kernel<T>, grid, dim3(kThreads), 0, stream, x, R * (C / 8), out, partial);
   } else if (!(flags & FP4_Q_RHT)) {
-    hipLaunchKernelGGL(amax_plain_kernel<T>, dim3(grid_for(R * (C / 8), kThreads * 4, cap)), dim3(kThreads), 0,
-                       stream, x, R, C, ld, out);
+    grid = dim3(grid_for(R * (C / 8), kThreads * 4, cap));
+    hipLaunchKernelGGL(amax_plain_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, out, partial);
   } else if (flags & FP4_Q_COLWISE) {
-    hipLaunchKernelGGL(amax_rht_cols_kernel<T>, dim3(grid_for((R / 16) * (C / 8), kThreads, cap)), dim3(kThreads),
-                       0, stream, x, R, C, ld, signs, out);
+    grid = dim3(grid_for((R / 16) * (C / 8), kThreads, cap));
+    hipLaunchKernelGGL(amax_rht_cols_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, out, partial);
   } else {
-    hipLaunchKernelGGL(amax_rht_rows_kernel<T>, dim3(grid_for(R * (C / 16), kThreads * 2, cap)), dim3(kThreads),
-                       0, stream, x, R, C, ld, signs, out);
+    grid = dim3(grid_for(R * (C / 16), kThreads * 2, cap));
+    hipLaunchKernelGGL(amax_rht_rows_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, out, partial);
   }
+  if (partial)
+    hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kThreads), 0, stream, partial, int(grid.x), 1, out, out);
   return hipGetLastError();
 }
 
@@ -648,7 +699,7 @@ template <typename T>
 hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, uint64_t seed,
                          uint64_t offset, const fp4_tensor *out, const fp4_tensor *out_t, hipStream_t stream) {
   if (!(flags & FP4_Q_AMAX_GIVEN)) {
-    hipError_t e = amax_impl(x, R, C, ld, flags, signs, out->amax, stream);
+    hipError_t e = amax_impl(x, R, C, ld, flags, signs, out->amax, partial_room(out), stream);
     if (e != hipSuccess) return e;
   }
   if (R == 0 || C == 0) return hipGetLastError();
@@ -692,16 +743,21 @@ hipError_t dual_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
                      hipStream_t stream) {
   const bool rht = flags & FP4_Q_RHT, sr = flags & FP4_Q_SR;
   if (!(flags & FP4_Q_AMAX_GIVEN)) {
-    hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(1), 0, stream, rows->amax, cols->amax);
+    float *partial = partial_room(rows);  // the rowwise codes (as many bytes as the columnwise ones)
+    if (R == 0 || C == 0 || !partial)
+      hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(1), 0, stream, rows->amax, cols->amax);
     if (R > 0 && C > 0) {
       // two workgroups per CU: on the MI355X this read 640 MB in 114 us and 160 MB in
       // 38 us, against 116 us and 45 us with four
       const dim3 grid(grid_for((R / 16) * (C / 8), kThreads, 512));
       if (rht)
         hipLaunchKernelGGL((amax_dual_kernel<T, true>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
-                           rows->amax, cols->amax);
+                           rows->amax, cols->amax, partial);
       else
         hipLaunchKernelGGL((amax_dual_kernel<T, false>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
+                           rows->amax, cols->amax, partial);
+      if (partial)
+        hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kThreads), 0, stream, partial, int(grid.x), 2,
                            rows->amax, cols->amax);
     }
   }
@@ -731,8 +787,8 @@ __global__ void copy_f32_kernel(const float *src, float *dst) { *dst = *src; }
 hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                        uint32_t signs, float *out, hipStream_t stream) {
   if (dtype == FP4_BF16)
-    return amax_impl(static_cast<const uint16_t *>(x), R, C, ld, flags, signs, out, stream);
-  return amax_impl(static_cast<const float *>(x), R, C, ld, flags, signs, out, stream);
+    return amax_impl(static_cast<const uint16_t *>(x), R, C, ld, flags, signs, out, nullptr, stream);
+  return amax_impl(static_cast<const float *>(x), R, C, ld, flags, signs, out, nullptr, stream);
 }
 
 hipError_t launch_quantize(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
