@@ -212,3 +212,58 @@ def test_quantize_dual_matches_two_single_quantizations(fp4, oracle, case, dtype
     fp4.fp4_quantize_dual(dev(xt), flags | fp4.Q_AMAX_GIVEN, signs, seed, o_r, o_c, qr2, qc2)
     assert_q_equal(host_q(qr2), ora_r, f"dual rows, amax given {case}")
     assert_q_equal(host_q(qc2), ora_c, f"dual cols, amax given {case}")
+
+
+STRIDED_MODES = {
+    "rows_rne": 0, "rows_sr": "SR", "rows_rht_sr": "RHT|SR", "cols_rne": "COLWISE", "cols_rht_sr": "COLWISE|RHT|SR",
+    "two_d": "2D", "two_d_colwise": "2D|COLWISE",
+}
+
+
+@pytest.mark.parametrize("mode", list(STRIDED_MODES))
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_strided_input(fp4, oracle, mode, dtype):
+    """x is a view of a wider matrix (row stride ld = cols + 40): the strided amax
+    and encoding kernels against the oracle on the same values."""
+    spec = STRIDED_MODES[mode]
+    flags = 0
+    for name in (spec.split("|") if spec else []):
+        flags |= {"SR": fp4.Q_SR, "RHT": fp4.Q_RHT, "COLWISE": fp4.Q_COLWISE, "2D": fp4.Q_2D}[name]
+    R, C = 272, 528
+    wide = make_x((R, C + 40), seed=R + C, kind="laplace", std=1e-3, dtype=dtype)
+    x = wide.to("cuda")[:, :C]
+    assert x.stride(0) == C + 40
+    colwise, two_d = bool(flags & fp4.Q_COLWISE), bool(flags & fp4.Q_2D)
+    lrows, lcols = (C, R) if colwise else (R, C)
+    q = fp4.QTensor(lrows, lcols, two_d)
+    q_t = fp4.QTensor(lcols, lrows, True) if two_d else None
+    fp4.fp4_quantize(x, flags, 0x6A95, 5, 9, q, q_t)
+    xf = workloads.widen(wide)[:, :C]
+    ora = oracle.quantize(xf, two_d=two_d, colwise=colwise, rht=bool(flags & fp4.Q_RHT), sr=bool(flags & fp4.Q_SR),
+                          signs=0x6A95, seed=5, offset=9)
+    assert_q_equal(host_q(q), ora, f"strided {mode}")
+    if q_t is not None:
+        assert_q_equal(host_q(q_t), oracle.quantize(xf, two_d=True, colwise=not colwise), f"strided {mode} (T)")
+    # both layouts at once from the same strided view
+    if mode == "rows_rne":
+        qr, qc = fp4.QTensor(R, C), fp4.QTensor(C, R)
+        fp4.fp4_quantize_dual(x, fp4.Q_SR | fp4.Q_RHT, 0x6A95, 5, 9, 10, qr, qc)
+        assert_q_equal(host_q(qr), oracle.quantize(xf, sr=True, seed=5, offset=9), "strided dual rows")
+        assert_q_equal(host_q(qc), oracle.quantize(xf, colwise=True, rht=True, sr=True, signs=0x6A95, seed=5,
+                                                   offset=10), "strided dual cols")
+
+
+@pytest.mark.parametrize("shape", [(32, 512), (16, 496), (64, 256), (48, 320)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_amax_pass_both_forms(fp4, oracle, shape):
+    """Tensors on both sides of 8 KB of codes: the amax pass keeps per-workgroup
+    maxima in the codes buffer (reduced by one workgroup) at and above it, and
+    folds them in with atomics below it.  Both give the oracle's amax and codes."""
+    R, C = shape
+    x_cpu = make_x(shape, seed=R * C, kind="outliers")
+    for flags in (0, fp4.Q_RHT | fp4.Q_SR, fp4.Q_COLWISE | fp4.Q_RHT):
+        run_case(fp4, oracle, x_cpu, flags, signs=0x1F2E, seed=3, offset=8)
+    qr, qc = fp4.QTensor(R, C), fp4.QTensor(C, R)
+    fp4.fp4_quantize_dual(dev(x_cpu), fp4.Q_RHT, 0x1F2E, 0, 0, 0, qr, qc)
+    xf = workloads.widen(x_cpu)
+    assert_q_equal(host_q(qr), oracle.quantize(xf), f"dual rows {shape}")
+    assert_q_equal(host_q(qc), oracle.quantize(xf, colwise=True, rht=True, signs=0x1F2E), f"dual cols {shape}")
