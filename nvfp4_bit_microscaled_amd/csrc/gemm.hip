@@ -534,7 +534,10 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   bool first = true;  // no epilogue stores in flight yet
   issue(0, 0);
   issue(min(1, nst - 1), 1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the first stage's DMA has landed; the second stage's NDMA loads (issued last,
+  // vector memory operations retire in order) stay in flight until quarter 3's wait
+  if (nst >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (;;) {
     // stage 0 of this tile is in buffer par and visible to every wave
