@@ -182,6 +182,20 @@ def main():
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
+    # one workspace for the GEMMs' split-K partial tiles, as large as the largest plan
+    # of the workload needs (the plans take no split for most shapes: then it is unused)
+    gemm_shapes = []
+    for lin in wl.linears:
+        if "fprop" in wl.passes:
+            gemm_shapes.append((lin.M, lin.N, lin.K))
+        if "dgrad" in wl.passes:
+            gemm_shapes.append((lin.M, lin.K, lin.N))
+        if "wgrad" in wl.passes:
+            gemm_shapes.append((lin.N, lin.K, lin.M))
+    ws_need = max(fp4.fp4_gemm_ws_bytes(*sh) for sh in gemm_shapes)
+    ws = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=dev)
+    split_shapes = [sh for sh in gemm_shapes if fp4.fp4_gemm_ws_bytes(*sh) > 0]
+
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     Q = fp4
@@ -218,7 +232,7 @@ def main():
                 timed("quant", N * K * (in_b + 2 * (0.5 + 1 / 256)), lambda: Q.fp4_quantize(w, Q.Q_2D, 0, 0, 0, b.wq,
                                                                                            b.wq_t))
             if fprop:
-                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm(b.xq, b.wq, o["y"]))
+                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm_ws(b.xq, b.wq, o["y"], ws))
             # dY: rowwise SR (dgrad) and/or transformed columnwise SR (wgrad)
             sd, od, ow = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
             if dgrad and wgrad:
@@ -230,9 +244,9 @@ def main():
                 timed("quant", M * N * (in_b + one_d),
                       lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR, inp.signs, sd, ow, b.dyq_t))
             if dgrad:
-                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm(b.dyq, b.wq_t, o["dx"]))
+                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm_ws(b.dyq, b.wq_t, o["dx"], ws))
             if wgrad:
-                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm(b.dyq_t, b.xq_t, o["dw"]))
+                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm_ws(b.dyq_t, b.xq_t, o["dw"], ws))
 
     for _ in range(args.warmup):
         step([])
@@ -264,9 +278,12 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4),
         "traffic": traffic,
-        "kernel": "nvfp4 block-scaled GEMM (f16 MFMA on exactly dequantized E2M1xE4M3 operands); one fp4_gemm call "
-                  "per pass: a persistent 256x256-tile launch, plus a 128x128-quarters launch when the tiles overrun "
-                  "whole rounds of the CUs (wgrad here)",
+        "kernel": "nvfp4 block-scaled GEMM (f16 MFMA on exactly dequantized E2M1xE4M3 operands); one fp4_gemm_ws "
+                  "call per pass: a persistent 256x256-tile launch, plus a 128x128-quarters launch when the tiles "
+                  "overrun whole rounds of the CUs by at most half a round, or split over K into a caller workspace "
+                  "and summed by a second launch when the plan for the shape takes a split",
+        "split_k_shapes": split_shapes,
+        "workspace_bytes": ws_need,
         "flops_per_call": gemm_flops / n_gemm,
         "avg_call_ms": round(gemm_ms / n_gemm, 4),
         "frac_of_fp4_dense_peak": round(gemm_tflops / PEAK_FP4_MFMA_TFLOPS, 4),

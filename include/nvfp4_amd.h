@@ -147,6 +147,23 @@ FP4_API fp4_status fp4_quantize_dual(const void *x, fp4_dtype dtype, int64_t row
 FP4_API fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                     hipStream_t stream);
 
+/* fp4_gemm with a caller workspace for split-K.  When a product has few 256x256
+ * output tiles for the CUs and a long K (a weight-gradient GEMM over many tokens
+ * with a small weight), each tile's K range is split into S parts that run as
+ * separate work items writing raw fp32 partial tiles into ws, and a second kernel
+ * sums the S partials of each tile in split order, applies the decode scales and
+ * writes C.  Same definition and tolerance as fp4_gemm (the split adds S-1 fp32
+ * additions per output).  S comes from a fixed plan of (M, N, K) on this GPU;
+ * fp4_gemm_ws_bytes gives the workspace the plan needs (0 when it takes no split).
+ * With ws_bytes below that, or a shape off the 256-K main path, this is fp4_gemm.
+ * ws: device memory, 16-byte aligned, owned by the caller, overwritten; calls that
+ * share a workspace must be ordered on one stream. */
+FP4_API fp4_status fp4_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes fp4_gemm_ws uses for an M x N x K product (0: no split). */
+FP4_API fp4_status fp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes);
+
 /* Linear layer y = x . w^T with x [M][K], w [N][K] (dtype), y [M][N] (y_dtype).
  * Forward: x 1D nearest-even into xq ([M][K]); w 2D (16x16) nearest-even into wq
  * ([N][K]); wq_t (nullable, [K][N]) receives w^T with the same tile scales, for the

@@ -26,8 +26,9 @@ STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_ALIGN"
           5: "FP4_ERR_MODE", 6: "FP4_ERR_MISMATCH", 7: "FP4_ERR_HIP"}
 
 # every symbol the header declares
-EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_gemm", "fp4_linear_fprop",
-           "fp4_linear_dgrad", "fp4_linear_wgrad", "fp4_linear_backward", "fp4_status_string")
+EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_gemm", "fp4_gemm_ws",
+           "fp4_gemm_ws_bytes", "fp4_linear_fprop", "fp4_linear_dgrad", "fp4_linear_wgrad", "fp4_linear_backward",
+           "fp4_status_string")
 
 
 class Fp4Error(RuntimeError):
@@ -62,6 +63,8 @@ def load():
         "fp4_quantize": [vp, i32, i64, i64, i64, u32, u32, u64, u64, tp, tp, vp],
         "fp4_quantize_dual": [vp, i32, i64, i64, i64, u32, u32, u64, u64, u64, tp, tp, vp],
         "fp4_gemm": [tp, tp, vp, i32, i64, vp],
+        "fp4_gemm_ws": [tp, tp, vp, i32, i64, vp, ctypes.c_size_t, vp],
+        "fp4_gemm_ws_bytes": [i64, i64, i64, sz],
         "fp4_linear_fprop": [vp, vp, i32, vp, i32, i64, i64, i64, tp, tp, tp, vp],
         "fp4_linear_dgrad": [vp, i32, tp, vp, i32, i64, i64, i64, u64, u64, tp, vp],
         "fp4_linear_wgrad": [vp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, tp, tp, vp],
@@ -155,6 +158,20 @@ def fp4_quantize_dual(x: torch.Tensor, flags: int, rht_signs: int, seed: int, of
 
 def fp4_gemm(a: QTensor, b: QTensor, c: torch.Tensor, stream=None):
     _check("fp4_gemm", load().fp4_gemm(a.desc, b.desc, c.data_ptr(), _dtype(c), c.stride(0), _stream(stream)))
+
+
+def fp4_gemm_ws_bytes(M: int, N: int, K: int) -> int:
+    n = ctypes.c_size_t()
+    _check("fp4_gemm_ws_bytes", load().fp4_gemm_ws_bytes(M, N, K, ctypes.byref(n)))
+    return n.value
+
+
+def fp4_gemm_ws(a: QTensor, b: QTensor, c: torch.Tensor, ws: torch.Tensor = None, stream=None):
+    """ws: a device byte tensor (at least fp4_gemm_ws_bytes(M, N, K) bytes for the split)."""
+    wp = ws.data_ptr() if ws is not None else None
+    wb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("fp4_gemm_ws", load().fp4_gemm_ws(a.desc, b.desc, c.data_ptr(), _dtype(c), c.stride(0), wp, wb,
+                                             _stream(stream)))
 
 
 def fp4_linear_fprop(x, w, y, xq: QTensor, wq: QTensor, wq_t: QTensor = None, stream=None):

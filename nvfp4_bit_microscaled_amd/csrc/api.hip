@@ -121,6 +121,21 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype
   return from_hip(nvfp4::launch_gemm(a, b, c, c_dtype, ldc, stream));
 }
 
+fp4_status fp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes) {
+  if (!bytes) return FP4_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return FP4_ERR_SHAPE;
+  *bytes = nvfp4::gemm_ws_bytes(M, N, K);
+  return FP4_OK;
+}
+
+fp4_status fp4_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc, void *ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  fp4_status s = check_gemm(a, b, c, c_dtype, ldc);
+  if (s != FP4_OK) return s;
+  if (ws_bytes > 0 && (!ws || !aligned(ws, 16))) return ws ? FP4_ERR_ALIGN : FP4_ERR_NULL;
+  return from_hip(nvfp4::launch_gemm_ws(a, b, c, c_dtype, ldc, ws, ws_bytes, stream));
+}
+
 fp4_status fp4_linear_fprop(const void *x, const void *w, fp4_dtype dtype, void *y, fp4_dtype y_dtype, int64_t M,
                             int64_t N, int64_t K, const fp4_tensor *xq, const fp4_tensor *wq,
                             const fp4_tensor *wq_t, hipStream_t stream) {

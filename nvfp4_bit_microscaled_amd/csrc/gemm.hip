@@ -73,6 +73,8 @@ struct GemmParams {
   int c_bf16;
   int tiles_main;  // gemm_kernel, 256x256: tiles [0, tiles_main) of the grouped order
   int tail_first;  // gemm_kernel, quarters: the quarters of 256x256 tiles tail_first .. last
+  int ksplit;      // gemm_kernel, 256x256: K splits per tile (1: none)
+  float *ws;       // ksplit > 1: raw partial tiles [tiles_main][256][256], item t * ksplit + s
 };
 
 // 8 E2M1 codes (one 32-bit word, element 2j in the low nibble of byte j) times the
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int64_t M = p.M, N = p.N;
   const uint32_t kbytes = uint32_t(p.K / 2), nkb = uint32_t(p.K / 16);
-  const int nst = int(p.K / 256);
+  const int nst = int(p.K / 256) / (QUARTERS ? 1 : p.ksplit);  // K stages of one work item
 
   // Persistent tiles.  The grid has at most one workgroup per CU; with a grid that
   // is a multiple of 8 and smaller than the tile count, workgroup w runs on XCD
@@ -328,6 +330,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   const u32x4 rssa = make_rsrc(p.a_scales, uint32_t((M + (1 << p.a_shift) - 1) >> p.a_shift) * nkb);
   const u32x4 rssb = make_rsrc(p.b_scales, uint32_t((N + (1 << p.b_shift) - 1) >> p.b_shift) * nkb);
   uint32_t va[CLAMP ? JA : 1], vb[CLAMP ? JB : 1], vs[NSC];
+  int ks0 = 0;  // first K stage of the current item's split (0 without splits)
   // tile coordinates of sequence position l (groups of 8 tile-rows) and its DMA offsets
   auto set_tile = [&](int l) {
     int tm, tn;
@@ -337,18 +340,22 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       n0 = int64_t(tn) * 256 + BN * (l & 1);
     } else {
       static_assert(QUARTERS || (BM == 256 && BN == 256), "tile grid of 256x256");
-      tile_at(l, num_m, num_n, tm, tn);
+      // work item l: K split l % ksplit of tile l / ksplit, its first stage ks0
+      const int t = l / p.ksplit;
+      ks0 = (l - t * p.ksplit) * nst;
+      tile_at(t, num_m, num_n, tm, tn);
       m0 = int64_t(tm) * BM;
       n0 = int64_t(tn) * BN;
     }
+    const uint32_t kc = uint32_t(ks0) * kRow, ksb = uint32_t(ks0) * kSc;  // the split's first K byte
 #pragma unroll
-    for (int j = 0; j < (CLAMP ? JA : 1); ++j) va[j] = uint32_t(m0 + row0 + NW * 8 * j) * kbytes + lchunk;
+    for (int j = 0; j < (CLAMP ? JA : 1); ++j) va[j] = uint32_t(m0 + row0 + NW * 8 * j) * kbytes + lchunk + kc;
 #pragma unroll
-    for (int j = 0; j < (CLAMP ? JB : 1); ++j) vb[j] = uint32_t(n0 + row0 + NW * 8 * j) * kbytes + lchunk;
+    for (int j = 0; j < (CLAMP ? JB : 1); ++j) vb[j] = uint32_t(n0 + row0 + NW * 8 * j) * kbytes + lchunk + kc;
 #pragma unroll
     for (int j = 0; j < NSC; ++j) {
       const int u = (j * NW + wave) * 64 + lane;
-      vs[j] = u < BM ? uint32_t((m0 + u) >> p.a_shift) * nkb : uint32_t((n0 + (u - BM)) >> p.b_shift) * nkb;
+      vs[j] = (u < BM ? uint32_t((m0 + u) >> p.a_shift) * nkb : uint32_t((n0 + (u - BM)) >> p.b_shift) * nkb) + ksb;
     }
   };
 
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
         if constexpr (q == 3 && s == 0 && !LAST) {
           // stage kt+1's DMA has landed: the newer operations (this stage's DMA issued so
           // far, and the previous tile's epilogue stores) may stay in flight
-          if (!CLAMP && after_epi && p.c_bf16)
+          if (!CLAMP && after_epi && p.c_bf16 && p.ksplit == 1)  // split partials are stored as fp32
             asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStoresBf16 + kDmaBeforeB < 63 ? kStoresBf16 + kDmaBeforeB : 63) : "memory");
           else if (!CLAMP && after_epi)
             asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStoresF32 + kDmaBeforeB < 63 ? kStoresF32 + kDmaBeforeB : 63) : "memory");
@@ -542,6 +549,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   for (;;) {
     // stage 0 of this tile is in buffer par and visible to every wave
     const int64_t mc = m0, nc = n0;
+    const int Lcur = L;
     const int Lnext = L + Lstride;
     const bool more = Lnext < Lend;
     // quarter 0 of stage 0 and the operands of its first substep
@@ -577,7 +585,16 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
         issue(0, par_next);
       }
     }
-    store_tiles_lds<TM, TN, CLAMP>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes, gscale);
+    if (!QUARTERS && p.ksplit > 1) {
+      // raw partial tile (no decode scales) into the item's 256x256 slot of the workspace
+      GemmParams pp = p;
+      pp.c = p.ws + int64_t(Lcur) * (256 * 256);
+      pp.ldc = 256;
+      pp.c_bf16 = 0;
+      store_tiles_lds<TM, TN, false>(pp, acc, wm, wn, lane, lds + 2 * STAGE + wave * kEpiBytes, 1.0f);
+    } else {
+      store_tiles_lds<TM, TN, CLAMP>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes, gscale);
+    }
     if (!more) break;
     if (nst == 1) {
       // a one-stage tile's first stage was only just issued
@@ -745,15 +762,88 @@ unsigned compute_units() {
   return cached[dev];
 }
 
+// Split-K reduction: C tile t = (sum over s of partial tile t * ksplit + s, in split
+// order) times the two tensor decode scales, converted and stored.  Workgroup b
+// covers 16 rows of tile b / 16; each thread four groups of 4 columns.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
+  const int num_m = int((p.M + 255) / 256), num_n = int((p.N + 255) / 256);
+  const int t = blockIdx.x >> 4, r0 = (blockIdx.x & 15) * 16;
+  int tm, tn;
+  tile_at(t, num_m, num_n, tm, tn);
+  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
+  const float *part = p.ws + int64_t(t) * p.ksplit * (256 * 256);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int f = threadIdx.x + 256 * i;  // float4 index within the 16 x 256 block
+    const int r = r0 + (f >> 6), c = (f & 63) * 4;
+    const int64_t m = int64_t(tm) * 256 + r, n = int64_t(tn) * 256 + c;
+    float4 v = *reinterpret_cast<const float4 *>(part + r * 256 + c);
+    for (int sp = 1; sp < p.ksplit; ++sp) {
+      const float4 w = *reinterpret_cast<const float4 *>(part + int64_t(sp) * (256 * 256) + r * 256 + c);
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    if (m >= p.M || n >= p.N) continue;  // N % 4 == 0: a group of 4 columns is inside or outside
+    if (p.c_bf16) {
+      const bf16x4 h = {(__bf16)(v.x * gscale), (__bf16)(v.y * gscale), (__bf16)(v.z * gscale),
+                        (__bf16)(v.w * gscale)};
+      *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = h;
+    } else {
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
+          make_float4(v.x * gscale, v.y * gscale, v.z * gscale, v.w * gscale);
+    }
+  }
+}
+
 template <int BM, int BN>
 unsigned tiles_for(const GemmParams &p) {
   return unsigned(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
 }
 
-}  // namespace
 
-hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
-                       hipStream_t stream) {
+// Split-K plan of the main path for an M x N x K product on `cus` CUs: the split
+// count S (1 = none) with the least estimated time, in units of one 256-K stage of
+// one 256x256 tile on one CU (about 5.7 us on the MI355X).  Without splits a tile
+// takes K/256 stages and the tiles run in rounds of `cus`, a short last round as
+// quarters at about 60% of the main kernel's rate; with S splits every tile is S
+// items of K/(256 S) stages (at least 4), plus the partial tiles' traffic: S written
+// and read again, and the output written, at about 4 TB/s.  A split is taken only
+// when it saves at least 5%.
+int splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus) {
+  if (K < 256 || K % 256 != 0) return 1;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256), z = K / 256;
+  const int64_t full = tiles / cus, rest = tiles % cus;
+  double base = double(full * z);
+  if (rest > 0) {
+    if (full > 0 && rest <= int64_t(cus) / 2)
+      base += double((4 * rest + cus - 1) / cus) * (double(z) / 4.0) / 0.6;
+    else
+      base += double(z);
+  }
+  const double stage_s = 5.7e-6, bw = 4.0e12, tile_bytes = 256.0 * 256.0 * 4.0;
+  int best = 1;
+  double best_cost = base;
+  for (int sp = 2; sp <= 16; sp *= 2) {
+    if (z % sp != 0 || z / sp < 4) continue;
+    const double rounds = double((tiles * sp + cus - 1) / cus);
+    const double cost = rounds * double(z / sp) + double(tiles) * tile_bytes * (2 * sp + 1) / bw / stage_s;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best_cost < 0.95 * base ? best : 1;
+}
+
+size_t splitk_ws_bytes(int64_t M, int64_t N, int64_t K, int ksplit) {
+  if (ksplit <= 1) return 0;
+  return size_t(((M + 255) / 256) * ((N + 255) / 256)) * size_t(ksplit) * 256 * 256 * sizeof(float);
+}
+
+hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
+                            void *ws, size_t ws_bytes, hipStream_t stream) {
   GemmParams p;
   p.a_codes = a->codes;
   p.a_scales = a->scales;
@@ -771,6 +861,8 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
   p.c_bf16 = c_dtype == FP4_BF16;
   p.tiles_main = 0;
   p.tail_first = -1;
+  p.ksplit = 1;
+  p.ws = nullptr;
   if (p.M == 0 || p.N == 0) return hipSuccess;
   auto al = [](const void *q, uintptr_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
   // main path: whole 256-element K stages, 16-byte aligned codes and scale rows,
@@ -780,6 +872,26 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
                          al(a->scales, 16) && al(b->scales, 16) && (p.M + 256) * (p.K / 2) < (int64_t(1) << 32) &&
                          (p.N + 256) * (p.K / 2) < (int64_t(1) << 32) &&
                          al(c, 16) && ldc % (p.c_bf16 ? 8 : 4) == 0 && p.N % 4 == 0;
+  if (main_path && ws) {
+    const unsigned cus = compute_units();
+    const int sp = splitk_plan(p.M, p.N, p.K, cus);
+    if (sp > 1 && ws_bytes >= splitk_ws_bytes(p.M, p.N, p.K, sp) && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
+      // every work item is a whole 256x256 tile over K / sp: partial tiles into ws,
+      // then one reduction launch writes C
+      const unsigned tiles = tiles_for<256, 256>(p);
+      p.ksplit = sp;
+      p.ws = static_cast<float *>(ws);
+      p.tiles_main = int(tiles) * sp;
+      const unsigned items = tiles * unsigned(sp);
+      const dim3 grid(items < cus ? items : cus);
+      if (p.M % 256 == 0 && p.N % 256 == 0)
+        hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false, false>), grid, dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true, false>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(tiles * 16), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   if (main_path) {
     // persistent: one workgroup per CU (its 160 KB of LDS admit no second one).
     // When the tiles overrun whole rounds of the CUs by at most half a round,
@@ -808,6 +920,23 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
     hipLaunchKernelGGL(gemm_edge_kernel, dim3(tiles_for<128, 128>(p)), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
+                       hipStream_t stream) {
+  return launch_gemm_impl(a, b, c, c_dtype, ldc, nullptr, 0, stream);
+}
+
+hipError_t launch_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc, void *ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return launch_gemm_impl(a, b, c, c_dtype, ldc, ws, ws_bytes, stream);
+}
+
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0) return 0;
+  return splitk_ws_bytes(M, N, K, splitk_plan(M, N, K, compute_units()));
 }
 
 }  // namespace nvfp4

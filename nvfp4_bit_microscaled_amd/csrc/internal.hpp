@@ -23,4 +23,11 @@ hipError_t launch_quantize_dual(const void *x, fp4_dtype dtype, int64_t R, int64
 hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                        hipStream_t stream);
 
+// launch_gemm with a caller workspace for split-K partial tiles (used only when the
+// split plan for the shape wants one and ws holds gemm_ws_bytes of the shape)
+hipError_t launch_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+
 }  // namespace nvfp4

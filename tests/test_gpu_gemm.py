@@ -144,3 +144,39 @@ def test_ldc_larger_than_n(fp4, oracle):
     assert np.all(y[:, 60:] == -1.0)
     y_ref, bound = oracle.gemm_ref(qa, qb)
     check_gemm(y[:, :60], y_ref, bound, False, "ldc")
+
+
+SPLITK_CASES = [
+    # (M, N, K, a2d, b2d, expected split): few tiles, long K
+    (512, 512, 8192, False, True, 8),      # 4 tiles, 8 splits of 1024
+    (300, 200, 4096, False, False, 4),     # ragged edges (rows/columns past M, N), 2 tiles
+    (1024, 256, 16384, True, False, 16),   # 4 tiles, 16 splits of 1024, 2D-scaled A
+    (256, 256, 256, False, False, 1),      # no split: the plain path
+]
+
+
+@pytest.mark.parametrize("case", SPLITK_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"_S{c[5]}")
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_gemm_split_k(fp4, oracle, case, out_dtype):
+    """fp4_gemm_ws: the split plan for the shape, partial tiles in the caller's
+    workspace, their sum against the oracle within the GEMM tolerance; run twice
+    on one workspace (the second call overwrites the first's partials), and once
+    with too small a workspace (the unsplit path)."""
+    M, N, K, a2d, b2d, want_split = case
+    need = fp4.fp4_gemm_ws_bytes(M, N, K)
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    assert need == (0 if want_split == 1 else tiles * want_split * 256 * 256 * 4), need
+    qa, qb = oracle_operands(oracle, M, N, K, seed=M + N + K, a2d=a2d, b2d=b2d, a_kind="laplace")
+    a, b = upload_q(fp4, qa), upload_q(fp4, qb)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")
+    y_ref, bound = oracle.gemm_ref(qa, qb)
+    for rep in range(2):
+        c = torch.full((M, N), float("nan"), dtype=out_dtype, device="cuda")
+        fp4.fp4_gemm_ws(a, b, c, ws)
+        torch.cuda.synchronize()
+        check_gemm(c.float().cpu().numpy(), y_ref, bound, out_dtype == torch.bfloat16, f"split-K {case} rep {rep}")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=out_dtype, device="cuda")
+    fp4.fp4_gemm_ws(a, b, c, small)
+    torch.cuda.synchronize()
+    check_gemm(c.float().cpu().numpy(), y_ref, bound, out_dtype == torch.bfloat16, f"small workspace {case}")

@@ -216,7 +216,14 @@ def test_block_3b_sampled(fp4, oracle):
         oxt = check_rows(oracle, xf, host_q(bufs.xq_t), kcols, colwise=True, rht=True, signs=inp.signs)
         y_ref, bound = oracle.gemm_ref(odt, oxt)
         check_gemm(dw.cpu().numpy()[np.ix_(nrows, kcols)], y_ref, bound, False, f"{lin.name} wgrad")
-        del y, dx, dw, bufs
+        # wgrad as the benchmark runs it: fp4_gemm_ws, split over K where the plan says so
+        # (O: 144 tiles of 256x256 over K = 32768, 8 splits; up and down: 2)
+        ws = torch.empty(max(fp4.fp4_gemm_ws_bytes(N, K, M), 16), dtype=torch.uint8, device="cuda")
+        dw2 = torch.empty(N, K, dtype=torch.float32, device="cuda")
+        fp4.fp4_gemm_ws(bufs.dyq_t, bufs.xq_t, dw2, ws)
+        torch.cuda.synchronize()
+        check_gemm(dw2.cpu().numpy()[np.ix_(nrows, kcols)], y_ref, bound, False, f"{lin.name} wgrad, fp4_gemm_ws")
+        del y, dx, dw, dw2, ws, bufs
 
 
 @pytest.mark.parametrize("quantize_x", [True, False], ids=["x_given", "xq_t_from_forward"])
