@@ -74,6 +74,7 @@ struct GemmParams {
   int tiles_main;  // gemm_kernel, 256x256: tiles [0, tiles_main) of the grouped order
   int tail_first;  // gemm_kernel, quarters: the quarters of 256x256 tiles tail_first .. last
   int ksplit;      // gemm_kernel, 256x256: K splits per tile (1: none)
+  int split_first; // ksplit > 1: the first split tile (the tiles before it run unsplit)
   float *ws;       // ksplit > 1: raw partial tiles [tiles_main][256][256], item t * ksplit + s
 };
 
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       // work item l: K split l % ksplit of tile l / ksplit, its first stage ks0
       const int t = l / p.ksplit;
       ks0 = (l - t * p.ksplit) * nst;
-      tile_at(t, num_m, num_n, tm, tn);
+      tile_at(p.split_first + t, num_m, num_n, tm, tn);
       m0 = int64_t(tm) * BM;
       n0 = int64_t(tn) * BN;
     }
@@ -762,14 +763,15 @@ unsigned compute_units() {
   return cached[dev];
 }
 
-// Split-K reduction: C tile t = (sum over s of partial tile t * ksplit + s, in split
-// order) times the two tensor decode scales, converted and stored.  Workgroup b
+// Split-K reduction: C tile split_first + t = (sum over s of partial tile
+// t * ksplit + s, in split order) times the two tensor decode scales, converted and
+// stored.  Workgroup b
 // covers 16 rows of tile b / 16; each thread four groups of 4 columns.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
   const int num_m = int((p.M + 255) / 256), num_n = int((p.N + 255) / 256);
-  const int t = blockIdx.x >> 4, r0 = (blockIdx.x & 15) * 16;
+  const int t = blockIdx.x >> 4, r0 = (blockIdx.x & 15) * 16;  // t: the t-th split tile
   int tm, tn;
-  tile_at(t, num_m, num_n, tm, tn);
+  tile_at(p.split_first + t, num_m, num_n, tm, tn);
   const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
   const float *part = p.ws + int64_t(t) * p.ksplit * (256 * 256);
 #pragma unroll
@@ -803,43 +805,60 @@ unsigned tiles_for(const GemmParams &p) {
 }
 
 
-// Split-K plan of the main path for an M x N x K product on `cus` CUs: the split
-// count S (1 = none) with the least estimated time, in units of one 256-K stage of
-// one 256x256 tile on one CU (about 5.7 us on the MI355X).  Without splits a tile
-// takes K/256 stages and the tiles run in rounds of `cus`, a short last round as
-// quarters at about 60% of the main kernel's rate; with S splits every tile is S
-// items of K/(256 S) stages (at least 4), plus the partial tiles' traffic: S written
-// and read again, and the output written, at about 4 TB/s.  A split is taken only
-// when it saves at least 5%.
-int splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus) {
-  if (K < 256 || K % 256 != 0) return 1;
+// Split-K plan of the main path for an M x N x K product on `cus` CUs, in units of
+// one 256-K stage of one 256x256 tile on one CU (about 5.7 us on the MI355X).
+// Without splits a tile takes Z = K/256 stages and the tiles run in rounds of
+// `cus`; a last round at most half full runs as 128x128 quarters, at about 60% of
+// the main kernel's rate.  A split runs a tile as S work items of Z/S stages (at
+// least 4), plus the partial tiles' traffic (S written and read again, the output
+// written, at about 4 TB/s).  Two splits are weighed: of every tile (few tiles, long
+// K), or of the last round's tiles only, after the whole rounds (in place of the
+// quarters).  A split is taken when it saves at least 5% of the time it replaces.
+struct SplitPlan {
+  int ksplit = 1;     // S (1: no split)
+  int64_t first = 0;  // first split tile, in the grouped tile order
+  int64_t tiles = 0;  // split tiles
+};
+
+SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus) {
+  SplitPlan none;
+  if (K < 256 || K % 256 != 0 || M <= 0 || N <= 0) return none;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256), z = K / 256;
   const int64_t full = tiles / cus, rest = tiles % cus;
-  double base = double(full * z);
-  if (rest > 0) {
-    if (full > 0 && rest <= int64_t(cus) / 2)
-      base += double((4 * rest + cus - 1) / cus) * (double(z) / 4.0) / 0.6;
-    else
-      base += double(z);
-  }
+  const bool quarters = full > 0 && rest > 0 && rest <= int64_t(cus) / 2;
+  const double tail = rest == 0 ? 0.0 : quarters ? double((4 * rest + cus - 1) / cus) * (double(z) / 4.0) / 0.6
+                                                 : double(z);
+  const double base = double(full * z) + tail;
   const double stage_s = 5.7e-6, bw = 4.0e12, tile_bytes = 256.0 * 256.0 * 4.0;
-  int best = 1;
+  auto split_cost = [&](int64_t n, int sp) {
+    return double((n * sp + cus - 1) / cus) * double(z / sp) + double(n) * tile_bytes * (2 * sp + 1) / bw / stage_s;
+  };
+  SplitPlan best;
   double best_cost = base;
   for (int sp = 2; sp <= 16; sp *= 2) {
     if (z % sp != 0 || z / sp < 4) continue;
-    const double rounds = double((tiles * sp + cus - 1) / cus);
-    const double cost = rounds * double(z / sp) + double(tiles) * tile_bytes * (2 * sp + 1) / bw / stage_s;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = sp;
+    const double whole = split_cost(tiles, sp);
+    if (whole < 0.95 * base && whole < best_cost) {
+      best_cost = whole;
+      best.ksplit = sp;
+      best.first = 0;
+      best.tiles = tiles;
+    }
+    if (full > 0 && rest > 0) {
+      const double t = split_cost(rest, sp);
+      if (t < 0.95 * tail && double(full * z) + t < best_cost) {
+        best_cost = double(full * z) + t;
+        best.ksplit = sp;
+        best.first = full * cus;
+        best.tiles = rest;
+      }
     }
   }
-  return best_cost < 0.95 * base ? best : 1;
+  return best;
 }
 
-size_t splitk_ws_bytes(int64_t M, int64_t N, int64_t K, int ksplit) {
-  if (ksplit <= 1) return 0;
-  return size_t(((M + 255) / 256) * ((N + 255) / 256)) * size_t(ksplit) * 256 * 256 * sizeof(float);
+size_t splitk_ws_bytes(const SplitPlan &sp) {
+  return sp.ksplit <= 1 ? 0 : size_t(sp.tiles) * size_t(sp.ksplit) * 256 * 256 * sizeof(float);
 }
 
 hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
@@ -862,6 +881,7 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
   p.tiles_main = 0;
   p.tail_first = -1;
   p.ksplit = 1;
+  p.split_first = 0;
   p.ws = nullptr;
   if (p.M == 0 || p.N == 0) return hipSuccess;
   auto al = [](const void *q, uintptr_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
@@ -874,21 +894,29 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
                          al(c, 16) && ldc % (p.c_bf16 ? 8 : 4) == 0 && p.N % 4 == 0;
   if (main_path && ws) {
     const unsigned cus = compute_units();
-    const int sp = splitk_plan(p.M, p.N, p.K, cus);
-    if (sp > 1 && ws_bytes >= splitk_ws_bytes(p.M, p.N, p.K, sp) && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
-      // every work item is a whole 256x256 tile over K / sp: partial tiles into ws,
-      // then one reduction launch writes C
-      const unsigned tiles = tiles_for<256, 256>(p);
-      p.ksplit = sp;
+    const SplitPlan sp = splitk_plan(p.M, p.N, p.K, cus);
+    if (sp.ksplit > 1 && ws_bytes >= splitk_ws_bytes(sp) && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
+      // whole tiles before the split ones (if any) in the usual persistent launch; then
+      // every split tile as ksplit work items of K / ksplit writing partial tiles into
+      // ws, and one reduction launch writing their part of C
+      const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
+      auto launch = [&](const GemmParams &q, unsigned items) {
+        const dim3 grid(items < cus ? items : cus);
+        if (exact)
+          hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false, false>), grid, dim3(256), 0, stream, q);
+        else
+          hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true, false>), grid, dim3(256), 0, stream, q);
+      };
+      if (sp.first > 0) {
+        p.tiles_main = int(sp.first);
+        launch(p, unsigned(sp.first));
+      }
+      p.ksplit = sp.ksplit;
+      p.split_first = int(sp.first);
       p.ws = static_cast<float *>(ws);
-      p.tiles_main = int(tiles) * sp;
-      const unsigned items = tiles * unsigned(sp);
-      const dim3 grid(items < cus ? items : cus);
-      if (p.M % 256 == 0 && p.N % 256 == 0)
-        hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false, false>), grid, dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true, false>), grid, dim3(256), 0, stream, p);
-      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(tiles * 16), dim3(256), 0, stream, p);
+      p.tiles_main = int(sp.tiles) * sp.ksplit;
+      launch(p, unsigned(p.tiles_main));
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned(sp.tiles) * 16), dim3(256), 0, stream, p);
       return hipGetLastError();
     }
   }
@@ -935,8 +963,7 @@ hipError_t launch_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4
 }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0) return 0;
-  return splitk_ws_bytes(M, N, K, splitk_plan(M, N, K, compute_units()));
+  return splitk_ws_bytes(splitk_plan(M, N, K, compute_units()));
 }
 
 }  // namespace nvfp4

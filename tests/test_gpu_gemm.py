@@ -147,25 +147,27 @@ def test_ldc_larger_than_n(fp4, oracle):
 
 
 SPLITK_CASES = [
-    # (M, N, K, a2d, b2d, expected split): few tiles, long K
-    (512, 512, 8192, False, True, 8),      # 4 tiles, 8 splits of 1024
-    (300, 200, 4096, False, False, 4),     # ragged edges (rows/columns past M, N), 2 tiles
-    (1024, 256, 16384, True, False, 16),   # 4 tiles, 16 splits of 1024, 2D-scaled A
-    (256, 256, 256, False, False, 1),      # no split: the plain path
+    # (M, N, K, a2d, b2d, split tiles, splits): every tile split (few tiles, long K), or
+    # only the tiles past the whole rounds of a 256-CU GPU (in place of quarters)
+    (512, 512, 8192, False, True, 4, 8),      # 4 tiles, 8 splits of 1024
+    (300, 200, 4096, False, False, 2, 4),     # ragged edges (rows/columns past M, N), 2 tiles
+    (1024, 256, 16384, True, False, 4, 16),   # 4 tiles, 16 splits of 1024, 2D-scaled A
+    (4352, 4096, 4096, False, True, 16, 4),   # 272 tiles: 256 whole, the last 16 split in 4
+    (4100, 4100, 8192, False, False, 33, 4),  # 289 tiles, ragged: the last 33 split in 4
+    (256, 256, 256, False, False, 0, 1),      # no split: the plain path
 ]
 
 
-@pytest.mark.parametrize("case", SPLITK_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"_S{c[5]}")
+@pytest.mark.parametrize("case", SPLITK_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"_{c[5]}x{c[6]}")
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
 def test_gemm_split_k(fp4, oracle, case, out_dtype):
     """fp4_gemm_ws: the split plan for the shape, partial tiles in the caller's
     workspace, their sum against the oracle within the GEMM tolerance; run twice
     on one workspace (the second call overwrites the first's partials), and once
     with too small a workspace (the unsplit path)."""
-    M, N, K, a2d, b2d, want_split = case
+    M, N, K, a2d, b2d, split_tiles, splits = case
     need = fp4.fp4_gemm_ws_bytes(M, N, K)
-    tiles = ((M + 255) // 256) * ((N + 255) // 256)
-    assert need == (0 if want_split == 1 else tiles * want_split * 256 * 256 * 4), need
+    assert need == split_tiles * splits * 256 * 256 * 4, need
     qa, qb = oracle_operands(oracle, M, N, K, seed=M + N + K, a2d=a2d, b2d=b2d, a_kind="laplace")
     a, b = upload_q(fp4, qa), upload_q(fp4, qb)
     ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")

@@ -141,8 +141,13 @@ def test_mlp_up_12b_sampled(fp4, oracle):
     fp4.fp4_gemm(bufs.xq, bufs.wq, y)
     fp4.fp4_linear_backward(dy, None, bufs.wq_t, dx, dw, inp.signs, workloads.SR_SEED, workloads.SR_OFFSET_DGRAD,
                             workloads.SR_OFFSET_WGRAD, bufs.dyq, bufs.dyq_t, bufs.xq_t)
+    # the wgrad GEMM as the benchmark runs it: fp4_gemm_ws, whose plan splits the last
+    # 64 of its 1600 tiles (dW rows 18432.., columns 3072..) over K instead of quarters
+    ws = torch.empty(max(fp4.fp4_gemm_ws_bytes(N, K, M), 16), dtype=torch.uint8, device="cuda")
+    dw2 = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    fp4.fp4_gemm_ws(bufs.dyq_t, bufs.xq_t, dw2, ws)
     torch.cuda.synchronize()
-    del x, w, dy
+    del x, w, dy, ws
     xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
     sr, off_d, off_w = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
 
@@ -163,14 +168,16 @@ def test_mlp_up_12b_sampled(fp4, oracle):
     check_gemm(dx.float().cpu().numpy()[rows], y_ref, bound, True, "dgrad 12B")
     del owtq, dx
 
-    # wgrad: sampled rows of dY^T (RHT+SR); X^T (RHT) in full; sampled dW rows
-    wrows = sample_rows(N, 16, 4)
+    # wgrad: sampled rows of dY^T (RHT+SR), some in the last tile-rows; X^T (RHT) in
+    # full; sampled dW rows, from fp4_linear_backward and from fp4_gemm_ws
+    wrows = np.union1d(sample_rows(N, 16, 4), sample_rows(N - 18432, 8, 5) + 18432)
     odt = check_rows(oracle, dyf, host_q(bufs.dyq_t), wrows, colwise=True, rht=True, sr=True, signs=inp.signs,
                      seed=sr, offset=off_w)
     oxtq = oracle.quantize(xf, colwise=True, rht=True, signs=inp.signs)
     assert_q_equal(host_q(bufs.xq_t), oxtq, "xq_t")
     y_ref, bound = oracle.gemm_ref(odt, oxtq)
     check_gemm(dw.cpu().numpy()[wrows], y_ref, bound, False, "wgrad 12B")
+    check_gemm(dw2.cpu().numpy()[wrows], y_ref, bound, False, "wgrad 12B, fp4_gemm_ws")
 
 
 def test_block_3b_sampled(fp4, oracle):
