@@ -466,16 +466,22 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   constexpr int kStoresBf16 = TM * TN * 2, kStoresF32 = TM * TN * 4;
   // One stage, in buffer (kt + par) & 1.  Quarters 0..2 read the next quarter of
   // this buffer during their first substep, so after quarter 2's first substep no
-  // wave reads this buffer again: there every wave passes a first barrier, and the
-  // DMA of stage kt_dma (of the tile whose offsets va/vb/vs hold) into this buffer
-  // is spread over the next four substeps.  At quarter 3 every wave waits for stage
-  // kt+1's DMA (issued one stage earlier) and passes a second barrier, then reads
-  // stage kt+1's first quarter from the other buffer.  The last stage has none of
-  // that.  The wait at quarter 3 lets the newer operations stay in flight: this
-  // stage's DMA issued so far and, after a tile change, the epilogue stores.
+  // wave reads this buffer again.  A first barrier opens quarter 2's last substep
+  // (by then a wave's reads have long landed, so its wait for them costs nothing;
+  // at the second substep it waited for the read just issued: measured 1% slower
+  // per GEMM), and the DMA of stage kt_dma (of the tile whose offsets va/vb/vs hold)
+  // into this buffer is spread over that substep and quarter 3's first three.  At
+  // quarter 3 every wave waits for stage kt+1's DMA (issued one stage earlier) and
+  // passes a second barrier, then reads stage kt+1's first quarter from the other
+  // buffer.  The last stage has none of that.  The wait at quarter 3 lets the newer
+  // operations stay in flight: this stage's DMA issued so far and, after a tile
+  // change, the epilogue stores.  (One barrier, at quarter 3 only, measured 0.8%
+  // slower.)
   constexpr int kDmaPer = (NDMA + 3) / 4;
   static_assert(kDmaPer <= NMF, "DMA loads fit the slots");
-  constexpr int kDmaBeforeB = (3 * kDmaPer < NDMA) ? 3 * kDmaPer : NDMA;  // issued before the second barrier
+  constexpr int kBarrierSub = 3;  // quarter 2's substep that opens with the first barrier
+  // DMA loads of this stage issued before the second barrier
+  constexpr int kDmaBeforeB = ((4 - kBarrierSub) * kDmaPer < NDMA) ? (4 - kBarrierSub) * kDmaPer : NDMA;
   auto stage = [&](int kt, auto last_tag, int par, int kt_dma, bool after_epi) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int buf = (kt + par) & 1;
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       static_for<4>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         constexpr int cur = s & 1;
-        if constexpr (q == 2 && s == 1 && !LAST) {
+        if constexpr (q == 2 && s == kBarrierSub && !LAST) {
           // every wave has read all of this buffer (quarter 3 was read at quarter 2, substep 0)
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           __syncthreads();
@@ -504,7 +510,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
         }
         constexpr bool has_next = s < 3 || next_q;
         constexpr int nslot = s < 3 ? slot : slot ^ 1, ns = s < 3 ? s + 1 : 0;
-        constexpr int dslot = (q == 2 && s >= 1) ? s - 1 : (q == 3 && s == 0) ? 3 : -1;
+        constexpr int dslot = (q == 2 && s >= kBarrierSub) ? s - kBarrierSub : (q == 3 && s < kBarrierSub) ? s + 4 - kBarrierSub : -1;
         static_for<NMF>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
           constexpr int i = k / TN, j = k % TN;
