@@ -104,6 +104,36 @@ def test_gemm_rejects_bad_arguments(lib):
     assert lib.fp4_gemm(None, Q(b), c, 1, 32, None) == 1
 
 
+def test_gemm_ws_rejects_bad_arguments(lib):
+    c = ctypes.c_void_p(0x1000)
+    Q = ctypes.byref
+    a, b = desc(64, 128), desc(32, 128)
+    assert lib.fp4_gemm_ws(Q(a), Q(desc(32, 96)), c, 1, 32, ctypes.c_void_p(0x2000), 4096, None) == 6
+    assert lib.fp4_gemm_ws(Q(a), Q(b), c, 1, 32, None, 4096, None) == 1  # bytes but no workspace
+    assert lib.fp4_gemm_ws(Q(a), Q(b), c, 1, 32, ctypes.c_void_p(0x2008), 4096, None) == 3  # misaligned
+
+
+def test_gemm_ws_bytes_follows_the_split_plan(lib):
+    """The split plan on a 256-CU GPU (the host query falls back to 256 without a
+    device): which products split, and the workspace = split tiles x splits x 256 KB."""
+    n = ctypes.c_size_t()
+    tile = 256 * 256 * 4
+
+    def need(M, N, K):
+        assert lib.fp4_gemm_ws_bytes(M, N, K, ctypes.byref(n)) == 0
+        return n.value
+    assert need(3072, 3072, 32768) == 144 * 8 * tile    # 144 tiles, every one in 8
+    assert need(8192, 3072, 32768) == 128 * 2 * tile    # 384 tiles: the last 128 in 2
+    assert need(9216, 3072, 32768) == 176 * 4 * tile    # 432 tiles: the last 176 in 4
+    assert need(20480, 5120, 16384) == 64 * 4 * tile    # 1600 tiles: the last 64 in 4
+    assert need(16384, 20480, 5120) == 0                # 20 whole rounds
+    assert need(8192, 4096, 4096) == 0                  # 2 whole rounds
+    assert need(256, 256, 256) == 0                     # one stage: nothing to split
+    assert need(300, 200, 4096) == 2 * 4 * tile         # ragged, 2 tiles in 4
+    assert lib.fp4_gemm_ws_bytes(64, 64, 40, ctypes.byref(n)) == 2  # K not a multiple of 16
+    assert lib.fp4_gemm_ws_bytes(64, 64, 64, None) == 1
+
+
 def test_linear_rejects_bad_arguments(lib):
     Q = ctypes.byref
     x, w, y = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
