@@ -352,7 +352,7 @@ def quantize_breakdown(layers, wl, reps=5):
 
     stream = torch.cuda.current_stream()
     flush = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
-    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def med_ms(fn):
         ts = []
