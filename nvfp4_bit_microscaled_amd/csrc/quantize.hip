@@ -402,12 +402,23 @@ __device__ __forceinline__ void store_col_tile(const uint8_t *lcodes, const uint
     }
   }
 }
-template <typename T, bool RHT, bool SR>
-__global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restrict__ x, int64_t R, int64_t C,
-                                                             int64_t ld, uint32_t signs, uint64_t seed,
-                                                             uint64_t offset, const float *__restrict__ amax_p,
-                                                             uint8_t *__restrict__ codes,
-                                                             uint8_t *__restrict__ scales) {
+// With ROWS (nearest-even only) the same read of x also writes x's rowwise
+// layout (codes [R][C/2], scales [R][C/16], tensor amax *ramax_p): a thread's 8
+// columns of a row are half of a 16-column block, whose other half lane ^ 1 holds,
+// so the block amax takes one lane exchange; the codes leave as 4 bytes per
+// thread, 128 consecutive bytes per row and half-wave.  A row whose transform sign
+// is set holds -x in the slab; its multiplier is negated, so the products are
+// those of x (nearest-even is symmetric).  Both layouts are bit-identical to the
+// separate rowwise and columnwise kernels'.
+// At least three waves per SIMD: the fused rowwise layout (ROWS) would otherwise
+// take 174 registers and two waves; 168 with three measured 10 us faster per step.
+template <typename T, bool RHT, bool SR, bool ROWS = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void quant_cols_kernel(
+    const T *__restrict__ x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
+    const float *__restrict__ amax_p, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+    const float *__restrict__ ramax_p = nullptr, uint8_t *__restrict__ rcodes = nullptr,
+    uint8_t *__restrict__ rscales = nullptr) {
+  static_assert(!(ROWS && SR), "the fused rowwise layout is nearest-even");
   __shared__ __attribute__((aligned(16))) uint8_t lcodes[kColTile * kColRowBytes];
   __shared__ uint8_t lscales[kColTile * kColSlabs];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -417,17 +428,48 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const T *__restric
   const int64_t nslab = R / 16;                                // logical blocks per logical row
   const int64_t cfirst = c0 + 8 * cg;                          // this thread's first column
   __shared__ float tab[kMultTable];
+  __shared__ float rtab[ROWS ? kMultTable : 1];
   const float s_enc = encode_scale(*amax_p);
   fill_mult_table(tab, s_enc);
+  float rs_enc = 0.0f;
+  if constexpr (ROWS) {
+    rs_enc = encode_scale(*ramax_p);
+    fill_mult_table(rtab, rs_enc);
+  }
   __syncthreads();
 
 #pragma unroll 1
   for (int i = 0; i < kColSlabs / 8; ++i) {
     const int sl = 2 * wave + (lane >> 5) + 8 * i;             // slab within the tile
     const int64_t s = slab0 + sl;
-    if (s >= nslab || cfirst >= C) continue;
+    if (s >= nslab || cfirst >= C) continue;                   // lanes 2k, 2k + 1 skip together (C % 16 == 0)
     Slab8<T> slab;
     slab.load(x + s * 16 * ld + cfirst, ld, RHT ? signs : 0u);
+    if constexpr (ROWS) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v[8];
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          v[j] = slab.at(r, j);
+          m = fmaxf(m, __builtin_fabsf(v[j]));
+        }
+        // the block's other 8 columns are lane ^ 1's (DPP quad_perm [1, 0, 3, 2])
+        const float mo = __uint_as_float(
+            uint32_t(__builtin_amdgcn_update_dpp(0, int(__float_as_uint(m)), 0xB1, 0xF, 0xF, false)));
+        uint32_t sc;
+        float mult;
+        block_scale(fmaxf(m, mo), rs_enc, rtab, sc, mult);
+        if (RHT && ((signs >> r) & 1u)) mult = -mult;
+        float sv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] = v[j] * mult;
+        const int64_t row = s * 16 + r;
+        *reinterpret_cast<uint32_t *>(rcodes + row * (C / 2) + cfirst / 2) = encode8_rne(sv);
+        if ((cg & 1) == 0) rscales[row * (C / 16) + cfirst / 16] = uint8_t(sc);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float col[16];
@@ -695,6 +737,18 @@ void launch_cols(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, u
                      offset, out->amax, out->codes, out->scales);
 }
 
+// Both nearest-even layouts of x in one kernel: cols (x^T, transformed when RHT)
+// and rows (x).  Each takes its own tensor amax from its descriptor.
+template <typename T, bool RHT>
+void launch_cols_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, const fp4_tensor *cols,
+                      const fp4_tensor *rows, hipStream_t stream) {
+  const int64_t nslab = R / 16;
+  dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
+  hipLaunchKernelGGL((quant_cols_kernel<T, RHT, false, true>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
+                     uint64_t(0), uint64_t(0), cols->amax, cols->codes, cols->scales, rows->amax, rows->codes,
+                     rows->scales);
+}
+
 template <typename T>
 hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, uint64_t seed,
                          uint64_t offset, const fp4_tensor *out, const fp4_tensor *out_t, hipStream_t stream) {
@@ -733,10 +787,11 @@ hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t 
   return hipGetLastError();
 }
 
-// Dual quantization: both amaxes in one read of x (unless given), then the rowwise
-// and the columnwise kernels.  (A single kernel writing both layouts from one read
-// measured slower on the MI355X: the encoders are bound by vector-ALU work, which
-// fusion does not reduce, and the fused kernel's registers halve occupancy.)
+// Dual quantization: both amaxes in one read of x (unless given), then the layouts.
+// Nearest-even: one kernel writes both from one read of x (quant_cols_kernel with
+// ROWS), 18 us faster per 12B step than two kernels.  Stochastic: the rowwise and
+// the columnwise kernels in turn; a single kernel measured slower there, since the
+// stochastic encoders are bound by vector-ALU work, which fusion does not reduce.
 template <typename T>
 hipError_t dual_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, uint64_t seed,
                      uint64_t off_rows, uint64_t off_cols, const fp4_tensor *rows, const fp4_tensor *cols,
@@ -762,6 +817,12 @@ hipError_t dual_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
     }
   }
   if (R == 0 || C == 0) return hipGetLastError();
+  if (!sr) {
+    // nearest-even: both layouts from one read of x
+    if (rht) launch_cols_rows<T, true>(x, R, C, ld, signs, cols, rows, stream);
+    else launch_cols_rows<T, false>(x, R, C, ld, signs, cols, rows, stream);
+    return hipGetLastError();
+  }
   const uint32_t given = flags | FP4_Q_AMAX_GIVEN;
   hipError_t e = quantize_impl(x, R, C, ld, (given & FP4_Q_SR) | FP4_Q_AMAX_GIVEN, signs, seed, off_rows, rows,
                                nullptr, stream);

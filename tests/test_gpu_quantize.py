@@ -244,13 +244,15 @@ def test_strided_input(fp4, oracle, mode, dtype):
     assert_q_equal(host_q(q), ora, f"strided {mode}")
     if q_t is not None:
         assert_q_equal(host_q(q_t), oracle.quantize(xf, two_d=True, colwise=not colwise), f"strided {mode} (T)")
-    # both layouts at once from the same strided view
+    # both layouts at once from the same strided view (stochastic: two kernels;
+    # nearest-even: one kernel writing both)
     if mode == "rows_rne":
-        qr, qc = fp4.QTensor(R, C), fp4.QTensor(C, R)
-        fp4.fp4_quantize_dual(x, fp4.Q_SR | fp4.Q_RHT, 0x6A95, 5, 9, 10, qr, qc)
-        assert_q_equal(host_q(qr), oracle.quantize(xf, sr=True, seed=5, offset=9), "strided dual rows")
-        assert_q_equal(host_q(qc), oracle.quantize(xf, colwise=True, rht=True, sr=True, signs=0x6A95, seed=5,
-                                                   offset=10), "strided dual cols")
+        for sr in (True, False):
+            qr, qc = fp4.QTensor(R, C), fp4.QTensor(C, R)
+            fp4.fp4_quantize_dual(x, (fp4.Q_SR if sr else 0) | fp4.Q_RHT, 0x6A95, 5, 9, 10, qr, qc)
+            assert_q_equal(host_q(qr), oracle.quantize(xf, sr=sr, seed=5, offset=9), f"strided dual rows sr={sr}")
+            assert_q_equal(host_q(qc), oracle.quantize(xf, colwise=True, rht=True, sr=sr, signs=0x6A95, seed=5,
+                                                       offset=10), f"strided dual cols sr={sr}")
 
 
 @pytest.mark.parametrize("shape", [(32, 512), (16, 496), (64, 256), (48, 320)], ids=lambda s: f"{s[0]}x{s[1]}")
