@@ -10,9 +10,9 @@ call includes its amax pass.  Inputs are seeded synthetic tensors
 Prints one JSON line.  `value` is whole-step NVFP4 linear TFLOP/s (3 GEMMs of
 2*M*N*K flops each, divided by the step time including every quantization);
 `roofline` is that of the dominant kernel (the block-scaled GEMM, timed with HIP
-events on its launch stream); `quantize.kernels` times each quantizer kernel on
-its own after the timed steps (input read from HBM, amax passes separate), with
-its algorithmic bytes and its bound (HBM, or the vector ALU for the stochastic
+events on its launch stream); `quantize.kernels` times each quantize call of the
+step, and its layout kernels alone, after the timed steps (input read from HBM),
+with algorithmic bytes and the bound (HBM, or the vector ALU for the stochastic
 encoders); `cpu_baseline` is the oracle timed on host cores on a bounded sample
 of the same workload, extrapolated to the step.
 """
@@ -338,13 +338,13 @@ def main():
 
 
 def quantize_breakdown(layers, wl, reps=5):
-    """Each quantizer kernel of the step on its own: the layout kernels through
-    their entry points with the amax given (the step's own amax is in place), the
-    amax passes as the difference between a call with and without its amax pass
-    (the amax kernel plus the one-workgroup reduction of its partial maxima).  A 512 MiB read runs before every timed call,
-    so each call reads its input from HBM, not from the 256 MB Infinity Cache.
-    Rates are algorithmic bytes (input read once, this kernel's outputs written
-    once) over the median of `reps` calls."""
+    """The quantize calls of the step timed one at a time, each after a 512 MiB read
+    so that its input comes from HBM, not from the 256 MB Infinity Cache: every call
+    whole (its amax pass included), and its layout kernels alone (amax given).  Rates
+    are algorithmic bytes over the median of `reps` calls: the input read once plus
+    the outputs written once (so a whole call, which reads its input once for the
+    amax and again for the layouts, is rated below its kernels).  The amax kernels'
+    own times are in the step's kernel trace."""
     import torch
 
     import nvfp4_bit_microscaled_amd as Q
@@ -368,6 +368,7 @@ def quantize_breakdown(layers, wl, reps=5):
 
     G = Q.Q_AMAX_GIVEN
     one_d = 0.5 + 1 / 16
+    two_d = 2 * (0.5 + 1 / 256)
     rows = []
 
     def add(name, kernel, nbytes, ms, bound):
@@ -382,34 +383,37 @@ def quantize_breakdown(layers, wl, reps=5):
         sd, od, ow = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
         fprop, dgrad, wgrad = ("fprop" in wl.passes), ("dgrad" in wl.passes), ("wgrad" in wl.passes)
         if fprop and wgrad:
-            full = med_ms(lambda: Q.fp4_quantize_dual(x, Q.Q_RHT, inp.signs, 0, 0, 0, b.xq, b.xq_t))
-            given = med_ms(lambda: Q.fp4_quantize_dual(x, Q.Q_RHT | G, inp.signs, 0, 0, 0, b.xq, b.xq_t))
-            add(f"{lin.name} X dual amax (plain + transformed; dual call minus the same call with amax given)",
-                "amax_dual_kernel", M * K * in_b, full - given, "hbm")
-        if fprop:
-            add(f"{lin.name} X rowwise nearest-even", "quant_rows_flat_kernel", M * K * (in_b + one_d),
+            xb = M * K * (in_b + 2 * one_d)
+            add(f"{lin.name} X dual call (amax pass + both layouts)", "amax_dual_kernel + quant_cols_kernel", xb,
+                med_ms(lambda: Q.fp4_quantize_dual(x, Q.Q_RHT, inp.signs, 0, 0, 0, b.xq, b.xq_t)), "call")
+            add(f"{lin.name} X rowwise + X^T columnwise transformed, one kernel (amax given)", "quant_cols_kernel",
+                xb, med_ms(lambda: Q.fp4_quantize_dual(x, Q.Q_RHT | G, inp.signs, 0, 0, 0, b.xq, b.xq_t)), "hbm")
+        elif fprop:
+            add(f"{lin.name} X rowwise nearest-even (amax given)", "quant_rows_flat_kernel", M * K * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(x, G, 0, 0, 0, b.xq)), "hbm")
-        if wgrad:
-            add(f"{lin.name} X^T columnwise transformed nearest-even", "quant_cols_kernel", M * K * (in_b + one_d),
+        elif wgrad:
+            add(f"{lin.name} X^T columnwise transformed (amax given)", "quant_cols_kernel", M * K * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(x, Q.Q_COLWISE | Q.Q_RHT | G, inp.signs, 0, 0, b.xq_t)), "hbm")
         if fprop or dgrad:
-            full = med_ms(lambda: Q.fp4_quantize(w, Q.Q_2D, 0, 0, 0, b.wq, b.wq_t))
-            given = med_ms(lambda: Q.fp4_quantize(w, Q.Q_2D | G, 0, 0, 0, b.wq, b.wq_t))
-            add(f"{lin.name} W amax (2D call minus the same call with amax given)", "amax_flat_kernel", N * K * in_b,
-                full - given, "hbm")
-            add(f"{lin.name} W 2D + W^T nearest-even", "quant_2d_kernel", N * K * (in_b + 2 * (0.5 + 1 / 256)), given,
-                "hbm")
+            wb = N * K * (in_b + two_d)
+            add(f"{lin.name} W 2D call (amax pass + W and W^T)", "amax_flat_kernel + quant_2d_kernel", wb,
+                med_ms(lambda: Q.fp4_quantize(w, Q.Q_2D, 0, 0, 0, b.wq, b.wq_t)), "call")
+            add(f"{lin.name} W 2D + W^T nearest-even (amax given)", "quant_2d_kernel", wb,
+                med_ms(lambda: Q.fp4_quantize(w, Q.Q_2D | G, 0, 0, 0, b.wq, b.wq_t)), "hbm")
+            scratch = torch.zeros(1, dtype=torch.float32, device="cuda")
+            add(f"{lin.name} W amax alone (fp4_amax: the same kernel, its atomic form)", "amax_flat_kernel",
+                N * K * in_b, med_ms(lambda: Q.fp4_amax(w, 0, 0, scratch)), "hbm")
         if dgrad and wgrad:
-            full = med_ms(lambda: Q.fp4_quantize_dual(dy, Q.Q_SR | Q.Q_RHT, inp.signs, sd, od, ow, b.dyq, b.dyq_t))
-            given = med_ms(lambda: Q.fp4_quantize_dual(dy, Q.Q_SR | Q.Q_RHT | G, inp.signs, sd, od, ow, b.dyq,
-                                                       b.dyq_t))
-            add(f"{lin.name} dY dual amax (plain + transformed; dual call minus the same call with amax given)",
-                "amax_dual_kernel", M * N * in_b, full - given, "hbm")
+            add(f"{lin.name} dY dual call (amax pass + two stochastic layouts)", "amax_dual_kernel + 2 kernels",
+                M * N * (in_b + 2 * one_d),
+                med_ms(lambda: Q.fp4_quantize_dual(dy, Q.Q_SR | Q.Q_RHT, inp.signs, sd, od, ow, b.dyq, b.dyq_t)),
+                "call")
         if dgrad:
-            add(f"{lin.name} dY rowwise stochastic", "quant_rows_flat_kernel", M * N * (in_b + one_d),
+            add(f"{lin.name} dY rowwise stochastic (amax given)", "quant_rows_flat_kernel", M * N * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(dy, Q.Q_SR | G, 0, sd, od, b.dyq)), "valu")
         if wgrad:
-            add(f"{lin.name} dY^T columnwise transformed stochastic", "quant_cols_kernel", M * N * (in_b + one_d),
+            add(f"{lin.name} dY^T columnwise transformed stochastic (amax given)", "quant_cols_kernel",
+                M * N * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR | G, inp.signs, sd, ow, b.dyq_t)),
                 "valu")
     del flush
