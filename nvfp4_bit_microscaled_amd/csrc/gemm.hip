@@ -482,8 +482,9 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   constexpr int kBarrierSub = 3;  // quarter 2's substep that opens with the first barrier
   // DMA loads of this stage issued before the second barrier
   constexpr int kDmaBeforeB = ((4 - kBarrierSub) * kDmaPer < NDMA) ? (4 - kBarrierSub) * kDmaPer : NDMA;
-  auto stage = [&](int kt, auto last_tag, int par, int kt_dma, bool after_epi) {
+  auto stage = [&](int kt, auto last_tag, int par, int kt_dma, bool after_epi, auto zero_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
+    constexpr bool ZERO = decltype(zero_tag)::value;  // a tile's first stage: its first MFMAs start from C = 0
     const int buf = (kt + par) & 1;
     static_for<4>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
@@ -514,7 +515,9 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
         static_for<NMF>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
           constexpr int i = k / TN, j = k % TN;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][TM + j], op[cur][i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][TM + j], op[cur][i],
+                                                              (ZERO && q == 0 && s == 0) ? f32x16{} : acc[i][j], 0,
+                                                              0, 0);
           if constexpr (has_next)
             slot_items(kc, HalfTiles{}, [&](auto hc) {
               constexpr int h = decltype(hc)::value;
@@ -569,15 +572,22 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       dequant_half(0, 0, 0, i, 0);
       dequant_half(0, 0, 0, i, 1);
     }
-    for (int kt = 0; kt + 2 < nst; ++kt) stage(kt, std::false_type{}, par, kt + 2, kt == 0 && !first);
+    // the first stage starts the accumulators (C = 0) when it is a plain one; for
+    // one- and two-stage tiles the accumulators were cleared after the last tile
+    int kt0 = 0;
+    if (nst >= 3) {
+      stage(0, std::false_type{}, par, 2, !first, std::true_type{});
+      kt0 = 1;
+    }
+    for (int kt = kt0; kt + 2 < nst; ++kt) stage(kt, std::false_type{}, par, kt + 2, false, std::false_type{});
     if (nst >= 2) {
       // the stage before last loads the next tile's first stage; without a next
       // tile it re-loads this tile's last stage into a buffer that is not read
       // again (drained below)
       if (more) set_tile(Lnext);
-      stage(nst - 2, std::false_type{}, par, more ? 0 : nst - 1, nst == 2 && !first);
+      stage(nst - 2, std::false_type{}, par, more ? 0 : nst - 1, nst == 2 && !first, std::false_type{});
     }
-    stage(nst - 1, std::true_type{}, par, 0, false);
+    stage(nst - 1, std::true_type{}, par, 0, false, std::false_type{});
 
     // every wave is done with this tile's stage buffers, and the DMA issued in the
     // stage before last has landed
@@ -611,10 +621,12 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
     L = Lnext;
     par = par_next;
     first = false;
+    if (nst < 3) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    }
   }
 }
 
