@@ -149,29 +149,32 @@ __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Epilogue of the main kernel through LDS, one 32x32 accumulator block at a
-// time (C^T layout as above: a lane holds 4 consecutive columns of a row per
-// group of 4 accumulators).  fp32 output: the block goes raw from the accumulator
-// registers into a private 4 KB region, 32 rows of 128 bytes with the 16-byte
-// chunks of a row XOR-swizzled by the row, and each lane reads back whole chunks
-// of rows and scales them (gscale: the product of the two tensor decode scales).
-// bf16 output: the lane scales and rounds its values first, so the block passes
-// through the region as 32 rows of 64 bytes, half the LDS traffic (measured 0.1%
-// faster per step than rounding after the round trip).  Either way every store
-// writes whole row runs of C (128 bytes fp32, 64 bytes bf16).  The region lies
-// outside the two stage buffers, so the next tile's stages can land while this
-// runs, and only one block's values pass through vector registers at a time.
-// The stores are non-temporal: the output is not read again by this kernel, and
-// the quantizer that follows in a linear layer's step then reads its input from
-// HBM without first evicting dirty output lines from the Infinity Cache
-// (measured 5% faster quantization per step on the MI355X).  CHECK: the tile may
-// stick out of C (rows or columns past the edge are skipped; the launcher
-// guarantees N % 4 == 0, a 16-byte aligned C and ldc % 4 == 0).
+// Epilogue of the main kernel through LDS (C^T layout as above: a lane holds 4
+// consecutive columns of a row per group of 4 accumulators).  A private 4 KB
+// region per wave holds 32 rows of 128 bytes, the 16-byte chunks of a row
+// XOR-swizzled by the row; each lane reads back whole chunks of rows and stores
+// them, so every store writes whole 128-byte row runs of C.
+//  * fp32 output: one 32x32 block at a time goes raw from the accumulator
+//    registers into the region and is scaled after the read-back (gscale: the
+//    product of the two tensor decode scales).
+//  * bf16 output: two neighbouring blocks at a time, each scaled and rounded in
+//    registers first: half the LDS traffic per block, and whole lines per store.
+//    One block at a time wrote 64-byte half lines, which were not merged (fprop
+//    wrote 860 MiB for 640 MiB of Y); pairing measured 0.4% faster per step.
+// The region lies outside the two stage buffers, so the next tile's stages can
+// land while this runs, and only one block's values pass through vector
+// registers at a time.  The stores are non-temporal: the output is not read again
+// by this kernel, and the quantizer that follows in a linear layer's step then
+// reads its input from HBM without first evicting dirty output lines from the
+// Infinity Cache (measured 5% faster quantization per step on the MI355X).
+// CHECK: the tile may stick out of C (rows or columns past the edge are skipped;
+// the launcher guarantees N % 4 == 0, a 16-byte aligned C and ldc % 4 == 0).
 constexpr int kEpiBytes = 4096;
 
 template <int TM, int TN, bool CHECK>
 __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
                                                 int64_t n0, int lane, uint8_t *region, float gscale) {
+  static_assert(TN % 2 == 0, "bf16 blocks go in pairs");
   const int lr = lane & 31, g = lane >> 5;
   const int wsw = (lr >> 1) & 7;  // swizzle of the row this lane writes
 #pragma unroll
@@ -179,28 +182,33 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if (p.c_bf16) {
-        // scaled and rounded in registers first, so the block passes through the
-        // region as 32 rows of 64 bytes: row lr, 16-byte chunk q (columns 8q .. 8q+7)
-        // at chunk q ^ ((lr / 4) % 4), lane half g writing its 8 bytes.  The explicit
-        // moves keep the compiler from moving all the accumulators out of the
-        // accumulator registers at once.
-        float a[16];
+        // blocks j and j + 1 together (at even j; odd j was done with its pair):
+        // scaled and rounded in registers first, so the pair passes through the
+        // region as 32 rows of 128 bytes: row lr, 16-byte chunk 4 (j & 1) + q
+        // (columns 8q .. 8q+7 of block j) at chunk ^ ((lr / 2) % 8), lane half g
+        // writing its 8 bytes.  The explicit moves keep the compiler from moving all
+        // the accumulators out of the accumulator registers at once.
+        if (j & 1) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a[r]) : "a"(acc[i][j][r]));
-        const int bsw = (lr >> 2) & 3;
+        for (int jj = 0; jj < 2; ++jj) {
+          float a[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bf16x4 h = {(__bf16)(a[4 * q] * gscale), (__bf16)(a[4 * q + 1] * gscale),
-                            (__bf16)(a[4 * q + 2] * gscale), (__bf16)(a[4 * q + 3] * gscale)};
-          *reinterpret_cast<bf16x4 *>(region + lr * 64 + ((q ^ bsw) << 4) + 8 * g) = h;
+          for (int r = 0; r < 16; ++r)
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a[r]) : "a"(acc[i][j + jj][r]));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x4 h = {(__bf16)(a[4 * q] * gscale), (__bf16)(a[4 * q + 1] * gscale),
+                              (__bf16)(a[4 * q + 2] * gscale), (__bf16)(a[4 * q + 3] * gscale)};
+            *reinterpret_cast<bf16x4 *>(region + lr * 128 + (((4 * jj + q) ^ wsw) << 4) + 8 * g) = h;
+          }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // lane: rows 16k + lane / 4 (k = 0, 1), chunk lane % 4 (8 columns)
+        // lane: rows 8k + lane / 8 (k = 0..3), chunk lane % 8 (8 columns): whole lines
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int r = 16 * k + (lane >> 2), c = lane & 3;
+        for (int k = 0; k < 4; ++k) {
+          const int r = 8 * k + (lane >> 3), c = lane & 7;
           typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-          const bf16x8 h = *reinterpret_cast<const bf16x8 *>(region + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+          const bf16x8 h = *reinterpret_cast<const bf16x8 *>(region + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
           const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 8 * c;
           uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n;
           if (!CHECK || (m < p.M && n + 8 <= p.N)) {
