@@ -41,6 +41,11 @@ CASES = [
     # main path with ragged edges (rows/columns past M, N read as zeros, not stored)
     (300, 272, 512, False, True),
     (300, 260, 512, False, False),
+    # bf16 output stores two neighbouring 32-column blocks together: N = 300 leaves the
+    # second block of a pair with one whole and one half 8-column chunk inside C,
+    # N = 288 the second block wholly outside
+    (260, 300, 768, False, False),
+    (96, 288, 256, False, True),
     # more 256x256 tiles than CUs: persistent loop; 17x16 = 272 tiles, 17x17 = 289
     # (an XCD split that is not even), ragged in both dimensions; on a 256-CU GPU
     # the tiles past the first 256 run as 128x128 quarters in a second launch
