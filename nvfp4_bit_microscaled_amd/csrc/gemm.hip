@@ -149,6 +149,16 @@ __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Epilogue of the main kernel through LDS (C^T layout as above: a lane holds 4
 // consecutive columns of a row per group of 4 accumulators).  A private 4 KB
 // region per wave holds 32 rows of 128 bytes, the 16-byte chunks of a row
@@ -160,7 +170,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 //  * bf16 output: two neighbouring blocks at a time, each scaled and rounded in
 //    registers first: half the LDS traffic per block, and whole lines per store.
 //    One block at a time wrote 64-byte half lines, which were not merged (fprop
-//    wrote 860 MiB for 640 MiB of Y); pairing measured 0.4% faster per step.
+//    wrote 860 MiB for 640 MiB of Y); pairing measured 0.4% faster per step.  The
+//    next pair is converted while this pair's read-back is in flight (0.3% faster
+//    GEMM).
 // The region lies outside the two stage buffers, so the next tile's stages can
 // land while this runs, and only one block's values pass through vector
 // registers at a time.  The stores are non-temporal: the output is not read again
@@ -177,65 +189,86 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
   static_assert(TN % 2 == 0, "bf16 blocks go in pairs");
   const int lr = lane & 31, g = lane >> 5;
   const int wsw = (lr >> 1) & 7;  // swizzle of the row this lane writes
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  if (p.c_bf16) {
+    // Blocks (i, j) and (i, j + 1), j even, together: scaled and rounded in registers
+    // first, so the pair passes through the region as 32 rows of 128 bytes: row lr,
+    // 16-byte chunk 4 jj + q (columns 8q .. 8q+7 of block j + jj) at
+    // chunk ^ ((lr / 2) % 8), lane half g writing its 8 bytes.  The next pair is
+    // converted while this pair's read-back is in flight.  The explicit moves keep
+    // the compiler from moving all the accumulators out of the accumulator
+    // registers at once.
+    constexpr int NP = TM * TN / 2;
+    bf16x4 cur[2][4];
+    auto convert = [&](auto pc) {
+      constexpr int P = decltype(pc)::value, i = P / (TN / 2), j = 2 * (P % (TN / 2));
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        float a[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a[r]) : "a"(acc[i][j + jj][r]));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          cur[jj][q] = bf16x4{(__bf16)(a[4 * q] * gscale), (__bf16)(a[4 * q + 1] * gscale),
+                              (__bf16)(a[4 * q + 2] * gscale), (__bf16)(a[4 * q + 3] * gscale)};
+      }
+    };
+    convert(std::integral_constant<int, 0>{});
+    static_for<NP>([&](auto pc) {
+      constexpr int P = decltype(pc)::value, i = P / (TN / 2), j = 2 * (P % (TN / 2));
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<bf16x4 *>(region + lr * 128 + (((4 * jj + q) ^ wsw) << 4) + 8 * g) = cur[jj][q];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // lane: rows 8k + lane / 8 (k = 0..3), chunk lane % 8 (8 columns): whole lines
+      bf16x8 h[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3), c = lane & 7;
+        h[k] = *reinterpret_cast<const bf16x8 *>(region + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+      }
+      if constexpr (P + 1 < NP) convert(std::integral_constant<int, P + 1>{});
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next pair
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3), c = lane & 7;
+        const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 8 * c;
+        uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n;
+        if (!CHECK || (m < p.M && n + 8 <= p.N)) {
+          __builtin_nontemporal_store(h[k], reinterpret_cast<bf16x8 *>(dst));
+        } else if (m < p.M && n < p.N) {
+          const bf16x4 lo = {h[k][0], h[k][1], h[k][2], h[k][3]};
+          __builtin_nontemporal_store(lo, reinterpret_cast<bf16x4 *>(dst));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      if (p.c_bf16) {
-        // blocks j and j + 1 together (at even j; odd j was done with its pair):
-        // scaled and rounded in registers first, so the pair passes through the
-        // region as 32 rows of 128 bytes: row lr, 16-byte chunk 4 (j & 1) + q
-        // (columns 8q .. 8q+7 of block j) at chunk ^ ((lr / 2) % 8), lane half g
-        // writing its 8 bytes.  The explicit moves keep the compiler from moving all
-        // the accumulators out of the accumulator registers at once.
-        if (j & 1) continue;
+      // fp32: one block, raw from the accumulator registers
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          float a[16];
+      for (int q = 0; q < 4; ++q) {  // columns 8q + 4g .. +3 of the block: chunk 2q + g
+        const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]);
+        *reinterpret_cast<float4 *>(region + lr * 128 + (((2 * q + g) ^ wsw) << 4)) = v;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // lane: rows 8k + lane / 8 (k = 0..3), chunk lane % 8 (4 columns)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a[r]) : "a"(acc[i][j + jj][r]));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bf16x4 h = {(__bf16)(a[4 * q] * gscale), (__bf16)(a[4 * q + 1] * gscale),
-                              (__bf16)(a[4 * q + 2] * gscale), (__bf16)(a[4 * q + 3] * gscale)};
-            *reinterpret_cast<bf16x4 *>(region + lr * 128 + (((4 * jj + q) ^ wsw) << 4) + 8 * g) = h;
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // lane: rows 8k + lane / 8 (k = 0..3), chunk lane % 8 (8 columns): whole lines
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int r = 8 * k + (lane >> 3), c = lane & 7;
-          typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-          const bf16x8 h = *reinterpret_cast<const bf16x8 *>(region + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-          const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 8 * c;
-          uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n;
-          if (!CHECK || (m < p.M && n + 8 <= p.N)) {
-            __builtin_nontemporal_store(h, reinterpret_cast<bf16x8 *>(dst));
-          } else if (m < p.M && n < p.N) {
-            const bf16x4 lo = {h[0], h[1], h[2], h[3]};
-            __builtin_nontemporal_store(lo, reinterpret_cast<bf16x4 *>(dst));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {  // columns 8q + 4g .. +3 of the block: chunk 2q + g
-          const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                       acc[i][j][4 * q + 3]);
-          *reinterpret_cast<float4 *>(region + lr * 128 + (((2 * q + g) ^ wsw) << 4)) = v;
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // lane: rows 8k + lane / 8 (k = 0..3), chunk lane % 8 (4 columns)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int r = 8 * k + (lane >> 3), c = lane & 7;
-          const float4 x = *reinterpret_cast<const float4 *>(region + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-          const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 4 * c;
-          if (!CHECK || (m < p.M && n < p.N)) {
-            const f32x4 y = {x.x * gscale, x.y * gscale, x.z * gscale, x.w * gscale};
-            __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n));
-          }
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3), c = lane & 7;
+        const float4 x = *reinterpret_cast<const float4 *>(region + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+        const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 4 * c;
+        if (!CHECK || (m < p.M && n < p.N)) {
+          const f32x4 y = {x.x * gscale, x.y * gscale, x.z * gscale, x.w * gscale};
+          __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n));
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next block
@@ -253,16 +286,6 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 1)) & 7; }
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
-template <class F, int... Is>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
