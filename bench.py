@@ -120,6 +120,48 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": x.numel() * 4, "launches": 3}), flush=True)
 
 
+
+class HipTimingEvent:
+    """A HIP event used only for timing, created with hipEventDisableSystemFence.  A
+    default event record ends with a system-scope fence that writes back and
+    invalidates the caches, which idled the GPU about 10 us at every recorded call
+    boundary of the step and slowed the call after it.  With the flag, and one record
+    per call boundary, the step measured as fast as with no per-call events at all
+    (0.4-0.6% faster than with default events, two per boundary).  Elapsed times are
+    read after a device synchronization."""
+    _lib = None
+
+    def __init__(self):
+        import ctypes
+        if HipTimingEvent._lib is None:
+            lib = ctypes.CDLL("libamdhip64.so")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipTimingEvent._lib = lib
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = HipTimingEvent._lib.hipEventCreateWithFlags(ctypes.byref(self.h), 0x20000000)  # hipEventDisableSystemFence
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self, stream):
+        rc = HipTimingEvent._lib.hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_time(self, end):
+        ms = self._ct.c_float()
+        rc = HipTimingEvent._lib.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if HipTimingEvent._lib is not None and self.h:
+            HipTimingEvent._lib.hipEventDestroy(self.h)
+
 def source_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -197,7 +239,7 @@ def main():
     split_shapes = [sh for sh in gemm_shapes if fp4.fp4_gemm_ws_bytes(*sh) > 0]
 
     stream = torch.cuda.current_stream()
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = HipTimingEvent  # per-call timing events on the step's stream
     Q = fp4
 
     def step(record):
@@ -205,16 +247,22 @@ def main():
         X's two layouts (rowwise for fprop, transformed columnwise for wgrad) come from
         one dual quantization, and so do dY's (rowwise SR for dgrad, transformed
         columnwise SR for wgrad); each dual call includes its one-read amax pass."""
+        chain = [None]
         for lin, inp, x, w, dy, b, o in layers:
             M, N, K = lin.M, lin.N, lin.K
             in_b = x.element_size()
             one_d = 0.5 + 1 / 16  # code + scale bytes per element of a 1D layout
 
             def timed(kind, amount, fn):
-                e0, e1 = ev(), ev()
-                e0.record(stream)
+                # calls are chained: a call's start event is the previous call's end
+                # event (the same point of the stream), one record per boundary
+                if chain[0] is None:
+                    chain[0] = ev()
+                    chain[0].record(stream)
+                e0, e1 = chain[0], ev()
                 fn()
                 e1.record(stream)
+                chain[0] = e1
                 record.append((kind, amount, e0, e1))
 
             fprop, dgrad, wgrad = ("fprop" in wl.passes), ("dgrad" in wl.passes), ("wgrad" in wl.passes)
