@@ -7,8 +7,6 @@
 
 namespace nvfp4 {
 
-__global__ void copy_f32_kernel(const float *src, float *dst);
-
 hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                        uint32_t signs, float *out, hipStream_t stream);
 

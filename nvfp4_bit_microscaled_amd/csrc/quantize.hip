@@ -557,7 +557,8 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(const T *__restrict_
                                                            uint8_t *__restrict__ d_codes,
                                                            uint8_t *__restrict__ d_scales,
                                                            uint8_t *__restrict__ t_codes,
-                                                           uint8_t *__restrict__ t_scales) {
+                                                           uint8_t *__restrict__ t_scales,
+                                                           float *__restrict__ amax_copy) {
   // transposed codes: [row of x^T in the block][16 tile-rows x 8 bytes]; the 8-byte
   // slot of tile-row t in row q sits at t ^ (q / 16 % 16), which spreads the 16
   // lanes that write one slot index over distinct banks
@@ -565,6 +566,8 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(const T *__restrict_
   __shared__ uint8_t tscales[16 * 16];  // [tile-column][tile-row]
   __shared__ float tab[kMultTable];
   const float s_enc = encode_scale(*amax_p);
+  // the tensor amax into the other layout's descriptor, once
+  if (amax_copy != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *amax_copy = *amax_p;
   fill_mult_table(tab, s_enc);
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -768,11 +771,9 @@ hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t 
     if (transp) { tcp = transp->codes; tsp = transp->scales; }
     const int64_t tiles_c = C / 16, tiles_r = R / 16;
     const dim3 grid(unsigned((tiles_c + 15) / 16), unsigned((tiles_r + 15) / 16));
+    float *amax_copy = (out_t && out_t->amax != out->amax) ? out_t->amax : nullptr;
     hipLaunchKernelGGL(quant_2d_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, out->amax, dc, ds, tcp,
-                       tsp);
-    if (out_t && out_t->amax != out->amax) {
-      hipLaunchKernelGGL(copy_f32_kernel, dim3(1), dim3(1), 0, stream, out->amax, out_t->amax);
-    }
+                       tsp, amax_copy);
   } else if (flags & FP4_Q_COLWISE) {
     if (rht && sr) launch_cols<T, true, true>(x, R, C, ld, signs, seed, offset, out, stream);
     else if (rht) launch_cols<T, true, false>(x, R, C, ld, signs, seed, offset, out, stream);
@@ -842,8 +843,6 @@ hipError_t launch_quantize_dual(const void *x, fp4_dtype dtype, int64_t R, int64
   return dual_impl(static_cast<const float *>(x), R, C, ld, flags, signs, seed, off_rows, off_cols, rows, cols,
                    stream);
 }
-
-__global__ void copy_f32_kernel(const float *src, float *dst) { *dst = *src; }
 
 hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                        uint32_t signs, float *out, hipStream_t stream) {
