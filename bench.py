@@ -406,11 +406,11 @@ def quantize_breakdown(layers, wl, reps=5):
         ts = []
         for _ in range(reps):
             torch.sum(flush, dim=0, out=sink)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = HipTimingEvent(), HipTimingEvent()
             e0.record(stream)
             fn()
             e1.record(stream)
-            e1.synchronize()
+            torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         return sorted(ts)[len(ts) // 2]
 
