@@ -9,8 +9,10 @@ call includes its amax pass.  Inputs are seeded synthetic tensors
 
 Prints one JSON line.  `value` is whole-step NVFP4 linear TFLOP/s (3 GEMMs of
 2*M*N*K flops each, divided by the step time including every quantization);
-`roofline` is that of the dominant kernel (the block-scaled GEMM, timed with HIP
-events on its launch stream); `quantize.kernels` times each quantize call of the
+`roofline` is that of the dominant kernel (the block-scaled GEMM, timed inside the
+timed steps with HIP events on its launch stream: events without the system-scope
+fence, one per call boundary, so that timing does not slow the step);
+`quantize.kernels` times each quantize call of the
 step, and its layout kernels alone, after the timed steps (input read from HBM),
 with algorithmic bytes and the bound (HBM, or the vector ALU for the stochastic
 encoders); `cpu_baseline` is the oracle timed on host cores on a bounded sample
