@@ -34,7 +34,8 @@ def run_case(fp4, oracle, x_cpu, flags, signs=0, seed=0, offset=0, with_t=True):
 
 
 ROW_SHAPES = [(1, 16), (333, 272), (64, 4096), (257, 1040)]
-COL_SHAPES = [(16, 8), (784, 1000), (4096, 64), (272, 520)]
+# 2048x2048: 8 column tiles x 8 slab groups, every tile whole
+COL_SHAPES = [(16, 8), (784, 1000), (4096, 64), (272, 520), (2048, 2048)]
 TILE_SHAPES = [(16, 16), (272, 400), (1024, 4096), (48, 2064)]
 
 
@@ -182,6 +183,9 @@ DUAL_CASES = [
     (512, 256, "rht"),
     (272, 400, "sr"),
     (48, 784, "none"),
+    # 8 x 8 whole tiles of the columnwise kernels
+    (2048, 2048, "rht"),
+    (2048, 2048, "sr_rht"),
 ]
 
 
