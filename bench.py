@@ -1,22 +1,27 @@
 """Benchmark: NVFP4 linear-layer step (fprop + dgrad + wgrad) on one MI355X.
 
-One step is the whole hot path over one batch: X 1D nearest-even and X^T with the
-16-point random Hadamard transform (one dual quantization), W 2D (16x16)
-nearest-even with W^T emitted, Y = X.W^T; dY 1D stochastic and dY^T transformed
-and stochastic (one dual quantization), dX = dY.W, dW = dY^T.X.  Each quantize
-call includes its amax pass.  Inputs are seeded synthetic tensors
-(workloads/) already resident in HBM when the timed region starts.
+One step is the whole hot path over one batch, through the library's linear-layer
+calls: fp4_linear_fprop quantizes X (rowwise nearest-even, and X^T with the
+16-point random Hadamard transform for wgrad, in one dual quantization) and W (2D
+16x16 nearest-even, W^T emitted), then Y = X.W^T; fp4_linear_backward quantizes dY
+once (rowwise stochastic for dgrad, dY^T transformed and stochastic for wgrad),
+then dX = dY.W and dW = dY^T.X, reading the forward pass's W^T and X^T.  Each
+quantization includes its amax pass; the GEMMs get the caller workspace sized by
+fp4_linear_ws_bytes, so their split-K plans run.  Inputs are seeded synthetic
+tensors (workloads/) already resident in HBM when the timed region starts.
 
 Prints one JSON line.  `value` is whole-step NVFP4 linear TFLOP/s (3 GEMMs of
 2*M*N*K flops each, divided by the step time including every quantization);
-`roofline` is that of the dominant kernel (the block-scaled GEMM, timed inside the
-timed steps with HIP events on its launch stream: events without the system-scope
-fence, one per call boundary, so that timing does not slow the step);
-`quantize.kernels` times each quantize call of the
+`roofline` is that of the dominant kernel, the block-scaled GEMM: its time comes
+from HIP events the linear calls record between their phases inside the timed
+steps (events without the system-scope fence, one per phase boundary, so that
+timing does not slow the step); `quantize.kernels` times each quantize call of the
 step, and its layout kernels alone, after the timed steps (input read from HBM),
 with algorithmic bytes and the bound (HBM, or the vector ALU for the stochastic
-encoders); `cpu_baseline` is the oracle timed on host cores on a bounded sample
-of the same workload, extrapolated to the step.
+encoders); `other_workloads` holds the same figures for the fprop 8k, wgrad 8k and
+3B-block configurations (fewer steps each); `cpu_baseline` is the oracle timed on
+the host cores this process may use, on a bounded sample of the same workload,
+extrapolated to the step.
 """
 import argparse
 import hashlib
@@ -42,6 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mlp_up_12b", choices=["mlp_up_12b", "fprop_8k", "wgrad_8k", "block_3b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="measure only --workload (default: also the other full-size configurations, fewer steps)")
+    ap.add_argument("--other-steps", type=int, default=10)
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel quantize breakdown (profiler runs that look at the steps only)")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
@@ -184,32 +192,16 @@ def measured_traffic(kernel_src):
     return float(t.group(1)) / 3.0
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the NVFP4 linear path here is measured "
-              f"on one GPU's shard; sharding across GPUs is designed, not built", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.error_vs_k:
-        error_vs_k()
-        return
-
-    import numpy as np
+def setup_workload(name, dev):
+    """Device tensors and caller-owned buffers of every linear of workload `name`,
+    plus one GEMM workspace sized by fp4_linear_ws_bytes for the largest layer."""
     import torch
 
     import nvfp4_bit_microscaled_amd as fp4
     import workloads
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    fp4.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = workloads.WORKLOADS[args.workload]
+    wl = workloads.WORKLOADS[name]
     t_gen = time.time()
-
     layers = []
     for li, lin in enumerate(wl.linears):
         inp = workloads.make_linear_inputs(lin, seed=li, x_outliers=wl.x_outliers, with_dy="dgrad" in wl.passes
@@ -225,9 +217,128 @@ def main():
         layers.append((lin, inp, x, w, dy, bufs, outs))
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
+    ws_need = max(fp4.fp4_linear_ws_bytes(lin.M, lin.N, lin.K) for lin in wl.linears)
+    ws = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=dev)
+    return wl, layers, ws, ws_need, t_gen
 
-    # one workspace for the GEMMs' split-K partial tiles, as large as the largest plan
-    # of the workload needs (the plans take no split for most shapes: then it is unused)
+
+def step(wl, layers, ws, stream, record):
+    """One pass of the whole hot path through the linear-layer calls.  `record`
+    collects (kind, bytes or flops, ev0, ev1) per phase: each call records the phase
+    events it documents, and a phase's start event is the previous phase's end event
+    (one record per boundary).  With fprop and wgrad, fp4_linear_fprop also writes
+    X^T transformed (one dual quantization of X) and the backward call reads it."""
+    import nvfp4_bit_microscaled_amd as Q
+    import workloads
+
+    ev = HipTimingEvent
+    chain = [None]
+    sd, od, ow = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
+    fprop, dgrad, wgrad = ("fprop" in wl.passes), ("dgrad" in wl.passes), ("wgrad" in wl.passes)
+
+    def call(phases, fn):
+        # phases: [(kind, amount)], one per interval between the call's events
+        if chain[0] is None:
+            chain[0] = ev()
+            chain[0].record(stream)
+        evs = [ev() for _ in phases]
+        fn([e.h.value for e in evs[:-1]])
+        evs[-1].record(stream)
+        prev = chain[0]
+        for (kind, amount), e in zip(phases, evs):
+            if kind is not None:
+                record.append((kind, amount, prev, e))
+            prev = e
+        chain[0] = evs[-1]
+
+    for lin, inp, x, w, dy, b, o in layers:
+        M, N, K = lin.M, lin.N, lin.K
+        in_b = x.element_size()
+        one_d = 0.5 + 1 / 16           # code + scale bytes per element of a 1D layout
+        two_d = 2 * (0.5 + 1 / 256)    # W and W^T of a 2D quantization
+        gflop = 2.0 * M * N * K
+        if fprop:
+            xt = b.xq_t if wgrad else None
+            call([("quant", M * K * (in_b + (2 if wgrad else 1) * one_d)), ("quant", N * K * (in_b + two_d)),
+                  ("gemm", gflop)],
+                 lambda m: Q.fp4_linear_fprop(x, w, o["y"], b.xq, b.wq, b.wq_t, xq_t=xt, rht_signs=inp.signs, ws=ws,
+                                              marks=m))
+        if dgrad and wgrad:
+            if fprop:  # X^T came with fprop's dual quantization: the X^T phase is empty
+                phases = [("quant", M * N * (in_b + 2 * one_d)), (None, 0), ("gemm", gflop), ("gemm", gflop)]
+            else:
+                phases = [("quant", M * N * (in_b + 2 * one_d)), ("quant", M * K * (in_b + one_d)), ("gemm", gflop),
+                          ("gemm", gflop)]
+            call(phases, lambda m: Q.fp4_linear_backward(dy, None if fprop else x, b.wq_t, o["dx"], o["dw"],
+                                                         inp.signs, sd, od, ow, b.dyq, b.dyq_t, b.xq_t, ws=ws,
+                                                         marks=m))
+        elif dgrad:
+            call([("quant", M * N * (in_b + one_d)), ("gemm", gflop)],
+                 lambda m: Q.fp4_linear_dgrad(dy, b.wq_t, o["dx"], sd, od, b.dyq, ws=ws, marks=m))
+        elif wgrad:
+            call([("quant", M * N * (in_b + one_d)), ("quant", M * K * (in_b + one_d)), ("gemm", gflop)],
+                 lambda m: Q.fp4_linear_wgrad(dy, x, o["dw"], inp.signs, sd, ow, b.dyq_t, b.xq_t, ws=ws, marks=m))
+
+
+def measure(wl, layers, ws, steps, warmup):
+    """Warm up, then time `steps` steps (host clock between two device
+    synchronizations) with the per-phase events; returns the step figures."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        step(wl, layers, ws, stream, [])
+    torch.cuda.synchronize()
+    records = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(wl, layers, ws, stream, records)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    gemm_ms = sum(e0.elapsed_time(e1) for k, _, e0, e1 in records if k == "gemm")
+    gemm_flops = sum(f for k, f, _, _ in records if k == "gemm")
+    n_gemm = sum(1 for k, *_ in records if k == "gemm")
+    quant_ms = sum(e0.elapsed_time(e1) for k, _, e0, e1 in records if k == "quant")
+    quant_bytes = sum(f for k, f, _, _ in records if k == "quant")
+    step_flops = gemm_flops / steps
+    return {
+        "ms_per_step": ms_per_step,
+        "step_flops": step_flops,
+        "value": step_flops / (ms_per_step * 1e-3) / 1e12,
+        "gemm_tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12,
+        "gemm_ms": gemm_ms,
+        "gemm_flops": gemm_flops,
+        "n_gemm": n_gemm,
+        "quant_ms": quant_ms,
+        "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the NVFP4 linear path here is measured "
+              f"on one GPU's shard; sharding across GPUs is designed, not built", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.error_vs_k:
+        error_vs_k()
+        return
+
+    import torch
+
+    import nvfp4_bit_microscaled_amd as fp4
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fp4.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl, layers, ws, ws_need, t_gen = setup_workload(args.workload, dev)
+    r = measure(wl, layers, ws, args.steps, args.warmup)
     gemm_shapes = []
     for lin in wl.linears:
         if "fprop" in wl.passes:
@@ -236,91 +347,11 @@ def main():
             gemm_shapes.append((lin.M, lin.K, lin.N))
         if "wgrad" in wl.passes:
             gemm_shapes.append((lin.N, lin.K, lin.M))
-    ws_need = max(fp4.fp4_gemm_ws_bytes(*sh) for sh in gemm_shapes)
-    ws = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=dev)
     split_shapes = [sh for sh in gemm_shapes if fp4.fp4_gemm_ws_bytes(*sh) > 0]
-
-    stream = torch.cuda.current_stream()
-    ev = HipTimingEvent  # per-call timing events on the step's stream
-    Q = fp4
-
-    def step(record):
-        """One pass of the whole hot path; `record` collects (kind, bytes/flops, ev0, ev1).
-        X's two layouts (rowwise for fprop, transformed columnwise for wgrad) come from
-        one dual quantization, and so do dY's (rowwise SR for dgrad, transformed
-        columnwise SR for wgrad); each dual call includes its one-read amax pass."""
-        chain = [None]
-        for lin, inp, x, w, dy, b, o in layers:
-            M, N, K = lin.M, lin.N, lin.K
-            in_b = x.element_size()
-            one_d = 0.5 + 1 / 16  # code + scale bytes per element of a 1D layout
-
-            def timed(kind, amount, fn):
-                # calls are chained: a call's start event is the previous call's end
-                # event (the same point of the stream), one record per boundary
-                if chain[0] is None:
-                    chain[0] = ev()
-                    chain[0].record(stream)
-                e0, e1 = chain[0], ev()
-                fn()
-                e1.record(stream)
-                chain[0] = e1
-                record.append((kind, amount, e0, e1))
-
-            fprop, dgrad, wgrad = ("fprop" in wl.passes), ("dgrad" in wl.passes), ("wgrad" in wl.passes)
-            # X: rowwise (fprop) and/or transformed columnwise (wgrad)
-            if fprop and wgrad:
-                timed("quant", M * K * (in_b + 2 * one_d),
-                      lambda: Q.fp4_quantize_dual(x, Q.Q_RHT, inp.signs, 0, 0, 0, b.xq, b.xq_t))
-            elif fprop:
-                timed("quant", M * K * (in_b + one_d), lambda: Q.fp4_quantize(x, 0, 0, 0, 0, b.xq))
-            elif wgrad:
-                timed("quant", M * K * (in_b + one_d),
-                      lambda: Q.fp4_quantize(x, Q.Q_COLWISE | Q.Q_RHT, inp.signs, 0, 0, b.xq_t))
-            # W: 16x16 tiles, W and W^T
-            if fprop or dgrad:
-                timed("quant", N * K * (in_b + 2 * (0.5 + 1 / 256)), lambda: Q.fp4_quantize(w, Q.Q_2D, 0, 0, 0, b.wq,
-                                                                                           b.wq_t))
-            if fprop:
-                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm_ws(b.xq, b.wq, o["y"], ws))
-            # dY: rowwise SR (dgrad) and/or transformed columnwise SR (wgrad)
-            sd, od, ow = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
-            if dgrad and wgrad:
-                timed("quant", M * N * (in_b + 2 * one_d),
-                      lambda: Q.fp4_quantize_dual(dy, Q.Q_SR | Q.Q_RHT, inp.signs, sd, od, ow, b.dyq, b.dyq_t))
-            elif dgrad:
-                timed("quant", M * N * (in_b + one_d), lambda: Q.fp4_quantize(dy, Q.Q_SR, 0, sd, od, b.dyq))
-            elif wgrad:
-                timed("quant", M * N * (in_b + one_d),
-                      lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR, inp.signs, sd, ow, b.dyq_t))
-            if dgrad:
-                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm_ws(b.dyq, b.wq_t, o["dx"], ws))
-            if wgrad:
-                timed("gemm", 2.0 * M * N * K, lambda: Q.fp4_gemm_ws(b.dyq_t, b.xq_t, o["dw"], ws))
-
-    for _ in range(args.warmup):
-        step([])
-    torch.cuda.synchronize()
-    records = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(records)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    gemm_ms = sum(e0.elapsed_time(e1) for k, _, e0, e1 in records if k == "gemm")
-    gemm_flops = sum(f for k, f, _, _ in records if k == "gemm")
-    n_gemm = sum(1 for k, *_ in records if k == "gemm")
-    quant_ms = sum(e0.elapsed_time(e1) for k, _, e0, e1 in records if k == "quant")
-    quant_bytes = sum(f for k, f, _, _ in records if k == "quant")
-    step_flops = gemm_flops / args.steps
-    value = step_flops / (ms_per_step * 1e-3) / 1e12
-    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
 
     kernel_src = os.path.join(ROOT, "nvfp4_bit_microscaled_amd", "csrc", "gemm.hip")
     traffic = measured_traffic(kernel_src)
+    gemm_tflops = r["gemm_tflops"]
     roofline = {
         "bound": "mfma",
         "achieved": round(gemm_tflops, 2),
@@ -328,33 +359,36 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4),
         "traffic": traffic,
-        "kernel": "nvfp4 block-scaled GEMM (f16 MFMA on exactly dequantized E2M1xE4M3 operands); one fp4_gemm_ws "
-                  "call per pass: a persistent 256x256-tile launch, plus a 128x128-quarters launch when the tiles "
-                  "overrun whole rounds of the CUs by at most half a round, or split over K into a caller workspace "
-                  "and summed by a second launch when the plan for the shape takes a split",
+        "kernel": "nvfp4 block-scaled GEMM (f16 MFMA on exactly dequantized E2M1xE4M3 operands); the GEMM phase of "
+                  "each linear-layer call: a persistent 256x256-tile launch, plus a 128x128-quarters launch when the "
+                  "tiles overrun whole rounds of the CUs by at most half a round, or split over K into the caller "
+                  "workspace and summed by a second launch when the plan for the shape takes a split",
         "split_k_shapes": split_shapes,
         "workspace_bytes": ws_need,
-        "flops_per_call": gemm_flops / n_gemm,
-        "avg_call_ms": round(gemm_ms / n_gemm, 4),
+        "flops_per_call": r["gemm_flops"] / r["n_gemm"],
+        "avg_call_ms": round(r["gemm_ms"] / r["n_gemm"], 4),
         "frac_of_fp4_dense_peak": round(gemm_tflops / PEAK_FP4_MFMA_TFLOPS, 4),
+        "note": "exact NVFP4 products run on the f16 matrix path (one E8M0 scale per 32 K of the FP4/FP8 MFMAs cannot "
+                "carry two E4M3 block scales), whose dense peak, 2.5 PFLOP/s, is half the MI355X's dense FP8 rate; "
+                "the pages quote FP4 GEMMs at 2x (GB200) and 3x (GB300) the FP8 rate on Blackwell",
     }
 
     breakdown = [] if args.no_breakdown else quantize_breakdown(layers, wl)
-    hbm_rows = [r for r in breakdown if r["bound"] == "hbm"]
+    hbm_rows = [row for row in breakdown if row["bound"] == "hbm"]
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(layers, wl, args.cpu_sample_rows, step_flops)
+        cpu = cpu_baseline(layers, wl, args.cpu_sample_rows, r["step_flops"])
 
     lin0 = wl.linears[0]
     out = {
         "metric": "NVFP4 linear TFLOPS (fprop/dgrad/wgrad) + quantize GB/s, % of roofline, 1 GPU",
-        "value": round(value, 2),
+        "value": round(r["value"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -369,21 +403,45 @@ def main():
             "parallelism": "single GPU",
         },
         "quantize": {
-            "achieved_gbs": round(quant_gbs, 1),
+            "achieved_gbs": round(r["quant_gbs"], 1),
             "peak_gbs": PEAK_HBM_GBS,
-            "frac": round(quant_gbs / PEAK_HBM_GBS, 4),
-            "note": "algorithmic bytes (input read once + codes + scales of every layout written) per quantize call; the time includes the amax pass",
-            "ms_per_step": round(quant_ms / args.steps, 4),
+            "frac": round(r["quant_gbs"] / PEAK_HBM_GBS, 4),
+            "note": "algorithmic bytes (input read once + codes + scales of every layout written) per quantize phase "
+                    "of the linear calls; the time includes the amax pass",
+            "ms_per_step": round(r["quant_ms"] / args.steps, 4),
             "kernels": breakdown,
-            "hbm_bound_kernels_frac": round(sum(r["bytes"] for r in hbm_rows) / (sum(r["us"] for r in hbm_rows)
-                                                                                 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+            "hbm_bound_kernels_frac": round(sum(row["bytes"] for row in hbm_rows) / (sum(row["us"] for row in hbm_rows)
+                                                                                     * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
             if hbm_rows else None,
         },
-        "gemm_ms_per_step": round(gemm_ms / args.steps, 4),
+        "gemm_ms_per_step": round(r["gemm_ms"] / args.steps, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "input_generation_s": round(t_gen, 1),
     }
+    del layers, ws
+    torch.cuda.empty_cache()
+    if not args.no_other_workloads:
+        others = []
+        for name in ("fprop_8k", "wgrad_8k", "block_3b"):
+            if name == args.workload:
+                continue
+            owl, olayers, ows, _, ogen = setup_workload(name, dev)
+            o = measure(owl, olayers, ows, args.other_steps, 2)
+            others.append({
+                "workload": owl.description, "name": name, "steps": args.other_steps,
+                "ms_per_step": round(o["ms_per_step"], 4), "value": round(o["value"], 2), "unit": "TFLOP/s",
+                "gemm_avg_call_ms": round(o["gemm_ms"] / o["n_gemm"], 4),
+                "gemm_tflops": round(o["gemm_tflops"], 2),
+                "gemm_frac_f16_peak": round(o["gemm_tflops"] / PEAK_F16_MFMA_TFLOPS, 4),
+                "quantize_ms_per_step": round(o["quant_ms"] / args.other_steps, 4),
+                "quantize_gbs": round(o["quant_gbs"], 1),
+                "quantize_frac_hbm": round(o["quant_gbs"] / PEAK_HBM_GBS, 4),
+                "input_generation_s": round(ogen, 1),
+            })
+            del olayers, ows
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
 
 
@@ -470,16 +528,53 @@ def quantize_breakdown(layers, wl, reps=5):
     return rows
 
 
+def host_cpu():
+    """The host cores this process may use: its CPU affinity, further limited by a
+    cgroup CPU quota when one is set; with nproc and the CPU model for the record."""
+    n_all = os.cpu_count() or 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = n_all
+    quota = None
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = int(q) / int(period)
+    except (OSError, ValueError):
+        pass
+    usable = aff if quota is None else max(1, min(aff, int(quota)))
+    model = None
+    try:
+        model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")),
+                     None)
+    except OSError:
+        pass
+    return {"usable": usable, "nproc": n_all, "affinity": aff, "cgroup_quota": quota, "model": model}
+
+
 def cpu_baseline(layers, wl, sample_rows, step_flops):
-    """The oracle, untuned, on the host: full-tensor amax passes, quantization of a
-    sample of logical rows of every operand, and the binary64 GEMM reference on a
-    sample x sample block of each pass; each part extrapolated linearly to the step."""
+    """The oracle, untuned, on the host cores this process may use (its own threads
+    and the BLAS pool of the binary64 products both limited to that count):
+    full-tensor amax passes, quantization of a sample of logical rows of every
+    operand, and the binary64 GEMM reference on a sample x sample block of each pass;
+    each part extrapolated linearly to the step."""
+    from threadpoolctl import threadpool_limits
+
+    cpu = host_cpu()
+    with threadpool_limits(limits=cpu["usable"]):
+        out = _cpu_baseline(layers, wl, sample_rows, step_flops, cpu["usable"])
+    out["cores"] = cpu["usable"]
+    out["host"] = cpu
+    return out
+
+
+def _cpu_baseline(layers, wl, sample_rows, step_flops, threads):
     import numpy as np
 
     import oracle
     import workloads
 
-    threads = oracle.default_threads()
     _ = np.ones((256, 256)) @ np.ones((256, 256))  # start the BLAS thread pool outside the timed parts
     total_s = 0.0
     parts = []

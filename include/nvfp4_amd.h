@@ -1,12 +1,25 @@
 /*
  * nvfp4_amd.h -- C ABI of the MI355X (gfx950) NVFP4 linear-layer library.
  *
- * NVFP4, as the NVFP4-12B page describes it (q2bstudio blog, "NVIDIA ... 4-bit
- * pretraining with NVFP4, 12B Mamba-Transformer", paragraph 2): 4-bit E2M1
- * elements in blocks of 16, one E4M3 scale per block and one FP32 scale per
- * tensor; NVFP4 is used only for the GEMMs of linear layers; the recipe adds 2D
- * block scaling for weights, 16x16 random Hadamard transforms on the
- * weight-gradient operands and stochastic rounding on gradients only.
+ * Sources, cited by page and paragraph throughout (q2bstudio blog pages):
+ *   NVFP4-12B page   -- NVIDIA's 4-bit NVFP4 pretraining of a 12B hybrid
+ *                       Mamba-Transformer; paragraph 2 holds the format
+ *                       sentence (16-element blocks, one E4M3 scale per block,
+ *                       one FP32 scale per tensor), the GEMM-only sentence
+ *                       (NVFP4 is applied to the GEMMs of linear layers alone),
+ *                       the four-part recipe sentence (about 16% of linears kept
+ *                       in BF16, 16x16 random Hadamard transforms on the
+ *                       weight-gradient operands, 2D block scaling for weights,
+ *                       stochastic rounding on gradients only) and the
+ *                       throughput sentence (FP4 GEMMs at 2x / 3x FP8 on
+ *                       GB200 / GB300, half the operand bytes);
+ *   Quartet II page  -- "Quartet II: Pre-entrenamiento de LLMs en NVFP4";
+ *                       paragraph 1 holds the sentence on stochastic rounding
+ *                       as the way to unbiased gradient estimates, the MS-EDEN
+ *                       sentence (an unbiased routine for microscale formats
+ *                       with more than 2x lower error than stochastic rounding)
+ *                       and the sentence on linear layers quantized fully to
+ *                       NVFP4, forward and backward.
  *
  * Numerical definition (the pages give no formulas; this is the reading the
  * library implements, bit for bit):
@@ -36,10 +49,12 @@
  * stays on the device.
  *
  * Errors: arguments are checked before anything is enqueued; a failed check
- * returns a non-zero fp4_status and enqueues nothing.  A launch failure reports
- * FP4_ERR_HIP.  Faults that occur later on the device surface at the caller's
- * next synchronization.  Non-finite inputs are outside the contract: their
- * results are unspecified.
+ * returns a non-zero fp4_status and enqueues nothing.  A launch that fails
+ * reports FP4_ERR_HIP (each launch's own status: an error left pending by the
+ * caller's earlier HIP work is neither reported nor cleared); the launches
+ * already enqueued by that call stay enqueued.  Faults that occur later on the
+ * device surface at the caller's next synchronization.  Non-finite inputs are
+ * outside the contract: their results are unspecified.
  */
 #ifndef NVFP4_AMD_H
 #define NVFP4_AMD_H
@@ -93,35 +108,55 @@ typedef struct fp4_tensor {
   int32_t two_d;
 } fp4_tensor;
 
-/* Bytes needed for the codes and scales of a rows x cols quantized tensor. */
+/* Bytes of the codes and scales of a rows x cols quantized tensor (the layout of
+ * fp4_tensor above: 0.5 B per element plus one E4M3 byte per 16-block, or per 16x16
+ * tile with two_d; NVFP4-12B page, paragraph 2, format and throughput sentences).
+ * Pure host arithmetic.  FP4_ERR_NULL for a NULL output, FP4_ERR_SHAPE for a
+ * negative size or cols not a multiple of 16. */
 FP4_API fp4_status fp4_tensor_bytes(int64_t rows, int64_t cols, int32_t two_d, size_t *codes_bytes, size_t *scales_bytes);
 
-/* Tensor amax of the logical tensor of x ([rows][cols] with row stride ld elements):
- * x itself, or x^T with FP4_Q_COLWISE; with FP4_Q_RHT the amax is taken after the
- * transform (blocks along the logical rows).  Writes one float at amax_out.
+/* Tensor amax -- the magnitude the per-tensor FP32 scale is taken from (NVFP4-12B
+ * page, paragraph 2, format sentence) -- of the logical tensor of x ([rows][cols]
+ * with row stride ld elements): x itself, or x^T with FP4_Q_COLWISE; with
+ * FP4_Q_RHT the amax is taken after the 16-point transform of the recipe sentence
+ * (blocks along the logical rows).  Writes one float at amax_out (device).
  * Needs: the blocked dimension (cols, or rows with COLWISE) a multiple of 16 when
- * FP4_Q_RHT is set; ld >= cols; x 16-byte aligned and ld a multiple of 8 elements. */
+ * FP4_Q_RHT is set; ld >= cols; x 16-byte aligned and ld a multiple of 8 elements.
+ * Errors: FP4_ERR_MODE (other flags), FP4_ERR_DTYPE, FP4_ERR_SHAPE, FP4_ERR_ALIGN,
+ * FP4_ERR_NULL (x with elements, or amax_out). */
 FP4_API fp4_status fp4_amax(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
                     uint32_t rht_signs, float *amax_out, hipStream_t stream);
 
-/* Quantize the logical tensor L of x (L = x, or x^T with FP4_Q_COLWISE) into *out
- * (out->rows x out->cols must equal L's shape; out->two_d must match FP4_Q_2D).
+/* NVFP4 quantization (NVFP4-12B page, paragraph 2: format sentence for the
+ * blocks and scales; recipe sentence for 2D weight scaling, the 16x16 random
+ * Hadamard transform of weight-gradient operands and stochastic rounding of
+ * gradients; Quartet II page, paragraph 1, for the unbiasedness stochastic
+ * rounding provides).  Quantizes the logical tensor L of x (L = x, or x^T with
+ * FP4_Q_COLWISE) into *out (out->rows x out->cols must equal L's shape;
+ * out->two_d must match FP4_Q_2D).
  * Without FP4_Q_AMAX_GIVEN the tensor amax is computed first into out->amax (the
  * amax pass keeps its per-workgroup maxima in out->codes, at most 8 KB, before the
  * codes are written; x must not overlap out->codes, as for any output).
  * out_t (FP4_Q_2D only, nullable) also receives L^T quantized with the same tile
  * scales: its codes and scales are the exact transposes of out's.
+ * rht_signs: the transform's 16-bit sign mask (FP4_Q_RHT); seed, offset: the
+ * Philox stream of stochastic rounding (FP4_Q_SR).
  * Modes: 1D with any of COLWISE, RHT, SR; 2D with COLWISE only (no RHT, no SR).
  * Needs: L's cols a multiple of 16 (and L's rows too for 2D); x 16-byte aligned,
  * ld a multiple of 8 elements; codes 16-byte and scales 8-byte aligned; with
- * COLWISE or 2D, x at most 16776960 rows (FP4_ERR_SHAPE otherwise). */
+ * COLWISE or 2D, x at most 16776960 rows (FP4_ERR_SHAPE otherwise).
+ * Errors: FP4_ERR_MODE, FP4_ERR_DTYPE, FP4_ERR_SHAPE, FP4_ERR_ALIGN, FP4_ERR_NULL,
+ * FP4_ERR_MISMATCH (descriptor shape or two_d), FP4_ERR_HIP. */
 FP4_API fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
                         uint32_t rht_signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
                         const fp4_tensor *out_t, hipStream_t stream);
 
-/* Both quantized layouts of one tensor x [rows][cols] in one call (the pair the
- * backward pass needs of dy -- dgrad takes dy rowwise, wgrad takes dy^T -- and the
- * pair fprop and wgrad need of x), with both tensor amaxes taken in one read of x:
+/* Both quantized layouts of one tensor x [rows][cols] in one call: the pair the
+ * backward pass needs of dy (dgrad takes dy rowwise with stochastic rounding, wgrad
+ * takes dy^T transformed with stochastic rounding) and the pair fprop and wgrad need
+ * of x (rowwise nearest-even, and x^T transformed) -- NVFP4-12B page, paragraph 2,
+ * recipe sentence, for which operand gets which treatment.  Both tensor amaxes are
+ * taken in one read of x:
  *   out_rows: x quantized 1D along its rows ([rows][cols], as fp4_quantize with flags 0
  *             or FP4_Q_SR, Philox offset offset_rows);
  *   out_cols: x^T quantized 1D (blocks down the columns of x, [cols][rows]), after the
@@ -130,62 +165,104 @@ FP4_API fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, in
  * Codes, scales and amaxes are bit-identical to those two fp4_quantize calls.
  * flags: FP4_Q_SR (both layouts stochastic), FP4_Q_RHT (columnwise layout
  * transformed), FP4_Q_AMAX_GIVEN (out_rows->amax and out_cols->amax already hold the
- * two tensor amaxes; otherwise both are computed first, in one read of x, then each
- * layout is written by its own kernel; the amax pass keeps its per-workgroup
- * maxima in out_rows->codes before the codes are written).
- * Needs: rows and cols multiples of 16; x 16-byte aligned, ld a multiple of 8. */
+ * two tensor amaxes; otherwise both are computed first, in one read of x; the amax
+ * pass keeps its per-workgroup maxima in out_rows->codes before the codes are
+ * written).
+ * Needs: rows and cols multiples of 16; x 16-byte aligned, ld a multiple of 8.
+ * Errors: as fp4_quantize. */
 FP4_API fp4_status fp4_quantize_dual(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
                                      uint32_t flags, uint32_t rht_signs, uint64_t seed, uint64_t offset_rows,
                                      uint64_t offset_cols, const fp4_tensor *out_rows, const fp4_tensor *out_cols,
                                      hipStream_t stream);
 
-/* Block-scaled GEMM with FP32 accumulation: C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k]
+/* Block-scaled GEMM with FP32 accumulation -- the operation NVFP4 is applied to
+ * (NVFP4-12B page, paragraph 2, GEMM-only sentence; the format sentence fixes the
+ * per-block and per-tensor scales each operand carries):
+ *   C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k]
  * for A [M][K] and B [N][K] (both K-major, M = a->rows, N = b->rows, K = a->cols =
  * b->cols, K a multiple of 16), written as fp32 or bf16 (nearest-even) with row
- * stride ldc elements.  The products of the dequantized operands are exact; the
- * accumulation is FP32. */
+ * stride ldc elements into c (device, caller-owned).  The products of the
+ * dequantized operands are exact; the accumulation is FP32.
+ * Errors: FP4_ERR_NULL, FP4_ERR_MISMATCH (K differs), FP4_ERR_SHAPE (K % 16, ldc < N,
+ * a 2D operand's rows not a multiple of 16), FP4_ERR_DTYPE, FP4_ERR_ALIGN (c not
+ * aligned to its element), FP4_ERR_HIP. */
 FP4_API fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                     hipStream_t stream);
 
-/* fp4_gemm with a caller workspace for split-K.  When a product has few 256x256
- * output tiles for the CUs and a long K (a weight-gradient GEMM over many tokens
- * with a small weight), each tile's K range is split into S parts that run as
- * separate work items writing raw fp32 partial tiles into ws, and a second kernel
- * sums the S partials of each tile in split order, applies the decode scales and
- * writes C.  Same definition and tolerance as fp4_gemm (the split adds S-1 fp32
- * additions per output).  S comes from a fixed plan of (M, N, K) on this GPU;
- * fp4_gemm_ws_bytes gives the workspace the plan needs (0 when it takes no split).
- * With ws_bytes below that, or a shape off the 256-K main path, this is fp4_gemm.
+/* fp4_gemm (same definition; NVFP4-12B page, paragraph 2, GEMM-only sentence) with
+ * a caller workspace for split-K.  When a product has few 256x256 output tiles for
+ * the CUs and a long K (a weight-gradient GEMM over many tokens with a small
+ * weight), each tile's K range is split into S parts that run as separate work
+ * items writing raw fp32 partial tiles into ws, and a second kernel sums the S
+ * partials of each tile in split order, applies the decode scales and writes C.
+ * The split adds S-1 fp32 additions per output.  S comes from a fixed plan of
+ * (M, N, K) on this GPU; fp4_gemm_ws_bytes gives the workspace the plan needs (0
+ * when it takes no split).  With ws_bytes below that, or a shape off the 256-K main
+ * path, this is fp4_gemm.
  * ws: device memory, 16-byte aligned, owned by the caller, overwritten; calls that
- * share a workspace must be ordered on one stream. */
+ * share a workspace must be ordered on one stream.  Errors: as fp4_gemm, plus
+ * FP4_ERR_NULL / FP4_ERR_ALIGN for a non-empty workspace that is NULL / misaligned. */
 FP4_API fp4_status fp4_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes fp4_gemm_ws uses for an M x N x K product (0: no split). */
+/* Workspace bytes fp4_gemm_ws uses for an M x N x K product (0: no split).  Pure
+ * host arithmetic on the device's CU count.  FP4_ERR_NULL, FP4_ERR_SHAPE. */
 FP4_API fp4_status fp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes);
 
-/* Linear layer y = x . w^T with x [M][K], w [N][K] (dtype), y [M][N] (y_dtype).
- * Forward: x 1D nearest-even into xq ([M][K]); w 2D (16x16) nearest-even into wq
- * ([N][K]); wq_t (nullable, [K][N]) receives w^T with the same tile scales, for the
- * backward pass.  Then y = gemm(xq, wq).  M, N, K multiples of 16. */
+/* Workspace bytes the linear-layer calls below need for a layer of M tokens, K
+ * input and N output features: the largest split plan of its three GEMMs (fprop
+ * M x N x K, dgrad M x K x N, wgrad N x K x M).  0 when none splits.  With less
+ * workspace the linear calls still run, without the split.  FP4_ERR_NULL,
+ * FP4_ERR_SHAPE. */
+FP4_API fp4_status fp4_linear_ws_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes);
+
+/* The linear-layer calls: the recipe of the NVFP4-12B page, paragraph 2 (GEMM-only
+ * sentence: NVFP4 is applied to the linear layers' GEMMs; recipe sentence: 2D block
+ * scaling for weights, 16x16 random Hadamard transforms on the weight-gradient
+ * operands, stochastic rounding on gradients only), with every operand of every
+ * GEMM quantized to NVFP4, forward and backward (Quartet II page, paragraph 1, the
+ * sentence on fully NVFP4 linear layers).  Common arguments:
+ *   dtype        input element type (bf16 or fp32); all inputs contiguous row-major;
+ *   ws, ws_bytes caller workspace for the GEMMs' split-K partial tiles
+ *                (fp4_linear_ws_bytes; NULL / 0 runs without splits), overwritten;
+ *   marks        nullable array of HIP events the call records on `stream` between
+ *                its phases, for callers that time them (the count is given per
+ *                call); the caller creates and owns them.
+ * M, N, K must be multiples of 16.  Errors: as the quantize and GEMM calls they
+ * compose; every check runs before the first launch. */
+
+/* Forward: y = x . w^T with x [M][K], w [N][K], y [M][N] (y_dtype).
+ *   x -> xq ([M][K]) 1D nearest-even; with xq_t (nullable, [K][M]) x^T is also
+ *   quantized, after the 16-point transform with rht_signs, nearest-even -- the
+ *   wgrad operand the backward pass then reads instead of x -- both layouts in one
+ *   fp4_quantize_dual (one read of x);
+ *   w -> wq ([N][K]) 2D (16x16) nearest-even, and wq_t (nullable, [K][N]) w^T with
+ *   the same tile scales, for dgrad;
+ *   y = gemm(xq, wq).
+ * marks (2): after x's quantization, after w's (before the GEMM). */
 FP4_API fp4_status fp4_linear_fprop(const void *x, const void *w, fp4_dtype dtype, void *y, fp4_dtype y_dtype, int64_t M,
-                            int64_t N, int64_t K, const fp4_tensor *xq, const fp4_tensor *wq,
-                            const fp4_tensor *wq_t, hipStream_t stream);
+                                    int64_t N, int64_t K, uint32_t rht_signs, const fp4_tensor *xq,
+                                    const fp4_tensor *xq_t, const fp4_tensor *wq, const fp4_tensor *wq_t, void *ws,
+                                    size_t ws_bytes, const hipEvent_t *marks, hipStream_t stream);
 
-/* Input gradient dx = dy . w with dy [M][N] (dtype), dx [M][K] (dx_dtype): dy is
- * quantized 1D with stochastic rounding (seed, offset) into dyq ([M][N]) and
- * multiplied with the forward pass's 2D-quantized w^T (wq_t, [K][N]). */
+/* Input gradient dx = dy . w with dy [M][N], dx [M][K] (dx_dtype): dy is quantized
+ * 1D with stochastic rounding (seed, offset) into dyq ([M][N]) and multiplied with
+ * the forward pass's 2D-quantized w^T (wq_t, [K][N]).
+ * marks (1): after dy's quantization (before the GEMM). */
 FP4_API fp4_status fp4_linear_dgrad(const void *dy, fp4_dtype dtype, const fp4_tensor *wq_t, void *dx, fp4_dtype dx_dtype,
-                            int64_t M, int64_t N, int64_t K, uint64_t seed, uint64_t offset,
-                            const fp4_tensor *dyq, hipStream_t stream);
+                                    int64_t M, int64_t N, int64_t K, uint64_t seed, uint64_t offset,
+                                    const fp4_tensor *dyq, void *ws, size_t ws_bytes, const hipEvent_t *marks,
+                                    hipStream_t stream);
 
-/* Weight gradient dw = dy^T . x with dy [M][N], x [M][K] (dtype), dw [N][K] (dw_dtype):
- * both operands are quantized transposed (blocks along the M tokens) after the random
- * Hadamard transform with the same signs; dy with stochastic rounding (seed, offset)
- * into dyq_t ([N][M]), x nearest-even into xq_t ([K][M]). */
+/* Weight gradient dw = dy^T . x with dy [M][N], x [M][K], dw [N][K] (dw_dtype):
+ * both operands are quantized transposed (blocks along the M tokens) after the
+ * random Hadamard transform with the same signs; dy with stochastic rounding (seed,
+ * offset) into dyq_t ([N][M]), x nearest-even into xq_t ([K][M]).
+ * marks (2): after dy^T's quantization, after x^T's (before the GEMM). */
 FP4_API fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dtype, void *dw, fp4_dtype dw_dtype,
-                            int64_t M, int64_t N, int64_t K, uint32_t rht_signs, uint64_t seed, uint64_t offset,
-                            const fp4_tensor *dyq_t, const fp4_tensor *xq_t, hipStream_t stream);
+                                    int64_t M, int64_t N, int64_t K, uint32_t rht_signs, uint64_t seed,
+                                    uint64_t offset, const fp4_tensor *dyq_t, const fp4_tensor *xq_t, void *ws,
+                                    size_t ws_bytes, const hipEvent_t *marks, hipStream_t stream);
 
 /* Backward pass of the linear layer y = x . w^T (x [M][K], w [N][K], dy [M][N]):
  *   dx = dy . w    (dx [M][K], dx_dtype)   and   dw = dy^T . x   (dw [N][K], dw_dtype).
@@ -194,17 +271,19 @@ FP4_API fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dty
  * with the 16-point transform (rht_signs) and stochastic rounding at offset_wgrad
  * into dyq_t ([N][M]).  wq_t ([K][N], 2D) is the forward pass's transposed weight.
  * x^T quantized with the same transform ([K][M], nearest-even) is read from xq_t;
- * if x is not NULL it is first quantized from x (dtype) into xq_t, otherwise xq_t
- * must already hold it (for instance from fp4_quantize_dual of x in the forward
- * pass).  The results equal fp4_linear_dgrad and fp4_linear_wgrad with the same
- * seeds, offsets and signs.  M, N, K multiples of 16. */
+ * if x is not NULL it is first quantized from x into xq_t, otherwise xq_t must
+ * already hold it (fp4_linear_fprop with xq_t writes it).  The results equal
+ * fp4_linear_dgrad and fp4_linear_wgrad with the same seeds, offsets and signs.
+ * marks (3): after dy's quantization, after x^T's (at the same point when x is
+ * NULL), after the dgrad GEMM (before the wgrad GEMM). */
 FP4_API fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, const fp4_tensor *wq_t,
                                        void *dx, fp4_dtype dx_dtype, void *dw, fp4_dtype dw_dtype, int64_t M, int64_t N,
                                        int64_t K, uint32_t rht_signs, uint64_t seed, uint64_t offset_dgrad,
                                        uint64_t offset_wgrad, const fp4_tensor *dyq, const fp4_tensor *dyq_t,
-                                       const fp4_tensor *xq_t, hipStream_t stream);
+                                       const fp4_tensor *xq_t, void *ws, size_t ws_bytes, const hipEvent_t *marks,
+                                       hipStream_t stream);
 
-/* A short static description of a status code. */
+/* A short static description of a status code (never NULL). */
 FP4_API const char *fp4_status_string(fp4_status status);
 
 #ifdef __cplusplus

@@ -27,8 +27,8 @@ STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_ALIGN"
 
 # every symbol the header declares
 EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_gemm", "fp4_gemm_ws",
-           "fp4_gemm_ws_bytes", "fp4_linear_fprop", "fp4_linear_dgrad", "fp4_linear_wgrad", "fp4_linear_backward",
-           "fp4_status_string")
+           "fp4_gemm_ws_bytes", "fp4_linear_ws_bytes", "fp4_linear_fprop", "fp4_linear_dgrad", "fp4_linear_wgrad",
+           "fp4_linear_backward", "fp4_status_string")
 
 
 class Fp4Error(RuntimeError):
@@ -57,6 +57,7 @@ def load():
     vp, i64, u32, u64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32
     tp = ctypes.POINTER(fp4_tensor)
     sz = ctypes.POINTER(ctypes.c_size_t)
+    szv = ctypes.c_size_t
     sigs = {
         "fp4_tensor_bytes": [i64, i64, i32, sz, sz],
         "fp4_amax": [vp, i32, i64, i64, i64, u32, u32, vp, vp],
@@ -65,10 +66,12 @@ def load():
         "fp4_gemm": [tp, tp, vp, i32, i64, vp],
         "fp4_gemm_ws": [tp, tp, vp, i32, i64, vp, ctypes.c_size_t, vp],
         "fp4_gemm_ws_bytes": [i64, i64, i64, sz],
-        "fp4_linear_fprop": [vp, vp, i32, vp, i32, i64, i64, i64, tp, tp, tp, vp],
-        "fp4_linear_dgrad": [vp, i32, tp, vp, i32, i64, i64, i64, u64, u64, tp, vp],
-        "fp4_linear_wgrad": [vp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, tp, tp, vp],
-        "fp4_linear_backward": [vp, vp, i32, tp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, u64, tp, tp, tp, vp],
+        "fp4_linear_ws_bytes": [i64, i64, i64, sz],
+        "fp4_linear_fprop": [vp, vp, i32, vp, i32, i64, i64, i64, u32, tp, tp, tp, tp, vp, szv, vp, vp],
+        "fp4_linear_dgrad": [vp, i32, tp, vp, i32, i64, i64, i64, u64, u64, tp, vp, szv, vp, vp],
+        "fp4_linear_wgrad": [vp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, tp, tp, vp, szv, vp, vp],
+        "fp4_linear_backward": [vp, vp, i32, tp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, u64, tp, tp, tp, vp,
+                                szv, vp, vp],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -174,44 +177,78 @@ def fp4_gemm_ws(a: QTensor, b: QTensor, c: torch.Tensor, ws: torch.Tensor = None
                                              _stream(stream)))
 
 
-def fp4_linear_fprop(x, w, y, xq: QTensor, wq: QTensor, wq_t: QTensor = None, stream=None):
+def fp4_linear_ws_bytes(M: int, N: int, K: int) -> int:
+    n = ctypes.c_size_t()
+    _check("fp4_linear_ws_bytes", load().fp4_linear_ws_bytes(M, N, K, ctypes.byref(n)))
+    return n.value
+
+
+def _ws(ws):
+    """(pointer, bytes) of an optional device byte tensor used as a workspace."""
+    if ws is None:
+        return None, 0
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _marks(marks):
+    """An optional list of HIP event handles (ints) as a C array."""
+    if marks is None:
+        return None
+    return (ctypes.c_void_p * len(marks))(*marks)
+
+
+def fp4_linear_fprop(x, w, y, xq: QTensor, wq: QTensor, wq_t: QTensor = None, xq_t: QTensor = None, rht_signs: int = 0,
+                     ws=None, marks=None, stream=None):
+    """xq_t (optional): x^T quantized after the 16-point transform with rht_signs, in
+    the same read of x as xq.  ws: optional device byte tensor (fp4_linear_ws_bytes).
+    marks: optional list of 2 HIP event handles recorded between the phases."""
     M, K = x.shape
     N = w.shape[0]
     assert x.dtype == w.dtype and x.is_contiguous() and w.is_contiguous() and y.is_contiguous()
-    _check("fp4_linear_fprop", load().fp4_linear_fprop(x.data_ptr(), w.data_ptr(), _dtype(x), y.data_ptr(), _dtype(y),
-                                                       M, N, K, xq.desc, wq.desc,
-                                                       wq_t.desc if wq_t is not None else None, _stream(stream)))
+    wp, wb = _ws(ws)
+    _check("fp4_linear_fprop", load().fp4_linear_fprop(
+        x.data_ptr(), w.data_ptr(), _dtype(x), y.data_ptr(), _dtype(y), M, N, K, rht_signs, xq.desc,
+        xq_t.desc if xq_t is not None else None, wq.desc, wq_t.desc if wq_t is not None else None, wp, wb,
+        _marks(marks), _stream(stream)))
 
 
-def fp4_linear_dgrad(dy, wq_t: QTensor, dx, seed: int, offset: int, dyq: QTensor, stream=None):
+def fp4_linear_dgrad(dy, wq_t: QTensor, dx, seed: int, offset: int, dyq: QTensor, ws=None, marks=None, stream=None):
     M, N = dy.shape
     K = dx.shape[1]
     assert dy.is_contiguous() and dx.is_contiguous()
+    wp, wb = _ws(ws)
     _check("fp4_linear_dgrad", load().fp4_linear_dgrad(dy.data_ptr(), _dtype(dy), wq_t.desc, dx.data_ptr(),
-                                                       _dtype(dx), M, N, K, seed, offset, dyq.desc, _stream(stream)))
+                                                       _dtype(dx), M, N, K, seed, offset, dyq.desc, wp, wb,
+                                                       _marks(marks), _stream(stream)))
 
 
-def fp4_linear_wgrad(dy, x, dw, rht_signs: int, seed: int, offset: int, dyq_t: QTensor, xq_t: QTensor, stream=None):
+def fp4_linear_wgrad(dy, x, dw, rht_signs: int, seed: int, offset: int, dyq_t: QTensor, xq_t: QTensor, ws=None,
+                     marks=None, stream=None):
     M, N = dy.shape
     K = x.shape[1]
     assert dy.dtype == x.dtype and dy.is_contiguous() and x.is_contiguous() and dw.is_contiguous()
+    wp, wb = _ws(ws)
     _check("fp4_linear_wgrad", load().fp4_linear_wgrad(dy.data_ptr(), x.data_ptr(), _dtype(dy), dw.data_ptr(),
                                                        _dtype(dw), M, N, K, rht_signs, seed, offset, dyq_t.desc,
-                                                       xq_t.desc, _stream(stream)))
+                                                       xq_t.desc, wp, wb, _marks(marks), _stream(stream)))
 
 
 def fp4_linear_backward(dy, x, wq_t: QTensor, dx, dw, rht_signs: int, seed: int, offset_dgrad: int,
-                        offset_wgrad: int, dyq: QTensor, dyq_t: QTensor, xq_t: QTensor, stream=None):
-    """x may be None when xq_t already holds the transformed, transposed x."""
+                        offset_wgrad: int, dyq: QTensor, dyq_t: QTensor, xq_t: QTensor, ws=None, marks=None,
+                        stream=None):
+    """x may be None when xq_t already holds the transformed, transposed x (for
+    instance from fp4_linear_fprop with xq_t).  marks: optional list of 3 HIP event
+    handles."""
     M, N = dy.shape
     K = dx.shape[1]
     assert dy.is_contiguous() and dx.is_contiguous() and dw.is_contiguous()
     if x is not None:
         assert x.dtype == dy.dtype and x.is_contiguous()
+    wp, wb = _ws(ws)
     _check("fp4_linear_backward", load().fp4_linear_backward(
         dy.data_ptr(), x.data_ptr() if x is not None else None, _dtype(dy), wq_t.desc, dx.data_ptr(), _dtype(dx),
         dw.data_ptr(), _dtype(dw), M, N, K, rht_signs, seed, offset_dgrad, offset_wgrad, dyq.desc, dyq_t.desc,
-        xq_t.desc, _stream(stream)))
+        xq_t.desc, wp, wb, _marks(marks), _stream(stream)))
 
 
 class LinearBuffers:

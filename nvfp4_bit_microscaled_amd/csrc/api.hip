@@ -67,6 +67,18 @@ fp4_status check_gemm(const fp4_tensor *a, const fp4_tensor *b, const void *c, f
   return FP4_OK;
 }
 
+// The workspace of the GEMMs' split-K partial tiles: empty, or 16-byte aligned.
+fp4_status check_ws(const void *ws, size_t ws_bytes) {
+  if (ws_bytes > 0 && !ws) return FP4_ERR_NULL;
+  if (ws_bytes > 0 && !aligned(ws, 16)) return FP4_ERR_ALIGN;
+  return FP4_OK;
+}
+
+// Record the caller's phase event i (if the caller passed events) on the stream.
+hipError_t mark(const hipEvent_t *marks, int i, hipStream_t stream) {
+  return marks ? hipEventRecord(marks[i], stream) : hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,58 +144,79 @@ fp4_status fp4_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
                        size_t ws_bytes, hipStream_t stream) {
   fp4_status s = check_gemm(a, b, c, c_dtype, ldc);
   if (s != FP4_OK) return s;
-  if (ws_bytes > 0 && (!ws || !aligned(ws, 16))) return ws ? FP4_ERR_ALIGN : FP4_ERR_NULL;
+  if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
   return from_hip(nvfp4::launch_gemm_ws(a, b, c, c_dtype, ldc, ws, ws_bytes, stream));
 }
 
+fp4_status fp4_linear_ws_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes) {
+  if (!bytes) return FP4_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
+  const size_t f = nvfp4::gemm_ws_bytes(M, N, K), d = nvfp4::gemm_ws_bytes(M, K, N), w = nvfp4::gemm_ws_bytes(N, K, M);
+  *bytes = f > d ? (f > w ? f : w) : (d > w ? d : w);
+  return FP4_OK;
+}
+
 fp4_status fp4_linear_fprop(const void *x, const void *w, fp4_dtype dtype, void *y, fp4_dtype y_dtype, int64_t M,
-                            int64_t N, int64_t K, const fp4_tensor *xq, const fp4_tensor *wq,
-                            const fp4_tensor *wq_t, hipStream_t stream) {
+                            int64_t N, int64_t K, uint32_t rht_signs, const fp4_tensor *xq, const fp4_tensor *xq_t,
+                            const fp4_tensor *wq, const fp4_tensor *wq_t, void *ws, size_t ws_bytes,
+                            const hipEvent_t *marks, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
   fp4_status s;
   if ((s = check_quantize(x, dtype, M, K, K, 0, xq, nullptr)) != FP4_OK) return s;
+  if (xq_t && (s = check_tensor(xq_t, K, M, 0)) != FP4_OK) return s;
   if ((s = check_quantize(w, dtype, N, K, K, FP4_Q_2D, wq, wq_t)) != FP4_OK) return s;
   if ((s = check_gemm(xq, wq, y, y_dtype, N)) != FP4_OK) return s;
-  hipError_t e = nvfp4::launch_quantize(x, dtype, M, K, K, 0, 0, 0, 0, xq, nullptr, stream);
+  if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
+  hipError_t e = xq_t ? nvfp4::launch_quantize_dual(x, dtype, M, K, K, FP4_Q_RHT, rht_signs & 0xFFFFu, 0, 0, 0, xq,
+                                                    xq_t, stream)
+                      : nvfp4::launch_quantize(x, dtype, M, K, K, 0, 0, 0, 0, xq, nullptr, stream);
+  if (e == hipSuccess) e = mark(marks, 0, stream);
   if (e == hipSuccess) e = nvfp4::launch_quantize(w, dtype, N, K, K, FP4_Q_2D, 0, 0, 0, wq, wq_t, stream);
-  if (e == hipSuccess) e = nvfp4::launch_gemm(xq, wq, y, y_dtype, N, stream);
+  if (e == hipSuccess) e = mark(marks, 1, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm_ws(xq, wq, y, y_dtype, N, ws, ws_bytes, stream);
   return from_hip(e);
 }
 
 fp4_status fp4_linear_dgrad(const void *dy, fp4_dtype dtype, const fp4_tensor *wq_t, void *dx, fp4_dtype dx_dtype,
-                            int64_t M, int64_t N, int64_t K, uint64_t seed, uint64_t offset,
-                            const fp4_tensor *dyq, hipStream_t stream) {
+                            int64_t M, int64_t N, int64_t K, uint64_t seed, uint64_t offset, const fp4_tensor *dyq,
+                            void *ws, size_t ws_bytes, const hipEvent_t *marks, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
   fp4_status s;
   if ((s = check_quantize(dy, dtype, M, N, N, FP4_Q_SR, dyq, nullptr)) != FP4_OK) return s;
   if ((s = check_tensor(wq_t, K, N, 1)) != FP4_OK) return s;
   if ((s = check_gemm(dyq, wq_t, dx, dx_dtype, K)) != FP4_OK) return s;
+  if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
   hipError_t e = nvfp4::launch_quantize(dy, dtype, M, N, N, FP4_Q_SR, 0, seed, offset, dyq, nullptr, stream);
-  if (e == hipSuccess) e = nvfp4::launch_gemm(dyq, wq_t, dx, dx_dtype, K, stream);
+  if (e == hipSuccess) e = mark(marks, 0, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm_ws(dyq, wq_t, dx, dx_dtype, K, ws, ws_bytes, stream);
   return from_hip(e);
 }
 
 fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dtype, void *dw, fp4_dtype dw_dtype,
                             int64_t M, int64_t N, int64_t K, uint32_t rht_signs, uint64_t seed, uint64_t offset,
-                            const fp4_tensor *dyq_t, const fp4_tensor *xq_t, hipStream_t stream) {
+                            const fp4_tensor *dyq_t, const fp4_tensor *xq_t, void *ws, size_t ws_bytes,
+                            const hipEvent_t *marks, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
   const uint32_t fdy = FP4_Q_COLWISE | FP4_Q_RHT | FP4_Q_SR, fx = FP4_Q_COLWISE | FP4_Q_RHT;
   fp4_status s;
   if ((s = check_quantize(dy, dtype, M, N, N, fdy, dyq_t, nullptr)) != FP4_OK) return s;
   if ((s = check_quantize(x, dtype, M, K, K, fx, xq_t, nullptr)) != FP4_OK) return s;
   if ((s = check_gemm(dyq_t, xq_t, dw, dw_dtype, K)) != FP4_OK) return s;
+  if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
   const uint32_t signs = rht_signs & 0xFFFFu;
   hipError_t e = nvfp4::launch_quantize(dy, dtype, M, N, N, fdy, signs, seed, offset, dyq_t, nullptr, stream);
+  if (e == hipSuccess) e = mark(marks, 0, stream);
   if (e == hipSuccess) e = nvfp4::launch_quantize(x, dtype, M, K, K, fx, signs, 0, 0, xq_t, nullptr, stream);
-  if (e == hipSuccess) e = nvfp4::launch_gemm(dyq_t, xq_t, dw, dw_dtype, K, stream);
+  if (e == hipSuccess) e = mark(marks, 1, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm_ws(dyq_t, xq_t, dw, dw_dtype, K, ws, ws_bytes, stream);
   return from_hip(e);
 }
 
 fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, const fp4_tensor *wq_t, void *dx,
                                fp4_dtype dx_dtype, void *dw, fp4_dtype dw_dtype, int64_t M, int64_t N, int64_t K,
                                uint32_t rht_signs, uint64_t seed, uint64_t offset_dgrad, uint64_t offset_wgrad,
-                               const fp4_tensor *dyq, const fp4_tensor *dyq_t, const fp4_tensor *xq_t,
-                               hipStream_t stream) {
+                               const fp4_tensor *dyq, const fp4_tensor *dyq_t, const fp4_tensor *xq_t, void *ws,
+                               size_t ws_bytes, const hipEvent_t *marks, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
   fp4_status s;
   if ((s = check_input(dy, dtype, M, N, N)) != FP4_OK) return s;
@@ -194,13 +227,17 @@ fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, c
   if ((s = check_tensor(wq_t, K, N, 1)) != FP4_OK) return s;
   if ((s = check_gemm(dyq, wq_t, dx, dx_dtype, K)) != FP4_OK) return s;
   if ((s = check_gemm(dyq_t, xq_t, dw, dw_dtype, K)) != FP4_OK) return s;
+  if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
   const uint32_t signs = rht_signs & 0xFFFFu;
   hipError_t e = nvfp4::launch_quantize_dual(dy, dtype, M, N, N, FP4_Q_SR | FP4_Q_RHT, signs, seed, offset_dgrad,
                                              offset_wgrad, dyq, dyq_t, stream);
+  if (e == hipSuccess) e = mark(marks, 0, stream);
   if (e == hipSuccess && x)
     e = nvfp4::launch_quantize(x, dtype, M, K, K, FP4_Q_COLWISE | FP4_Q_RHT, signs, 0, 0, xq_t, nullptr, stream);
-  if (e == hipSuccess) e = nvfp4::launch_gemm(dyq, wq_t, dx, dx_dtype, K, stream);
-  if (e == hipSuccess) e = nvfp4::launch_gemm(dyq_t, xq_t, dw, dw_dtype, K, stream);
+  if (e == hipSuccess) e = mark(marks, 1, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm_ws(dyq, wq_t, dx, dx_dtype, K, ws, ws_bytes, stream);
+  if (e == hipSuccess) e = mark(marks, 2, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm_ws(dyq_t, xq_t, dw, dw_dtype, K, ws, ws_bytes, stream);
   return from_hip(e);
 }
 

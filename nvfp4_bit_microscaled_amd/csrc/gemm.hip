@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -298,15 +299,20 @@ __device__ __forceinline__ u32x4 make_rsrc(const void *p, uint32_t bytes) {
 }
 
 // 16-byte DMA from a buffer into LDS: lane l reads voffset + soffset and writes
-// dst + 16 l (dst is wave-uniform).  Issued as inline assembly on purpose: the
-// compiler then keeps no count of these loads, so it does not stall later LDS
-// reads of the other stage buffer on them (it cannot tell the two buffers
-// apart).  The kernel orders them itself, with vmcnt(0) before every barrier
-// that precedes a read of the buffer they fill and before it exits.  M0 is a
-// reserved register (never allocated to values), so writing it here is safe.
+// dst + 16 l (dst is wave-uniform; M0 carries it).  Issued as inline assembly on
+// purpose: the compiler then keeps no count of these loads, so it does not stall
+// later LDS reads of the other stage buffer on them (it cannot tell the two buffers
+// apart).  The kernel orders them itself, with vmcnt(0) before every barrier that
+// precedes a read of the buffer they fill and before it exits.
+// M0 is a reserved register: the compiler allocates no value to it, and a clobber
+// of it would not be honoured.  No compiler-generated instruction of this file's
+// kernels reads or writes M0 (tests/test_lib_abi.py checks the assembly), so these
+// statements are its only users.  A scalar write of M0 needs one wait state before
+// an LDS DMA reads it (the compiler inserts one after its own M0 writes; inside one
+// asm statement its hazard recognizer cannot), hence the s_nop between the two.
 __device__ __forceinline__ void dma16(const u32x4 &rsrc, void *dst, uint32_t voffset, uint32_t soffset) {
   const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(dst));  // low half of a flat LDS address = offset
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset));
 }
@@ -813,17 +819,20 @@ __global__ __launch_bounds__(256) void gemm_edge_kernel(GemmParams p) {
   store_tiles<TM, TN>(p, acc, m0 + wm, n0 + wn, lr, g);
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; concurrent first
+// calls store the same value).
 unsigned compute_units() {
-  static unsigned cached[64] = {};
+  static std::atomic<unsigned> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = unsigned(n);
+  unsigned n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int q = 0;
+    if (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || q <= 0) q = 256;
+    n = unsigned(q);
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Split-K reduction: C tile split_first + t = (sum over s of partial tile
@@ -963,24 +972,23 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
       // every split tile as ksplit work items of K / ksplit writing partial tiles into
       // ws, and one reduction launch writing their part of C
       const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
-      auto launch = [&](const GemmParams &q, unsigned items) {
+      auto main = [&](const GemmParams &q, unsigned items) {
         const dim3 grid(items < cus ? items : cus);
-        if (exact)
-          hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false, false>), grid, dim3(256), 0, stream, q);
-        else
-          hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true, false>), grid, dim3(256), 0, stream, q);
+        return exact ? launch(gemm_kernel<256, 256, 2, 2, false, false>, grid, dim3(256), stream, q)
+                     : launch(gemm_kernel<256, 256, 2, 2, true, false>, grid, dim3(256), stream, q);
       };
+      hipError_t e = hipSuccess;
       if (sp.first > 0) {
         p.tiles_main = int(sp.first);
-        launch(p, unsigned(sp.first));
+        e = main(p, unsigned(sp.first));
       }
       p.ksplit = sp.ksplit;
       p.split_first = int(sp.first);
       p.ws = static_cast<float *>(ws);
       p.tiles_main = int(sp.tiles) * sp.ksplit;
-      launch(p, unsigned(p.tiles_main));
-      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned(sp.tiles) * 16), dim3(256), 0, stream, p);
-      return hipGetLastError();
+      if (e == hipSuccess) e = main(p, unsigned(p.tiles_main));
+      if (e == hipSuccess) e = launch(splitk_reduce_kernel, dim3(unsigned(sp.tiles) * 16), dim3(256), stream, p);
+      return e;
     }
   }
   if (main_path) {
@@ -995,22 +1003,17 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
     p.tiles_main = int(split ? tiles - rest : tiles);
     const dim3 grid(tiles < cus ? tiles : cus);
     const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
-    if (exact)
-      hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, false, false>), grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 2, true, false>), grid, dim3(256), 0, stream, p);
-    if (split) {
+    hipError_t e = exact ? launch(gemm_kernel<256, 256, 2, 2, false, false>, grid, dim3(256), stream, p)
+                         : launch(gemm_kernel<256, 256, 2, 2, true, false>, grid, dim3(256), stream, p);
+    if (e == hipSuccess && split) {
       p.tail_first = p.tiles_main;
       const dim3 qgrid(4 * rest < cus ? 4 * rest : cus);
-      if (exact)
-        hipLaunchKernelGGL((gemm_kernel<128, 128, 2, 2, false, true>), qgrid, dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((gemm_kernel<128, 128, 2, 2, true, true>), qgrid, dim3(256), 0, stream, p);
+      e = exact ? launch(gemm_kernel<128, 128, 2, 2, false, true>, qgrid, dim3(256), stream, p)
+                : launch(gemm_kernel<128, 128, 2, 2, true, true>, qgrid, dim3(256), stream, p);
     }
-  } else {
-    hipLaunchKernelGGL(gemm_edge_kernel, dim3(tiles_for<128, 128>(p)), dim3(256), 0, stream, p);
+    return e;
   }
-  return hipGetLastError();
+  return launch(gemm_edge_kernel, dim3(tiles_for<128, 128>(p)), dim3(256), stream, p);
 }
 
 }  // namespace

@@ -7,6 +7,23 @@
 
 namespace nvfp4 {
 
+template <typename T>
+struct same_type {
+  using type = T;
+};
+
+// Launch `kernel` on `stream` and return that launch's own status.  hipLaunchKernel
+// reports the error of this launch alone, so a failure left behind by the caller's
+// earlier HIP work is neither returned as ours nor cleared (hipGetLastError after a
+// launch would do both).  The arguments are converted to the kernel's parameter
+// types here, so the pointers below point at exactly what the kernel expects.
+template <typename... P>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                  typename same_type<P>::type... args) {
+  void *ptrs[] = {static_cast<void *>(&args)..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream);
+}
+
 hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                        uint32_t signs, float *out, hipStream_t stream);
 

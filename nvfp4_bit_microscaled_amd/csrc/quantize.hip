@@ -691,65 +691,64 @@ float *partial_room(const fp4_tensor *t) {
 template <typename T>
 hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, float *out,
                      float *partial, hipStream_t stream) {
-  if (R == 0 || C == 0 || !partial) hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, stream, out);
-  if (R == 0 || C == 0) return hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (R == 0 || C == 0 || !partial) e = launch(zero_f32_kernel, dim3(1), dim3(1), stream, out);
+  if (e != hipSuccess || R == 0 || C == 0) return e;
   const int64_t cap = partial ? 1024 : 256 * 16;  // 16 workgroups per CU are plenty for a streaming reduction
   dim3 grid;
   if (!(flags & FP4_Q_RHT) && ld == C) {
     // four workgroups per CU: on the MI355X a 200 MB read-only stream took 37 us with
     // 1024 workgroups, 52 us with 512 (kernel time without the atomics)
     grid = dim3(grid_for(R * (C / 8), kThreads * 4, 1024));
-    hipLaunchKernelGGL(amax_flat_kernel<T>, grid, dim3(kThreads), 0, stream, x, R * (C / 8), out, partial);
+    e = launch(amax_flat_kernel<T>, grid, dim3(kThreads), stream, x, R * (C / 8), out, partial);
   } else if (!(flags & FP4_Q_RHT)) {
     grid = dim3(grid_for(R * (C / 8), kThreads * 4, cap));
-    hipLaunchKernelGGL(amax_plain_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, out, partial);
+    e = launch(amax_plain_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, out, partial);
   } else if (flags & FP4_Q_COLWISE) {
     grid = dim3(grid_for((R / 16) * (C / 8), kThreads, cap));
-    hipLaunchKernelGGL(amax_rht_cols_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, out, partial);
+    e = launch(amax_rht_cols_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
   } else {
     grid = dim3(grid_for(R * (C / 16), kThreads * 2, cap));
-    hipLaunchKernelGGL(amax_rht_rows_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, out, partial);
+    e = launch(amax_rht_rows_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
   }
-  if (partial)
-    hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kThreads), 0, stream, partial, int(grid.x), 1, out, out);
-  return hipGetLastError();
+  if (e == hipSuccess && partial)
+    e = launch(amax_finish_kernel, dim3(1), dim3(kThreads), stream, partial, int(grid.x), 1, out, out);
+  return e;
 }
 
 template <typename T, bool RHT, bool SR>
-void launch_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
-                 const fp4_tensor *out, hipStream_t stream) {
+hipError_t launch_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
+                       const fp4_tensor *out, hipStream_t stream) {
   const int64_t nkb = C / 16;
   if (ld == C) {
     const int64_t nblocks = R * nkb;
-    hipLaunchKernelGGL((quant_rows_flat_kernel<T, RHT, SR>), dim3(grid_for(nblocks, 2 * kThreads, 1 << 20)),
-                       dim3(kThreads), 0, stream, x, nblocks, signs, seed, offset, out->amax, out->codes,
-                       out->scales);
-    return;
+    return launch(quant_rows_flat_kernel<T, RHT, SR>, dim3(grid_for(nblocks, 2 * kThreads, 1 << 20)), dim3(kThreads),
+                  stream, x, nblocks, signs, seed, offset, out->amax, out->codes, out->scales);
   }
   dim3 grid(unsigned((nkb + kThreads - 1) / kThreads), unsigned(R < 65535 ? R : 65535));
-  hipLaunchKernelGGL((quant_rows_kernel<T, RHT, SR>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, seed,
-                     offset, out->amax, out->codes, out->scales);
+  return launch(quant_rows_kernel<T, RHT, SR>, grid, dim3(kThreads), stream, x, R, C, ld, signs, seed, offset,
+                out->amax, out->codes, out->scales);
 }
 
 template <typename T, bool RHT, bool SR>
-void launch_cols(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
-                 const fp4_tensor *out, hipStream_t stream) {
+hipError_t launch_cols(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
+                       const fp4_tensor *out, hipStream_t stream) {
   const int64_t nslab = R / 16;
   dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
-  hipLaunchKernelGGL((quant_cols_kernel<T, RHT, SR>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs, seed,
-                     offset, out->amax, out->codes, out->scales);
+  return launch(quant_cols_kernel<T, RHT, SR, false>, grid, dim3(kThreads), stream, x, R, C, ld, signs, seed, offset,
+                out->amax, out->codes, out->scales, nullptr, nullptr, nullptr);
 }
 
 // Both nearest-even layouts of x in one kernel: cols (x^T, transformed when RHT)
 // and rows (x).  Each takes its own tensor amax from its descriptor.
 template <typename T, bool RHT>
-void launch_cols_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, const fp4_tensor *cols,
-                      const fp4_tensor *rows, hipStream_t stream) {
+hipError_t launch_cols_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, const fp4_tensor *cols,
+                            const fp4_tensor *rows, hipStream_t stream) {
   const int64_t nslab = R / 16;
   dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
-  hipLaunchKernelGGL((quant_cols_kernel<T, RHT, false, true>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
-                     uint64_t(0), uint64_t(0), cols->amax, cols->codes, cols->scales, rows->amax, rows->codes,
-                     rows->scales);
+  return launch(quant_cols_kernel<T, RHT, false, true>, grid, dim3(kThreads), stream, x, R, C, ld, signs,
+                uint64_t(0), uint64_t(0), cols->amax, cols->codes, cols->scales, rows->amax, rows->codes,
+                rows->scales);
 }
 
 template <typename T>
@@ -759,7 +758,7 @@ hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t 
     hipError_t e = amax_impl(x, R, C, ld, flags, signs, out->amax, partial_room(out), stream);
     if (e != hipSuccess) return e;
   }
-  if (R == 0 || C == 0) return hipGetLastError();
+  if (R == 0 || C == 0) return hipSuccess;
   const bool rht = flags & FP4_Q_RHT, sr = flags & FP4_Q_SR;
   if (flags & FP4_Q_2D) {
     // direct layout is x's; with COLWISE the logical tensor is x^T, so `out` takes
@@ -772,20 +771,19 @@ hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t 
     const int64_t tiles_c = C / 16, tiles_r = R / 16;
     const dim3 grid(unsigned((tiles_c + 15) / 16), unsigned((tiles_r + 15) / 16));
     float *amax_copy = (out_t && out_t->amax != out->amax) ? out_t->amax : nullptr;
-    hipLaunchKernelGGL(quant_2d_kernel<T>, grid, dim3(kThreads), 0, stream, x, R, C, ld, out->amax, dc, ds, tcp,
-                       tsp, amax_copy);
-  } else if (flags & FP4_Q_COLWISE) {
-    if (rht && sr) launch_cols<T, true, true>(x, R, C, ld, signs, seed, offset, out, stream);
-    else if (rht) launch_cols<T, true, false>(x, R, C, ld, signs, seed, offset, out, stream);
-    else if (sr) launch_cols<T, false, true>(x, R, C, ld, signs, seed, offset, out, stream);
-    else launch_cols<T, false, false>(x, R, C, ld, signs, seed, offset, out, stream);
-  } else {
-    if (rht && sr) launch_rows<T, true, true>(x, R, C, ld, signs, seed, offset, out, stream);
-    else if (rht) launch_rows<T, true, false>(x, R, C, ld, signs, seed, offset, out, stream);
-    else if (sr) launch_rows<T, false, true>(x, R, C, ld, signs, seed, offset, out, stream);
-    else launch_rows<T, false, false>(x, R, C, ld, signs, seed, offset, out, stream);
+    return launch(quant_2d_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, out->amax, dc, ds, tcp, tsp,
+                  amax_copy);
   }
-  return hipGetLastError();
+  if (flags & FP4_Q_COLWISE) {
+    if (rht && sr) return launch_cols<T, true, true>(x, R, C, ld, signs, seed, offset, out, stream);
+    if (rht) return launch_cols<T, true, false>(x, R, C, ld, signs, seed, offset, out, stream);
+    if (sr) return launch_cols<T, false, true>(x, R, C, ld, signs, seed, offset, out, stream);
+    return launch_cols<T, false, false>(x, R, C, ld, signs, seed, offset, out, stream);
+  }
+  if (rht && sr) return launch_rows<T, true, true>(x, R, C, ld, signs, seed, offset, out, stream);
+  if (rht) return launch_rows<T, true, false>(x, R, C, ld, signs, seed, offset, out, stream);
+  if (sr) return launch_rows<T, false, true>(x, R, C, ld, signs, seed, offset, out, stream);
+  return launch_rows<T, false, false>(x, R, C, ld, signs, seed, offset, out, stream);
 }
 
 // Dual quantization: both amaxes in one read of x (unless given), then the layouts.
@@ -798,37 +796,33 @@ hipError_t dual_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
                      uint64_t off_rows, uint64_t off_cols, const fp4_tensor *rows, const fp4_tensor *cols,
                      hipStream_t stream) {
   const bool rht = flags & FP4_Q_RHT, sr = flags & FP4_Q_SR;
+  hipError_t e = hipSuccess;
   if (!(flags & FP4_Q_AMAX_GIVEN)) {
     float *partial = partial_room(rows);  // the rowwise codes (as many bytes as the columnwise ones)
     if (R == 0 || C == 0 || !partial)
-      hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(1), 0, stream, rows->amax, cols->amax);
-    if (R > 0 && C > 0) {
+      e = launch(zero2_f32_kernel, dim3(1), dim3(1), stream, rows->amax, cols->amax);
+    if (e == hipSuccess && R > 0 && C > 0) {
       // two workgroups per CU: on the MI355X this read 640 MB in 114 us and 160 MB in
       // 38 us, against 116 us and 45 us with four
       const dim3 grid(grid_for((R / 16) * (C / 8), kThreads, 512));
-      if (rht)
-        hipLaunchKernelGGL((amax_dual_kernel<T, true>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
-                           rows->amax, cols->amax, partial);
-      else
-        hipLaunchKernelGGL((amax_dual_kernel<T, false>), grid, dim3(kThreads), 0, stream, x, R, C, ld, signs,
-                           rows->amax, cols->amax, partial);
-      if (partial)
-        hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kThreads), 0, stream, partial, int(grid.x), 2,
-                           rows->amax, cols->amax);
+      e = rht ? launch(amax_dual_kernel<T, true>, grid, dim3(kThreads), stream, x, R, C, ld, signs, rows->amax,
+                       cols->amax, partial)
+              : launch(amax_dual_kernel<T, false>, grid, dim3(kThreads), stream, x, R, C, ld, signs, rows->amax,
+                       cols->amax, partial);
+      if (e == hipSuccess && partial)
+        e = launch(amax_finish_kernel, dim3(1), dim3(kThreads), stream, partial, int(grid.x), 2, rows->amax,
+                   cols->amax);
     }
   }
-  if (R == 0 || C == 0) return hipGetLastError();
+  if (e != hipSuccess || R == 0 || C == 0) return e;
   if (!sr) {
     // nearest-even: both layouts from one read of x
-    if (rht) launch_cols_rows<T, true>(x, R, C, ld, signs, cols, rows, stream);
-    else launch_cols_rows<T, false>(x, R, C, ld, signs, cols, rows, stream);
-    return hipGetLastError();
+    return rht ? launch_cols_rows<T, true>(x, R, C, ld, signs, cols, rows, stream)
+               : launch_cols_rows<T, false>(x, R, C, ld, signs, cols, rows, stream);
   }
-  const uint32_t given = flags | FP4_Q_AMAX_GIVEN;
-  hipError_t e = quantize_impl(x, R, C, ld, (given & FP4_Q_SR) | FP4_Q_AMAX_GIVEN, signs, seed, off_rows, rows,
-                               nullptr, stream);
+  e = quantize_impl(x, R, C, ld, FP4_Q_SR | FP4_Q_AMAX_GIVEN, signs, seed, off_rows, rows, nullptr, stream);
   if (e != hipSuccess) return e;
-  const uint32_t fc = FP4_Q_COLWISE | FP4_Q_AMAX_GIVEN | (rht ? FP4_Q_RHT : 0u) | (sr ? FP4_Q_SR : 0u);
+  const uint32_t fc = FP4_Q_COLWISE | FP4_Q_AMAX_GIVEN | FP4_Q_SR | (rht ? FP4_Q_RHT : 0u);
   return quantize_impl(x, R, C, ld, fc, signs, seed, off_cols, cols, nullptr, stream);
 }
 

@@ -270,3 +270,65 @@ def test_linear_backward_equals_dgrad_and_wgrad(fp4, oracle, quantize_x):
     check_gemm(dx_b.float().cpu().numpy(), y_ref, bound, True, "backward dgrad")
     y_ref, bound = oracle.gemm_ref(odytq, oxtq)
     check_gemm(dw_b.cpu().numpy(), y_ref, bound, False, "backward wgrad")
+
+
+def test_linear_calls_equal_the_primitive_composition(fp4, oracle):
+    """fp4_linear_fprop (with X^T) + fp4_linear_backward with a workspace give bit for
+    bit the quantized operands and outputs of the same step composed from
+    fp4_quantize_dual, fp4_quantize and fp4_gemm_ws, including a wgrad GEMM that
+    takes the split-K path; the phase events they record complete in order; and the
+    operands match the oracle (outputs within the GEMM tolerance)."""
+    import bench
+
+    M, N, K = 2048, 768, 1024
+    assert fp4.fp4_gemm_ws_bytes(N, K, M) > 0, "the wgrad product is expected to split over K"
+    inp = workloads.make_linear_inputs(workloads.Linear("t", M, N, K), seed=77)
+    x, w, dy = dev(inp.x), dev(inp.w), dev(inp.dy)
+    sr, od, ow = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
+    ws = torch.empty(fp4.fp4_linear_ws_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    assert ws.numel() >= fp4.fp4_gemm_ws_bytes(N, K, M)
+    outs = []
+    for composed in (False, True):
+        b = fp4.LinearBuffers(M, N, K)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
+        if composed:
+            fp4.fp4_quantize_dual(x, fp4.Q_RHT, inp.signs, 0, 0, 0, b.xq, b.xq_t)
+            fp4.fp4_quantize(w, fp4.Q_2D, 0, 0, 0, b.wq, b.wq_t)
+            fp4.fp4_gemm_ws(b.xq, b.wq, y, ws)
+            fp4.fp4_quantize_dual(dy, fp4.Q_SR | fp4.Q_RHT, inp.signs, sr, od, ow, b.dyq, b.dyq_t)
+            fp4.fp4_gemm_ws(b.dyq, b.wq_t, dx, ws)
+            fp4.fp4_gemm_ws(b.dyq_t, b.xq_t, dw, ws)
+        else:
+            stream = torch.cuda.current_stream()
+            evs = [bench.HipTimingEvent() for _ in range(7)]
+            evs[0].record(stream)
+            fp4.fp4_linear_fprop(x, w, y, b.xq, b.wq, b.wq_t, xq_t=b.xq_t, rht_signs=inp.signs, ws=ws,
+                                 marks=[evs[1].h.value, evs[2].h.value])
+            fp4.fp4_linear_backward(dy, None, b.wq_t, dx, dw, inp.signs, sr, od, ow, b.dyq, b.dyq_t, b.xq_t, ws=ws,
+                                    marks=[evs[3].h.value, evs[4].h.value, evs[5].h.value])
+            evs[6].record(stream)
+        torch.cuda.synchronize()
+        if not composed:
+            gaps = [evs[i].elapsed_time(evs[i + 1]) for i in range(6)]
+            assert all(g >= 0.0 for g in gaps), gaps
+            assert gaps[3] < 0.05 * sum(gaps), "the X^T phase of the backward call is empty when x is NULL"
+        outs.append((b, y, dx, dw))
+    (a, ya, dxa, dwa), (c, yc, dxc, dwc) = outs
+    for name in ("xq", "xq_t", "wq", "wq_t", "dyq", "dyq_t"):
+        qa, qc = getattr(a, name), getattr(c, name)
+        assert torch.equal(qa.codes, qc.codes) and torch.equal(qa.scales, qc.scales), name
+        assert torch.equal(qa.amax, qc.amax), name
+    assert torch.equal(ya, yc) and torch.equal(dxa, dxc) and torch.equal(dwa, dwc)
+    # and against the oracle
+    xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
+    oxq, owq = oracle.linear_fprop(xf, wf)
+    odyq, owtq = oracle.linear_dgrad(dyf, wf, sr, od)
+    odytq, oxtq = oracle.linear_wgrad(dyf, xf, inp.signs, sr, ow)
+    for name, o in (("xq", oxq), ("wq", owq), ("wq_t", owtq), ("dyq", odyq), ("dyq_t", odytq), ("xq_t", oxtq)):
+        assert_q_equal(host_q(getattr(a, name)), o, name)
+    for name, out, qa, qb, bf16 in (("fprop", ya, oxq, owq, True), ("dgrad", dxa, odyq, owtq, True),
+                                    ("wgrad", dwa, odytq, oxtq, False)):
+        ref, bound = oracle.gemm_ref(qa, qb)
+        check_gemm(out.float().cpu().numpy(), ref, bound, bf16, name)

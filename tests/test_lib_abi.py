@@ -137,13 +137,45 @@ def test_gemm_ws_bytes_follows_the_split_plan(lib):
 def test_linear_rejects_bad_arguments(lib):
     Q = ctypes.byref
     x, w, y = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    ws = ctypes.c_void_p(0x5000)
     M, N, K = 64, 32, 48
     ok = lib.fp4_linear_fprop
-    assert ok(x, w, 0, y, 0, M, N, 40, Q(desc(M, 40)), Q(desc(N, 40, 1)), None, None) == 2
-    assert ok(x, w, 0, y, 0, M, N, K, Q(desc(M, K)), Q(desc(N, K, 0)), None, None) == 6  # W must be 2D
-    assert ok(x, w, 0, y, 0, M, N, K, Q(desc(M, K)), Q(desc(N, K, 1)), Q(desc(N, K, 1)), None) == 6  # W^T shape
-    assert lib.fp4_linear_dgrad(x, 0, Q(desc(N, K, 1)), y, 0, M, N, K, 0, 1, Q(desc(M, N)), None) == 6
-    assert lib.fp4_linear_wgrad(x, w, 0, y, 1, M, N, K, 0, 0, 2, Q(desc(N, M)), Q(desc(M, K)), None) == 6
+    tail = (None, 0, None, None)  # ws, ws_bytes, marks, stream
+    assert ok(x, w, 0, y, 0, M, N, 40, 0, Q(desc(M, 40)), None, Q(desc(N, 40, 1)), None, *tail) == 2
+    assert ok(x, w, 0, y, 0, M, N, K, 0, Q(desc(M, K)), None, Q(desc(N, K, 0)), None, *tail) == 6  # W must be 2D
+    assert ok(x, w, 0, y, 0, M, N, K, 0, Q(desc(M, K)), None, Q(desc(N, K, 1)), Q(desc(N, K, 1)), *tail) == 6  # W^T
+    assert ok(x, w, 0, y, 0, M, N, K, 0, Q(desc(M, K)), Q(desc(M, K)), Q(desc(N, K, 1)), None, *tail) == 6  # X^T
+    # workspace: bytes without a pointer, misaligned pointer
+    assert ok(x, w, 0, y, 0, M, N, K, 0, Q(desc(M, K)), None, Q(desc(N, K, 1)), None, None, 64, None, None) == 1
+    assert ok(x, w, 0, y, 0, M, N, K, 0, Q(desc(M, K)), None, Q(desc(N, K, 1)), None,
+              ctypes.c_void_p(0x5004), 64, None, None) == 3
+    assert lib.fp4_linear_dgrad(x, 0, Q(desc(N, K, 1)), y, 0, M, N, K, 0, 1, Q(desc(M, N)), *tail) == 6
+    assert lib.fp4_linear_dgrad(x, 0, Q(desc(K, N, 1)), y, 0, M, N, K, 0, 1, Q(desc(M, N)), None, 16, None,
+                                None) == 1
+    assert lib.fp4_linear_wgrad(x, w, 0, y, 1, M, N, K, 0, 0, 2, Q(desc(N, M)), Q(desc(M, K)), *tail) == 6
+    assert lib.fp4_linear_wgrad(x, w, 0, y, 1, M, N, K, 0, 0, 2, Q(desc(N, M)), Q(desc(K, M)),
+                                ctypes.c_void_p(0x5008), 256, None, None) == 3
+    del ws
+
+
+def test_linear_ws_bytes_is_the_largest_gemm_plan(lib):
+    """fp4_linear_ws_bytes = the largest split plan of fprop (M, N, K), dgrad
+    (M, K, N) and wgrad (N, K, M)."""
+    n = ctypes.c_size_t()
+
+    def gemm(M, N, K):
+        assert lib.fp4_gemm_ws_bytes(M, N, K, ctypes.byref(n)) == 0
+        return n.value
+
+    def linear(M, N, K):
+        assert lib.fp4_linear_ws_bytes(M, N, K, ctypes.byref(n)) == 0
+        return n.value
+    for M, N, K in ((16384, 20480, 5120), (32768, 3072, 3072), (32768, 9216, 3072), (8192, 4096, 4096),
+                    (32768, 3072, 8192), (256, 256, 256)):
+        assert linear(M, N, K) == max(gemm(M, N, K), gemm(M, K, N), gemm(N, K, M))
+    assert linear(16384, 20480, 5120) == 64 * 4 * 256 * 256 * 4  # the 12B wgrad tail
+    assert lib.fp4_linear_ws_bytes(64, 40, 64, ctypes.byref(n)) == 2
+    assert lib.fp4_linear_ws_bytes(64, 64, 64, None) == 1
 
 
 def test_quantize_dual_rejects_bad_arguments(lib):
@@ -167,9 +199,30 @@ def test_linear_backward_rejects_bad_arguments(lib):
     dy, x, dx, dw = (ctypes.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000))
     M, N, K = 64, 32, 48
     f = lib.fp4_linear_backward
-    good = (Q(desc(K, N, 1)), dx, 1, dw, 0, M, N, K, 0, 0, 1, 2, Q(desc(M, N)), Q(desc(N, M)), Q(desc(K, M)), None)
+    good = (Q(desc(K, N, 1)), dx, 1, dw, 0, M, N, K, 0, 0, 1, 2, Q(desc(M, N)), Q(desc(N, M)), Q(desc(K, M)),
+            None, 0, None, None)
     assert f(dy, x, 0, *good[:5], M, N, 40, *good[8:]) == 2  # K % 16
     assert f(dy, x, 0, Q(desc(K, N, 0)), *good[1:]) == 6  # W^T must be 2D
     assert f(dy, x, 0, *good[:12], Q(desc(N, M)), *good[13:]) == 6  # dY rowwise shape
-    assert f(dy, x, 0, *good[:14], Q(desc(M, K)), None) == 6  # X^T shape
+    assert f(dy, x, 0, *good[:14], Q(desc(M, K)), *good[15:]) == 6  # X^T shape
     assert f(None, x, 0, *good) == 1
+    assert f(dy, x, 0, *good[:15], None, 32, None, None) == 1  # workspace bytes without a pointer
+
+
+def test_gemm_m0_is_only_written_by_the_lds_dma_statement(tmp_path):
+    """The GEMM's LDS DMA sets M0 in inline assembly, which the compiler cannot see.
+    That is sound only while no compiler-generated instruction of gemm.hip uses M0:
+    compile its device code to assembly and check that every line naming m0 is the
+    DMA statement's own write, followed by one wait state and the LDS DMA load."""
+    import subprocess
+    from nvfp4_bit_microscaled_amd import build
+    out = tmp_path / "gemm.s"
+    cmd = [build.HIPCC, *build.FLAGS, "--cuda-device-only", "-S", os.path.join(build.CSRC, "gemm.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    lines = [ln.strip() for ln in out.read_text().splitlines()]
+    uses = [i for i, ln in enumerate(lines) if re.search(r"\bm0\b", ln) and not ln.startswith(";")]
+    assert uses, "the DMA statement is expected in the assembly"
+    for i in uses:
+        assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi|ttmp\d+)", lines[i]), lines[i]
+        assert lines[i + 1] == "s_nop 0", lines[i + 1]
+        assert lines[i + 2].startswith("buffer_load_dwordx4") and lines[i + 2].endswith("offen lds"), lines[i + 2]
