@@ -79,7 +79,8 @@ typedef enum fp4_status {
   FP4_ERR_DTYPE = 4,       /* unknown input or output dtype */
   FP4_ERR_MODE = 5,        /* unsupported combination of quantization flags */
   FP4_ERR_MISMATCH = 6,    /* descriptor sizes do not agree with the call */
-  FP4_ERR_HIP = 7          /* a HIP launch or runtime call failed */
+  FP4_ERR_HIP = 7,         /* a HIP launch or runtime call failed */
+  FP4_ERR_WORKSPACE = 8    /* the shape's split-K plan needs more scratch than the static buffer holds */
 } fp4_status;
 
 typedef enum fp4_dtype {
@@ -204,6 +205,21 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, f
  * FP4_ERR_NULL / FP4_ERR_ALIGN for a non-empty workspace that is NULL / misaligned. */
 FP4_API fp4_status fp4_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc: fp4_gemm_ws with the
+ * library's own static scratch in place of a caller workspace.  The scratch is a
+ * 64 MiB (FP4_STATIC_SCRATCH_BYTES) device array per GPU, held from the first call
+ * on that GPU until the process ends; this call allocates nothing.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap on one GPU (different
+ * streams, or different host threads without ordering) race; calls ordered on one
+ * stream do not.  A shape whose split-K plan needs more than the maximum (see
+ * fp4_gemm_ws_bytes) returns FP4_ERR_WORKSPACE and enqueues nothing (fp4_gemm runs
+ * any shape without scratch).  Otherwise the result is that of fp4_gemm_ws with a
+ * workspace of fp4_gemm_ws_bytes.  Errors: as fp4_gemm_ws, plus FP4_ERR_WORKSPACE. */
+#define FP4_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+FP4_API fp4_status fp4_gemm_noalloc(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
+                                    hipStream_t stream);
 
 /* Workspace bytes fp4_gemm_ws uses for an M x N x K product (0: no split).  Pure
  * host arithmetic on the device's CU count.  FP4_ERR_NULL, FP4_ERR_SHAPE. */

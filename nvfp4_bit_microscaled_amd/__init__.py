@@ -23,11 +23,12 @@ Q_SR = 1 << 3
 Q_AMAX_GIVEN = 1 << 4
 
 STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_ALIGN", 4: "FP4_ERR_DTYPE",
-          5: "FP4_ERR_MODE", 6: "FP4_ERR_MISMATCH", 7: "FP4_ERR_HIP"}
+          5: "FP4_ERR_MODE", 6: "FP4_ERR_MISMATCH", 7: "FP4_ERR_HIP", 8: "FP4_ERR_WORKSPACE"}
+STATIC_SCRATCH_BYTES = 64 << 20
 
 # every symbol the header declares
 EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_gemm", "fp4_gemm_ws",
-           "fp4_gemm_ws_bytes", "fp4_linear_ws_bytes", "fp4_linear_fprop", "fp4_linear_dgrad", "fp4_linear_wgrad",
+           "fp4_gemm_ws_bytes", "fp4_gemm_noalloc", "fp4_linear_ws_bytes", "fp4_linear_fprop", "fp4_linear_dgrad", "fp4_linear_wgrad",
            "fp4_linear_backward", "fp4_status_string")
 
 
@@ -66,6 +67,7 @@ def load():
         "fp4_gemm": [tp, tp, vp, i32, i64, vp],
         "fp4_gemm_ws": [tp, tp, vp, i32, i64, vp, ctypes.c_size_t, vp],
         "fp4_gemm_ws_bytes": [i64, i64, i64, sz],
+        "fp4_gemm_noalloc": [tp, tp, vp, i32, i64, vp],
         "fp4_linear_ws_bytes": [i64, i64, i64, sz],
         "fp4_linear_fprop": [vp, vp, i32, vp, i32, i64, i64, i64, u32, tp, tp, tp, tp, vp, szv, vp, vp],
         "fp4_linear_dgrad": [vp, i32, tp, vp, i32, i64, i64, i64, u64, u64, tp, vp, szv, vp, vp],
@@ -175,6 +177,12 @@ def fp4_gemm_ws(a: QTensor, b: QTensor, c: torch.Tensor, ws: torch.Tensor = None
     wb = ws.numel() * ws.element_size() if ws is not None else 0
     _check("fp4_gemm_ws", load().fp4_gemm_ws(a.desc, b.desc, c.data_ptr(), _dtype(c), c.stride(0), wp, wb,
                                              _stream(stream)))
+
+
+def fp4_gemm_noalloc(a: QTensor, b: QTensor, c: torch.Tensor, stream=None):
+    """fp4_gemm_ws with the library's static split-K scratch (no allocation)."""
+    _check("fp4_gemm_noalloc", load().fp4_gemm_noalloc(a.desc, b.desc, c.data_ptr(), _dtype(c), c.stride(0),
+                                                       _stream(stream)))
 
 
 def fp4_linear_ws_bytes(M: int, N: int, K: int) -> int:

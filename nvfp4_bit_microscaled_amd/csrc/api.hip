@@ -148,6 +148,17 @@ fp4_status fp4_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
   return from_hip(nvfp4::launch_gemm_ws(a, b, c, c_dtype, ldc, ws, ws_bytes, stream));
 }
 
+fp4_status fp4_gemm_noalloc(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
+                            hipStream_t stream) {
+  fp4_status s = check_gemm(a, b, c, c_dtype, ldc);
+  if (s != FP4_OK) return s;
+  if (nvfp4::gemm_ws_bytes(a->rows, b->rows, a->cols) > nvfp4::kStaticScratchBytes) return FP4_ERR_WORKSPACE;
+  void *scratch = nullptr;
+  hipError_t e = nvfp4::static_scratch(&scratch);
+  if (e != hipSuccess) return FP4_ERR_HIP;
+  return from_hip(nvfp4::launch_gemm_ws(a, b, c, c_dtype, ldc, scratch, nvfp4::kStaticScratchBytes, stream));
+}
+
 fp4_status fp4_linear_ws_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes) {
   if (!bytes) return FP4_ERR_NULL;
   if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 16) return FP4_ERR_SHAPE;
@@ -251,6 +262,7 @@ const char *fp4_status_string(fp4_status status) {
     case FP4_ERR_MODE: return "unsupported combination of quantization flags";
     case FP4_ERR_MISMATCH: return "descriptor sizes do not agree with the call";
     case FP4_ERR_HIP: return "a HIP launch or runtime call failed";
+    case FP4_ERR_WORKSPACE: return "the split-K plan of this shape needs more scratch than the static buffer holds";
   }
   return "unknown status";
 }

@@ -48,6 +48,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1017,6 +1018,33 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
 }
 
 }  // namespace
+
+// The library's own split-K scratch, for callers that cannot allocate: a
+// file-scope device array (one copy per GPU, at that GPU's own address, held from
+// module load until the process ends).  Host code never passes the array's name to
+// a kernel -- on the host it is only a stand-in for the symbol -- but the device
+// address hipGetSymbolAddress returns, looked up once per device with that device
+// current.  Every work item writes its whole partial tile before the reduction
+// reads it, so nothing in it needs clearing between calls.
+__device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                        hipStream_t stream) {

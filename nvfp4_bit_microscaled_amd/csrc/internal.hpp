@@ -45,4 +45,11 @@ hipError_t launch_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 
+// Size of the library's static split-K scratch (fp4_gemm_noalloc), per GPU.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+
+// Device address of the static scratch on the current device (looked up once per
+// device; allocates nothing).
+hipError_t static_scratch(void **ptr);
+
 }  // namespace nvfp4

@@ -44,7 +44,7 @@ def test_library_does_not_export_internals():
 
 def test_status_strings(lib):
     import nvfp4_bit_microscaled_amd as m
-    for code in range(8):
+    for code in range(9):
         assert m.status_string(code)
     assert m.status_string(0) == "ok"
 
@@ -156,6 +156,22 @@ def test_linear_rejects_bad_arguments(lib):
     assert lib.fp4_linear_wgrad(x, w, 0, y, 1, M, N, K, 0, 0, 2, Q(desc(N, M)), Q(desc(K, M)),
                                 ctypes.c_void_p(0x5008), 256, None, None) == 3
     del ws
+
+
+def test_gemm_noalloc_rejects_before_touching_the_device(lib):
+    """fp4_gemm_noalloc checks its arguments and the static scratch limit on the
+    host: a shape whose split plan needs more than 64 MiB (the 3B block's O-projection
+    wgrad, 144 tiles in 8 splits = 288 MiB) is rejected with FP4_ERR_WORKSPACE."""
+    import nvfp4_bit_microscaled_amd as m
+    Q = ctypes.byref
+    c = ctypes.c_void_p(0x100000)
+    n = ctypes.c_size_t()
+    assert lib.fp4_gemm_ws_bytes(3072, 3072, 32768, ctypes.byref(n)) == 0 and n.value > m.STATIC_SCRATCH_BYTES
+    assert lib.fp4_gemm_noalloc(Q(desc(3072, 32768)), Q(desc(3072, 32768)), c, 1, 3072, None) == 8
+    assert lib.fp4_gemm_noalloc(Q(desc(64, 128)), Q(desc(32, 96)), c, 1, 32, None) == 6  # K mismatch
+    assert lib.fp4_gemm_noalloc(Q(desc(64, 128)), Q(desc(32, 128)), None, 1, 32, None) == 1
+    # the 12B weight-gradient plan fits exactly
+    assert lib.fp4_gemm_ws_bytes(20480, 5120, 16384, ctypes.byref(n)) == 0 and n.value == m.STATIC_SCRATCH_BYTES
 
 
 def test_linear_ws_bytes_is_the_largest_gemm_plan(lib):
