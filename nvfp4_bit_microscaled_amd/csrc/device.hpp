@@ -105,6 +105,32 @@ __device__ __forceinline__ void block_scale_quarter(float u[16], float s_enc, co
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Codes 2 sel and 2 sel + 1 of a word of 8 E2M1 codes (element 2j in the low nibble
+// of byte j) as two f16, unscaled: every E2M1 value is an f16 value.  gfx950's
+// converter applies only the exponent of its f32 scale operand, so that operand is
+// 1 and the E4M3 block scale is applied by a separate f16 multiply.
+__device__ __forceinline__ f16x2 fp4x2_to_f16(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
+
+// Two E4M3 scale codes (the low 16 bits of w) as two f16: every E4M3 value,
+// subnormals included, is an f16 value, so the conversion is exact.
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+
+// Codes 2 sel, 2 sel + 1 of w times the block scale s: E2M1 x E4M3 has at most 6
+// significant bits and lies in [2^-10, 2688], so the f16 product is exact.
+__device__ __forceinline__ f16x2 dequant2(uint32_t w, int sel, _Float16 s) {
+  return fp4x2_to_f16(w, sel) * f16x2{s, s};
+}
 
 // Canonical zero: clear the sign bit of every code whose magnitude is 0 (the
 // converters write -0 for negative values that round to zero).  Per nibble,

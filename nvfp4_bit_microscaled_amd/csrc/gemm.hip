@@ -83,17 +83,11 @@ struct GemmParams {
 // 8 E2M1 codes (one 32-bit word, element 2j in the low nibble of byte j) times the
 // block scale, as 8 f16.  Exact: see the header comment.
 __device__ __forceinline__ half8 dequant8(uint32_t w, _Float16 s) {
-  const half2v sc = half2v{s, s};
-  const half2v h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
-  const half2v h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
-  const half2v h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
-  const half2v h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
+  const half2v h0 = dequant2(w, 0, s), h1 = dequant2(w, 1, s), h2 = dequant2(w, 2, s), h3 = dequant2(w, 3, s);
   return half8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-// Two E4M3 scale codes (the low 16 bits of w) as two f16: every E4M3 value,
-// subnormals included, is an f16 value, so the conversion is exact.
-__device__ __forceinline__ half2v scales2(uint32_t w) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false); }
+__device__ __forceinline__ half2v scales2(uint32_t w) { return e4m3x2_to_f16(w); }
 
 __device__ __forceinline__ uint32_t word(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
@@ -472,11 +466,8 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   auto dequant_half = [&](int slot, int s, int dst, int i, int h) {
     const uint32_t w = word(ch[slot][i], s);
     const _Float16 sv = scd[slot][i][s >> 1];
-    const half2v sc = half2v{sv, sv};
-    const half2v lo = (h == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)
-                              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)) * sc;
-    const half2v hi = (h == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)
-                              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)) * sc;
+    const half2v lo = dequant2(w, 2 * h, sv);
+    const half2v hi = dequant2(w, 2 * h + 1, sv);
     op[dst][i][4 * h + 0] = lo[0];
     op[dst][i][4 * h + 1] = lo[1];
     op[dst][i][4 * h + 2] = hi[0];
