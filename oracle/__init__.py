@@ -22,6 +22,8 @@ Q_2D = 1 << 0
 Q_COLWISE = 1 << 1
 Q_RHT = 1 << 2
 Q_SR = 1 << 3
+Q_RHT64 = 1 << 5
+Q_EDEN = 1 << 6
 
 _lib = None
 
@@ -62,6 +64,14 @@ def lib():
         L.nvo_e2m1_encode_n.argtypes = [f32p, i64, ctypes.c_int, u32p, u8p]
         L.nvo_e4m3_encode_n.restype = None
         L.nvo_e4m3_encode_n.argtypes = [f32p, i64, u8p]
+        L.nvo_e4m3_sr_n.restype = None
+        L.nvo_e4m3_sr_n.argtypes = [f32p, i64, u32p, u8p]
+        L.nvo_e4m3_sr.restype = ctypes.c_uint
+        L.nvo_e4m3_sr.argtypes = [ctypes.c_float, ctypes.c_uint32]
+        L.nvo_rht64_signs.restype = None
+        L.nvo_rht64_signs.argtypes = [ctypes.c_uint64, ctypes.c_uint32, u32p]
+        L.nvo_rht64.restype = None
+        L.nvo_rht64.argtypes = [f32p, u32p]
         _lib = L
     return _lib
 
@@ -123,6 +133,33 @@ def rht16(v, signs: int) -> np.ndarray:
     return a
 
 
+def e4m3_sr(y: float, u16: int) -> int:
+    return lib().nvo_e4m3_sr(y, u16 & 0xFFFF)
+
+
+def e4m3_sr_n(y, u16) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32).reshape(-1)
+    u = np.ascontiguousarray(np.broadcast_to(np.asarray(u16, dtype=np.uint32), y.shape))
+    out = np.empty(y.size, dtype=np.uint8)
+    lib().nvo_e4m3_sr_n(_ptr(y, ctypes.c_float), y.size, _ptr(u, ctypes.c_uint32), _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def rht64_signs(group: int, key: int):
+    out = (ctypes.c_uint32 * 2)()
+    lib().nvo_rht64_signs(group, key & 0xFFFFFFFF, out)
+    return [int(out[0]), int(out[1])]
+
+
+def rht64(v, group: int, key: int) -> np.ndarray:
+    """The 64-point random Hadamard transform of group `group` under `key`."""
+    a = np.ascontiguousarray(v, dtype=np.float32).copy()
+    assert a.shape == (64,)
+    sg = (ctypes.c_uint32 * 2)(*rht64_signs(group, key))
+    lib().nvo_rht64(_ptr(a, ctypes.c_float), sg)
+    return a
+
+
 def decode_scale(amax: float) -> float:
     return lib().nvo_decode_scale(amax)
 
@@ -151,30 +188,39 @@ def _as_f32(x) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32)
 
 
-def amax(x, colwise=False, rht=False, signs=0, threads=None) -> float:
+def amax(x, colwise=False, rht=False, rht64=False, signs=0, threads=None) -> float:
+    """Tensor amax of the logical tensor (after the 16-point transform with the 16-bit
+    mask `signs`, or the 64-point one keyed by the 32-bit `signs`)."""
     x = _as_f32(x)
-    flags = (Q_COLWISE if colwise else 0) | (Q_RHT if rht else 0)
-    return float(lib().nvo_amax(_ptr(x, ctypes.c_float), x.shape[0], x.shape[1], x.shape[1], flags,
-                                signs & 0xFFFF, threads or default_threads()))
+    flags = (Q_COLWISE if colwise else 0) | (Q_RHT if rht else 0) | (Q_RHT64 if rht64 else 0)
+    a = float(lib().nvo_amax(_ptr(x, ctypes.c_float), x.shape[0], x.shape[1], x.shape[1], flags,
+                             signs & 0xFFFFFFFF, threads or default_threads()))
+    if a < 0:
+        raise ValueError(f"oracle amax rejected shape {x.shape} flags {flags}")
+    return a
 
 
-def quantize(x, *, two_d=False, colwise=False, rht=False, sr=False, signs=0, seed=0, offset=0,
-             amax_in=None, rows=None, threads=None) -> QTensor:
+def quantize(x, *, two_d=False, colwise=False, rht=False, sr=False, rht64=False, eden=False, signs=0, seed=0,
+             offset=0, amax_in=None, rows=None, threads=None) -> QTensor:
     """Quantize the logical tensor (x, or x^T when colwise) of the fp32 array x.
 
+    rht: the 16-point transform with the 16-bit mask `signs`; rht64: the 64-point
+    transform keyed by the 32-bit `signs`; eden: MS-EDEN (needs rht64; the stored
+    amax is 7/4 of the transformed tensor's); sr / eden draw from (seed, offset).
     rows: optional (row0, row1) range of logical rows to produce (amax is still
     that of the whole tensor)."""
     x = _as_f32(x)
     R, C = x.shape
     nrows_all, K = (C, R) if colwise else (R, C)
     r0, r1 = rows if rows is not None else (0, nrows_all)
-    flags = (Q_2D if two_d else 0) | (Q_COLWISE if colwise else 0) | (Q_RHT if rht else 0) | (Q_SR if sr else 0)
+    flags = (Q_2D if two_d else 0) | (Q_COLWISE if colwise else 0) | (Q_RHT if rht else 0) | (Q_SR if sr else 0) \
+        | (Q_RHT64 if rht64 else 0) | (Q_EDEN if eden else 0)
     n = r1 - r0
     codes = np.zeros((n, K // 2), dtype=np.uint8)
     scales = np.zeros(((n // 16) if two_d else n, K // 16), dtype=np.uint8)
     a_out = np.zeros(1, dtype=np.float32)
     a_in = None if amax_in is None else np.array([amax_in], dtype=np.float32)
-    rc = lib().nvo_quantize(_ptr(x, ctypes.c_float), R, C, C, flags, signs & 0xFFFF, seed, offset,
+    rc = lib().nvo_quantize(_ptr(x, ctypes.c_float), R, C, C, flags, signs & 0xFFFFFFFF, seed, offset,
                             None if a_in is None else _ptr(a_in, ctypes.c_float), r0, n,
                             _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
                             _ptr(a_out, ctypes.c_float), threads or default_threads())

@@ -17,7 +17,16 @@
  *     weight-gradient operands, stochastic rounding on gradients only
  *     (NVFP4-12B page, paragraph 2, the four-part recipe sentence);
  *   - stochastic rounding is used because it is unbiased (Quartet II page,
- *     paragraph 1, the sentence on earlier quantized training).
+ *     paragraph 1, the sentence on earlier quantized training);
+ *   - MS-EDEN, an unbiased quantization routine for microscale formats with
+ *     more than 2x lower error than stochastic rounding (Quartet II page,
+ *     paragraph 1, the MS-EDEN sentence).  The page names the method only; the
+ *     reading here follows EDEN (Vargaftik et al., ICML 2022): a random rotation,
+ *     deterministic rounding, then a scale correction that makes the estimate
+ *     unbiased over the rotation.  The rotation is a random-sign Hadamard over
+ *     64-element groups (orthonormal with the exact factor 1/8), the rounding is
+ *     nearest-even, and each 16-block's correction factor is folded into its
+ *     E4M3 scale by stochastic rounding.
  * The pages print no formula for any step.  Every step below follows one plain
  * reading (the E2M1 grid {0,0.5,1,1.5,2,3,4,6}, OCP E4M3, s_enc = 2688/amax,
  * Philox4x32-10 counters, Sylvester H16 scaled by 1/4); each reading is listed
@@ -32,7 +41,10 @@
  * H*H^T = 16 I and the Kronecker construction of H16; Philox against the
  * published known-answer vectors; stochastic rounding against its expectation;
  * the scale recipe against the "one value per block at near-FP8 precision"
- * property; dequantization against exact small cases.
+ * property; dequantization against exact small cases; the 64-point transform
+ * against the Kronecker H64 on integers; MS-EDEN's scale rounding against its
+ * exact expectation, its correction against EDEN's projection identity, and its
+ * unbiasedness and its error against stochastic rounding statistically.
  */
 #include <float.h>
 #include <math.h>
@@ -48,6 +60,8 @@
 #define NVO_COLWISE (1u << 1) /* logical tensor is x^T: blocks run down the columns of x */
 #define NVO_RHT (1u << 2)     /* random Hadamard transform of each 16-block before quantizing */
 #define NVO_SR (1u << 3)      /* stochastic rounding of the elements (else nearest-even) */
+#define NVO_RHT64 (1u << 5)   /* random Hadamard transform of each 64-group before quantizing */
+#define NVO_EDEN (1u << 6)    /* MS-EDEN: EDEN scale correction, stochastically rounded block scales */
 
 /* ------------------------------------------------------------------------- */
 /* E2M1 element format.                                                        */
@@ -129,6 +143,23 @@ NVO_EXPORT unsigned nvo_e4m3_encode(float u) {
   return ((unsigned)(E + 7) << 3) | m;
 }
 
+/* Stochastic rounding of a non-negative binary32 y onto the E4M3 grid (MS-EDEN's
+ * corrected block scales): between the neighbouring E4M3 values lo <= y < hi, the
+ * position f = (y - lo) / (hi - lo) is cut to 16 fraction bits, F = floor(f 2^16),
+ * and the value goes up when u16 + F >= 2^16 -- the same add-and-truncate rule as
+ * the elements' stochastic rounding, unbiased to 2^-16 of a step.  y >= 448
+ * saturates to 448 (code 0x7E); zero stays zero. */
+NVO_EXPORT unsigned nvo_e4m3_sr(float y, uint32_t u16) {
+  if (!(y > 0.0f)) return 0;
+  if (y >= 448.0f) return 0x7E;
+  unsigned lo = 0; /* walk up the grid to the largest value <= y */
+  while (lo < 0x7E && nvo_e4m3_value(lo + 1) <= (double)y) lo++;
+  double step = nvo_e4m3_value(lo + 1) - nvo_e4m3_value(lo); /* a power of two */
+  double frac = ((double)y - nvo_e4m3_value(lo)) / step;      /* exact */
+  uint32_t F = (uint32_t)floor(frac * 65536.0);
+  return lo + (((u16 & 0xFFFFu) + F >= 65536u) ? 1u : 0u);
+}
+
 /* ------------------------------------------------------------------------- */
 /* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy  */
 /* as 1, 2, 3", SC'11): ten rounds of two 32x32->64 multiplies, the key bumped  */
@@ -185,6 +216,36 @@ NVO_EXPORT void nvo_rht16(float v[16], uint32_t signs) {
 }
 
 /* ------------------------------------------------------------------------- */
+/* Random Hadamard transform of one 64-element group (the rotation of MS-EDEN): */
+/* the 64 random signs of group j are the first two words of Philox4x32-10 with */
+/* counter (j as two words, 0, 0) and key (the caller's 32-bit key, 0), element */
+/* t taking bit t % 32 of word t / 32; then the Sylvester-ordered H64 by the    */
+/* butterflies at distance 1, 2, 4, 8, 16, 32, and the factor 1/8 that makes it */
+/* orthonormal (exact: a power of two).                                          */
+/* ------------------------------------------------------------------------- */
+NVO_EXPORT void nvo_rht64_signs(uint64_t group, uint32_t key, uint32_t out[2]) {
+  uint32_t ctr[4] = {(uint32_t)group, (uint32_t)(group >> 32), 0u, 0u};
+  uint32_t k[2] = {key, 0u};
+  uint32_t w[4];
+  nvo_philox4x32_10(ctr, k, w);
+  out[0] = w[0];
+  out[1] = w[1];
+}
+
+NVO_EXPORT void nvo_rht64(float v[64], const uint32_t signs[2]) {
+  for (int t = 0; t < 64; ++t)
+    if ((signs[t >> 5] >> (t & 31)) & 1u) v[t] = -v[t];
+  for (int h = 1; h < 64; h <<= 1)
+    for (int i = 0; i < 64; ++i)
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  for (int t = 0; t < 64; ++t) v[t] = v[t] * 0.125f;
+}
+
+/* ------------------------------------------------------------------------- */
 /* The logical tensor.  Without COLWISE it is x itself ([R][C], row stride ld,  */
 /* K = C); with COLWISE it is x^T ([C][R], K = R).  Blocks are 16 consecutive  */
 /* elements along K; with RHT each block is transformed before anything else.  */
@@ -204,11 +265,25 @@ static logical_t make_logical(const float *x, int64_t R, int64_t C, int64_t ld, 
   return L;
 }
 
+static float load_elem(const logical_t *L, int64_t r, int64_t k) {
+  return (L->flags & NVO_COLWISE) ? L->x[k * L->ld + r] : L->x[r * L->ld + k];
+}
+
+/* Block kb of logical row r, transformed: with RHT its 16 elements, with RHT64 its
+ * quarter of the transformed 64-group it belongs to (the group is transformed
+ * whole for each of its blocks). */
 static void load_block(const logical_t *L, int64_t r, int64_t kb, float v[16]) {
-  for (int j = 0; j < 16; ++j) {
-    int64_t k = kb * 16 + j;
-    v[j] = (L->flags & NVO_COLWISE) ? L->x[k * L->ld + r] : L->x[r * L->ld + k];
+  if (L->flags & NVO_RHT64) {
+    float g[64];
+    uint32_t sg[2];
+    int64_t j = kb / 4;
+    for (int t = 0; t < 64; ++t) g[t] = load_elem(L, r, j * 64 + t);
+    nvo_rht64_signs((uint64_t)j, L->signs, sg);
+    nvo_rht64(g, sg);
+    for (int t = 0; t < 16; ++t) v[t] = g[(kb % 4) * 16 + t];
+    return;
   }
+  for (int j = 0; j < 16; ++j) v[j] = load_elem(L, r, kb * 16 + j);
   if (L->flags & NVO_RHT) nvo_rht16(v, L->signs);
 }
 
@@ -218,6 +293,7 @@ NVO_EXPORT float nvo_amax(const float *x, int64_t R, int64_t C, int64_t ld, unsi
   logical_t L = make_logical(x, R, C, ld, flags, signs);
   float amax = 0.0f;
   int64_t nkb = L.K / 16;
+  if (L.K % 16 != 0 || ((flags & NVO_RHT64) && L.K % 64 != 0)) return -1.0f; /* no such blocks */
 #pragma omp parallel for schedule(static) reduction(max : amax) num_threads(nthreads)
   for (int64_t r = 0; r < L.rows; ++r)
     for (int64_t kb = 0; kb < nkb; ++kb) {
@@ -268,6 +344,31 @@ static void encode_block(const float v[16], float mult, int sr, int64_t i0, uint
   }
 }
 
+/* MS-EDEN on one (transformed) block, after its scale code sc and multiplier are
+ * set: the elements are encoded nearest-even; with s the scaled values and e the
+ * grid values they round to, EDEN's correction factor is c = sum s^2 / sum s e (1
+ * when the second sum is not positive), so that the corrected block c e has the
+ * block's own projection onto s; c is folded into the block scale, whose decoded
+ * value times c is rounded back to E4M3 stochastically with the block's 16 random
+ * bits u16.  Sums run over the 16 elements in order, one binary32 operation per
+ * step.  Writes the 8 code bytes and returns the new scale code. */
+static unsigned eden_block(const float v[16], float mult, unsigned sc, uint32_t u16, uint8_t *codes_out) {
+  float s[16], e[16];
+  for (int j = 0; j < 16; ++j) {
+    s[j] = v[j] * mult;
+    unsigned c = nvo_e2m1_encode(s[j], 0, 0);
+    e[j] = (float)nvo_e2m1_value(c);
+    if (j & 1) codes_out[j / 2] |= (uint8_t)(c << 4);
+    else codes_out[j / 2] = (uint8_t)c;
+  }
+  float n = 0.0f, d = 0.0f;
+  for (int j = 0; j < 16; ++j) n = n + s[j] * s[j];
+  for (int j = 0; j < 16; ++j) d = d + s[j] * e[j];
+  float c = (d > 0.0f) ? n / d : 1.0f;
+  float y = (float)nvo_e4m3_value(sc) * c;
+  return nvo_e4m3_sr(y, u16);
+}
+
 /* Quantize logical rows [row0, row0 + nrows) of x.
  *   codes:  [nrows][K/2] bytes, two elements per byte, low nibble first
  *   scales: 1D [nrows][K/16]; 2D [nrows/16][K/16] (row0, nrows multiples of 16)
@@ -277,10 +378,16 @@ NVO_EXPORT int nvo_quantize(const float *x, int64_t R, int64_t C, int64_t ld, un
                             uint64_t seed, uint64_t offset, const float *amax_in, int64_t row0, int64_t nrows,
                             uint8_t *codes, uint8_t *scales, float *amax_out, int nthreads) {
   logical_t L = make_logical(x, R, C, ld, flags, signs);
-  int two_d = (flags & NVO_2D) != 0, sr = (flags & NVO_SR) != 0;
+  int two_d = (flags & NVO_2D) != 0, sr = (flags & NVO_SR) != 0, eden = (flags & NVO_EDEN) != 0;
   if (L.K % 16 != 0 || row0 < 0 || nrows < 0 || row0 + nrows > L.rows) return -1;
   if (two_d && (row0 % 16 != 0 || nrows % 16 != 0)) return -1;
+  if ((flags & NVO_RHT64) && (L.K % 64 != 0 || (flags & NVO_RHT) || two_d)) return -1;
+  if (eden && (!(flags & NVO_RHT64) || sr)) return -1;
   float amax = amax_in ? *amax_in : nvo_amax(x, R, C, ld, flags, signs, nthreads);
+  /* MS-EDEN keeps 7/4 of headroom in the tensor scale: the stored amax is 7/4 of the
+   * transformed tensor's, so that a block scale times its correction factor (about
+   * 1 +- 0.3) stays below the largest E4M3 value */
+  if (eden && !amax_in) amax = 1.75f * amax;
   if (amax_out) *amax_out = amax;
   float s_enc = encode_scale(amax);
   int64_t nkb = L.K / 16;
@@ -296,8 +403,13 @@ NVO_EXPORT int nvo_quantize(const float *x, int64_t R, int64_t C, int64_t ld, un
         for (int j = 0; j < 16; ++j)
           if (fabsf(v[j]) > amax_b) amax_b = fabsf(v[j]);
         block_scale(amax_b, s_enc, &sc, &mult);
+        if (eden) {
+          sc = eden_block(v, mult, sc, sr_bits((uint64_t)(r * nkb + kb), seed, offset),
+                          codes + rr * (L.K / 2) + kb * 8);
+        } else {
+          encode_block(v, mult, sr, r * L.K + kb * 16, seed, offset, codes + rr * (L.K / 2) + kb * 8);
+        }
         scales[rr * nkb + kb] = (uint8_t)sc;
-        encode_block(v, mult, sr, r * L.K + kb * 16, seed, offset, codes + rr * (L.K / 2) + kb * 8);
       }
     }
   } else {
@@ -352,4 +464,8 @@ NVO_EXPORT void nvo_e2m1_encode_n(const float *s, int64_t n, int stochastic, con
 
 NVO_EXPORT void nvo_e4m3_encode_n(const float *u, int64_t n, uint8_t *out) {
   for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)nvo_e4m3_encode(u[i]);
+}
+
+NVO_EXPORT void nvo_e4m3_sr_n(const float *y, int64_t n, const uint32_t *u16, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)nvo_e4m3_sr(y[i], u16[i]);
 }
