@@ -94,6 +94,8 @@ typedef enum fp4_dtype {
 #define FP4_Q_RHT (1u << 2)        /* random Hadamard transform of every 16-block first */
 #define FP4_Q_SR (1u << 3)         /* stochastic rounding (Philox4x32-10), else nearest-even */
 #define FP4_Q_AMAX_GIVEN (1u << 4) /* *out->amax already holds the tensor amax: skip its pass */
+#define FP4_Q_RHT64 (1u << 5)      /* random Hadamard transform of every 64-group first (MS-EDEN's rotation) */
+#define FP4_Q_EDEN (1u << 6)       /* MS-EDEN (with FP4_Q_RHT64): EDEN-corrected, stochastically rounded scales */
 
 /* A quantized logical tensor of `rows` x `cols`; cols is the blocked (contraction) dimension.
  *   codes : [rows][cols/2] bytes, element 2j in the low nibble of byte j
@@ -122,8 +124,9 @@ FP4_API fp4_status fp4_tensor_bytes(int64_t rows, int64_t cols, int32_t two_d, s
  * FP4_Q_RHT the amax is taken after the 16-point transform of the recipe sentence
  * (blocks along the logical rows).  Writes one float at amax_out (device).
  * Needs: the blocked dimension (cols, or rows with COLWISE) a multiple of 16 when
- * FP4_Q_RHT is set; ld >= cols; x 16-byte aligned and ld a multiple of 8 elements.
- * Errors: FP4_ERR_MODE (other flags), FP4_ERR_DTYPE, FP4_ERR_SHAPE, FP4_ERR_ALIGN,
+ * FP4_Q_RHT is set (of 64 with FP4_Q_RHT64, the 64-point transform of fp4_quantize,
+ * keyed by the 32-bit rht_signs); ld >= cols; x 16-byte aligned and ld a multiple of
+ * 8 elements.  Errors: FP4_ERR_MODE (other flags, or RHT with RHT64), FP4_ERR_DTYPE, FP4_ERR_SHAPE, FP4_ERR_ALIGN,
  * FP4_ERR_NULL (x with elements, or amax_out). */
 FP4_API fp4_status fp4_amax(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
                     uint32_t rht_signs, float *amax_out, hipStream_t stream);
@@ -140,9 +143,28 @@ FP4_API fp4_status fp4_amax(const void *x, fp4_dtype dtype, int64_t rows, int64_
  * codes are written; x must not overlap out->codes, as for any output).
  * out_t (FP4_Q_2D only, nullable) also receives L^T quantized with the same tile
  * scales: its codes and scales are the exact transposes of out's.
- * rht_signs: the transform's 16-bit sign mask (FP4_Q_RHT); seed, offset: the
- * Philox stream of stochastic rounding (FP4_Q_SR).
- * Modes: 1D with any of COLWISE, RHT, SR; 2D with COLWISE only (no RHT, no SR).
+ * rht_signs: the transform's 16-bit sign mask (FP4_Q_RHT), or the 32-bit key of the
+ * 64-point transform's signs (FP4_Q_RHT64); seed, offset: the Philox stream of
+ * stochastic rounding (FP4_Q_SR) or of MS-EDEN's scale rounding (FP4_Q_EDEN).
+ * MS-EDEN (Quartet II page, paragraph 1, MS-EDEN sentence: an unbiased routine for
+ * microscale formats with more than 2x lower error than stochastic rounding),
+ * read after EDEN's rotate - round - correct scheme:
+ *   FP4_Q_RHT64: in each 64-group along the blocked dimension, negate the elements
+ *     whose sign bit is set (group j's 64 bits: words 0 and 1 of Philox4x32-10 with
+ *     counter (j as two words, 0, 0) and key (rht_signs, 0), element t at bit t % 32
+ *     of word t / 32), apply Sylvester's H64 (butterflies at distance 1 .. 32) and
+ *     multiply by 1/8;
+ *   FP4_Q_EDEN (needs RHT64, excludes SR): elements nearest-even; per block, with
+ *     s the scaled values and e their grid values, c = sum s^2 / sum s e (in element
+ *     order; 1 if the second sum is not positive) and the scale code becomes
+ *     decode(S) * c rounded stochastically onto E4M3 (block b of the logical tensor
+ *     draws half-word b & 7 of Philox with counter (b >> 3, offset), key seed; it
+ *     goes up when those 16 bits plus the first 16 bits of the position between the
+ *     two E4M3 neighbours reach 2^16; 448 and above saturate); the stored tensor amax
+ *     is RN(7/4 * max |v|) -- with FP4_Q_AMAX_GIVEN, *out->amax holds that value.
+ * Modes: 1D with any of COLWISE, RHT, SR; 1D with RHT64 (and COLWISE, and SR or
+ * EDEN); 2D with COLWISE only (no RHT, no SR).  RHT64 needs L's cols a multiple of
+ * 64.
  * Needs: L's cols a multiple of 16 (and L's rows too for 2D); x 16-byte aligned,
  * ld a multiple of 8 elements; codes 16-byte and scales 8-byte aligned; with
  * COLWISE or 2D, x at most 16776960 rows (FP4_ERR_SHAPE otherwise).

@@ -21,6 +21,8 @@ Q_COLWISE = 1 << 1
 Q_RHT = 1 << 2
 Q_SR = 1 << 3
 Q_AMAX_GIVEN = 1 << 4
+Q_RHT64 = 1 << 5
+Q_EDEN = 1 << 6
 
 STATUS = {0: "FP4_OK", 1: "FP4_ERR_NULL", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_ALIGN", 4: "FP4_ERR_DTYPE",
           5: "FP4_ERR_MODE", 6: "FP4_ERR_MISMATCH", 7: "FP4_ERR_HIP", 8: "FP4_ERR_WORKSPACE"}

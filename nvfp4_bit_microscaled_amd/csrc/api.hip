@@ -33,10 +33,12 @@ fp4_status check_input(const void *x, fp4_dtype dtype, int64_t rows, int64_t col
 
 fp4_status check_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
                           const fp4_tensor *out, const fp4_tensor *out_t) {
-  const uint32_t known = FP4_Q_2D | FP4_Q_COLWISE | FP4_Q_RHT | FP4_Q_SR | FP4_Q_AMAX_GIVEN;
+  const uint32_t known = FP4_Q_2D | FP4_Q_COLWISE | FP4_Q_RHT | FP4_Q_SR | FP4_Q_AMAX_GIVEN | FP4_Q_RHT64 | FP4_Q_EDEN;
   if (flags & ~known) return FP4_ERR_MODE;
   const bool two_d = flags & FP4_Q_2D;
-  if (two_d && (flags & (FP4_Q_RHT | FP4_Q_SR))) return FP4_ERR_MODE;
+  if (two_d && (flags & (FP4_Q_RHT | FP4_Q_SR | FP4_Q_RHT64 | FP4_Q_EDEN))) return FP4_ERR_MODE;
+  if ((flags & FP4_Q_RHT) && (flags & FP4_Q_RHT64)) return FP4_ERR_MODE;
+  if ((flags & FP4_Q_EDEN) && (!(flags & FP4_Q_RHT64) || (flags & FP4_Q_SR))) return FP4_ERR_MODE;
   if (out_t && !two_d) return FP4_ERR_MODE;
   fp4_status s = check_input(x, dtype, rows, cols, ld);
   if (s != FP4_OK) return s;
@@ -45,6 +47,7 @@ fp4_status check_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t 
   if (lcols % 16 != 0) return FP4_ERR_SHAPE;
   if (two_d && lrows % 16 != 0) return FP4_ERR_SHAPE;
   if ((flags & FP4_Q_RHT) && colwise && rows % 16 != 0) return FP4_ERR_SHAPE;
+  if ((flags & FP4_Q_RHT64) && lcols % 64 != 0) return FP4_ERR_SHAPE;
   // columnwise and 2D launches give each 256 rows of x one grid row (at most 65535)
   if ((colwise || two_d) && (rows + 255) / 256 > 65535) return FP4_ERR_SHAPE;
   if ((s = check_tensor(out, lrows, lcols, two_d)) != FP4_OK) return s;
@@ -66,6 +69,9 @@ fp4_status check_gemm(const fp4_tensor *a, const fp4_tensor *b, const void *c, f
   if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
   return FP4_OK;
 }
+
+// The transform's signs: a 16-bit mask (16-point transform) or a 32-bit key (64-point).
+uint32_t sign_key(uint32_t flags, uint32_t rht_signs) { return (flags & FP4_Q_RHT64) ? rht_signs : rht_signs & 0xFFFFu; }
 
 // The workspace of the GEMMs' split-K partial tiles: empty, or 16-byte aligned.
 fp4_status check_ws(const void *ws, size_t ws_bytes) {
@@ -93,15 +99,15 @@ fp4_status fp4_tensor_bytes(int64_t rows, int64_t cols, int32_t two_d, size_t *c
 
 fp4_status fp4_amax(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
                     uint32_t rht_signs, float *amax_out, hipStream_t stream) {
-  if (flags & ~(FP4_Q_COLWISE | FP4_Q_RHT)) return FP4_ERR_MODE;
+  if (flags & ~(FP4_Q_COLWISE | FP4_Q_RHT | FP4_Q_RHT64)) return FP4_ERR_MODE;
+  if ((flags & FP4_Q_RHT) && (flags & FP4_Q_RHT64)) return FP4_ERR_MODE;
   fp4_status s = check_input(x, dtype, rows, cols, ld);
   if (s != FP4_OK) return s;
   if (!amax_out) return FP4_ERR_NULL;
-  if (flags & FP4_Q_RHT) {
-    const int64_t blocked = (flags & FP4_Q_COLWISE) ? rows : cols;
-    if (blocked % 16 != 0) return FP4_ERR_SHAPE;
-  }
-  return from_hip(nvfp4::launch_amax(x, dtype, rows, cols, ld, flags, rht_signs & 0xFFFFu, amax_out, stream));
+  const int64_t blocked = (flags & FP4_Q_COLWISE) ? rows : cols;
+  if ((flags & FP4_Q_RHT) && blocked % 16 != 0) return FP4_ERR_SHAPE;
+  if ((flags & FP4_Q_RHT64) && blocked % 64 != 0) return FP4_ERR_SHAPE;
+  return from_hip(nvfp4::launch_amax(x, dtype, rows, cols, ld, flags, sign_key(flags, rht_signs), amax_out, stream));
 }
 
 fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,
@@ -109,8 +115,8 @@ fp4_status fp4_quantize(const void *x, fp4_dtype dtype, int64_t rows, int64_t co
                         const fp4_tensor *out_t, hipStream_t stream) {
   fp4_status s = check_quantize(x, dtype, rows, cols, ld, flags, out, out_t);
   if (s != FP4_OK) return s;
-  return from_hip(
-      nvfp4::launch_quantize(x, dtype, rows, cols, ld, flags, rht_signs & 0xFFFFu, seed, offset, out, out_t, stream));
+  return from_hip(nvfp4::launch_quantize(x, dtype, rows, cols, ld, flags, sign_key(flags, rht_signs), seed, offset,
+                                         out, out_t, stream));
 }
 
 fp4_status fp4_quantize_dual(const void *x, fp4_dtype dtype, int64_t rows, int64_t cols, int64_t ld, uint32_t flags,

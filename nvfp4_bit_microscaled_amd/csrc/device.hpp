@@ -216,6 +216,85 @@ __device__ __forceinline__ void sr_bits16(uint64_t i0, uint64_t seed, uint64_t o
   r[4] = b.v[0]; r[5] = b.v[1]; r[6] = b.v[2]; r[7] = b.v[3];
 }
 
+// The 64 random signs of 64-group j of the 64-point transform (MS-EDEN's rotation):
+// words 0 and 1 of Philox4x32-10 with counter (j as two words, 0, 0) and key (key, 0);
+// element t of the group takes bit t % 32 of word t / 32.
+__device__ __forceinline__ void rht64_signs(uint64_t group, uint32_t key, uint32_t &w0, uint32_t &w1) {
+  const Philox4 p = philox4x32_10(uint32_t(group), uint32_t(group >> 32), 0u, 0u, key, 0u);
+  w0 = p.v[0];
+  w1 = p.v[1];
+}
+
+// The 16 bits of a 64-group's signs that belong to its quarter q (elements 16 q ..
+// 16 q + 15), bit r for element 16 q + r.
+__device__ __forceinline__ uint32_t rht64_quarter(uint32_t w0, uint32_t w1, int q) {
+  return ((q & 2) ? w1 : w0) >> (16 * (q & 1)) & 0xFFFFu;
+}
+
+// The 16 random bits of logical block b (MS-EDEN's scale rounding): half-word b & 7
+// of Philox4x32-10 with counter (b >> 3 as two words, offset as two words), key seed.
+__device__ __forceinline__ uint32_t block_bits16(uint64_t b, uint64_t seed, uint64_t offset) {
+  const uint64_t g = b >> 3;
+  const Philox4 p = philox4x32_10(uint32_t(g), uint32_t(g >> 32), uint32_t(offset), uint32_t(offset >> 32),
+                                  uint32_t(seed), uint32_t(seed >> 32));
+  const uint32_t j = uint32_t(b & 7u);
+  return (p.v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+}
+
+// Stochastic rounding of a non-negative binary32 y onto the E4M3 grid: with F the
+// first 16 bits of y's position between its neighbouring E4M3 values, y goes up one
+// code when u16 + F >= 2^16 (the add-and-truncate rule of the elements).  E4M3 codes
+// are consecutive in value, so going up is code + 1.  Normal range (y >= 2^-6): the
+// code is y's exponent and top 3 mantissa bits, F the next 16 bits.  Subnormal range:
+// y * 2^9 (exact) splits into the code (its integer part) and the position.  y >=
+// 448 saturates to 0x7E; zero stays zero.
+__device__ __forceinline__ uint32_t e4m3_sr(float y, uint32_t u16) {
+  if (!(y > 0.0f)) return 0u;
+  if (y >= 448.0f) return 0x7Eu;
+  uint32_t lo, F;
+  if (y >= 0x1p-6f) {
+    const uint32_t b = __float_as_uint(y);
+    lo = ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);
+    F = (b >> 4) & 0xFFFFu;
+  } else {
+    const float t = y * 512.0f;
+    const float fl = __builtin_floorf(t);
+    lo = uint32_t(fl);
+    F = uint32_t(__builtin_floorf((t - fl) * 65536.0f));
+  }
+  return lo + ((u16 + F) >> 16);
+}
+
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// MS-EDEN's correction of one block: s the 16 scaled values, codes their
+// nearest-even E2M1 codes (two words), sc the block's scale code.  With e the grid
+// values of the codes, c = sum s^2 / sum s e (1 when the second sum is not positive),
+// each sum over the 16 elements in order, one binary32 operation per step; the new
+// scale code is decode(sc) * c rounded stochastically with the block's 16 bits.
+// The E2M1 grid values come from gfx950's FP4 -> f32 converter (exact: every E2M1
+// value is a binary32 value).
+__device__ __forceinline__ uint32_t eden_scale(const float s[16], uint2 codes, uint32_t sc, uint32_t u16) {
+  float e[16];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w = h == 0 ? codes.x : codes.y;
+    const f32x2v e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2v e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2v e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2v e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    e[8 * h + 0] = e0[0]; e[8 * h + 1] = e0[1]; e[8 * h + 2] = e1[0]; e[8 * h + 3] = e1[1];
+    e[8 * h + 4] = e2[0]; e[8 * h + 5] = e2[1]; e[8 * h + 6] = e3[0]; e[8 * h + 7] = e3[1];
+  }
+  float n = 0.0f, d = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) n = n + s[j] * s[j];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) d = d + s[j] * e[j];
+  const float c = d > 0.0f ? n / d : 1.0f;
+  return e4m3_sr(e4m3_to_f32(sc) * c, u16);
+}
+
 // Butterflies of the 16-point Hadamard transform (distances 1, 2, 4, 8), without
 // its factor 1/4: for a maximum of |v| the factor is applied once to the result,
 // which gives the same value (multiplying by 1/4 and rounding is monotone, so the

@@ -146,9 +146,10 @@ __device__ __forceinline__ void block_max_to(float v, float *out, float *partial
   __syncthreads();  // part[] is reused by a second reduction in the same kernel
 }
 
-// out[t] = max of partial[t * n .. t * n + n) for t < nout (one workgroup).
+// out[t] = factor * (max of partial[t * n .. t * n + n)) for t < nout (one
+// workgroup; factor 1, or MS-EDEN's headroom 7/4).
 __global__ __launch_bounds__(kThreads) void amax_finish_kernel(const float *__restrict__ partial, int n, int nout,
-                                                               float *out0, float *out1) {
+                                                               float *out0, float *out1, float factor) {
   __shared__ float part[kThreads / 64];
   for (int t = 0; t < nout; ++t) {
     float m = 0.0f;
@@ -158,13 +159,14 @@ __global__ __launch_bounds__(kThreads) void amax_finish_kernel(const float *__re
     __syncthreads();
     if (threadIdx.x == 0) {
       for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, part[i]);
-      *(t == 0 ? out0 : out1) = m;
+      *(t == 0 ? out0 : out1) = factor * m;
     }
     __syncthreads();
   }
 }
 
 __global__ void zero_f32_kernel(float *p) { *p = 0.0f; }
+__global__ void scale_f32_kernel(float *p, float factor) { *p = factor * *p; }
 __global__ void zero2_f32_kernel(float *p, float *q) {
   *p = 0.0f;
   *q = 0.0f;
@@ -539,6 +541,215 @@ __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict
                                                                                             // factor, once
 }
 
+// ---------------------------------------------------------------------------
+// The 64-point transform (MS-EDEN's rotation) and the kernels that use it.  A
+// 64-group is four 16-blocks; each block sits in one thread, and the butterflies at
+// distance 16 and 32 pair the block with the group's other blocks held by other
+// lanes: lanes 4k .. 4k+3 (rowwise, DPP quad exchanges) or lanes l, l ^ 16, l ^ 32,
+// l ^ 48 (columnwise, a 16-row slab per lane).  The butterflies run in the order
+// 1, 2, 4, 8 (in registers), then 16 and 32; the factor 1/8 comes last.
+
+// Partner exchange inside a DPP quad: lane ^ 1 (quad_perm [1,0,3,2]) or lane ^ 2
+// ([2,3,0,1]).  Every lane of the quad is active whenever one is.
+template <int XOR>
+__device__ __forceinline__ float quad_xor(float v) {
+  constexpr int ctrl = XOR == 1 ? 0xB1 : 0x4E;
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// One butterfly stage across lanes: the lane holding the group's lower half keeps
+// a + b, the upper one a - b (a from the lower half, b from the upper).
+__device__ __forceinline__ float butterfly(float own, float partner, bool upper) {
+  return upper ? partner - own : own + partner;
+}
+
+// Rowwise: v holds quarter q (= lane & 3 of its quad) of a 64-group, its signs
+// (the quarter's 16 bits) not yet applied.
+__device__ __forceinline__ void rotate64_quad(float v[16], uint32_t sign16, int q) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = ((sign16 >> j) & 1u) ? -v[j] : v[j];
+  hadamard16_unscaled(v);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = butterfly(v[j], quad_xor<1>(v[j]), q & 1);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = butterfly(v[j], quad_xor<2>(v[j]), q & 2);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.125f;
+}
+
+// Columnwise: col holds one column of the 16-row slab that is quarter q (= lane >> 4)
+// of its 64-group, signs already applied; partners are lanes ^ 16 and ^ 32.
+__device__ __forceinline__ void rotate64_cols(float col[16], int q) {
+  hadamard16_unscaled(col);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) col[r] = butterfly(col[r], __shfl_xor(col[r], 16, 64), q & 1);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) col[r] = butterfly(col[r], __shfl_xor(col[r], 32, 64), q & 2);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) col[r] = col[r] * 0.125f;
+}
+
+// One transformed block: scale, then the elements nearest-even (with EDEN, the
+// scale code then corrected), or stochastically.  eb: the block's logical index
+// (EDEN's random bits); i0: its first element's logical index (element SR).
+template <bool EDEN, bool SR>
+__device__ __forceinline__ void quant_block64(const float v[16], float s_enc, const float *tab, uint64_t eb, uint64_t i0,
+                                              uint64_t seed, uint64_t offset, uint2 &codes, uint32_t &sc) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, __builtin_fabsf(v[j]));
+  float mult;
+  block_scale(amax_b, s_enc, tab, sc, mult);
+  float s[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s[j] = v[j] * mult;
+  if (SR) {
+    uint32_t rb[8];
+    sr_bits16(i0, seed, offset, rb);
+    codes = make_uint2(encode8_sr(s, rb), encode8_sr(s + 8, rb + 4));
+  } else {
+    codes = make_uint2(encode8_rne(s), encode8_rne(s + 8));
+    if (EDEN) sc = eden_scale(s, codes, sc, block_bits16(eb, seed, offset));
+  }
+}
+
+// Rowwise quantization with the 64-point transform, x [R][C] with row stride ld
+// (C a multiple of 64): thread q of the grid-stride loop owns logical block q (row
+// q / (C/16), block q % (C/16)); quads of lanes hold whole 64-groups.
+template <typename T, bool EDEN, bool SR>
+__global__ __launch_bounds__(kThreads) void quant_rows64_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                               int64_t ld, uint32_t key, uint64_t seed,
+                                                               uint64_t offset, const float *__restrict__ amax_p,
+                                                               uint8_t *__restrict__ codes,
+                                                               uint8_t *__restrict__ scales) {
+  __shared__ float tab[kMultTable];
+  const float s_enc = encode_scale(*amax_p);
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
+  const int64_t nkb = C / 16, total = R * nkb;
+  for (int64_t q = int64_t(blockIdx.x) * kThreads + threadIdx.x; q < total; q += int64_t(gridDim.x) * kThreads) {
+    const int64_t r = q / nkb, kb = q - r * nkb;
+    float v[16];
+    load8(x + r * ld + kb * 16, v);
+    load8(x + r * ld + kb * 16 + 8, v + 8);
+    uint32_t w0, w1;
+    rht64_signs(uint64_t(kb >> 2), key, w0, w1);
+    rotate64_quad(v, rht64_quarter(w0, w1, int(kb & 3)), int(kb & 3));
+    uint2 c;
+    uint32_t sc;
+    quant_block64<EDEN, SR>(v, s_enc, tab, uint64_t(q), uint64_t(r) * uint64_t(C) + uint64_t(kb) * 16u, seed, offset,
+                            c, sc);
+    *reinterpret_cast<uint2 *>(codes + q * 8) = c;
+    scales[q] = uint8_t(sc);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_rht64_rows_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                                  int64_t ld, uint32_t key, float *out,
+                                                                  float *partial) {
+  const int64_t nkb = C / 16, total = R * nkb;
+  float m = 0.0f;
+  for (int64_t q = int64_t(blockIdx.x) * kThreads + threadIdx.x; q < total; q += int64_t(gridDim.x) * kThreads) {
+    const int64_t r = q / nkb, kb = q - r * nkb;
+    float v[16];
+    load8(x + r * ld + kb * 16, v);
+    load8(x + r * ld + kb * 16 + 8, v + 8);
+    uint32_t w0, w1;
+    rht64_signs(uint64_t(kb >> 2), key, w0, w1);
+    rotate64_quad(v, rht64_quarter(w0, w1, int(kb & 3)), int(kb & 3));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+  }
+  block_max_to(m, out, partial);
+}
+
+// Columnwise quantization with the 64-point transform (logical tensor x^T, groups
+// of 64 rows of x; R a multiple of 64).  A workgroup covers kColTile columns and
+// kColSlabs 16-row slabs (four groups), as quant_cols_kernel, and leaves through the
+// same LDS gather.  Thread (wave w, lane l): columns 128 (w & 1) + 8 (l & 15) .. +7
+// of the tile, slab 4 g + (l >> 4) of group g = (w >> 1) + 2 i (i = 0, 1), so the
+// four slabs of a group sit in lanes l, l ^ 16, l ^ 32, l ^ 48 of one wave.
+template <typename T, bool EDEN, bool SR>
+__global__ __launch_bounds__(kThreads) void quant_cols64_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                               int64_t ld, uint32_t key, uint64_t seed,
+                                                               uint64_t offset, const float *__restrict__ amax_p,
+                                                               uint8_t *__restrict__ codes,
+                                                               uint8_t *__restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint8_t lcodes[kColTile * kColRowBytes];
+  __shared__ uint8_t lscales[kColTile * kColSlabs];
+  __shared__ float tab[kMultTable];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = lane & 15, sq = lane >> 4;
+  const int64_t c0 = int64_t(blockIdx.x) * kColTile;
+  const int64_t slab0 = int64_t(blockIdx.y) * kColSlabs;
+  const int64_t nslab = R / 16;
+  const int64_t cfirst = c0 + 128 * (wave & 1) + 8 * cg;
+  const float s_enc = encode_scale(*amax_p);
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
+#pragma unroll 1
+  for (int i = 0; i < 2; ++i) {
+    const int sl = 4 * ((wave >> 1) + 2 * i) + sq;  // slab within the tile
+    const int64_t s = slab0 + sl;
+    // a group is inside or outside x whole (nslab % 4 == 0); lanes l ^ 16, l ^ 32
+    // own the same columns, so exchange partners are active together
+    if (s >= nslab || cfirst >= C) continue;
+    uint32_t w0, w1;
+    rht64_signs(uint64_t(s >> 2), key, w0, w1);
+    Slab8<T> slab;
+    slab.load(x + s * 16 * ld + cfirst, ld, rht64_quarter(w0, w1, sq));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
+      rotate64_cols(col, sq);
+      const int64_t c = cfirst + j;  // logical row
+      uint2 packed;
+      uint32_t sc;
+      quant_block64<EDEN, SR>(col, s_enc, tab, uint64_t(c) * uint64_t(nslab) + uint64_t(s),
+                              uint64_t(c) * uint64_t(R) + uint64_t(s) * 16u, seed, offset, packed, sc);
+      const int row = 128 * (wave & 1) + 8 * cg + j;  // logical row within the tile
+      const int pair = (sl >> 1) ^ ((row >> 3) & 7);
+      *reinterpret_cast<uint2 *>(&lcodes[row * kColRowBytes + pair * 16 + (sl & 1) * 8]) = packed;
+      lscales[row * kColSlabs + sl] = uint8_t(sc);
+    }
+  }
+  __syncthreads();
+  store_col_tile(lcodes, lscales, R, C, c0, slab0, codes, scales);
+}
+
+// amax after the 64-point transform down columns: each wave takes units of one
+// group (64 rows) x 128 columns, lanes as in quant_cols64_kernel.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_rht64_cols_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                                  int64_t ld, uint32_t key, float *out,
+                                                                  float *partial) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = lane & 15, sq = lane >> 4;
+  const int64_t cblocks = (C + 127) / 128, units = (R / 64) * cblocks;
+  float m = 0.0f;
+  for (int64_t u = int64_t(blockIdx.x) * 4 + wave; u < units; u += int64_t(gridDim.x) * 4) {
+    const int64_t g = u / cblocks, cfirst = (u - g * cblocks) * 128 + 8 * cg;
+    if (cfirst >= C) continue;  // lanes l ^ 16, l ^ 32 skip together
+    uint32_t w0, w1;
+    rht64_signs(uint64_t(g), key, w0, w1);
+    Slab8<T> slab;
+    slab.load(x + (4 * g + sq) * 16 * ld + cfirst, ld, rht64_quarter(w0, w1, sq));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
+      rotate64_cols(col, sq);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, __builtin_fabsf(col[r]));
+    }
+  }
+  block_max_to(m, out, partial);
+}
+
 // 2D (16x16 tile) nearest-even quantization of x [R][C] (R, C multiples of 16).
 // Writes the direct layout (codes [R][C/2], scales [R/16][C/16]) to d_* and/or the
 // transposed layout (codes [C][R/2], scales [C/16][R/16]) to t_*; either may be null.
@@ -688,15 +899,23 @@ float *partial_room(const fp4_tensor *t) {
 // Tensor amax into *out.  With `partial` (room for 1024 floats), every workgroup
 // stores its maximum there and amax_finish_kernel reduces them; without it, *out
 // is zeroed and every workgroup folds its maximum in with an atomic.
+// With FP4_Q_EDEN the stored amax is 7/4 of the pass's (MS-EDEN's headroom).
 template <typename T>
 hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flags, uint32_t signs, float *out,
                      float *partial, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  const float factor = (flags & FP4_Q_EDEN) ? 1.75f : 1.0f;
   if (R == 0 || C == 0 || !partial) e = launch(zero_f32_kernel, dim3(1), dim3(1), stream, out);
   if (e != hipSuccess || R == 0 || C == 0) return e;
   const int64_t cap = partial ? 1024 : 256 * 16;  // 16 workgroups per CU are plenty for a streaming reduction
   dim3 grid;
-  if (!(flags & FP4_Q_RHT) && ld == C) {
+  if ((flags & FP4_Q_RHT64) && (flags & FP4_Q_COLWISE)) {
+    grid = dim3(grid_for((R / 64) * ((C + 127) / 128), 4, cap));
+    e = launch(amax_rht64_cols_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
+  } else if (flags & FP4_Q_RHT64) {
+    grid = dim3(grid_for(R * (C / 16), kThreads * 2, cap));
+    e = launch(amax_rht64_rows_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
+  } else if (!(flags & FP4_Q_RHT) && ld == C) {
     // four workgroups per CU: on the MI355X a 200 MB read-only stream took 37 us with
     // 1024 workgroups, 52 us with 512 (kernel time without the atomics)
     grid = dim3(grid_for(R * (C / 8), kThreads * 4, 1024));
@@ -712,7 +931,9 @@ hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
     e = launch(amax_rht_rows_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
   }
   if (e == hipSuccess && partial)
-    e = launch(amax_finish_kernel, dim3(1), dim3(kThreads), stream, partial, int(grid.x), 1, out, out);
+    e = launch(amax_finish_kernel, dim3(1), dim3(kThreads), stream, partial, int(grid.x), 1, out, out, factor);
+  else if (e == hipSuccess && factor != 1.0f)
+    e = launch(scale_f32_kernel, dim3(1), dim3(1), stream, out, factor);
   return e;
 }
 
@@ -739,6 +960,19 @@ hipError_t launch_cols(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t si
                 out->amax, out->codes, out->scales, nullptr, nullptr, nullptr);
 }
 
+template <typename T, bool EDEN, bool SR>
+hipError_t launch_rht64(const T *x, int64_t R, int64_t C, int64_t ld, bool colwise, uint32_t key, uint64_t seed,
+                        uint64_t offset, const fp4_tensor *out, hipStream_t stream) {
+  if (colwise) {
+    const int64_t nslab = R / 16;
+    dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
+    return launch(quant_cols64_kernel<T, EDEN, SR>, grid, dim3(kThreads), stream, x, R, C, ld, key, seed, offset,
+                  out->amax, out->codes, out->scales);
+  }
+  return launch(quant_rows64_kernel<T, EDEN, SR>, dim3(grid_for(R * (C / 16), kThreads, 1 << 20)), dim3(kThreads),
+                stream, x, R, C, ld, key, seed, offset, out->amax, out->codes, out->scales);
+}
+
 // Both nearest-even layouts of x in one kernel: cols (x^T, transformed when RHT)
 // and rows (x).  Each takes its own tensor amax from its descriptor.
 template <typename T, bool RHT>
@@ -760,6 +994,12 @@ hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t 
   }
   if (R == 0 || C == 0) return hipSuccess;
   const bool rht = flags & FP4_Q_RHT, sr = flags & FP4_Q_SR;
+  if (flags & FP4_Q_RHT64) {
+    const bool cw = flags & FP4_Q_COLWISE;
+    if (flags & FP4_Q_EDEN) return launch_rht64<T, true, false>(x, R, C, ld, cw, signs, seed, offset, out, stream);
+    if (sr) return launch_rht64<T, false, true>(x, R, C, ld, cw, signs, seed, offset, out, stream);
+    return launch_rht64<T, false, false>(x, R, C, ld, cw, signs, seed, offset, out, stream);
+  }
   if (flags & FP4_Q_2D) {
     // direct layout is x's; with COLWISE the logical tensor is x^T, so `out` takes
     // the transposed layout and `out_t` the direct one.
@@ -811,7 +1051,7 @@ hipError_t dual_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
                        cols->amax, partial);
       if (e == hipSuccess && partial)
         e = launch(amax_finish_kernel, dim3(1), dim3(kThreads), stream, partial, int(grid.x), 2, rows->amax,
-                   cols->amax);
+                   cols->amax, 1.0f);
     }
   }
   if (e != hipSuccess || R == 0 || C == 0) return e;

@@ -294,12 +294,22 @@ NVO_EXPORT float nvo_amax(const float *x, int64_t R, int64_t C, int64_t ld, unsi
   float amax = 0.0f;
   int64_t nkb = L.K / 16;
   if (L.K % 16 != 0 || ((flags & NVO_RHT64) && L.K % 64 != 0)) return -1.0f; /* no such blocks */
+  /* with RHT64 each transformed block is read once: block 4 j + q of a group is
+   * quarter q of the group's transform, so taking whole groups covers every block */
+  int64_t step = (flags & NVO_RHT64) ? 4 : 1, width = 16 * step;
 #pragma omp parallel for schedule(static) reduction(max : amax) num_threads(nthreads)
   for (int64_t r = 0; r < L.rows; ++r)
-    for (int64_t kb = 0; kb < nkb; ++kb) {
-      float v[16];
-      load_block(&L, r, kb, v);
-      for (int j = 0; j < 16; ++j)
+    for (int64_t kb = 0; kb < nkb; kb += step) {
+      float v[64];
+      if (flags & NVO_RHT64) {
+        uint32_t sg[2];
+        for (int t = 0; t < 64; ++t) v[t] = load_elem(&L, r, kb * 16 + t);
+        nvo_rht64_signs((uint64_t)(kb / 4), L.signs, sg);
+        nvo_rht64(v, sg);
+      } else {
+        load_block(&L, r, kb, v);
+      }
+      for (int j = 0; j < width; ++j)
         if (fabsf(v[j]) > amax) amax = fabsf(v[j]);
     }
   return amax;

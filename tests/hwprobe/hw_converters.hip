@@ -152,6 +152,20 @@ __global__ __launch_bounds__(kThreads) void dequant_table_kernel(uint32_t *__res
   }
 }
 
+// The FP4 -> f32 converter MS-EDEN reads its grid values with (scale operand 1):
+// out[(c * 4 + sel) * 2 + e] = element e of byte c placed at byte sel.
+__global__ __launch_bounds__(kThreads) void fp4_f32_table_kernel(float *__restrict__ out) {
+  for (int c = threadIdx.x; c < 256; c += kThreads) {
+    const f32x2v a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uint32_t(c), 1.0f, 0);
+    const f32x2v b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uint32_t(c) << 8, 1.0f, 1);
+    const f32x2v d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uint32_t(c) << 16, 1.0f, 2);
+    const f32x2v g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uint32_t(c) << 24, 1.0f, 3);
+    const int o = c * 8;
+    out[o + 0] = a[0]; out[o + 1] = a[1]; out[o + 2] = b[0]; out[o + 3] = b[1];
+    out[o + 4] = d[0]; out[o + 5] = d[1]; out[o + 6] = g[0]; out[o + 7] = g[1];
+  }
+}
+
 // The FP4 -> f16 converter with an f32 scale operand other than 1 (the property
 // that makes the GEMM apply the E4M3 scale by a separate multiply): the two
 // elements of code byte bytes[i] (at byte 0) with scale operand scales[i], as one
@@ -222,6 +236,11 @@ __attribute__((visibility("default"))) int hwc_fp4_cvt_scaled(const uint8_t *byt
                                                               uint32_t *out, int64_t n, hipStream_t stream) {
   hipLaunchKernelGGL(fp4_cvt_scaled_kernel, dim3(grid(uint64_t(n))), dim3(kThreads), 0, stream, bytes, scales, out,
                      n);
+  return int(hipPeekAtLastError());
+}
+
+__attribute__((visibility("default"))) int hwc_fp4_f32_table(float *out, hipStream_t stream) {
+  hipLaunchKernelGGL(fp4_f32_table_kernel, dim3(1), dim3(kThreads), 0, stream, out);
   return int(hipPeekAtLastError());
 }
 

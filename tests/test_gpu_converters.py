@@ -12,7 +12,9 @@ device helpers from nvfp4_bit_microscaled_amd/csrc/device.hpp):
   whose unbiasedness is what the Quartet II page (paragraph 1) asks of SR;
 * the GEMM's operand dequantization (dequant2: FP4 -> f16 converter, times the f16
   of the E4M3 scale) for every code byte, byte position and scale code;
-* the FP4 -> f16 converter's f32 scale operand acting as its power of two only.
+* the FP4 -> f16 converter's f32 scale operand acting as its power of two only;
+* the FP4 -> f32 converter MS-EDEN reads grid values with, for every code byte and
+  byte position.
 
 The expected values come from the oracle alone: each encoder of the oracle is a
 monotone step function of its input (nearest-even of a magnitude; for stochastic
@@ -48,6 +50,7 @@ def hw(fp4):
         "hwc_fp4_sr_encode": [vp, vp, vp, i64, vp],
         "hwc_dequant_table": [vp, vp],
         "hwc_fp4_cvt_scaled": [vp, vp, vp, i64, vp],
+        "hwc_fp4_f32_table": [vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -249,3 +252,14 @@ def test_fp4_converter_scale_operand_is_a_power_of_two(hw, oracle):
     e2 = np.array([oracle.e2m1_value(c) for c in range(16)])
     want = np.stack([e2[cb & 15], e2[cb >> 4]], axis=1) * np.ldexp(1.0, kk)[:, None]
     np.testing.assert_array_equal(got, want)
+
+
+def test_fp4_to_f32_converter_every_code(hw, oracle):
+    out = torch.empty(256 * 8, dtype=torch.float32, device="cuda")
+    assert hw.hwc_fp4_f32_table(ctypes.c_void_p(out.data_ptr()), _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64).reshape(256, 4, 2)
+    e2 = np.array([oracle.e2m1_value(c) for c in range(16)])
+    for c in range(256):
+        for sel in range(4):
+            assert got[c, sel, 0] == e2[c & 15] and got[c, sel, 1] == e2[c >> 4], (c, sel)
