@@ -67,7 +67,16 @@ ERROR_MODES = {  # operand A (activation- or gradient-like), operand B (weight-l
     "rht": ("rht", "rht"),
     "sr": ("sr", 0),
     "rht_sr": ("rht_sr", "rht"),
+    "rht64_sr": ("rht64_sr", "rht64"),
+    "eden": ("eden", "rht64"),
 }
+
+
+def mode_flag(fp4, m):
+    """fp4_quantize flags of an operand mode of ERROR_MODES (rht: the 16-point
+    transform; rht64: the 64-point one; eden: MS-EDEN)."""
+    return {0: 0, "rne": 0, "rht": fp4.Q_RHT, "sr": fp4.Q_SR, "rht_sr": fp4.Q_RHT | fp4.Q_SR, "rht64": fp4.Q_RHT64,
+            "rht64_sr": fp4.Q_RHT64 | fp4.Q_SR, "eden": fp4.Q_RHT64 | fp4.Q_EDEN}[m]
 
 
 def quantized_gemm_error(fp4, a, b, mode, signs, seed=0, offset=1):
@@ -78,17 +87,104 @@ def quantized_gemm_error(fp4, a, b, mode, signs, seed=0, offset=1):
     quantization) and stochastic rounding of A.  Returns (error, C_q)."""
     import torch
     fa, fb = ERROR_MODES[mode]
-    flag = {0: 0, "rht": fp4.Q_RHT, "sr": fp4.Q_SR, "rht_sr": fp4.Q_RHT | fp4.Q_SR}
     M, K = a.shape
     N = b.shape[0]
     qa, qb = fp4.QTensor(M, K), fp4.QTensor(N, K)
-    fp4.fp4_quantize(a, flag[fa], signs, seed, offset, qa)
-    fp4.fp4_quantize(b, flag[fb], signs, seed, offset, qb)
+    fp4.fp4_quantize(a, mode_flag(fp4, fa), signs, seed, offset, qa)
+    fp4.fp4_quantize(b, mode_flag(fp4, fb), signs, seed, offset, qb)
     c = torch.empty(M, N, dtype=torch.float32, device=a.device)
     fp4.fp4_gemm(qa, qb, c)
     ref = a.double() @ b.double().T.contiguous()
     err = float(torch.linalg.norm(c.double() - ref) / torch.linalg.norm(ref))
     return err, c
+
+
+QUANT_MODES = {  # A's mode -> the rotation of the identity that undoes A's
+    "rne": 0, "sr": 0, "rht_sr": "rht", "rht64_sr": "rht64", "rht64": "rht64", "eden": "rht64"}
+
+
+def identity_operand(fp4, K, mode, signs, device="cuda"):
+    """The K x K identity quantized nearest-even with the rotation of `mode`'s
+    operand A: its rows are the rotated unit vectors (entries 0, +-1/4 or +-1/8, all
+    exact in NVFP4), so deq(A_q) . deq(I_q)^T is A's dequantized estimate rotated
+    back -- the quantizer's output in A's own coordinates, from the product path."""
+    import torch
+    eye = torch.eye(K, dtype=torch.bfloat16, device=device)
+    q = fp4.QTensor(K, K)
+    fp4.fp4_quantize(eye, mode_flag(fp4, QUANT_MODES[mode]), signs, 0, 0, q)
+    return q
+
+
+def quantizer_estimate(fp4, a, mode, signs, ident, seed=0, offset=1):
+    """A's NVFP4 estimate in A's coordinates (fp32 [M, K]): A quantized in `mode`,
+    times the identity quantized with the same rotation."""
+    import torch
+    M, K = a.shape
+    qa = fp4.QTensor(M, K)
+    fp4.fp4_quantize(a, mode_flag(fp4, mode), signs, seed, offset, qa)
+    c = torch.empty(M, K, dtype=torch.float32, device=a.device)
+    fp4.fp4_gemm(qa, ident, c)
+    return c
+
+
+def quantizer_errors(fp4, data, K=4096, M=512, draws=4):
+    """Relative mean squared error |A_hat - A|^2 / |A|^2 of each quantizer mode, over
+    `draws` seeds and rotation keys, on activation-like, outlier-heavy and
+    gradient-like data: the quantity the Quartet II page compares between MS-EDEN and
+    stochastic rounding."""
+    import torch
+
+    import workloads
+    rows = []
+    for kind in data:
+        if kind == "laplace":
+            a = workloads.random_matrix((M, K), seed=K + 7, kind="laplace", std=1e-3)
+        else:
+            a = workloads.random_matrix((M, K), seed=K + 7, kind="outliers" if kind == "outliers" else "normal")
+        a = a.cuda()
+        ad = a.double()
+        na = float((ad ** 2).sum())
+        res = {}
+        for mode in ("rne", "sr", "rht_sr", "rht64_sr", "eden"):
+            errs = []
+            for d in range(draws):
+                key = 0x2545F491 * (d + 1) & 0xFFFFFFFF
+                signs = key & 0xFFFF if mode == "rht_sr" else key
+                ident = identity_operand(fp4, K, mode, signs)
+                c = quantizer_estimate(fp4, a, mode, signs, ident, seed=d, offset=1)
+                errs.append(float(((c.double() - ad) ** 2).sum()) / na)
+            res[mode] = sum(errs) / len(errs)
+        rows.append({"data": kind, "M": M, "K": K, "draws": draws, "rel_mse": {k: round(v, 6) for k, v in res.items()},
+                     "sr_over_eden": round(res["sr"] / res["eden"], 3),
+                     "rht_sr_over_eden": round(res["rht_sr"] / res["eden"], 3)})
+        torch.cuda.synchronize()
+    return rows
+
+
+def eden_bias(fp4, M=64, K=4096, draws=4096):
+    """The mean of the estimate over `draws` rotation keys (and scale draws), for
+    MS-EDEN and for the same rotation with nearest-even and no correction: the
+    distance of the mean from A relative to |A|, against the noise floor
+    sqrt(E|A_hat - A|^2 / draws) / |A|.  An unbiased quantizer sits at the floor."""
+    import torch
+
+    import workloads
+    a = workloads.random_matrix((M, K), seed=3, kind="laplace", std=1e-3).cuda()
+    ad = a.double()
+    na = float(torch.linalg.norm(ad))
+    out = {}
+    for mode in ("eden", "rht64"):
+        acc = torch.zeros_like(ad)
+        sq = 0.0
+        for d in range(draws):
+            key = (0x9E3779B1 * (d + 1)) & 0xFFFFFFFF
+            c = quantizer_estimate(fp4, a, mode, key, identity_operand(fp4, K, mode, key), seed=d, offset=7).double()
+            acc += c
+            sq += float(((c - ad) ** 2).sum())
+        bias = float(torch.linalg.norm(acc / draws - ad)) / na
+        floor = (sq / draws) ** 0.5 / na / draws ** 0.5
+        out[mode] = {"rel_bias": round(bias, 6), "noise_floor": round(floor, 6), "ratio": round(bias / floor, 3)}
+    return {"M": M, "K": K, "draws": draws, "data": "Laplace(0, 1e-3)", "modes": out}
 
 
 def error_vs_k():
@@ -111,10 +207,14 @@ def error_vs_k():
                 rows.append({"K": K, "data": "outliers" if outliers else "gaussian", "mode": mode,
                              "rel_fro_error": round(err, 6)})
     torch.cuda.synchronize()
+    quant = quantizer_errors(fp4, ("gaussian", "outliers", "laplace"))
+    bias = eden_bias(fp4)
     print(json.dumps({"analysis": "NVFP4 GEMM relative Frobenius error vs K against the unquantized binary64 product",
                       "M": M, "N": N, "operands": "A ~ N(0,1) (optionally 0.1% x50 outliers), B ~ N(0, 0.02^2); bf16",
                       "modes": {k: f"A {v[0] or 'rne'}, B {v[1] or 'rne'}" for k, v in ERROR_MODES.items()},
-                      "rows": rows}), flush=True)
+                      "rows": rows,
+                      "quantizer": quant,
+                      "unbiasedness": bias}), flush=True)
 
 
 def copy_calibration():
@@ -524,6 +624,19 @@ def quantize_breakdown(layers, wl, reps=5):
                 M * N * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR | G, inp.signs, sd, ow, b.dyq_t)),
                 "valu")
+            # MS-EDEN in place of the 16-point transform + SR for dY^T, and its GEMM
+            # partner X^T with the same 64-point rotation (not in the timed step)
+            key = 0x9E3779B9
+            add(f"{lin.name} dY^T MS-EDEN call (64-point transform, amax pass + layout)",
+                "amax_rht64_cols_kernel + quant_cols64_kernel", M * N * (in_b + one_d),
+                med_ms(lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT64 | Q.Q_EDEN, key, sd, ow, b.dyq_t)), "call")
+            add(f"{lin.name} dY^T columnwise 64-point transform + MS-EDEN (amax given)", "quant_cols64_kernel",
+                M * N * (in_b + one_d),
+                med_ms(lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT64 | Q.Q_EDEN | G, key, sd, ow, b.dyq_t)),
+                "valu")
+            add(f"{lin.name} X^T columnwise 64-point transform nearest-even (amax given)", "quant_cols64_kernel",
+                M * K * (in_b + one_d),
+                med_ms(lambda: Q.fp4_quantize(x, Q.Q_COLWISE | Q.Q_RHT64 | G, key, 0, 0, b.xq_t)), "hbm")
     del flush
     return rows
 
