@@ -268,3 +268,73 @@ def linear_wgrad(dy, x, signs, seed, offset):
     dytq = quantize(dy, colwise=True, rht=True, sr=True, signs=signs, seed=seed, offset=offset)
     xtq = quantize(x, colwise=True, rht=True, signs=signs)
     return dytq, xtq
+
+
+# ---------------------------------------------------------------- Newton-Schulz
+# The Full-Stack FP4 pages (paragraph 1, optimizer sentence) run the Muon
+# optimizer's Newton-Schulz iterations natively in NVFP4 and give no polynomial;
+# the reading here is Muon's quintic X' = a X + (b A + c A A^T) X, A = X X^T, with
+# every GEMM operand quantized (variants: nearest-even; 16-point transform + SR;
+# MS-EDEN left operands with 64-point-rotated nearest-even right operands), the
+# products the binary64 reference of the dequantized operands, the combinations in
+# binary32 (one IEEE operation per step).
+
+MUON_QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+def ns_normalize(g, eps=1e-7):
+    """X_0 = g * s, s = RN32(1 / (sqrt(sum g^2) + eps)), the sum in binary64."""
+    g = _as_f32(g)
+    ss = float(np.sum(g.astype(np.float64) ** 2))
+    s = np.float32(1.0 / (np.sqrt(ss) + eps))
+    return (g * s).astype(np.float32)
+
+
+def ns_operand(x, variant, side, signs, seed, offset, colwise=False):
+    """A GEMM operand of the iteration: x (or x^T) quantized per variant and side."""
+    if variant == "rne":
+        kw = {}
+    elif variant == "rht_sr":
+        kw = dict(rht=True, sr=True, signs=signs & 0xFFFF)
+    elif variant == "eden":
+        kw = dict(rht64=True, eden=(side == "left"), signs=signs)
+    else:
+        raise ValueError(variant)
+    return quantize(x, colwise=colwise, seed=seed, offset=offset, **kw)
+
+
+def ns_step(x, variant="rne", coeffs=MUON_QUINTIC, signs=0, seed=0, offset=0, a_in=None, b_in=None, bx_in=None):
+    """One NVFP4 Newton-Schulz iteration on the fp32 array x [m][n]; operand k draws
+    Philox offset `offset + k` (k = 0 X left, 1 X right, 2 A left, 3 A right, 4 B,
+    5 X^T).  The products are the binary64 references rounded to binary32, unless
+    a_in (A), b_in (B) or bx_in (B X) supply the values to continue from (a stage-wise
+    comparison feeds the device's results in).  Returns every stage."""
+    a_c, b_c, c_c = (np.float32(v) for v in coeffs)
+    x = _as_f32(x)
+    st = {"x": x}
+    st["x_left"] = ns_operand(x, variant, "left", signs, seed, offset + 0)
+    st["x_right"] = ns_operand(x, variant, "right", signs, seed, offset + 1)
+    st["a_ref"], st["a_bound"] = gemm_ref(st["x_left"], st["x_right"])
+    a = st["a_ref"].astype(np.float32) if a_in is None else _as_f32(a_in)
+    st["a"] = a
+    st["a_left"] = ns_operand(a, variant, "left", signs, seed, offset + 2)
+    st["a_right"] = ns_operand(a, variant, "right", signs, seed, offset + 3)
+    st["a2_ref"], st["a2_bound"] = gemm_ref(st["a_left"], st["a_right"])
+    b = (b_c * a + c_c * st["a2_ref"].astype(np.float32)).astype(np.float32) if b_in is None else _as_f32(b_in)
+    st["b"] = b
+    st["b_q"] = ns_operand(b, variant, "left", signs, seed, offset + 4)
+    st["xt"] = ns_operand(x, variant, "right", signs, seed, offset + 5, colwise=True)
+    st["bx_ref"], st["bx_bound"] = gemm_ref(st["b_q"], st["xt"])
+    bx = st["bx_ref"].astype(np.float32) if bx_in is None else _as_f32(bx_in)
+    st["bx"] = bx
+    st["x_next"] = (a_c * x + bx).astype(np.float32)
+    return st
+
+
+def newton_schulz(g, iters=5, variant="rne", coeffs=MUON_QUINTIC, signs=0, seed=0, offset=0, normalize=True):
+    """The whole chain on the CPU: X_0 = g / (|g| + 1e-7), then `iters` iterations,
+    iteration t with Philox offsets offset + 8 t + k."""
+    x = ns_normalize(g) if normalize else _as_f32(g)
+    for t in range(iters):
+        x = ns_step(x, variant, coeffs, signs, seed, offset + 8 * t)["x_next"]
+    return x
