@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mlp_up_12b", choices=["mlp_up_12b", "fprop_8k", "wgrad_8k", "block_3b"])
+    ap.add_argument("--workload", default="mlp_up_12b",
+                    choices=["mlp_up_12b", "fprop_8k", "wgrad_8k", "block_3b", "newton_schulz"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="measure only --workload (default: also the other full-size configurations, fewer steps)")
@@ -292,6 +293,118 @@ def measured_traffic(kernel_src):
     return float(t.group(1)) / 3.0
 
 
+NS_SHAPE = (5120, 20480)  # X = G^T of the 12B MLP up-projection's weight gradient (20480 x 5120)
+NS_ITERS = 5
+NS_VARIANTS = ("rne", "rht_sr", "eden")
+
+
+def ns_flags(fp4, variant):
+    return {"rne": 0, "rht_sr": fp4.Q_RHT | fp4.Q_SR, "eden": fp4.Q_RHT64 | fp4.Q_EDEN}[variant]
+
+
+def newton_schulz_timing(steps, warmup, dev, variants=NS_VARIANTS):
+    """Muon's NVFP4 Newton-Schulz (5 iterations from X_0 = G / |G|) on a Gaussian G of
+    the 12B MLP weight-gradient shape, per operand variant: time per call (HIP events
+    on the stream), TFLOP/s over its 15 GEMMs, and each of its three GEMM shapes timed
+    alone on the call's own quantized operands."""
+    import torch
+
+    import nvfp4_bit_microscaled_amd as fp4
+    import workloads
+
+    m, n = NS_SHAPE
+    g = workloads.random_matrix((m, n), seed=0, dtype=torch.float32).to(dev)
+    x = torch.empty_like(g)
+    bufs = fp4.NsBuffers(m, n, device=dev)
+    stream = torch.cuda.current_stream()
+    flops_iter = 2.0 * m * m * n + 2.0 * m * m * m + 2.0 * m * n * m
+    out = {}
+    for variant in variants:
+        f = ns_flags(fp4, variant)
+        for _ in range(warmup):
+            fp4.fp4_newton_schulz(g, x, NS_ITERS, bufs, flags=f, rht_signs=0x1234ACE1, seed=1, offset=0)
+        evs = [HipTimingEvent() for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(steps):
+            fp4.fp4_newton_schulz(g, x, NS_ITERS, bufs, flags=f, rht_signs=0x1234ACE1, seed=1, offset=0)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(steps)) / steps
+        # the three GEMM shapes alone, on this call's last operands
+        gem = []
+        for name, qa, qb, c, flops in (("A = X X^T", bufs.x_left, bufs.x_right, bufs.a, 2.0 * m * m * n),
+                                       ("A A^T", bufs.a_left, bufs.a_right, bufs.b, 2.0 * m * m * m),
+                                       ("B X", bufs.b_q, bufs.xt, bufs.bx, 2.0 * m * n * m)):
+            e0, e1 = HipTimingEvent(), HipTimingEvent()
+            e0.record(stream)
+            for _ in range(5):
+                fp4.fp4_gemm_ws(qa, qb, c, bufs.ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gms = e0.elapsed_time(e1) / 5
+            gem.append({"gemm": name, "M": qa.rows, "N": qb.rows, "K": qa.cols, "ms": round(gms, 4),
+                        "tflops": round(flops / (gms * 1e-3) / 1e12, 1),
+                        "frac_f16_peak": round(flops / (gms * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS, 4)})
+        out[variant] = {"ms_per_call": round(ms, 4), "iters": NS_ITERS,
+                        "tflops": round(NS_ITERS * flops_iter / (ms * 1e-3) / 1e12, 1), "gemms": gem}
+    return {"X": [m, n], "flops_per_call": NS_ITERS * flops_iter, "variants": out}
+
+
+def newton_schulz_divergence(dev, m=1024, n=4096):
+    """Singular values after 5 iterations from the same Gaussian G, per variant, and in
+    exact arithmetic (binary64 products, no quantization); the relative distance of each
+    NVFP4 result from the exact one."""
+    import torch
+
+    import nvfp4_bit_microscaled_amd as fp4
+    import workloads
+
+    a_, b_, c_ = fp4.MUON_QUINTIC
+    g = workloads.random_matrix((m, n), seed=1, dtype=torch.float32).to(dev)
+    xe = g.double() / (torch.linalg.norm(g.double()) + 1e-7)
+    for _ in range(NS_ITERS):
+        a = xe @ xe.T
+        xe = a_ * xe + (b_ * a + c_ * (a @ a)) @ xe
+    sve = torch.linalg.svdvals(xe)
+    res = {"G": [m, n], "exact": {"sigma_max": round(float(sve.max()), 4), "sigma_min": round(float(sve.min()), 4)}}
+    bufs = fp4.NsBuffers(m, n, device=dev)
+    x = torch.empty_like(g)
+    for variant in NS_VARIANTS:
+        fp4.fp4_newton_schulz(g, x, NS_ITERS, bufs, flags=ns_flags(fp4, variant), rht_signs=0x1234ACE1, seed=1,
+                              offset=0)
+        sv = torch.linalg.svdvals(x.double())
+        res[variant] = {"sigma_max": round(float(sv.max()), 4), "sigma_min": round(float(sv.min()), 6),
+                        "rel_distance_from_exact": round(float(torch.linalg.norm(x.double() - xe)
+                                                               / torch.linalg.norm(xe)), 4)}
+    return res
+
+
+def run_newton_schulz(args, dev):
+    import torch
+    t = newton_schulz_timing(args.steps, args.warmup, dev)
+    torch.cuda.empty_cache()
+    d = newton_schulz_divergence(dev)
+    v = t["variants"]["rne"]
+    gem = max(v["gemms"], key=lambda r: r["tflops"])
+    out = {
+        "metric": "NVFP4 linear TFLOPS (fprop/dgrad/wgrad) + quantize GB/s, % of roofline, 1 GPU",
+        "value": v["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": v["ms_per_call"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 operands (e2m1 x e4m3 block scale), f16 MFMA products, f32 accumulate",
+        "data": "synthetic (seeded: G ~ N(0,1) fp32)",
+        "config": {"workload": f"Muon Newton-Schulz in NVFP4: quintic (3.4445, -4.7750, 2.0315), {NS_ITERS} "
+                               f"iterations on X {t['X'][0]}x{t['X'][1]} (the 12B MLP up-projection's weight "
+                               f"gradient, transposed), every GEMM operand quantized",
+                   "name": "newton_schulz", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": gem["tflops"], "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gem["tflops"] / PEAK_F16_MFMA_TFLOPS, 4), "traffic": None,
+                     "kernel": f"block-scaled GEMM {gem['gemm']} ({gem['M']}x{gem['N']}x{gem['K']}) alone"},
+        "newton_schulz": t, "divergence": d, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def setup_workload(name, dev):
     """Device tensors and caller-owned buffers of every linear of workload `name`,
     plus one GEMM workspace sized by fp4_linear_ws_bytes for the largest layer."""
@@ -436,6 +549,9 @@ def main():
     fp4.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "newton_schulz":
+        run_newton_schulz(args, dev)
+        return
 
     wl, layers, ws, ws_need, t_gen = setup_workload(args.workload, dev)
     r = measure(wl, layers, ws, args.steps, args.warmup)
@@ -541,6 +657,12 @@ def main():
             })
             del olayers, ows
             torch.cuda.empty_cache()
+        nt = newton_schulz_timing(3, 1, dev, variants=("rne",))
+        v = nt["variants"]["rne"]
+        others.append({"workload": f"Muon Newton-Schulz in NVFP4, {NS_ITERS} iterations on X {nt['X'][0]}x{nt['X'][1]}",
+                       "name": "newton_schulz", "steps": 3, "ms_per_step": v["ms_per_call"], "value": v["tflops"],
+                       "unit": "TFLOP/s", "gemms": v["gemms"]})
+        torch.cuda.empty_cache()
         out["other_workloads"] = others
     print(json.dumps(out), flush=True)
 

@@ -321,6 +321,59 @@ FP4_API fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype 
                                        const fp4_tensor *xq_t, void *ws, size_t ws_bytes, const hipEvent_t *marks,
                                        hipStream_t stream);
 
+/* NVFP4 Newton-Schulz: the Muon optimizer's orthogonalising iteration with every
+ * GEMM operand in NVFP4 (Full-Stack FP4 pages, paragraph 1, the optimizer
+ * sentence: Newton-Schulz iterations native in NVFP4; the pages give no
+ * polynomial, so the coefficients are the caller's -- Muon's quintic is
+ * (3.4445, -4.7750, 2.0315)).  One iteration on X [m][n] (fp32, row-major):
+ *   A = X X^T              fp4_gemm(X left, X right), fp32 [m][m]
+ *   A2 = A A^T             fp4_gemm(A left, A right) (A is symmetric up to rounding)
+ *   B = b A + c A2         fl(fl(b A) + fl(c A2)), in place of A2
+ *   BX = B X               fp4_gemm(B, X^T), X^T quantized columnwise
+ *   X' = a X + BX          fl(fl(a X) + BX), in place of X
+ * Operand quantization by variant (flags):
+ *   0                        every operand 1D nearest-even;
+ *   FP4_Q_RHT | FP4_Q_SR     every operand with the 16-point transform (mask
+ *                            rht_signs) and stochastic rounding;
+ *   FP4_Q_RHT64 | FP4_Q_EDEN left operands (X left, A left, B) MS-EDEN, right
+ *                            operands (X right, A right, X^T) the 64-point transform
+ *                            (key rht_signs) nearest-even.
+ * In iteration t the operands draw Philox offsets offset + 8 t + k, k = 0 (X left),
+ * 1 (X right), 2 (A left), 3 (A right), 4 (B), 5 (X^T), all with key seed. */
+typedef struct fp4_ns_config {
+  float a, b, c;      /* X' = a X + (b A + c A A^T) X */
+  uint32_t flags;     /* operand variant, as above */
+  uint32_t rht_signs; /* 16-bit mask (FP4_Q_RHT) or 32-bit key (FP4_Q_RHT64) */
+  uint64_t seed, offset;
+} fp4_ns_config;
+
+/* The iteration's intermediates, all caller-owned device memory, overwritten; after
+ * a call they hold the last iteration's values.  Descriptors as for fp4_quantize:
+ * x_left, x_right [m][n]; a_left, a_right, b_q [m][m]; xt [n][m]; none 2D. */
+typedef struct fp4_ns_buffers {
+  float *a;  /* [m][m]: A */
+  float *b;  /* [m][m]: A A^T, then B */
+  float *bx; /* [m][n]: B X */
+  fp4_tensor x_left, x_right, a_left, a_right, b_q, xt;
+  void *ws;  /* GEMM split-K workspace and the normalisation's scratch (fp4_newton_schulz_ws_bytes), 16-byte aligned */
+  size_t ws_bytes;
+} fp4_ns_buffers;
+
+/* x = X_iters from X_0, where X_0 = g / (|g|_F + 1e-7) when normalize is non-zero
+ * (|g|_F^2 summed in binary64 on the device, the scale 1 / (|g|_F + 1e-7) rounded
+ * once to binary32, each element one product), else X_0 = g.  g and x [m][n] fp32,
+ * device, may be the same buffer; m and n multiples of 16 (of 64 with
+ * FP4_Q_RHT64).  iters >= 0.  Errors: FP4_ERR_NULL, FP4_ERR_SHAPE, FP4_ERR_MODE (an
+ * unknown variant), FP4_ERR_MISMATCH (a descriptor's shape), FP4_ERR_ALIGN,
+ * FP4_ERR_WORKSPACE (ws below fp4_newton_schulz_ws_bytes), FP4_ERR_HIP. */
+FP4_API fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int32_t iters, int32_t normalize,
+                                     const fp4_ns_config *cfg, const fp4_ns_buffers *bufs, hipStream_t stream);
+
+/* Workspace bytes fp4_newton_schulz needs for X [m][n]: the largest split-K plan of
+ * its three GEMMs (m x m x n, m x m x m, m x n x m), and at least the normalisation's
+ * 8196 bytes.  FP4_ERR_NULL, FP4_ERR_SHAPE. */
+FP4_API fp4_status fp4_newton_schulz_ws_bytes(int64_t m, int64_t n, size_t *bytes);
+
 /* A short static description of a status code (never NULL). */
 FP4_API const char *fp4_status_string(fp4_status status);
 

@@ -31,7 +31,7 @@ STATIC_SCRATCH_BYTES = 64 << 20
 # every symbol the header declares
 EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_gemm", "fp4_gemm_ws",
            "fp4_gemm_ws_bytes", "fp4_gemm_noalloc", "fp4_linear_ws_bytes", "fp4_linear_fprop", "fp4_linear_dgrad", "fp4_linear_wgrad",
-           "fp4_linear_backward", "fp4_status_string")
+           "fp4_linear_backward", "fp4_newton_schulz", "fp4_newton_schulz_ws_bytes", "fp4_status_string")
 
 
 class Fp4Error(RuntimeError):
@@ -43,6 +43,17 @@ class Fp4Error(RuntimeError):
 class fp4_tensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("amax", ctypes.c_void_p),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("two_d", ctypes.c_int32)]
+
+
+class fp4_ns_config(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("rht_signs", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+
+
+class fp4_ns_buffers(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("bx", ctypes.c_void_p), ("x_left", fp4_tensor),
+                ("x_right", fp4_tensor), ("a_left", fp4_tensor), ("a_right", fp4_tensor), ("b_q", fp4_tensor),
+                ("xt", fp4_tensor), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -76,6 +87,9 @@ def load():
         "fp4_linear_wgrad": [vp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, tp, tp, vp, szv, vp, vp],
         "fp4_linear_backward": [vp, vp, i32, tp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, u64, tp, tp, tp, vp,
                                 szv, vp, vp],
+        "fp4_newton_schulz": [vp, vp, i64, i64, i32, i32, ctypes.POINTER(fp4_ns_config),
+                              ctypes.POINTER(fp4_ns_buffers), vp],
+        "fp4_newton_schulz_ws_bytes": [i64, i64, sz],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -259,6 +273,46 @@ def fp4_linear_backward(dy, x, wq_t: QTensor, dx, dw, rht_signs: int, seed: int,
         dy.data_ptr(), x.data_ptr() if x is not None else None, _dtype(dy), wq_t.desc, dx.data_ptr(), _dtype(dx),
         dw.data_ptr(), _dtype(dw), M, N, K, rht_signs, seed, offset_dgrad, offset_wgrad, dyq.desc, dyq_t.desc,
         xq_t.desc, wp, wb, _marks(marks), _stream(stream)))
+
+
+MUON_QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+def fp4_newton_schulz_ws_bytes(m: int, n: int) -> int:
+    v = ctypes.c_size_t()
+    _check("fp4_newton_schulz_ws_bytes", load().fp4_newton_schulz_ws_bytes(m, n, ctypes.byref(v)))
+    return v.value
+
+
+class NsBuffers:
+    """Caller-owned intermediates of fp4_newton_schulz for X [m][n]; after a call
+    they hold the last iteration's A, B (= b A + c A A^T), B X and quantized
+    operands."""
+
+    def __init__(self, m: int, n: int, device="cuda"):
+        f32 = dict(dtype=torch.float32, device=device)
+        self.a = torch.empty(m, m, **f32)
+        self.b = torch.empty(m, m, **f32)
+        self.bx = torch.empty(m, n, **f32)
+        self.x_left, self.x_right = QTensor(m, n, device=device), QTensor(m, n, device=device)
+        self.a_left, self.a_right = QTensor(m, m, device=device), QTensor(m, m, device=device)
+        self.b_q = QTensor(m, m, device=device)
+        self.xt = QTensor(n, m, device=device)
+        self.ws = torch.empty(max(fp4_newton_schulz_ws_bytes(m, n), 16), dtype=torch.uint8, device=device)
+        self._s = fp4_ns_buffers(self.a.data_ptr(), self.b.data_ptr(), self.bx.data_ptr(), self.x_left._desc,
+                                 self.x_right._desc, self.a_left._desc, self.a_right._desc, self.b_q._desc,
+                                 self.xt._desc, self.ws.data_ptr(), self.ws.numel())
+
+
+def fp4_newton_schulz(g: torch.Tensor, x: torch.Tensor, iters: int, bufs: NsBuffers, normalize: bool = True,
+                      coeffs=MUON_QUINTIC, flags: int = 0, rht_signs: int = 0, seed: int = 0, offset: int = 0,
+                      stream=None):
+    """x = X_iters of the NVFP4 Newton-Schulz iteration from g (fp32 [m][n])."""
+    m, n = g.shape
+    assert g.dtype == torch.float32 and x.dtype == torch.float32 and g.is_contiguous() and x.is_contiguous()
+    cfg = fp4_ns_config(coeffs[0], coeffs[1], coeffs[2], flags, rht_signs & 0xFFFFFFFF, seed, offset)
+    _check("fp4_newton_schulz", load().fp4_newton_schulz(g.data_ptr(), x.data_ptr(), m, n, iters, int(normalize),
+                                                         ctypes.byref(cfg), ctypes.byref(bufs._s), _stream(stream)))
 
 
 class LinearBuffers:

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4_amd.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "ns.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -258,6 +258,75 @@ fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, c
   return from_hip(e);
 }
 
+fp4_status fp4_newton_schulz_ws_bytes(int64_t m, int64_t n, size_t *bytes) {
+  if (!bytes) return FP4_ERR_NULL;
+  if (m < 0 || n < 0 || m % 16 || n % 16) return FP4_ERR_SHAPE;
+  size_t w = nvfp4::normalize_scratch_bytes();
+  const size_t g[3] = {nvfp4::gemm_ws_bytes(m, m, n), nvfp4::gemm_ws_bytes(m, m, m), nvfp4::gemm_ws_bytes(m, n, m)};
+  for (size_t v : g) w = v > w ? v : w;
+  *bytes = w;
+  return FP4_OK;
+}
+
+fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int32_t iters, int32_t normalize,
+                             const fp4_ns_config *cfg, const fp4_ns_buffers *bufs, hipStream_t stream) {
+  if (!cfg || !bufs) return FP4_ERR_NULL;
+  if (m < 0 || n < 0 || iters < 0 || m % 16 || n % 16) return FP4_ERR_SHAPE;
+  uint32_t fl, fr;  // quantization flags of the left and right operands
+  if (cfg->flags == 0) {
+    fl = fr = 0;
+  } else if (cfg->flags == (FP4_Q_RHT | FP4_Q_SR)) {
+    fl = fr = FP4_Q_RHT | FP4_Q_SR;
+  } else if (cfg->flags == (FP4_Q_RHT64 | FP4_Q_EDEN)) {
+    fl = FP4_Q_RHT64 | FP4_Q_EDEN;
+    fr = FP4_Q_RHT64;
+    if (m % 64 || n % 64) return FP4_ERR_SHAPE;
+  } else {
+    return FP4_ERR_MODE;
+  }
+  if ((!g || !x) && m > 0 && n > 0) return FP4_ERR_NULL;
+  if ((!bufs->a || !bufs->b || !bufs->bx) && m > 0 && n > 0) return FP4_ERR_NULL;
+  if (!aligned(g, 16) || !aligned(x, 16) || !aligned(bufs->a, 16) || !aligned(bufs->b, 16) || !aligned(bufs->bx, 16))
+    return FP4_ERR_ALIGN;
+  fp4_status s;
+  if ((s = check_quantize(x, FP4_FP32, m, n, n, fl, &bufs->x_left, nullptr)) != FP4_OK) return s;
+  if ((s = check_quantize(x, FP4_FP32, m, n, n, fr, &bufs->x_right, nullptr)) != FP4_OK) return s;
+  if ((s = check_quantize(bufs->a, FP4_FP32, m, m, m, fl, &bufs->a_left, nullptr)) != FP4_OK) return s;
+  if ((s = check_quantize(bufs->a, FP4_FP32, m, m, m, fr, &bufs->a_right, nullptr)) != FP4_OK) return s;
+  if ((s = check_quantize(bufs->b, FP4_FP32, m, m, m, fl, &bufs->b_q, nullptr)) != FP4_OK) return s;
+  if ((s = check_quantize(x, FP4_FP32, m, n, n, fr | FP4_Q_COLWISE, &bufs->xt, nullptr)) != FP4_OK) return s;
+  if ((s = check_ws(bufs->ws, bufs->ws_bytes)) != FP4_OK) return s;
+  size_t need = 0;
+  fp4_newton_schulz_ws_bytes(m, n, &need);
+  if (bufs->ws_bytes < need) return FP4_ERR_WORKSPACE;
+  if (m == 0 || n == 0) return FP4_OK;
+  const uint32_t key = (fl & FP4_Q_RHT64) ? cfg->rht_signs : cfg->rht_signs & 0xFFFFu;
+  hipError_t e = hipSuccess;
+  if (normalize) e = nvfp4::launch_normalize(g, x, m * n, 1e-7f, bufs->ws, stream);
+  else if (g != x) e = hipMemcpyAsync(x, g, size_t(m * n) * sizeof(float), hipMemcpyDeviceToDevice, stream);
+  for (int32_t t = 0; t < iters && e == hipSuccess; ++t) {
+    const uint64_t o = cfg->offset + 8u * uint64_t(t);
+    auto q = [&](const float *src, int64_t r, int64_t c, uint32_t f, uint64_t off, const fp4_tensor *out) {
+      return nvfp4::launch_quantize(src, FP4_FP32, r, c, c, f, key, cfg->seed, off, out, nullptr, stream);
+    };
+    e = q(x, m, n, fl, o + 0, &bufs->x_left);
+    if (e == hipSuccess) e = q(x, m, n, fr, o + 1, &bufs->x_right);
+    if (e == hipSuccess)
+      e = nvfp4::launch_gemm_ws(&bufs->x_left, &bufs->x_right, bufs->a, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
+    if (e == hipSuccess) e = q(bufs->a, m, m, fl, o + 2, &bufs->a_left);
+    if (e == hipSuccess) e = q(bufs->a, m, m, fr, o + 3, &bufs->a_right);
+    if (e == hipSuccess)
+      e = nvfp4::launch_gemm_ws(&bufs->a_left, &bufs->a_right, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
+    if (e == hipSuccess) e = nvfp4::launch_axpby(cfg->b, bufs->a, cfg->c, bufs->b, m * m, stream);
+    if (e == hipSuccess) e = q(bufs->b, m, m, fl, o + 4, &bufs->b_q);
+    if (e == hipSuccess) e = q(x, m, n, fr | FP4_Q_COLWISE, o + 5, &bufs->xt);
+    if (e == hipSuccess)
+      e = nvfp4::launch_gemm_ws(&bufs->b_q, &bufs->xt, bufs->bx, FP4_FP32, n, bufs->ws, bufs->ws_bytes, stream);
+    if (e == hipSuccess) e = nvfp4::launch_axpby(1.0f, bufs->bx, cfg->a, x, m * n, stream);
+  }
+  return from_hip(e);
+}
+
 const char *fp4_status_string(fp4_status status) {
   switch (status) {
     case FP4_OK: return "ok";

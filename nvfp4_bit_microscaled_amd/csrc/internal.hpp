@@ -52,4 +52,9 @@ constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 // device; allocates nothing).
 hipError_t static_scratch(void **ptr);
 
+// The Newton-Schulz iteration's binary32 steps (ns.hip).
+hipError_t launch_axpby(float alpha, const float *x, float beta, float *y, int64_t n, hipStream_t stream);
+size_t normalize_scratch_bytes();
+hipError_t launch_normalize(const float *g, float *x, int64_t n, float eps, void *scratch, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -1,0 +1,96 @@
+// ns.hip -- the element-wise and reduction kernels of the NVFP4 Newton-Schulz
+// iteration (Full-Stack FP4 pages, paragraph 1: the Muon optimizer's
+// Newton-Schulz iterations run natively in NVFP4).  The iteration's products are
+// fp4_gemm calls on quantized operands; what runs here is binary32 arithmetic
+// between them, one IEEE operation per step (built with -ffp-contract=off):
+//   y = alpha x + beta y          (fl(fl(alpha x) + fl(beta y)))
+//   x0 = g * s, s = RN32(1 / (sqrt(sum g^2) + eps)), the sum of squares in binary64
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSumBlocks = 1024;  // workgroups of the sum of squares (and binary64 partials)
+
+// y[i] = alpha * x[i] + beta * y[i], 4 elements per thread-step when aligned.
+__global__ __launch_bounds__(kThreads) void axpby_kernel(float alpha, const float *__restrict__ x, float beta,
+                                                         float *__restrict__ y, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads) {
+    const float p = alpha * x[i];
+    const float q = beta * y[i];
+    y[i] = p + q;
+  }
+}
+
+// Per-workgroup binary64 partial sums of g[i]^2 (each square exact in binary64),
+// in a fixed order: thread t of workgroup b sums i = b * T + t + k * G * T in k
+// order, then the workgroup sums its threads pairwise by a fixed tree.
+__global__ __launch_bounds__(kThreads) void sumsq_kernel(const float *__restrict__ g, int64_t n,
+                                                         double *__restrict__ partial) {
+  __shared__ double part[kThreads];
+  double s = 0.0;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads) {
+    const double v = double(g[i]);
+    s += v * v;
+  }
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if (int(threadIdx.x) < h) part[threadIdx.x] += part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = part[0];
+}
+
+// s = RN32(1 / (sqrt(sum of the partials) + eps)) into *scale (one workgroup; the
+// partials summed in index order by thread 0).
+__global__ __launch_bounds__(64) void inv_norm_kernel(const double *__restrict__ partial, int nparts, float eps,
+                                                      float *scale) {
+  if (threadIdx.x == 0) {
+    double ss = 0.0;
+    for (int i = 0; i < nparts; ++i) ss += partial[i];
+    *scale = float(1.0 / (sqrt(ss) + double(eps)));
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void scale_kernel(const float *__restrict__ g, const float *__restrict__ scale,
+                                                         float *__restrict__ x, int64_t n) {
+  const float s = *scale;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads)
+    x[i] = g[i] * s;
+}
+
+unsigned grid_of(int64_t n) {
+  const int64_t g = (n + kThreads - 1) / kThreads;
+  return unsigned(g < 1 ? 1 : (g > 4096 ? 4096 : g));
+}
+
+}  // namespace
+
+hipError_t launch_axpby(float alpha, const float *x, float beta, float *y, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  return launch(axpby_kernel, dim3(grid_of(n)), dim3(kThreads), stream, alpha, x, beta, y, n);
+}
+
+size_t normalize_scratch_bytes() { return kSumBlocks * sizeof(double) + sizeof(float); }
+
+// x = g / (|g|_F + eps); scratch: normalize_scratch_bytes(), 8-byte aligned.
+hipError_t launch_normalize(const float *g, float *x, int64_t n, float eps, void *scratch, hipStream_t stream) {
+  double *partial = static_cast<double *>(scratch);
+  float *scale = reinterpret_cast<float *>(partial + kSumBlocks);
+  const int64_t blocks64 = (n + kThreads - 1) / kThreads;
+  const int nparts = int(blocks64 < 1 ? 1 : (blocks64 > kSumBlocks ? kSumBlocks : blocks64));
+  hipError_t e = launch(sumsq_kernel, dim3(nparts), dim3(kThreads), stream, g, n, partial);
+  if (e == hipSuccess) e = launch(inv_norm_kernel, dim3(1), dim3(64), stream, static_cast<const double *>(partial),
+                                  nparts, eps, scale);
+  if (e == hipSuccess && n > 0)
+    e = launch(scale_kernel, dim3(grid_of(n)), dim3(kThreads), stream, g, static_cast<const float *>(scale), x, n);
+  return e;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,73 @@
+"""GPU parity of the NVFP4 Newton-Schulz iteration (fp4_newton_schulz; Full-Stack FP4
+pages, paragraph 1, optimizer sentence) against the oracle, stage by stage: each
+iteration runs on the GPU, and the oracle redoes it from the GPU's own inputs to
+that stage, so every quantized operand is compared bit for bit, every product
+within the GEMM tolerance, and X' = a X + B X bit for bit given the GPU's B X."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import assert_q_equal, check_gemm, dev, host_q
+
+pytestmark = pytest.mark.gpu
+
+SIGNS = 0x1234ACE1
+A_, B_, C_ = 3.4445, -4.7750, 2.0315
+
+
+def variant_flags(fp4, variant):
+    return {"rne": 0, "rht_sr": fp4.Q_RHT | fp4.Q_SR, "eden": fp4.Q_RHT64 | fp4.Q_EDEN}[variant]
+
+
+@pytest.mark.parametrize("variant", ["rne", "rht_sr", "eden"])
+@pytest.mark.parametrize("shape", [(128, 256), (256, 768), (1024, 4096)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_newton_schulz_stagewise(fp4, oracle, variant, shape):
+    m, n = shape
+    iters = 3 if m < 1024 else 1
+    g_cpu = workloads.random_matrix((m, n), seed=m + n, dtype=torch.float32)
+    g = dev(g_cpu)
+    x = torch.empty_like(g)
+    bufs = fp4.NsBuffers(m, n)
+    flags = variant_flags(fp4, variant)
+    fp4.fp4_newton_schulz(g, x, 0, bufs, normalize=True, flags=flags, rht_signs=SIGNS, seed=7, offset=100)
+    torch.cuda.synchronize()
+    xt = x.cpu().numpy()
+    o0 = oracle.ns_normalize(workloads.widen(g_cpu))
+    # the scale is rounded once to binary32 from a binary64 sum whose order differs
+    # from the oracle's: equal unless that sum sits within 1e-16 of a rounding edge
+    assert np.all(np.abs(xt - o0) <= np.spacing(np.abs(o0)))
+    for t in range(iters):
+        fp4.fp4_newton_schulz(x, x, 1, bufs, normalize=False, flags=flags, rht_signs=SIGNS, seed=7,
+                              offset=100 + 8 * t)
+        torch.cuda.synchronize()
+        a, b, bx, xn = (v.cpu().numpy() for v in (bufs.a, bufs.b, bufs.bx, x))
+        st = oracle.ns_step(xt, variant, signs=SIGNS, seed=7, offset=100 + 8 * t, a_in=a, b_in=b, bx_in=bx)
+        for name in ("x_left", "x_right", "a_left", "a_right", "b_q", "xt"):
+            assert_q_equal(host_q(getattr(bufs, name)), st[name], f"{variant} iteration {t} {name}")
+        check_gemm(a, st["a_ref"], st["a_bound"], False, f"{variant} iteration {t} A = X X^T")
+        # B = fl(fl(b A) + fl(c A2)) with the GPU's A2 within the GEMM tolerance
+        b_ref = B_ * a.astype(np.float64) + C_ * st["a2_ref"]
+        tol = abs(C_) * 1e-5 * st["a2_bound"] + 2.0 ** -22 * (np.abs(B_ * a) + np.abs(C_ * st["a2_ref"]))
+        assert np.all(np.abs(b - b_ref) <= tol), f"{variant} iteration {t} B"
+        check_gemm(bx, st["bx_ref"], st["bx_bound"], False, f"{variant} iteration {t} B X")
+        assert np.array_equal(xn, st["x_next"]), f"{variant} iteration {t} X'"
+        xt = xn
+    if iters > 1:
+        # several iterations in one call equal the same iterations one call each
+        x2 = torch.empty_like(g)
+        fp4.fp4_newton_schulz(g, x2, iters, fp4.NsBuffers(m, n), normalize=True, flags=flags, rht_signs=SIGNS,
+                              seed=7, offset=100)
+        torch.cuda.synchronize()
+        assert torch.equal(x2, x)
+
+
+def test_newton_schulz_rejects_bad_arguments(fp4):
+    g = torch.zeros(64, 96, dtype=torch.float32, device="cuda")
+    bufs = fp4.NsBuffers(64, 96)
+    with pytest.raises(fp4.Fp4Error, match="SHAPE"):  # the 64-point transform needs multiples of 64
+        fp4.fp4_newton_schulz(g, g, 1, bufs, flags=fp4.Q_RHT64 | fp4.Q_EDEN)
+    with pytest.raises(fp4.Fp4Error, match="MODE"):
+        fp4.fp4_newton_schulz(g, g, 1, bufs, flags=fp4.Q_SR)
+    with pytest.raises(fp4.Fp4Error, match="MISMATCH"):
+        fp4.fp4_newton_schulz(torch.zeros(64, 128, device="cuda"), torch.zeros(64, 128, device="cuda"), 1, bufs)
