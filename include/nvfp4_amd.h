@@ -332,7 +332,10 @@ FP4_API fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype 
  *   BX = B X               fp4_gemm(B, X^T), X^T quantized columnwise
  *   X' = a X + BX          fl(fl(a X) + BX), in place of X
  * Operand quantization by variant (flags):
- *   0                        every operand 1D nearest-even;
+ *   0                        every operand 1D nearest-even (the two operands of
+ *                            X X^T, and of A A^T, are then the same quantization:
+ *                            x_left and a_left serve both sides, and x_right and
+ *                            a_right are not written);
  *   FP4_Q_RHT | FP4_Q_SR     every operand with the 16-point transform (mask
  *                            rht_signs) and stochastic rounding;
  *   FP4_Q_RHT64 | FP4_Q_EDEN left operands (X left, A left, B) MS-EDEN, right

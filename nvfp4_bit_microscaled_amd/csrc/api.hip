@@ -309,14 +309,17 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
     auto q = [&](const float *src, int64_t r, int64_t c, uint32_t f, uint64_t off, const fp4_tensor *out) {
       return nvfp4::launch_quantize(src, FP4_FP32, r, c, c, f, key, cfg->seed, off, out, nullptr, stream);
     };
+    // nearest-even: both operands of X X^T (and of A A^T) are the same quantization
+    const bool same = cfg->flags == 0;
+    const fp4_tensor *xr = same ? &bufs->x_left : &bufs->x_right, *ar = same ? &bufs->a_left : &bufs->a_right;
     e = q(x, m, n, fl, o + 0, &bufs->x_left);
-    if (e == hipSuccess) e = q(x, m, n, fr, o + 1, &bufs->x_right);
+    if (e == hipSuccess && !same) e = q(x, m, n, fr, o + 1, &bufs->x_right);
     if (e == hipSuccess)
-      e = nvfp4::launch_gemm_ws(&bufs->x_left, &bufs->x_right, bufs->a, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
+      e = nvfp4::launch_gemm_ws(&bufs->x_left, xr, bufs->a, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
     if (e == hipSuccess) e = q(bufs->a, m, m, fl, o + 2, &bufs->a_left);
-    if (e == hipSuccess) e = q(bufs->a, m, m, fr, o + 3, &bufs->a_right);
+    if (e == hipSuccess && !same) e = q(bufs->a, m, m, fr, o + 3, &bufs->a_right);
     if (e == hipSuccess)
-      e = nvfp4::launch_gemm_ws(&bufs->a_left, &bufs->a_right, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
+      e = nvfp4::launch_gemm_ws(&bufs->a_left, ar, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
     if (e == hipSuccess) e = nvfp4::launch_axpby(cfg->b, bufs->a, cfg->c, bufs->b, m * m, stream);
     if (e == hipSuccess) e = q(bufs->b, m, m, fl, o + 4, &bufs->b_q);
     if (e == hipSuccess) e = q(x, m, n, fr | FP4_Q_COLWISE, o + 5, &bufs->xt);

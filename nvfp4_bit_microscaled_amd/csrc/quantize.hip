@@ -213,6 +213,34 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict
   block_max_to(m, out, partial);
 }
 
+// bf16: the bit patterns of non-negative finite values order like the values, so
+// the maximum of |x| is taken on the raw 16-bit patterns with the sign bits
+// cleared (one packed integer max per two elements) and widened once at the end.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <>
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel<uint16_t>(const uint16_t *__restrict__ x, int64_t nchunks,
+                                                                       float *out, float *partial) {
+  u16x2 m = {0, 0};
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nchunks; i += 4 * stride) {
+    uint4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = i + u * stride;
+      q[u] = j < nchunks ? *reinterpret_cast<const uint4 *>(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
+    }
+  }
+  const uint32_t top = m[0] > m[1] ? m[0] : m[1];
+  block_max_to(__uint_as_float(top << 16), out, partial);
+}
+
 // amax after the Hadamard transform along rows (16 contiguous elements).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const T *__restrict__ x, int64_t R, int64_t C,
@@ -578,7 +606,9 @@ __device__ __forceinline__ void rotate64_quad(float v[16], uint32_t sign16, int 
 }
 
 // Columnwise: col holds one column of the 16-row slab that is quarter q (= lane >> 4)
-// of its 64-group, signs already applied; partners are lanes ^ 16 and ^ 32.
+// of its 64-group, signs already applied; partners are lanes ^ 16 and ^ 32, reached
+// through the LDS crossbar (ds_bpermute), which runs beside the vector ALU this
+// kernel is bound by.  gfx950's permlane swaps (vector-ALU moves) measured 6% slower.
 __device__ __forceinline__ void rotate64_cols(float col[16], int q) {
   hadamard16_unscaled(col);
 #pragma unroll
