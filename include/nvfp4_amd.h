@@ -335,7 +335,9 @@ FP4_API fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype 
  *   0                        every operand 1D nearest-even (the two operands of
  *                            X X^T, and of A A^T, are then the same quantization:
  *                            x_left and a_left serve both sides, and x_right and
- *                            a_right are not written);
+ *                            a_right are not written; x_left and xt come from one
+ *                            read of X, and the amaxes of B and of the next X are
+ *                            taken as the element-wise steps write them);
  *   FP4_Q_RHT | FP4_Q_SR     every operand with the 16-point transform (mask
  *                            rht_signs) and stochastic rounding;
  *   FP4_Q_RHT64 | FP4_Q_EDEN left operands (X left, A left, B) MS-EDEN, right
@@ -358,7 +360,8 @@ typedef struct fp4_ns_buffers {
   float *b;  /* [m][m]: A A^T, then B */
   float *bx; /* [m][n]: B X */
   fp4_tensor x_left, x_right, a_left, a_right, b_q, xt;
-  void *ws;  /* GEMM split-K workspace and the normalisation's scratch (fp4_newton_schulz_ws_bytes), 16-byte aligned */
+  void *ws;  /* GEMM split-K workspace and the element-wise steps' scratch (fp4_newton_schulz_ws_bytes), 16-byte
+              * aligned */
   size_t ws_bytes;
 } fp4_ns_buffers;
 
@@ -373,8 +376,9 @@ FP4_API fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_
                                      const fp4_ns_config *cfg, const fp4_ns_buffers *bufs, hipStream_t stream);
 
 /* Workspace bytes fp4_newton_schulz needs for X [m][n]: the largest split-K plan of
- * its three GEMMs (m x m x n, m x m x m, m x n x m), and at least the normalisation's
- * 8196 bytes.  FP4_ERR_NULL, FP4_ERR_SHAPE. */
+ * its three GEMMs (m x m x n, m x m x m, m x n x m), and at least 16384 bytes (the
+ * normalisation's binary64 partial sums, the per-workgroup maxima of the
+ * element-wise steps).  FP4_ERR_NULL, FP4_ERR_SHAPE. */
 FP4_API fp4_status fp4_newton_schulz_ws_bytes(int64_t m, int64_t n, size_t *bytes);
 
 /* A short static description of a status code (never NULL). */

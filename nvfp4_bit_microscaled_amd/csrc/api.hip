@@ -262,6 +262,7 @@ fp4_status fp4_newton_schulz_ws_bytes(int64_t m, int64_t n, size_t *bytes) {
   if (!bytes) return FP4_ERR_NULL;
   if (m < 0 || n < 0 || m % 16 || n % 16) return FP4_ERR_SHAPE;
   size_t w = nvfp4::normalize_scratch_bytes();
+  if (nvfp4::axpby_partial_bytes() > w) w = nvfp4::axpby_partial_bytes();
   const size_t g[3] = {nvfp4::gemm_ws_bytes(m, m, n), nvfp4::gemm_ws_bytes(m, m, m), nvfp4::gemm_ws_bytes(m, n, m)};
   for (size_t v : g) w = v > w ? v : w;
   *bytes = w;
@@ -309,23 +310,47 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
     auto q = [&](const float *src, int64_t r, int64_t c, uint32_t f, uint64_t off, const fp4_tensor *out) {
       return nvfp4::launch_quantize(src, FP4_FP32, r, c, c, f, key, cfg->seed, off, out, nullptr, stream);
     };
-    // nearest-even: both operands of X X^T (and of A A^T) are the same quantization
+    // Nearest-even: both operands of X X^T (and of A A^T) are the same quantization,
+    // X's rowwise and columnwise layouts come from one read of X (the dual
+    // quantization), and the amaxes of B and of the next X are taken by the axpby
+    // steps that write them (per-workgroup maxima in the workspace), so those
+    // tensors are quantized with their amax given.  The next X's maxima are reduced
+    // into X's descriptors at the start of the next iteration, so that after the
+    // call every descriptor describes the operand it holds.
     const bool same = cfg->flags == 0;
     const fp4_tensor *xr = same ? &bufs->x_left : &bufs->x_right, *ar = same ? &bufs->a_left : &bufs->a_right;
-    e = q(x, m, n, fl, o + 0, &bufs->x_left);
-    if (e == hipSuccess && !same) e = q(x, m, n, fr, o + 1, &bufs->x_right);
+    float *partial = static_cast<float *>(bufs->ws);
+    if (same) {
+      if (t > 0) e = nvfp4::launch_max_finish(partial, nvfp4::axpby_parts(m * n), bufs->x_left.amax, bufs->xt.amax,
+                                              stream);
+      if (e == hipSuccess)
+        e = nvfp4::launch_quantize_dual(x, FP4_FP32, m, n, n, t > 0 ? FP4_Q_AMAX_GIVEN : 0u, key, cfg->seed, o + 0,
+                                        o + 5, &bufs->x_left, &bufs->xt, stream);
+    } else {
+      e = q(x, m, n, fl, o + 0, &bufs->x_left);
+      if (e == hipSuccess) e = q(x, m, n, fr, o + 1, &bufs->x_right);
+    }
     if (e == hipSuccess)
       e = nvfp4::launch_gemm_ws(&bufs->x_left, xr, bufs->a, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
     if (e == hipSuccess) e = q(bufs->a, m, m, fl, o + 2, &bufs->a_left);
     if (e == hipSuccess && !same) e = q(bufs->a, m, m, fr, o + 3, &bufs->a_right);
     if (e == hipSuccess)
       e = nvfp4::launch_gemm_ws(&bufs->a_left, ar, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
-    if (e == hipSuccess) e = nvfp4::launch_axpby(cfg->b, bufs->a, cfg->c, bufs->b, m * m, stream);
-    if (e == hipSuccess) e = q(bufs->b, m, m, fl, o + 4, &bufs->b_q);
-    if (e == hipSuccess) e = q(x, m, n, fr | FP4_Q_COLWISE, o + 5, &bufs->xt);
+    if (same) {
+      if (e == hipSuccess) e = nvfp4::launch_axpby_amax(cfg->b, bufs->a, cfg->c, bufs->b, m * m, partial, stream);
+      if (e == hipSuccess)
+        e = nvfp4::launch_max_finish(partial, nvfp4::axpby_parts(m * m), bufs->b_q.amax, nullptr, stream);
+      if (e == hipSuccess) e = q(bufs->b, m, m, fl | FP4_Q_AMAX_GIVEN, o + 4, &bufs->b_q);
+    } else {
+      if (e == hipSuccess) e = nvfp4::launch_axpby(cfg->b, bufs->a, cfg->c, bufs->b, m * m, stream);
+      if (e == hipSuccess) e = q(bufs->b, m, m, fl, o + 4, &bufs->b_q);
+      if (e == hipSuccess) e = q(x, m, n, fr | FP4_Q_COLWISE, o + 5, &bufs->xt);
+    }
     if (e == hipSuccess)
       e = nvfp4::launch_gemm_ws(&bufs->b_q, &bufs->xt, bufs->bx, FP4_FP32, n, bufs->ws, bufs->ws_bytes, stream);
-    if (e == hipSuccess) e = nvfp4::launch_axpby(1.0f, bufs->bx, cfg->a, x, m * n, stream);
+    if (e == hipSuccess)
+      e = same ? nvfp4::launch_axpby_amax(1.0f, bufs->bx, cfg->a, x, m * n, partial, stream)
+               : nvfp4::launch_axpby(1.0f, bufs->bx, cfg->a, x, m * n, stream);
   }
   return from_hip(e);
 }

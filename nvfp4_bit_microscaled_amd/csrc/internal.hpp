@@ -52,8 +52,16 @@ constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 // device; allocates nothing).
 hipError_t static_scratch(void **ptr);
 
-// The Newton-Schulz iteration's binary32 steps (ns.hip).
+// The Newton-Schulz iteration's binary32 steps (ns.hip).  n % 4 == 0 and 16-byte
+// aligned vectors for the axpby launches.
 hipError_t launch_axpby(float alpha, const float *x, float beta, float *y, int64_t n, hipStream_t stream);
+// axpby that also leaves per-workgroup maxima of |y| in partial[0 .. axpby_parts(n))
+// (axpby_partial_bytes() at most), reduced by launch_max_finish into *out0 (and *out1)
+int axpby_parts(int64_t n);
+size_t axpby_partial_bytes();
+hipError_t launch_axpby_amax(float alpha, const float *x, float beta, float *y, int64_t n, float *partial,
+                             hipStream_t stream);
+hipError_t launch_max_finish(const float *partial, int n, float *out0, float *out1, hipStream_t stream);
 size_t normalize_scratch_bytes();
 hipError_t launch_normalize(const float *g, float *x, int64_t n, float eps, void *scratch, hipStream_t stream);
 

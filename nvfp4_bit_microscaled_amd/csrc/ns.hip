@@ -3,7 +3,7 @@
 // Newton-Schulz iterations run natively in NVFP4).  The iteration's products are
 // fp4_gemm calls on quantized operands; what runs here is binary32 arithmetic
 // between them, one IEEE operation per step (built with -ffp-contract=off):
-//   y = alpha x + beta y          (fl(fl(alpha x) + fl(beta y)))
+//   y = alpha x + beta y          (fl(fl(alpha x) + fl(beta y))), optionally with max |y|
 //   x0 = g * s, s = RN32(1 / (sqrt(sum g^2) + eps)), the sum of squares in binary64
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -17,13 +17,56 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSumBlocks = 1024;  // workgroups of the sum of squares (and binary64 partials)
 
-// y[i] = alpha * x[i] + beta * y[i], 4 elements per thread-step when aligned.
-__global__ __launch_bounds__(kThreads) void axpby_kernel(float alpha, const float *__restrict__ x, float beta,
-                                                         float *__restrict__ y, int64_t n) {
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads) {
-    const float p = alpha * x[i];
-    const float q = beta * y[i];
-    y[i] = p + q;
+// y[i] = alpha * x[i] + beta * y[i], four elements per thread-step (n % 4 == 0,
+// both 16-byte aligned).  With AMAX, workgroup b also stores the maximum |y| over
+// the elements it wrote at partial[b] (max_finish_kernel reduces those): the
+// amax that the quantization of y would otherwise take in a pass of its own.
+template <bool AMAX>
+__global__ __launch_bounds__(kThreads) void axpby_kernel(float alpha, const float4 *__restrict__ x, float beta,
+                                                         float4 *__restrict__ y, int64_t n4, float *partial) {
+  float m = 0.0f;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n4; i += int64_t(gridDim.x) * kThreads) {
+    const float4 a = x[i], b = y[i];
+    const float va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b.x, b.y, b.z, b.w};
+    float r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float p = alpha * va[k];
+      const float q = beta * vb[k];
+      r[k] = p + q;
+      if (AMAX) m = fmaxf(m, __builtin_fabsf(r[k]));
+    }
+    y[i] = make_float4(r[0], r[1], r[2], r[3]);
+  }
+  if constexpr (AMAX) {
+    __shared__ float part[kThreads / 64];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, part[w]);
+      partial[blockIdx.x] = m;
+    }
+  }
+}
+
+// *out0 (and *out1 when given) = max of partial[0 .. n) (one workgroup).
+__global__ __launch_bounds__(kThreads) void max_finish_kernel(const float *__restrict__ partial, int n, float *out0,
+                                                              float *out1) {
+  __shared__ float part[kThreads / 64];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, partial[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, part[w]);
+    *out0 = m;
+    if (out1) *out1 = m;
   }
 }
 
@@ -74,10 +117,27 @@ unsigned grid_of(int64_t n) {
 
 hipError_t launch_axpby(float alpha, const float *x, float beta, float *y, int64_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  return launch(axpby_kernel, dim3(grid_of(n)), dim3(kThreads), stream, alpha, x, beta, y, n);
+  return launch(axpby_kernel<false>, dim3(grid_of(n / 4)), dim3(kThreads), stream, alpha,
+                reinterpret_cast<const float4 *>(x), beta, reinterpret_cast<float4 *>(y), n / 4,
+                static_cast<float *>(nullptr));
+}
+
+int axpby_parts(int64_t n) { return int(grid_of(n / 4)); }
+
+hipError_t launch_axpby_amax(float alpha, const float *x, float beta, float *y, int64_t n, float *partial,
+                             hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  return launch(axpby_kernel<true>, dim3(grid_of(n / 4)), dim3(kThreads), stream, alpha,
+                reinterpret_cast<const float4 *>(x), beta, reinterpret_cast<float4 *>(y), n / 4, partial);
+}
+
+hipError_t launch_max_finish(const float *partial, int n, float *out0, float *out1, hipStream_t stream) {
+  return launch(max_finish_kernel, dim3(1), dim3(kThreads), stream, partial, n, out0, out1);
 }
 
 size_t normalize_scratch_bytes() { return kSumBlocks * sizeof(double) + sizeof(float); }
+
+size_t axpby_partial_bytes() { return 4096 * sizeof(float); }  // grid_of's cap
 
 // x = g / (|g|_F + eps); scratch: normalize_scratch_bytes(), 8-byte aligned.
 hipError_t launch_normalize(const float *g, float *x, int64_t n, float eps, void *scratch, hipStream_t stream) {
