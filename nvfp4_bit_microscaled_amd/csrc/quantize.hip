@@ -432,23 +432,13 @@ __device__ __forceinline__ void store_col_tile(const uint8_t *lcodes, const uint
     }
   }
 }
-// With ROWS (nearest-even only) the same read of x also writes x's rowwise
-// layout (codes [R][C/2], scales [R][C/16], tensor amax *ramax_p): a thread's 8
-// columns of a row are half of a 16-column block, whose other half lane ^ 1 holds,
-// so the block amax takes one lane exchange; the codes leave as 4 bytes per
-// thread, 128 consecutive bytes per row and half-wave.  A row whose transform sign
-// is set holds -x in the slab; its multiplier is negated, so the products are
-// those of x (nearest-even is symmetric).  Both layouts are bit-identical to the
-// separate rowwise and columnwise kernels'.
-// At least three waves per SIMD: the fused rowwise layout (ROWS) would otherwise
-// take 174 registers and two waves; 168 with three measured 10 us faster per step.
-template <typename T, bool RHT, bool SR, bool ROWS = false>
+// At most 168 registers (three waves per SIMD); held to four waves (128) the
+// stochastic variant spilled to scratch memory and measured 250 us instead of 212
+// per 12B step.
+template <typename T, bool RHT, bool SR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void quant_cols_kernel(
     const T *__restrict__ x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
-    const float *__restrict__ amax_p, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-    const float *__restrict__ ramax_p = nullptr, uint8_t *__restrict__ rcodes = nullptr,
-    uint8_t *__restrict__ rscales = nullptr) {
-  static_assert(!(ROWS && SR), "the fused rowwise layout is nearest-even");
+    const float *__restrict__ amax_p, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
   __shared__ __attribute__((aligned(16))) uint8_t lcodes[kColTile * kColRowBytes];
   __shared__ uint8_t lscales[kColTile * kColSlabs];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -458,14 +448,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int64_t nslab = R / 16;                                // logical blocks per logical row
   const int64_t cfirst = c0 + 8 * cg;                          // this thread's first column
   __shared__ float tab[kMultTable];
-  __shared__ float rtab[ROWS ? kMultTable : 1];
   const float s_enc = encode_scale(*amax_p);
   fill_mult_table(tab, s_enc);
-  float rs_enc = 0.0f;
-  if constexpr (ROWS) {
-    rs_enc = encode_scale(*ramax_p);
-    fill_mult_table(rtab, rs_enc);
-  }
   __syncthreads();
 
 #pragma unroll 1
@@ -475,31 +459,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (s >= nslab || cfirst >= C) continue;                   // lanes 2k, 2k + 1 skip together (C % 16 == 0)
     Slab8<T> slab;
     slab.load(x + s * 16 * ld + cfirst, ld, RHT ? signs : 0u);
-    if constexpr (ROWS) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v[8];
-        float m = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          v[j] = slab.at(r, j);
-          m = fmaxf(m, __builtin_fabsf(v[j]));
-        }
-        // the block's other 8 columns are lane ^ 1's (DPP quad_perm [1, 0, 3, 2])
-        const float mo = __uint_as_float(
-            uint32_t(__builtin_amdgcn_update_dpp(0, int(__float_as_uint(m)), 0xB1, 0xF, 0xF, false)));
-        uint32_t sc;
-        float mult;
-        block_scale(fmaxf(m, mo), rs_enc, rtab, sc, mult);
-        if (RHT && ((signs >> r) & 1u)) mult = -mult;
-        float sv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] = v[j] * mult;
-        const int64_t row = s * 16 + r;
-        *reinterpret_cast<uint32_t *>(rcodes + row * (C / 2) + cfirst / 2) = encode8_rne(sv);
-        if ((cg & 1) == 0) rscales[row * (C / 16) + cfirst / 16] = uint8_t(sc);
-      }
-    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float col[16];
@@ -528,6 +487,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       const int pair = (sl >> 1) ^ ((row >> 3) & 7);
       *reinterpret_cast<uint2 *>(&lcodes[row * kColRowBytes + pair * 16 + (sl & 1) * 8]) = packed;
       lscales[row * kColSlabs + sl] = uint8_t(sc);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();
@@ -535,6 +495,188 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   store_col_tile(lcodes, lscales, R, C, c0, slab0, codes, scales);
 }
 
+
+// Raw buffer access from a wave-uniform base: the descriptor sits in scalar
+// registers, each row's byte offset in a scalar register, and only the lane's
+// column offset in a vector register, so 16 rows cost no vector address
+// arithmetic.  The base pointer is made explicitly uniform (its value is the same
+// in every lane of the wave); the range field is left at its maximum and every
+// access stays inside the tensor.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a)), hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((uint64_t(hi) << 32) | lo), short(0), 0x7FFFFFFF,
+                                           0x00020000);
+}
+
+// 16 rows x 4 adjacent columns of x (one 16-row slab), as loaded; row r negated
+// when bit r of `neg` is set.  Column j is widened to binary32 when it is used.
+// rs: a buffer at the slab's first element of the workgroup's first column; ldb:
+// the row stride in bytes; lane owns columns 4 lane .. 4 lane + 3 from there.
+template <typename T>
+struct Slab4;
+
+template <>
+struct Slab4<uint16_t> {
+  uint2 w[16];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int lane, uint32_t neg) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, int(uint32_t(r) * ldb), 0);
+      const uint32_t f = ((neg >> r) & 1u) ? 0x80008000u : 0u;
+      w[r] = make_uint2(q[0] ^ f, q[1] ^ f);
+    }
+  }
+  __device__ __forceinline__ float at(int r, int j) const {
+    const uint32_t v = (j >> 1) ? w[r].y : w[r].x;
+    return __uint_as_float((j & 1) ? (v & 0xFFFF0000u) : (v << 16));
+  }
+};
+
+template <>
+struct Slab4<float> {
+  float v[16][4];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int lane, uint32_t neg) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, int(uint32_t(r) * ldb), 0);
+      const uint32_t f = ((neg >> r) & 1u) ? 0x80000000u : 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[r][j] = __uint_as_float(q[j] ^ f);
+    }
+  }
+  __device__ __forceinline__ float at(int r, int j) const { return v[r][j]; }
+};
+
+// v of quad lane o, in every lane of the quad (DPP quad_perm [o, o, o, o]); o is a
+// constant once the caller's loop is unrolled.
+template <int O>
+__device__ __forceinline__ float quad_bcast_c(float v) {
+  return __uint_as_float(uint32_t(__builtin_amdgcn_mov_dpp(int(__float_as_uint(v)), O * 0x55, 0xF, 0xF, false)));
+}
+
+__device__ __forceinline__ float quad_bcast(float v, int o) {
+  switch (o) {
+    case 0: return quad_bcast_c<0>(v);
+    case 1: return quad_bcast_c<1>(v);
+    case 2: return quad_bcast_c<2>(v);
+    default: return quad_bcast_c<3>(v);
+  }
+}
+
+// Both nearest-even layouts of x from one read: the columnwise layout (x^T, with
+// the transform down 16-row slabs when RHT) and x's rowwise layout (no transform;
+// codes [R][C/2], scales [R][C/16], tensor amax *ramax_p).  The tile of a
+// workgroup is that of quant_cols_kernel (kColTile columns, kColSlabs slabs), with
+// the columnwise codes gathered in LDS the same way and leaving as whole lines.
+// Thread (wave w, lane l) owns columns 4 l .. 4 l + 3 of the tile and slabs
+// w + 4 i (i < kColSlabs / 4): 16 x 4 elements per step, half of what
+// quant_cols_kernel's threads hold, so that four waves share a SIMD (126
+// registers; the LDS tile allows no more).  Rows are addressed through buffer
+// descriptors with scalar row offsets, which keeps 16 row pointers out of the
+// vector registers.
+//  * Columnwise: each of the thread's 4 columns is a whole 16-block.
+//  * Rowwise: a 16-column block is 4 lanes (a DPP quad); its amax takes two lane
+//    exchanges, lane q of the quad computes the scales of rows q, q + 4, q + 8 and
+//    q + 12 (and stores their bytes), and each row's multiplier is broadcast from
+//    its lane.  The codes leave as 2 bytes per lane, 128 contiguous bytes per row
+//    and wave.  A row whose transform sign is set holds -x in the slab; its
+//    multiplier is negated, so the products are those of x (nearest-even is
+//    symmetric).
+// Bit-identical to the separate rowwise and columnwise kernels, and tested so.
+// On the MI355X it takes 55 us for the 12B MLP's X (16384 x 5120 bf16, with the
+// transform), where the 8-column form with both layouts took 60 us.
+template <typename T, bool RHT>
+__global__ __launch_bounds__(kThreads) void quant_dual_ne_kernel(
+    const T *__restrict__ x, int64_t R, int64_t C, int64_t ld, uint32_t signs, const float *__restrict__ amax_p,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, const float *__restrict__ ramax_p,
+    uint8_t *__restrict__ rcodes, uint8_t *__restrict__ rscales) {
+  __shared__ __attribute__((aligned(16))) uint8_t lcodes[kColTile * kColRowBytes];
+  __shared__ uint8_t lscales[kColTile * kColSlabs];
+  __shared__ float tab[kMultTable], rtab[kMultTable];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = int64_t(blockIdx.x) * kColTile;      // first column of the tile
+  const int64_t slab0 = int64_t(blockIdx.y) * kColSlabs;  // first slab of the tile
+  const int64_t nslab = R / 16;
+  const int64_t cfirst = c0 + 4 * lane;                    // this thread's first column
+  const float s_enc = encode_scale(*amax_p), rs_enc = encode_scale(*ramax_p);
+  fill_mult_table(tab, s_enc);
+  fill_mult_table(rtab, rs_enc);
+  __syncthreads();
+
+#pragma unroll 1
+  for (int i = 0; i < kColSlabs / 4; ++i) {
+    const int sl = wave + 4 * i;  // slab within the tile
+    const int64_t s = slab0 + sl;
+    if (s >= nslab || cfirst >= C) continue;  // a lane quad skips together (C % 16 == 0)
+    // wave-uniform bases (the launcher keeps 16 rows of x within 2^31 bytes)
+    Slab4<T> slab;
+    slab.load(wave_rsrc(x + s * 16 * ld + c0), uint32_t(ld * int64_t(sizeof(T))), lane, RHT ? signs : 0u);
+    const __amdgpu_buffer_rsrc_t rc = wave_rsrc(rcodes + s * 16 * (C / 2) + c0 / 2);
+    const __amdgpu_buffer_rsrc_t rs = wave_rsrc(rscales + s * 16 * (C / 16) + c0 / 16);
+    // Rowwise.  Block maxima of the 16 rows: the lane's 4 columns, then the quad's
+    // other lanes (DPP quad_perm [1, 0, 3, 2], then [2, 3, 0, 1]), as integers (the
+    // bit patterns of non-negative floats order like the values).
+    uint32_t mb[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, __builtin_fabsf(slab.at(r, j)));
+      uint32_t u = __float_as_uint(m);
+      u = max(u, uint32_t(__builtin_amdgcn_mov_dpp(int(u), 0xB1, 0xF, 0xF, true)));
+      u = max(u, uint32_t(__builtin_amdgcn_mov_dpp(int(u), 0x4E, 0xF, 0xF, true)));
+      mb[r] = u;
+    }
+    // Lane q of a quad takes the scales of rows q, q + 4, q + 8 and q + 12, and
+    // stores their scale bytes; each row's multiplier comes from its lane (DPP
+    // quad_perm broadcast).
+    const int q = lane & 3;
+    float multk[4];
+    uint32_t sck[4], w = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t mq = q == 0 ? mb[4 * k] : q == 1 ? mb[4 * k + 1] : q == 2 ? mb[4 * k + 2] : mb[4 * k + 3];
+      block_scale(__uint_as_float(mq), rs_enc, rtab, sck[k], multk[k]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float mult = quad_bcast(multk[r >> 2], r & 3);
+      if (RHT) mult = __uint_as_float(__float_as_uint(mult) ^ (((signs >> r) & 1u) << 31));
+      // bytes 0 and 1 of w; the others are not stored (canon_zero works per nibble)
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, slab.at(r, 0) * mult, slab.at(r, 1) * mult, 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, slab.at(r, 2) * mult, slab.at(r, 3) * mult, 1.0f, 1);
+      __builtin_amdgcn_raw_buffer_store_b16(uint16_t(canon_zero(w)), rc, 2 * lane, int(r * (C / 2)), 0);
+      if (q == (r & 3)) __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sck[r >> 2]), rs, lane >> 2, int(r * (C / 16)), 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
+      uint32_t sc;
+      float mult;
+      if (RHT) {
+        hadamard16_unscaled(col);
+        block_scale_quarter(col, s_enc, tab, sc, mult);
+      } else {
+        float amax_b = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) amax_b = fmaxf(amax_b, __builtin_fabsf(col[r]));
+        block_scale(amax_b, s_enc, tab, sc, mult);
+      }
+      const uint2 packed = encode16_rne(col, mult);
+      const int row = 4 * lane + j;  // logical row within the tile
+      const int pair = (sl >> 1) ^ ((row >> 3) & 7);
+      *reinterpret_cast<uint2 *>(&lcodes[row * kColRowBytes + pair * 16 + (sl & 1) * 8]) = packed;
+      lscales[row * kColSlabs + sl] = uint8_t(sc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+
+  store_col_tile(lcodes, lscales, R, C, c0, slab0, codes, scales);
+}
 
 // Both tensor amaxes of a dual quantization in one read: |x| (rowwise layout) and
 // |x| after the transform down 16-row slabs (columnwise layout).  A thread owns 8
@@ -986,8 +1128,8 @@ hipError_t launch_cols(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t si
                        const fp4_tensor *out, hipStream_t stream) {
   const int64_t nslab = R / 16;
   dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
-  return launch(quant_cols_kernel<T, RHT, SR, false>, grid, dim3(kThreads), stream, x, R, C, ld, signs, seed, offset,
-                out->amax, out->codes, out->scales, nullptr, nullptr, nullptr);
+  return launch(quant_cols_kernel<T, RHT, SR>, grid, dim3(kThreads), stream, x, R, C, ld, signs, seed, offset,
+                out->amax, out->codes, out->scales);
 }
 
 template <typename T, bool EDEN, bool SR>
@@ -1009,10 +1151,14 @@ template <typename T, bool RHT>
 hipError_t launch_cols_rows(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t signs, const fp4_tensor *cols,
                             const fp4_tensor *rows, hipStream_t stream) {
   const int64_t nslab = R / 16;
+  if (16 * ld * int64_t(sizeof(T)) >= (int64_t(1) << 31)) {
+    // rows too long for the fused kernel's 32-bit offsets: one kernel per layout
+    hipError_t e = launch_cols<T, RHT, false>(x, R, C, ld, signs, 0, 0, cols, stream);
+    return e == hipSuccess ? launch_rows<T, false, false>(x, R, C, ld, signs, 0, 0, rows, stream) : e;
+  }
   dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
-  return launch(quant_cols_kernel<T, RHT, false, true>, grid, dim3(kThreads), stream, x, R, C, ld, signs,
-                uint64_t(0), uint64_t(0), cols->amax, cols->codes, cols->scales, rows->amax, rows->codes,
-                rows->scales);
+  return launch(quant_dual_ne_kernel<T, RHT>, grid, dim3(kThreads), stream, x, R, C, ld, signs, cols->amax,
+                cols->codes, cols->scales, rows->amax, rows->codes, rows->scales);
 }
 
 template <typename T>
@@ -1057,8 +1203,8 @@ hipError_t quantize_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t 
 }
 
 // Dual quantization: both amaxes in one read of x (unless given), then the layouts.
-// Nearest-even: one kernel writes both from one read of x (quant_cols_kernel with
-// ROWS), 18 us faster per 12B step than two kernels.  Stochastic: the rowwise and
+// Nearest-even: one kernel writes both from one read of x (quant_dual_ne_kernel),
+// 18 us faster per 12B step than two kernels.  Stochastic: the rowwise and
 // the columnwise kernels in turn; a single kernel measured slower there, since the
 // stochastic encoders are bound by vector-ALU work, which fusion does not reduce.
 template <typename T>

@@ -183,6 +183,9 @@ DUAL_CASES = [
     (512, 256, "rht"),
     (272, 400, "sr"),
     (48, 784, "none"),
+    # the nearest-even pair at ragged tiles: a partial last column tile and slab tile
+    (272, 400, "rht"),
+    (48, 784, "rht"),
     # 8 x 8 whole tiles of the columnwise kernels
     (2048, 2048, "rht"),
     (2048, 2048, "sr_rht"),
