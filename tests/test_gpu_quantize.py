@@ -276,3 +276,24 @@ def test_amax_pass_both_forms(fp4, oracle, shape):
     xf = workloads.widen(x_cpu)
     assert_q_equal(host_q(qr), oracle.quantize(xf), f"dual rows {shape}")
     assert_q_equal(host_q(qc), oracle.quantize(xf, colwise=True, rht=True, signs=0x1F2E), f"dual cols {shape}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_dual_with_a_row_stride_beyond_the_fused_kernel(fp4, oracle, dtype):
+    """16 rows that span 2^31 bytes (row stride 2^31 / (16 * element size) elements)
+    are beyond the one-kernel dual layouts' 32-bit row offsets: the call takes one
+    kernel per layout and gives the same bits (a 2 GiB strided view, 16 x 256)."""
+    R, C = 16, 256
+    ld = (1 << 31) // (16 * torch.finfo(dtype).bits // 8)
+    x_cpu = make_x((R, C), seed=77, dtype=dtype)
+    full = torch.empty((R, ld), dtype=dtype, device="cuda")
+    x = full[:, :C]
+    x.copy_(x_cpu.to("cuda"))
+    assert x.stride(0) == ld
+    qr, qc = fp4.QTensor(R, C), fp4.QTensor(C, R)
+    fp4.fp4_quantize_dual(x, fp4.Q_RHT, 0x2C4B, 0, 0, 0, qr, qc)
+    xf = workloads.widen(x_cpu)
+    assert_q_equal(host_q(qr), oracle.quantize(xf), "wide-stride dual rows")
+    assert_q_equal(host_q(qc), oracle.quantize(xf, colwise=True, rht=True, signs=0x2C4B), "wide-stride dual cols")
+    del full, x
+    torch.cuda.empty_cache()
