@@ -56,12 +56,18 @@ def test_newton_schulz_stagewise(fp4, oracle, variant, shape):
         assert np.array_equal(xn, st["x_next"]), f"{variant} iteration {t} X'"
         xt = xn
     if iters > 1:
-        # several iterations in one call equal the same iterations one call each
+        # several iterations in one call equal the same iterations one call each; the
+        # last iteration's operands too (with nearest-even, a call's later iterations
+        # take X's amax from the axpby that wrote X, the first from an amax pass)
         x2 = torch.empty_like(g)
-        fp4.fp4_newton_schulz(g, x2, iters, fp4.NsBuffers(m, n), normalize=True, flags=flags, rht_signs=SIGNS,
-                              seed=7, offset=100)
+        bufs2 = fp4.NsBuffers(m, n)
+        fp4.fp4_newton_schulz(g, x2, iters, bufs2, normalize=True, flags=flags, rht_signs=SIGNS, seed=7, offset=100)
         torch.cuda.synchronize()
         assert torch.equal(x2, x)
+        for name in names:
+            c1, s1, a1 = host_q(getattr(bufs2, name))
+            c2, s2, a2 = host_q(getattr(bufs, name))
+            assert a1 == a2 and np.array_equal(s1, s2) and np.array_equal(c1, c2), f"{variant} one call, {name}"
 
 
 def test_newton_schulz_rejects_bad_arguments(fp4):
