@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (the known-size reference that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters into bytes) and exit")
+    ap.add_argument("--stream-rates", action="store_true",
+                    help="only measure streaming rates (the library's amax pass at 256 MiB to 2 GiB of bf16, and a "
+                         "2 GiB device copy) and print one JSON line")
     return ap.parse_args()
 
 
@@ -230,6 +233,45 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": x.numel() * 4, "launches": 3}), flush=True)
 
+
+
+def stream_rates():
+    """The practical HBM read rate by size: fp4_amax (a read-only pass, atomic form)
+    over 256 MiB, 512 MiB and 2 GiB of bf16 (the 256 MB Infinity Cache holds at most
+    the first), and a 2 GiB device copy; median of 10 launches each, after 3 warm-up
+    launches, timed with HIP events on the current stream."""
+    import torch
+
+    import nvfp4_bit_microscaled_amd as fp4
+    fp4.load()
+    x = torch.randn(2**30 // 4096, 4096, dtype=torch.bfloat16, device="cuda")  # 2 GiB
+    y = torch.empty_like(x)
+    a = torch.zeros(1, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def med_ms(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = HipTimingEvent(), HipTimingEvent()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[reps // 2]
+
+    out = {"unit": "TB/s", "amax_read": {}}
+    for mib in (256, 512, 2048):
+        xs = x.view(-1)[:mib * 2**20 // 2].view(-1, 4096)
+        ms = med_ms(lambda: fp4.fp4_amax(xs, 0, 0, a))
+        out["amax_read"][f"{mib} MiB"] = {"ms": round(ms, 4), "rate": round(mib * 2**20 / (ms * 1e-3) / 1e12, 3)}
+    ms = med_ms(lambda: y.copy_(x))
+    out["copy_2GiB"] = {"ms": round(ms, 4), "rate": round(2 * 2**31 / (ms * 1e-3) / 1e12, 3),
+                        "bytes": "read + written"}
+    print(json.dumps(out), flush=True)
 
 
 class HipTimingEvent:
@@ -536,6 +578,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.stream_rates:
+        stream_rates()
         return
     if args.error_vs_k:
         error_vs_k()
