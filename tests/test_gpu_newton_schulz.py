@@ -21,7 +21,7 @@ def variant_flags(fp4, variant):
 
 
 @pytest.mark.parametrize("variant", ["rne", "rht_sr", "eden"])
-@pytest.mark.parametrize("shape", [(128, 256), (256, 768), (1024, 4096)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("shape", [(128, 256), (256, 768), (1024, 4096), (512, 128)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_newton_schulz_stagewise(fp4, oracle, variant, shape):
     m, n = shape
     iters = 3 if m < 1024 else 1
