@@ -381,7 +381,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T *__restric
   }
 }
 
-// Columnwise 1D quantization (logical tensor x^T, blocks down the columns of x).
+// Columnwise 1D quantization (logical tensor x^T, blocks down the columns of x),
+// the form for rows too long for quant_cols4_kernel's 32-bit row offsets.
 // A workgroup covers kColTile columns of x and kColSlabs 16-row slabs of it.
 // Thread (wave w, lane l) owns columns 8 (l % 32) .. +7 of the tile and slabs
 // 2 w + l / 32 + 8 i (i < kColSlabs / 8).  Codes go to LDS as [column][slab]
@@ -564,6 +565,81 @@ __device__ __forceinline__ float quad_bcast(float v, int o) {
   }
 }
 
+// Column j of a 4-column slab as one columnwise 16-block (logical row `row` of the
+// workgroup's tile, logical block `sl`): the transform down the slab when RHT,
+// block scale, then nearest-even or stochastic codes (the 16 random half-words of
+// logical index i0) into the LDS tile, swizzled as in quant_cols_kernel.
+template <typename T, bool RHT, bool SR>
+__device__ __forceinline__ void col_block4(const Slab4<T> &slab, int j, float s_enc, const float *tab, int row, int sl,
+                                           uint64_t i0, uint64_t seed, uint64_t offset, uint8_t *lcodes,
+                                           uint8_t *lscales) {
+  float col[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
+  uint32_t sc;
+  float mult;
+  if (RHT) {
+    hadamard16_unscaled(col);
+    block_scale_quarter(col, s_enc, tab, sc, mult);
+  } else {
+    float amax_b = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) amax_b = fmaxf(amax_b, __builtin_fabsf(col[r]));
+    block_scale(amax_b, s_enc, tab, sc, mult);
+  }
+  uint2 packed;
+  if (SR) {
+    uint32_t rb[8];
+    sr_bits16(i0, seed, offset, rb);
+    packed = encode16_sr(col, mult, rb);
+  } else {
+    packed = encode16_rne(col, mult);
+  }
+  const int pair = (sl >> 1) ^ ((row >> 3) & 7);
+  *reinterpret_cast<uint2 *>(&lcodes[row * kColRowBytes + pair * 16 + (sl & 1) * 8]) = packed;
+  lscales[row * kColSlabs + sl] = uint8_t(sc);
+}
+
+// Columnwise 1D quantization with a thread owning 4 columns of a 16-row slab (the
+// tile, LDS gathering and stores of quant_cols_kernel): half the registers of
+// that kernel's 8 columns, so four waves share a SIMD, and rows read through
+// buffer descriptors with scalar row offsets.  The launcher keeps 16 rows of x
+// within 2^31 bytes (beyond that, quant_cols_kernel).  Bit-identical to it.
+template <typename T, bool RHT, bool SR>
+__global__ __launch_bounds__(kThreads) void quant_cols4_kernel(
+    const T *__restrict__ x, int64_t R, int64_t C, int64_t ld, uint32_t signs, uint64_t seed, uint64_t offset,
+    const float *__restrict__ amax_p, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint8_t lcodes[kColTile * kColRowBytes];
+  __shared__ uint8_t lscales[kColTile * kColSlabs];
+  __shared__ float tab[kMultTable];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = int64_t(blockIdx.x) * kColTile;      // first column of the tile
+  const int64_t slab0 = int64_t(blockIdx.y) * kColSlabs;  // first slab of the tile
+  const int64_t nslab = R / 16;
+  const int64_t cfirst = c0 + 4 * lane;                    // this thread's first column
+  const float s_enc = encode_scale(*amax_p);
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
+
+#pragma unroll 1
+  for (int i = 0; i < kColSlabs / 4; ++i) {
+    const int sl = wave + 4 * i;  // slab within the tile
+    const int64_t s = slab0 + sl;
+    if (s >= nslab || cfirst >= C) continue;  // a lane quad skips together (C % 16 == 0)
+    Slab4<T> slab;
+    slab.load(wave_rsrc(x + s * 16 * ld + c0), uint32_t(ld * int64_t(sizeof(T))), lane, RHT ? signs : 0u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      col_block4<T, RHT, SR>(slab, j, s_enc, tab, 4 * lane + j, sl, uint64_t(cfirst + j) * uint64_t(R) + uint64_t(s) * 16u,
+                             seed, offset, lcodes, lscales);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+
+  store_col_tile(lcodes, lscales, R, C, c0, slab0, codes, scales);
+}
+
 // Both nearest-even layouts of x from one read: the columnwise layout (x^T, with
 // the transform down 16-row slabs when RHT) and x's rowwise layout (no transform;
 // codes [R][C/2], scales [R][C/16], tensor amax *ramax_p).  The tile of a
@@ -651,25 +727,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_ne_kernel(
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float col[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
-      uint32_t sc;
-      float mult;
-      if (RHT) {
-        hadamard16_unscaled(col);
-        block_scale_quarter(col, s_enc, tab, sc, mult);
-      } else {
-        float amax_b = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) amax_b = fmaxf(amax_b, __builtin_fabsf(col[r]));
-        block_scale(amax_b, s_enc, tab, sc, mult);
-      }
-      const uint2 packed = encode16_rne(col, mult);
-      const int row = 4 * lane + j;  // logical row within the tile
-      const int pair = (sl >> 1) ^ ((row >> 3) & 7);
-      *reinterpret_cast<uint2 *>(&lcodes[row * kColRowBytes + pair * 16 + (sl & 1) * 8]) = packed;
-      lscales[row * kColSlabs + sl] = uint8_t(sc);
+      col_block4<T, RHT, false>(slab, j, s_enc, tab, 4 * lane + j, sl, 0, 0, 0, lcodes, lscales);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -1128,6 +1186,9 @@ hipError_t launch_cols(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t si
                        const fp4_tensor *out, hipStream_t stream) {
   const int64_t nslab = R / 16;
   dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
+  if (16 * ld * int64_t(sizeof(T)) < (int64_t(1) << 31))
+    return launch(quant_cols4_kernel<T, RHT, SR>, grid, dim3(kThreads), stream, x, R, C, ld, signs, seed, offset,
+                  out->amax, out->codes, out->scales);
   return launch(quant_cols_kernel<T, RHT, SR>, grid, dim3(kThreads), stream, x, R, C, ld, signs, seed, offset,
                 out->amax, out->codes, out->scales);
 }
