@@ -512,18 +512,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *p) {
 
 // 16 rows x 4 adjacent columns of x (one 16-row slab), as loaded; row r negated
 // when bit r of `neg` is set.  Column j is widened to binary32 when it is used.
-// rs: a buffer at the slab's first element of the workgroup's first column; ldb:
-// the row stride in bytes; lane owns columns 4 lane .. 4 lane + 3 from there.
+// rs: a buffer whose row 0 is the slab's first row; ldb: the row stride in bytes;
+// voff: the byte offset of the lane's first element from the buffer's base.
 template <typename T>
 struct Slab4;
 
 template <>
 struct Slab4<uint16_t> {
   uint2 w[16];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int lane, uint32_t neg) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, uint32_t voff, uint32_t neg) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, int(uint32_t(r) * ldb), 0);
+      const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, int(voff), int(uint32_t(r) * ldb), 0);
       const uint32_t f = ((neg >> r) & 1u) ? 0x80008000u : 0u;
       w[r] = make_uint2(q[0] ^ f, q[1] ^ f);
     }
@@ -537,10 +537,10 @@ struct Slab4<uint16_t> {
 template <>
 struct Slab4<float> {
   float v[16][4];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int lane, uint32_t neg) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, uint32_t voff, uint32_t neg) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, int(uint32_t(r) * ldb), 0);
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, int(voff), int(uint32_t(r) * ldb), 0);
       const uint32_t f = ((neg >> r) & 1u) ? 0x80000000u : 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[r][j] = __uint_as_float(q[j] ^ f);
@@ -627,7 +627,8 @@ __global__ __launch_bounds__(kThreads) void quant_cols4_kernel(
     const int64_t s = slab0 + sl;
     if (s >= nslab || cfirst >= C) continue;  // a lane quad skips together (C % 16 == 0)
     Slab4<T> slab;
-    slab.load(wave_rsrc(x + s * 16 * ld + c0), uint32_t(ld * int64_t(sizeof(T))), lane, RHT ? signs : 0u);
+    slab.load(wave_rsrc(x + s * 16 * ld + c0), uint32_t(ld * int64_t(sizeof(T))), uint32_t(lane * 4 * sizeof(T)),
+              RHT ? signs : 0u);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       col_block4<T, RHT, SR>(slab, j, s_enc, tab, 4 * lane + j, sl, uint64_t(cfirst + j) * uint64_t(R) + uint64_t(s) * 16u,
@@ -687,7 +688,8 @@ __global__ __launch_bounds__(kThreads) void quant_dual_ne_kernel(
     if (s >= nslab || cfirst >= C) continue;  // a lane quad skips together (C % 16 == 0)
     // wave-uniform bases (the launcher keeps 16 rows of x within 2^31 bytes)
     Slab4<T> slab;
-    slab.load(wave_rsrc(x + s * 16 * ld + c0), uint32_t(ld * int64_t(sizeof(T))), lane, RHT ? signs : 0u);
+    slab.load(wave_rsrc(x + s * 16 * ld + c0), uint32_t(ld * int64_t(sizeof(T))), uint32_t(lane * 4 * sizeof(T)),
+              RHT ? signs : 0u);
     const __amdgpu_buffer_rsrc_t rc = wave_rsrc(rcodes + s * 16 * (C / 2) + c0 / 2);
     const __amdgpu_buffer_rsrc_t rs = wave_rsrc(rscales + s * 16 * (C / 16) + c0 / 16);
     // Rowwise.  Block maxima of the 16 rows: the lane's 4 columns, then the quad's
@@ -950,6 +952,69 @@ __global__ __launch_bounds__(kThreads) void quant_cols64_kernel(const T *__restr
   store_col_tile(lcodes, lscales, R, C, c0, slab0, codes, scales);
 }
 
+// quant_cols64_kernel with a thread owning 4 columns (half the registers, four
+// waves per SIMD) and rows read through buffer descriptors.  Wave w takes columns
+// 64 w .. 64 w + 63 of the tile and, in step i, group i (slabs 4 i .. 4 i + 3);
+// lane l owns columns 64 w + 4 (l & 15) .. +3 of slab 4 i + (l >> 4), so a group's
+// four slabs sit in lanes l, l ^ 16, l ^ 32, l ^ 48 as there.  The launcher keeps
+// 64 rows of x within 2^31 bytes (beyond that, quant_cols64_kernel).  Bit-identical
+// to it.
+template <typename T, bool EDEN, bool SR>
+__global__ __launch_bounds__(kThreads) void quant_cols64q_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                                int64_t ld, uint32_t key, uint64_t seed,
+                                                                uint64_t offset, const float *__restrict__ amax_p,
+                                                                uint8_t *__restrict__ codes,
+                                                                uint8_t *__restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint8_t lcodes[kColTile * kColRowBytes];
+  __shared__ uint8_t lscales[kColTile * kColSlabs];
+  __shared__ float tab[kMultTable];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = lane & 15, sq = lane >> 4;
+  const int64_t c0 = int64_t(blockIdx.x) * kColTile;
+  const int64_t slab0 = int64_t(blockIdx.y) * kColSlabs;
+  const int64_t nslab = R / 16;
+  const int64_t cw = c0 + 64 * wave;  // the wave's first column
+  const int64_t cfirst = cw + 4 * cg;
+  const uint32_t ldb = uint32_t(ld * int64_t(sizeof(T)));
+  const float s_enc = encode_scale(*amax_p);
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
+#pragma unroll 1
+  for (int i = 0; i < kColSlabs / 4; ++i) {
+    const int sl = 4 * i + sq;  // slab within the tile
+    const int64_t s = slab0 + sl;
+    // a group is inside or outside x whole (nslab % 4 == 0); lanes l ^ 16, l ^ 32
+    // own the same columns, so exchange partners are active together
+    if (s >= nslab || cfirst >= C) continue;
+    const int64_t g = (slab0 >> 2) + i;  // the group
+    uint32_t w0, w1;
+    rht64_signs(uint64_t(g), key, w0, w1);
+    // the group's first row is the wave-uniform base; the lane's slab is 16 sq rows on
+    Slab4<T> slab;
+    slab.load(wave_rsrc(x + g * 64 * ld + cw), ldb, 16u * uint32_t(sq) * ldb + uint32_t(cg * 4 * sizeof(T)),
+              rht64_quarter(w0, w1, sq));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
+      rotate64_cols(col, sq);
+      const int64_t c = cfirst + j;  // logical row
+      uint2 packed;
+      uint32_t sc;
+      quant_block64<EDEN, SR>(col, s_enc, tab, uint64_t(c) * uint64_t(nslab) + uint64_t(s),
+                              uint64_t(c) * uint64_t(R) + uint64_t(s) * 16u, seed, offset, packed, sc);
+      const int row = 64 * wave + 4 * cg + j;  // logical row within the tile
+      const int pair = (sl >> 1) ^ ((row >> 3) & 7);
+      *reinterpret_cast<uint2 *>(&lcodes[row * kColRowBytes + pair * 16 + (sl & 1) * 8]) = packed;
+      lscales[row * kColSlabs + sl] = uint8_t(sc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+  store_col_tile(lcodes, lscales, R, C, c0, slab0, codes, scales);
+}
+
 // amax after the 64-point transform down columns: each wave takes units of one
 // group (64 rows) x 128 columns, lanes as in quant_cols64_kernel.
 template <typename T>
@@ -1199,6 +1264,9 @@ hipError_t launch_rht64(const T *x, int64_t R, int64_t C, int64_t ld, bool colwi
   if (colwise) {
     const int64_t nslab = R / 16;
     dim3 grid(unsigned((C + kColTile - 1) / kColTile), unsigned((nslab + kColSlabs - 1) / kColSlabs));
+    if (64 * ld * int64_t(sizeof(T)) < (int64_t(1) << 31))
+      return launch(quant_cols64q_kernel<T, EDEN, SR>, grid, dim3(kThreads), stream, x, R, C, ld, key, seed, offset,
+                    out->amax, out->codes, out->scales);
     return launch(quant_cols64_kernel<T, EDEN, SR>, grid, dim3(kThreads), stream, x, R, C, ld, key, seed, offset,
                   out->amax, out->codes, out->scales);
   }
