@@ -137,3 +137,23 @@ def test_eden_wgrad_gemm(fp4, oracle, tokens):
     exact = dyf.astype(np.float64).T @ xf.astype(np.float64)
     rel = np.linalg.norm(dw.cpu().numpy() - exact) / np.linalg.norm(exact)
     assert rel < 0.2, rel
+
+
+@pytest.mark.parametrize("mode", ["rne", "eden"])
+def test_rht64_columns_with_a_row_stride_beyond_the_4_column_kernel(fp4, oracle, mode):
+    """64 rows that span 2^31 bytes are beyond the 4-column kernel's 32-bit row
+    offsets: the columnwise 64-point quantization takes the 8-column kernel and gives
+    the oracle's bits (a 2 GiB strided bf16 view, 64 x 256)."""
+    R, C = 64, 256
+    ld = (1 << 31) // (64 * 2)
+    x_cpu = workloads.random_matrix((R, C), seed=64, kind="laplace", std=1e-3)
+    full = torch.empty((R, ld), dtype=torch.bfloat16, device="cuda")
+    x = full[:, :C]
+    x.copy_(x_cpu.to("cuda"))
+    assert x.stride(0) == ld
+    q = fp4.QTensor(C, R)
+    fp4.fp4_quantize(x, mode_flags(fp4, mode) | fp4.Q_COLWISE, KEY, 4, 6, q)
+    o = oracle.quantize(workloads.widen(x_cpu), colwise=True, signs=KEY, seed=4, offset=6, **oracle_kw(mode))
+    assert_q_equal(host_q(q), o, f"wide-stride rht64 cols {mode}")
+    del full, x
+    torch.cuda.empty_cache()
