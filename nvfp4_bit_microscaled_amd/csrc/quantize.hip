@@ -1045,6 +1045,39 @@ __global__ __launch_bounds__(kThreads) void amax_rht64_cols_kernel(const T *__re
   block_max_to(m, out, partial);
 }
 
+// amax_rht64_cols_kernel with units of one group x 64 columns and 4 columns per
+// lane (lanes as in quant_cols64q_kernel, rows through buffer descriptors); the
+// launcher keeps 64 rows of x within 2^31 bytes.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_rht64_cols4_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                                   int64_t ld, uint32_t key, float *out,
+                                                                   float *partial) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = lane & 15, sq = lane >> 4;
+  const int64_t cblocks = (C + 63) / 64, units = (R / 64) * cblocks;
+  const uint32_t ldb = uint32_t(ld * int64_t(sizeof(T)));
+  float m = 0.0f;
+  for (int64_t u = int64_t(blockIdx.x) * 4 + wave; u < units; u += int64_t(gridDim.x) * 4) {
+    const int64_t g = u / cblocks, cw = (u - g * cblocks) * 64;
+    if (cw + 4 * cg >= C) continue;  // lanes l ^ 16, l ^ 32 skip together
+    uint32_t w0, w1;
+    rht64_signs(uint64_t(g), key, w0, w1);
+    Slab4<T> slab;
+    slab.load(wave_rsrc(x + g * 64 * ld + cw), ldb, 16u * uint32_t(sq) * ldb + uint32_t(cg * 4 * sizeof(T)),
+              rht64_quarter(w0, w1, sq));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
+      rotate64_cols(col, sq);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, __builtin_fabsf(col[r]));
+    }
+  }
+  block_max_to(m, out, partial);
+}
+
 // 2D (16x16 tile) nearest-even quantization of x [R][C] (R, C multiples of 16).
 // Writes the direct layout (codes [R][C/2], scales [R/16][C/16]) to d_* and/or the
 // transposed layout (codes [C][R/2], scales [C/16][R/16]) to t_*; either may be null.
@@ -1204,7 +1237,10 @@ hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
   if (e != hipSuccess || R == 0 || C == 0) return e;
   const int64_t cap = partial ? 1024 : 256 * 16;  // 16 workgroups per CU are plenty for a streaming reduction
   dim3 grid;
-  if ((flags & FP4_Q_RHT64) && (flags & FP4_Q_COLWISE)) {
+  if ((flags & FP4_Q_RHT64) && (flags & FP4_Q_COLWISE) && 64 * ld * int64_t(sizeof(T)) < (int64_t(1) << 31)) {
+    grid = dim3(grid_for((R / 64) * ((C + 63) / 64), 4, cap));
+    e = launch(amax_rht64_cols4_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
+  } else if ((flags & FP4_Q_RHT64) && (flags & FP4_Q_COLWISE)) {
     grid = dim3(grid_for((R / 64) * ((C + 127) / 128), 4, cap));
     e = launch(amax_rht64_cols_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
   } else if (flags & FP4_Q_RHT64) {
