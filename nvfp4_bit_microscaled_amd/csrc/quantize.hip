@@ -771,6 +771,41 @@ __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict
                                                                                             // factor, once
 }
 
+// amax_dual_kernel with wave units of one 16-row slab x 256 columns, 4 columns per
+// lane and rows read through buffer descriptors (scalar row offsets); the launcher
+// keeps 16 rows of x within 2^31 bytes.
+template <typename T, bool RHT>
+__global__ __launch_bounds__(kThreads) void amax_dual4_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                             int64_t ld, uint32_t signs, float *out_rows,
+                                                             float *out_cols, float *partial) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t cblocks = (C + 255) / 256, units = (R / 16) * cblocks;
+  const uint32_t ldb = uint32_t(ld * int64_t(sizeof(T)));
+  float mr = 0.0f, mc = 0.0f;
+  for (int64_t u = int64_t(blockIdx.x) * 4 + wave; u < units; u += int64_t(gridDim.x) * 4) {
+    const int64_t sl = u / cblocks, cw = (u - sl * cblocks) * 256;
+    if (cw + 4 * lane >= C) continue;  // a lane quad skips together (C % 16 == 0)
+    Slab4<T> slab;
+    slab.load(wave_rsrc(x + sl * 16 * ld + cw), ldb, uint32_t(lane * 4 * sizeof(T)), RHT ? signs : 0u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        col[r] = slab.at(r, j);
+        mr = fmaxf(mr, __builtin_fabsf(col[r]));  // the signs do not change |x|
+      }
+      if (RHT) hadamard16_unscaled(col);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mc = fmaxf(mc, __builtin_fabsf(col[r]));
+    }
+  }
+  // partials: rows at [0, grid), columns at [grid, 2 grid)
+  block_max_to(mr, out_rows, partial);
+  block_max_to(RHT ? mc * 0.25f : mc, out_cols, partial ? partial + gridDim.x : nullptr);  // the transform's
+                                                                                            // factor, once
+}
+
 // ---------------------------------------------------------------------------
 // The 64-point transform (MS-EDEN's rotation) and the kernels that use it.  A
 // 64-group is four 16-blocks; each block sits in one thread, and the butterflies at
@@ -1383,13 +1418,23 @@ hipError_t dual_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
     if (R == 0 || C == 0 || !partial)
       e = launch(zero2_f32_kernel, dim3(1), dim3(1), stream, rows->amax, cols->amax);
     if (e == hipSuccess && R > 0 && C > 0) {
-      // two workgroups per CU: on the MI355X this read 640 MB in 114 us and 160 MB in
-      // 38 us, against 116 us and 45 us with four
-      const dim3 grid(grid_for((R / 16) * (C / 8), kThreads, 512));
-      e = rht ? launch(amax_dual_kernel<T, true>, grid, dim3(kThreads), stream, x, R, C, ld, signs, rows->amax,
-                       cols->amax, partial)
-              : launch(amax_dual_kernel<T, false>, grid, dim3(kThreads), stream, x, R, C, ld, signs, rows->amax,
-                       cols->amax, partial);
+      // two workgroups per CU; with wave units of 256 columns (amax_dual4_kernel) dY of
+      // the 12B layer (640 MB) reads in 114-117 us and X (160 MB) in 29-30 us on the
+      // MI355X, where per-thread slabs of 8 columns took 123 and 33 us
+      dim3 grid;
+      if (16 * ld * int64_t(sizeof(T)) < (int64_t(1) << 31)) {
+        grid = dim3(grid_for((R / 16) * ((C + 255) / 256), 4, 512));
+        e = rht ? launch(amax_dual4_kernel<T, true>, grid, dim3(kThreads), stream, x, R, C, ld, signs, rows->amax,
+                         cols->amax, partial)
+                : launch(amax_dual4_kernel<T, false>, grid, dim3(kThreads), stream, x, R, C, ld, signs, rows->amax,
+                         cols->amax, partial);
+      } else {
+        grid = dim3(grid_for((R / 16) * (C / 8), kThreads, 512));
+        e = rht ? launch(amax_dual_kernel<T, true>, grid, dim3(kThreads), stream, x, R, C, ld, signs, rows->amax,
+                         cols->amax, partial)
+                : launch(amax_dual_kernel<T, false>, grid, dim3(kThreads), stream, x, R, C, ld, signs, rows->amax,
+                         cols->amax, partial);
+      }
       if (e == hipSuccess && partial)
         e = launch(amax_finish_kernel, dim3(1), dim3(kThreads), stream, partial, int(grid.x), 2, rows->amax,
                    cols->amax, 1.0f);
