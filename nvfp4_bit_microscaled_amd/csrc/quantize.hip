@@ -773,8 +773,9 @@ __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict
 
 // amax_dual_kernel with wave units of one 16-row slab x 256 columns, 4 columns per
 // lane and rows read through buffer descriptors (scalar row offsets); the launcher
-// keeps 16 rows of x within 2^31 bytes.
-template <typename T, bool RHT>
+// keeps 16 rows of x within 2^31 bytes.  Without ROWS only the columnwise amax is
+// taken (out_rows unused; partials of the columns at [grid, 2 grid)).
+template <typename T, bool RHT, bool ROWS = true>
 __global__ __launch_bounds__(kThreads) void amax_dual4_kernel(const T *__restrict__ x, int64_t R, int64_t C,
                                                              int64_t ld, uint32_t signs, float *out_rows,
                                                              float *out_cols, float *partial) {
@@ -793,7 +794,7 @@ __global__ __launch_bounds__(kThreads) void amax_dual4_kernel(const T *__restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         col[r] = slab.at(r, j);
-        mr = fmaxf(mr, __builtin_fabsf(col[r]));  // the signs do not change |x|
+        if (ROWS) mr = fmaxf(mr, __builtin_fabsf(col[r]));  // the signs do not change |x|
       }
       if (RHT) hadamard16_unscaled(col);
 #pragma unroll
@@ -801,7 +802,7 @@ __global__ __launch_bounds__(kThreads) void amax_dual4_kernel(const T *__restric
     }
   }
   // partials: rows at [0, grid), columns at [grid, 2 grid)
-  block_max_to(mr, out_rows, partial);
+  if (ROWS) block_max_to(mr, out_rows, partial);
   block_max_to(RHT ? mc * 0.25f : mc, out_cols, partial ? partial + gridDim.x : nullptr);  // the transform's
                                                                                             // factor, once
 }
@@ -1289,6 +1290,12 @@ hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
   } else if (!(flags & FP4_Q_RHT)) {
     grid = dim3(grid_for(R * (C / 8), kThreads * 4, cap));
     e = launch(amax_plain_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, out, partial);
+  } else if ((flags & FP4_Q_COLWISE) && 16 * ld * int64_t(sizeof(T)) < (int64_t(1) << 31)) {
+    // the dual amax kernel's columnwise half; its partials sit at [grid, 2 grid)
+    grid = dim3(grid_for((R / 16) * ((C + 255) / 256), 4, partial ? 512 : cap));
+    e = launch(amax_dual4_kernel<T, true, false>, grid, dim3(kThreads), stream, x, R, C, ld, signs,
+               static_cast<float *>(nullptr), out, partial);
+    if (partial) partial += grid.x;
   } else if (flags & FP4_Q_COLWISE) {
     grid = dim3(grid_for((R / 16) * (C / 8), kThreads, cap));
     e = launch(amax_rht_cols_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
