@@ -347,8 +347,9 @@ def ns_flags(fp4, variant):
 def newton_schulz_timing(steps, warmup, dev, variants=NS_VARIANTS):
     """Muon's NVFP4 Newton-Schulz (5 iterations from X_0 = G / |G|) on a Gaussian G of
     the 12B MLP weight-gradient shape, per operand variant: time per call (HIP events
-    on the stream), TFLOP/s over its 15 GEMMs, and each of its three GEMM shapes timed
-    alone on the call's own quantized operands."""
+    on the stream) with X' = a X + B X taken in the B X GEMM's epilogue, the same with
+    B X written out and a separate a X + B X pass, TFLOP/s over its 15 GEMMs, and each
+    of its three GEMM shapes timed alone on the call's own quantized operands."""
     import torch
 
     import nvfp4_bit_microscaled_amd as fp4
@@ -357,27 +358,33 @@ def newton_schulz_timing(steps, warmup, dev, variants=NS_VARIANTS):
     m, n = NS_SHAPE
     g = workloads.random_matrix((m, n), seed=0, dtype=torch.float32).to(dev)
     x = torch.empty_like(g)
-    bufs = fp4.NsBuffers(m, n, device=dev)
+    bufs = fp4.NsBuffers(m, n, device=dev, keep_bx=False)
+    bufs_bx = fp4.NsBuffers(m, n, device=dev, keep_bx=True)
     stream = torch.cuda.current_stream()
     flops_iter = 2.0 * m * m * n + 2.0 * m * m * m + 2.0 * m * n * m
-    out = {}
-    for variant in variants:
-        f = ns_flags(fp4, variant)
+
+    def per_call(b, f):
         for _ in range(warmup):
-            fp4.fp4_newton_schulz(g, x, NS_ITERS, bufs, flags=f, rht_signs=0x1234ACE1, seed=1, offset=0)
+            fp4.fp4_newton_schulz(g, x, NS_ITERS, b, flags=f, rht_signs=0x1234ACE1, seed=1, offset=0)
         evs = [HipTimingEvent() for _ in range(steps + 1)]
         torch.cuda.synchronize()
         evs[0].record(stream)
         for i in range(steps):
-            fp4.fp4_newton_schulz(g, x, NS_ITERS, bufs, flags=f, rht_signs=0x1234ACE1, seed=1, offset=0)
+            fp4.fp4_newton_schulz(g, x, NS_ITERS, b, flags=f, rht_signs=0x1234ACE1, seed=1, offset=0)
             evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(steps)) / steps
+        return sum(evs[i].elapsed_time(evs[i + 1]) for i in range(steps)) / steps
+
+    out = {}
+    for variant in variants:
+        f = ns_flags(fp4, variant)
+        ms_sep = per_call(bufs_bx, f)
+        ms = per_call(bufs, f)
         # the three GEMM shapes alone, on this call's last operands
         gem = []
         for name, qa, qb, c, flops in (("A = X X^T", bufs.x_left, bufs.x_right, bufs.a, 2.0 * m * m * n),
                                        ("A A^T", bufs.a_left, bufs.a_right, bufs.b, 2.0 * m * m * m),
-                                       ("B X", bufs.b_q, bufs.xt, bufs.bx, 2.0 * m * n * m)):
+                                       ("B X", bufs.b_q, bufs.xt, bufs_bx.bx, 2.0 * m * n * m)):
             e0, e1 = HipTimingEvent(), HipTimingEvent()
             e0.record(stream)
             for _ in range(5):
@@ -388,7 +395,8 @@ def newton_schulz_timing(steps, warmup, dev, variants=NS_VARIANTS):
             gem.append({"gemm": name, "M": qa.rows, "N": qb.rows, "K": qa.cols, "ms": round(gms, 4),
                         "tflops": round(flops / (gms * 1e-3) / 1e12, 1),
                         "frac_f16_peak": round(flops / (gms * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS, 4)})
-        out[variant] = {"ms_per_call": round(ms, 4), "iters": NS_ITERS,
+        out[variant] = {"ms_per_call": round(ms, 4), "ms_per_call_separate_axpby": round(ms_sep, 4),
+                        "iters": NS_ITERS,
                         "tflops": round(NS_ITERS * flops_iter / (ms * 1e-3) / 1e12, 1), "gemms": gem}
     return {"X": [m, n], "flops_per_call": NS_ITERS * flops_iter, "variants": out}
 
@@ -410,7 +418,7 @@ def newton_schulz_divergence(dev, m=1024, n=4096):
         xe = a_ * xe + (b_ * a + c_ * (a @ a)) @ xe
     sve = torch.linalg.svdvals(xe)
     res = {"G": [m, n], "exact": {"sigma_max": round(float(sve.max()), 4), "sigma_min": round(float(sve.min()), 4)}}
-    bufs = fp4.NsBuffers(m, n, device=dev)
+    bufs = fp4.NsBuffers(m, n, device=dev, keep_bx=False)
     x = torch.empty_like(g)
     for variant in NS_VARIANTS:
         fp4.fp4_newton_schulz(g, x, NS_ITERS, bufs, flags=ns_flags(fp4, variant), rht_signs=0x1234ACE1, seed=1,
@@ -705,7 +713,8 @@ def main():
         nt = newton_schulz_timing(3, 1, dev, variants=("rne",))
         v = nt["variants"]["rne"]
         others.append({"workload": f"Muon Newton-Schulz in NVFP4, {NS_ITERS} iterations on X {nt['X'][0]}x{nt['X'][1]}",
-                       "name": "newton_schulz", "steps": 3, "ms_per_step": v["ms_per_call"], "value": v["tflops"],
+                       "name": "newton_schulz", "steps": 3, "ms_per_step": v["ms_per_call"],
+                       "ms_per_step_separate_axpby": v["ms_per_call_separate_axpby"], "value": v["tflops"],
                        "unit": "TFLOP/s", "gemms": v["gemms"]})
         torch.cuda.empty_cache()
         out["other_workloads"] = others

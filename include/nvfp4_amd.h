@@ -358,7 +358,9 @@ typedef struct fp4_ns_config {
 typedef struct fp4_ns_buffers {
   float *a;  /* [m][m]: A */
   float *b;  /* [m][m]: A A^T, then B */
-  float *bx; /* [m][n]: B X */
+  float *bx; /* [m][n]: B X; or NULL: X' = a X + B X is then taken in the B X GEMM's epilogue
+              * (C = fl(v + fl(a X)) for each product v, X updated in place; the same values;
+              * with variant 0 that epilogue also takes the next X's amax) */
   fp4_tensor x_left, x_right, a_left, a_right, b_q, xt;
   void *ws;  /* GEMM split-K workspace and the element-wise steps' scratch (fp4_newton_schulz_ws_bytes), 16-byte
               * aligned */
@@ -376,9 +378,10 @@ FP4_API fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_
                                      const fp4_ns_config *cfg, const fp4_ns_buffers *bufs, hipStream_t stream);
 
 /* Workspace bytes fp4_newton_schulz needs for X [m][n]: the largest split-K plan of
- * its three GEMMs (m x m x n, m x m x m, m x n x m), and at least 16384 bytes (the
+ * its three GEMMs (m x m x n, m x m x m, m x n x m), at least 16384 bytes (the
  * normalisation's binary64 partial sums, the per-workgroup maxima of the
- * element-wise steps).  FP4_ERR_NULL, FP4_ERR_SHAPE. */
+ * element-wise steps), rounded up to 256, plus 256 (the next X's maximum from the
+ * fused epilogue).  FP4_ERR_NULL, FP4_ERR_SHAPE. */
 FP4_API fp4_status fp4_newton_schulz_ws_bytes(int64_t m, int64_t n, size_t *bytes);
 
 /* A short static description of a status code (never NULL). */

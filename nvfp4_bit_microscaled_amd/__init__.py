@@ -287,21 +287,23 @@ def fp4_newton_schulz_ws_bytes(m: int, n: int) -> int:
 class NsBuffers:
     """Caller-owned intermediates of fp4_newton_schulz for X [m][n]; after a call
     they hold the last iteration's A, B (= b A + c A A^T), B X and quantized
-    operands."""
+    operands.  keep_bx=False leaves B X out: X' = a X + B X is then taken in the
+    B X GEMM's epilogue (the same values, without B X's pass through memory; with
+    nearest-even operands the epilogue also takes the next X's amax)."""
 
-    def __init__(self, m: int, n: int, device="cuda"):
+    def __init__(self, m: int, n: int, device="cuda", keep_bx: bool = True):
         f32 = dict(dtype=torch.float32, device=device)
         self.a = torch.empty(m, m, **f32)
         self.b = torch.empty(m, m, **f32)
-        self.bx = torch.empty(m, n, **f32)
+        self.bx = torch.empty(m, n, **f32) if keep_bx else None
         self.x_left, self.x_right = QTensor(m, n, device=device), QTensor(m, n, device=device)
         self.a_left, self.a_right = QTensor(m, m, device=device), QTensor(m, m, device=device)
         self.b_q = QTensor(m, m, device=device)
         self.xt = QTensor(n, m, device=device)
         self.ws = torch.empty(max(fp4_newton_schulz_ws_bytes(m, n), 16), dtype=torch.uint8, device=device)
-        self._s = fp4_ns_buffers(self.a.data_ptr(), self.b.data_ptr(), self.bx.data_ptr(), self.x_left._desc,
-                                 self.x_right._desc, self.a_left._desc, self.a_right._desc, self.b_q._desc,
-                                 self.xt._desc, self.ws.data_ptr(), self.ws.numel())
+        self._s = fp4_ns_buffers(self.a.data_ptr(), self.b.data_ptr(), self.bx.data_ptr() if keep_bx else None,
+                                 self.x_left._desc, self.x_right._desc, self.a_left._desc, self.a_right._desc,
+                                 self.b_q._desc, self.xt._desc, self.ws.data_ptr(), self.ws.numel())
 
 
 def fp4_newton_schulz(g: torch.Tensor, x: torch.Tensor, iters: int, bufs: NsBuffers, normalize: bool = True,

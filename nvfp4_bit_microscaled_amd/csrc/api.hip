@@ -258,14 +258,21 @@ fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, c
   return from_hip(e);
 }
 
-fp4_status fp4_newton_schulz_ws_bytes(int64_t m, int64_t n, size_t *bytes) {
-  if (!bytes) return FP4_ERR_NULL;
-  if (m < 0 || n < 0 || m % 16 || n % 16) return FP4_ERR_SHAPE;
+// Newton-Schulz workspace: the normalisation's scratch, the axpby maxima and the
+// three GEMMs' split-K partial tiles share its start; then one 256-byte slot whose
+// first word takes the next X's maximum from the B X GEMM's fused epilogue.
+static size_t ns_max_slot(int64_t m, int64_t n) {
   size_t w = nvfp4::normalize_scratch_bytes();
   if (nvfp4::axpby_partial_bytes() > w) w = nvfp4::axpby_partial_bytes();
   const size_t g[3] = {nvfp4::gemm_ws_bytes(m, m, n), nvfp4::gemm_ws_bytes(m, m, m), nvfp4::gemm_ws_bytes(m, n, m)};
   for (size_t v : g) w = v > w ? v : w;
-  *bytes = w;
+  return (w + 255) / 256 * 256;
+}
+
+fp4_status fp4_newton_schulz_ws_bytes(int64_t m, int64_t n, size_t *bytes) {
+  if (!bytes) return FP4_ERR_NULL;
+  if (m < 0 || n < 0 || m % 16 || n % 16) return FP4_ERR_SHAPE;
+  *bytes = ns_max_slot(m, n) + 256;
   return FP4_OK;
 }
 
@@ -286,9 +293,11 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
     return FP4_ERR_MODE;
   }
   if ((!g || !x) && m > 0 && n > 0) return FP4_ERR_NULL;
-  if ((!bufs->a || !bufs->b || !bufs->bx) && m > 0 && n > 0) return FP4_ERR_NULL;
+  if ((!bufs->a || !bufs->b) && m > 0 && n > 0) return FP4_ERR_NULL;
   if (!aligned(g, 16) || !aligned(x, 16) || !aligned(bufs->a, 16) || !aligned(bufs->b, 16) || !aligned(bufs->bx, 16))
     return FP4_ERR_ALIGN;
+  // without bx, X' = a X + B X is taken in the B X GEMM's epilogue (X updated in place)
+  const bool fused = bufs->bx == nullptr;
   fp4_status s;
   if ((s = check_quantize(x, FP4_FP32, m, n, n, fl, &bufs->x_left, nullptr)) != FP4_OK) return s;
   if ((s = check_quantize(x, FP4_FP32, m, n, n, fr, &bufs->x_right, nullptr)) != FP4_OK) return s;
@@ -317,14 +326,20 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
     // tensors are quantized with their amax given.  The next X's maxima are reduced
     // into X's descriptors at the start of the next iteration, so that after the
     // call every descriptor describes the operand it holds.
+    // With the fused epilogue the B X GEMM leaves the next X's maximum in the
+    // workspace's last slot instead.
     const bool same = cfg->flags == 0;
     const fp4_tensor *xr = same ? &bufs->x_left : &bufs->x_right, *ar = same ? &bufs->a_left : &bufs->a_right;
     float *partial = static_cast<float *>(bufs->ws);
+    float *xmax = same && fused ? reinterpret_cast<float *>(static_cast<char *>(bufs->ws) + ns_max_slot(m, n)) : nullptr;
     if (same) {
-      if (t > 0) e = nvfp4::launch_max_finish(partial, nvfp4::axpby_parts(m * n), bufs->x_left.amax, bufs->xt.amax,
-                                              stream);
+      const bool given = t > 0;  // the previous iteration left X's maxima
+      if (given)
+        e = fused ? nvfp4::launch_max_finish(xmax, 1, bufs->x_left.amax, bufs->xt.amax, stream)
+                  : nvfp4::launch_max_finish(partial, nvfp4::axpby_parts(m * n), bufs->x_left.amax, bufs->xt.amax,
+                                             stream);
       if (e == hipSuccess)
-        e = nvfp4::launch_quantize_dual(x, FP4_FP32, m, n, n, t > 0 ? FP4_Q_AMAX_GIVEN : 0u, key, cfg->seed, o + 0,
+        e = nvfp4::launch_quantize_dual(x, FP4_FP32, m, n, n, given ? FP4_Q_AMAX_GIVEN : 0u, key, cfg->seed, o + 0,
                                         o + 5, &bufs->x_left, &bufs->xt, stream);
     } else {
       e = q(x, m, n, fl, o + 0, &bufs->x_left);
@@ -346,11 +361,14 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
       if (e == hipSuccess) e = q(bufs->b, m, m, fl, o + 4, &bufs->b_q);
       if (e == hipSuccess) e = q(x, m, n, fr | FP4_Q_COLWISE, o + 5, &bufs->xt);
     }
-    if (e == hipSuccess)
+    if (e == hipSuccess && fused) {
+      e = nvfp4::launch_gemm_ws_acc(&bufs->b_q, &bufs->xt, x, n, cfg->a, xmax, bufs->ws, bufs->ws_bytes, stream);
+    } else if (e == hipSuccess) {
       e = nvfp4::launch_gemm_ws(&bufs->b_q, &bufs->xt, bufs->bx, FP4_FP32, n, bufs->ws, bufs->ws_bytes, stream);
-    if (e == hipSuccess)
-      e = same ? nvfp4::launch_axpby_amax(1.0f, bufs->bx, cfg->a, x, m * n, partial, stream)
-               : nvfp4::launch_axpby(1.0f, bufs->bx, cfg->a, x, m * n, stream);
+      if (e == hipSuccess)
+        e = same ? nvfp4::launch_axpby_amax(1.0f, bufs->bx, cfg->a, x, m * n, partial, stream)
+                 : nvfp4::launch_axpby(1.0f, bufs->bx, cfg->a, x, m * n, stream);
+    }
   }
   return from_hip(e);
 }

@@ -14,6 +14,17 @@ namespace nvfp4 {
 // the tensor amax is mapped onto it.
 constexpr float kTensorRange = 2688.0f;
 
+// Raw buffer descriptor for a wave-uniform base pointer p (its value is the same
+// in every lane of the wave; it is made explicitly uniform so that the descriptor
+// sits in scalar registers).  The range field is left at its maximum: callers keep
+// every access inside the tensor.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a)), hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((uint64_t(hi) << 32) | lo), short(0), 0x7FFFFFFF,
+                                           0x00020000);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // Round a binary32 value to bf16, nearest-even (inputs are finite).

@@ -78,7 +78,19 @@ struct GemmParams {
   int ksplit;      // gemm_kernel, 256x256: K splits per tile (1: none)
   int split_first; // ksplit > 1: the first split tile (the tiles before it run unsplit)
   float *ws;       // ksplit > 1: raw partial tiles [tiles_main][256][256], item t * ksplit + s
+  int acc_c;       // fp32 output only: 0 stores the product v; 1 stores C = fl(v + fl(beta * C))
+  float beta;
+  unsigned *amax_bits;  // acc_c only, or null: atomic max of |C| over the stored elements, as the
+                        // bits of a non-negative float (those order as unsigned integers)
 };
+
+// Wave-wide maximum of a non-negative lane value, merged into *bits by an atomic
+// integer max of its bit pattern.  Every lane of the wave calls it.
+__device__ __forceinline__ void wave_amax(unsigned *bits, float m, int lane) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) atomicMax(bits, __float_as_uint(m));
+}
 
 // 8 E2M1 codes (one 32-bit word, element 2j in the low nibble of byte j) times the
 // block scale, as 8 f16.  Exact: see the header comment.
@@ -119,6 +131,7 @@ template <int TM, int TN>
 __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0, int64_t n0,
                                             int lr, int g) {
   const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
+  float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -129,13 +142,18 @@ __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&
         const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         if (m < p.M && n < p.N) {
           const float v = acc[i][j][r] * gscale;
-          if (p.c_bf16)
+          if (p.c_bf16) {
             reinterpret_cast<uint16_t *>(p.c)[m * p.ldc + n] = f32_to_bf16(v);
-          else
-            reinterpret_cast<float *>(p.c)[m * p.ldc + n] = v;
+          } else {
+            float *dst = reinterpret_cast<float *>(p.c) + m * p.ldc + n;
+            const float y = p.acc_c ? v + p.beta * *dst : v;
+            *dst = y;
+            mx = fmaxf(mx, __builtin_fabsf(y));
+          }
         }
       }
     }
+  if (p.amax_bits) wave_amax(p.amax_bits, mx, threadIdx.x & 63);
 }
 
 // Epilogue of the main kernel, whose MFMAs take the B tile as first operand so
@@ -144,6 +162,11 @@ __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&
 // .. +3.
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Cache-policy operand of the raw buffer builtins for a non-temporal store (the
+// nt bit).
+constexpr int kNontemporal = 2;
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
 template <class F, int... Is>
@@ -179,9 +202,78 @@ __device__ __forceinline__ void static_for(F &&f) {
 // the launcher guarantees N % 4 == 0, a 16-byte aligned C and ldc % 4 == 0).
 constexpr int kEpiBytes = 4096;
 
+// fp32 accumulating epilogue, C = fl(v + fl(beta * C)), block by block as the
+// plain fp32 path.  The old C of each block is loaded kAccAhead blocks ahead into
+// a ring of registers: a load issued only when its block is stored waits a whole
+// memory latency per block, with no other wave on the SIMD to cover it.  C is
+// addressed as a raw buffer from the wave's corner: the lane's offset in one
+// vector register, the block's row and column offsets in scalar ones (a wave's 128
+// rows of C span less than 2^31 bytes, else the launcher takes the edge kernel).  mx takes the maximum of |C|
+// over the lane's stored elements.
+constexpr int kAccAhead = 8, kAccAheadCheck = 8;
+
 template <int TM, int TN, bool CHECK>
+__device__ __forceinline__ void store_tiles_lds_acc(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
+                                                    int64_t n0, int lane, uint8_t *region, float gscale, float &mx) {
+  constexpr int NB = TM * TN, AH = CHECK ? kAccAheadCheck : kAccAhead, D = NB < AH ? NB : AH;
+  const int lr = lane & 31, g = lane >> 5;
+  const int wsw = (lr >> 1) & 7;  // swizzle of the row this lane writes
+  const int rq = lane >> 3, ch = lane & 7;  // read-back: row 8k + rq of the block, columns 4 ch .. +3
+  const uint32_t ldb = uint32_t(p.ldc) * 4u;
+  const __amdgpu_buffer_rsrc_t rs = wave_rsrc(reinterpret_cast<float *>(p.c) + m0 * p.ldc + n0);
+  const uint32_t voff = uint32_t(rq) * ldb + 16u * uint32_t(ch);
+  const int64_t mlim = p.M - m0, nlim = p.N - n0;
+  // block b = (i, j): rows 32 i + 8 k + rq, columns 32 j + 4 ch
+  auto inside = [&](int i, int j, int k) { return !CHECK || (32 * i + 8 * k + rq < mlim && 32 * j + 4 * ch < nlim); };
+  auto soff = [&](int i, int j, int k) { return int(uint32_t(32 * i + 8 * k) * ldb + 128u * uint32_t(j)); };
+  u32x4 old[D][4];
+  auto fetch = [&](auto bc) {
+    constexpr int b = decltype(bc)::value, i = b / TN, j = b % TN;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (inside(i, j, k)) old[b % D][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, int(voff), soff(i, j, k), 0);
+  };
+  static_for<D>(fetch);
+  static_for<NB>([&](auto bc) {
+    constexpr int b = decltype(bc)::value, i = b / TN, j = b % TN;
+    // explicit moves out of the accumulator registers, one block at a time (else the
+    // compiler may move them all at once, next to the ring of old values)
+    float a[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = acc[i][j][r];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // columns 8q + 4g .. +3 of the block: chunk 2q + g
+      const float4 v = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+      *reinterpret_cast<float4 *>(region + lr * 128 + (((2 * q + g) ^ wsw) << 4)) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * k + rq;
+      const float4 x = *reinterpret_cast<const float4 *>(region + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+      if (inside(i, j, k)) {
+        const u32x4 o = old[b % D][k];
+        const float y0 = x.x * gscale + p.beta * __uint_as_float(o[0]);
+        const float y1 = x.y * gscale + p.beta * __uint_as_float(o[1]);
+        const float y2 = x.z * gscale + p.beta * __uint_as_float(o[2]);
+        const float y3 = x.w * gscale + p.beta * __uint_as_float(o[3]);
+        const u32x4 y = {__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
+        __builtin_amdgcn_raw_buffer_store_b128(y, rs, int(voff), soff(i, j, k), kNontemporal);
+        mx = fmaxf(fmaxf(mx, fmaxf(__builtin_fabsf(y0), __builtin_fabsf(y1))),
+                   fmaxf(__builtin_fabsf(y2), __builtin_fabsf(y3)));
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next block
+    if constexpr (b + D < NB) fetch(std::integral_constant<int, b + D>{});
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// ACC: the accumulating fp32 path (p.acc_c set), a kernel instantiation of its own
+// so that the plain kernels keep their registers.
+template <int TM, int TN, bool CHECK, bool ACC>
 __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
-                                                int64_t n0, int lane, uint8_t *region, float gscale) {
+                                                int64_t n0, int lane, uint8_t *region, float gscale, float &mx) {
   static_assert(TN % 2 == 0, "bf16 blocks go in pairs");
   const int lr = lane & 31, g = lane >> 5;
   const int wsw = (lr >> 1) & 7;  // swizzle of the row this lane writes
@@ -244,6 +336,10 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
     });
     return;
   }
+  if constexpr (ACC) {
+    store_tiles_lds_acc<TM, TN, CHECK>(p, acc, m0, n0, lane, region, gscale, mx);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -264,7 +360,8 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
         const int64_t m = m0 + 32 * i + r, n = n0 + 32 * j + 4 * c;
         if (!CHECK || (m < p.M && n < p.N)) {
           const f32x4 y = {x.x * gscale, x.y * gscale, x.z * gscale, x.w * gscale};
-          __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n));
+          f32x4 *dst = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n);
+          __builtin_nontemporal_store(y, dst);
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next block
@@ -283,7 +380,6 @@ __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 1)) & 7; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource for `bytes` bytes at p: raw and untyped (stride 0; dword 3 as
 // for gfx9 raw buffers).  Loads whose per-lane offset is at or past `bytes`
@@ -312,7 +408,7 @@ __device__ __forceinline__ void dma16(const u32x4 &rsrc, void *dst, uint32_t vof
                : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP, bool QUARTERS>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP, bool QUARTERS, bool ACC>
 __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams p) {
   static_assert(!QUARTERS || (BM == 128 && BN == 128), "quarters of 256x256 tiles");
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
@@ -592,6 +688,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   set_tile(L);
   int par = 0;
   bool first = true;  // no epilogue stores in flight yet
+  float amx = 0.0f;   // with p.amax_bits: max |C| over this lane's stored elements
   issue(0, 0);
   issue(min(1, nst - 1), 1);
   // the first stage's DMA has landed; the second stage's NDMA loads (issued last,
@@ -651,9 +748,12 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       pp.c = p.ws + int64_t(Lcur) * (256 * 256);
       pp.ldc = 256;
       pp.c_bf16 = 0;
-      store_tiles_lds<TM, TN, false>(pp, acc, wm, wn, lane, lds + 2 * STAGE + wave * kEpiBytes, 1.0f);
+      pp.acc_c = 0;
+      pp.amax_bits = nullptr;
+      store_tiles_lds<TM, TN, false, false>(pp, acc, wm, wn, lane, lds + 2 * STAGE + wave * kEpiBytes, 1.0f, amx);
     } else {
-      store_tiles_lds<TM, TN, CLAMP>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes, gscale);
+      store_tiles_lds<TM, TN, CLAMP, ACC>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes, gscale,
+                                          amx);
     }
     if (!more) break;
     if (nst == 1) {
@@ -671,6 +771,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
     }
   }
+  if (ACC && p.amax_bits) wave_amax(p.amax_bits, amx, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -838,6 +939,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
   tile_at(p.split_first + t, num_m, num_n, tm, tn);
   const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
   const float *part = p.ws + int64_t(t) * p.ksplit * (256 * 256);
+  float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int f = threadIdx.x + 256 * i;  // float4 index within the 16 x 256 block
@@ -857,10 +959,24 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
                         (__bf16)(v.w * gscale)};
       *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = h;
     } else {
-      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
-          make_float4(v.x * gscale, v.y * gscale, v.z * gscale, v.w * gscale);
+      float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n);
+      float4 y = make_float4(v.x * gscale, v.y * gscale, v.z * gscale, v.w * gscale);
+      if (p.acc_c) {
+        const float4 old = *dst;
+        const float4 q = make_float4(p.beta * old.x, p.beta * old.y, p.beta * old.z, p.beta * old.w);
+        y = make_float4(y.x + q.x, y.y + q.y, y.z + q.z, y.w + q.w);
+      }
+      *dst = y;
+      mx = fmaxf(fmaxf(mx, fmaxf(__builtin_fabsf(y.x), __builtin_fabsf(y.y))),
+                 fmaxf(__builtin_fabsf(y.z), __builtin_fabsf(y.w)));
     }
   }
+  if (p.amax_bits) wave_amax(p.amax_bits, mx, threadIdx.x & 63);
+}
+
+// *w = 0 ahead of a GEMM that merges its output's maximum into *w.
+__global__ __launch_bounds__(64) void zero_word_kernel(unsigned *w) {
+  if (threadIdx.x == 0) *w = 0u;
 }
 
 template <int BM, int BN>
@@ -921,12 +1037,25 @@ SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus) {
   return best;
 }
 
+// The persistent kernel for p: CLAMP unless M and N are whole tiles (exact), the
+// accumulating instantiation for an accumulated C stored by the kernel itself
+// (split items store raw partial tiles; the reduction accumulates).
+template <int BM, int BN, bool QUARTERS>
+hipError_t launch_tiles(bool exact, const dim3 &grid, hipStream_t stream, const GemmParams &p) {
+  if (p.acc_c && (QUARTERS || p.ksplit == 1))
+    return exact ? launch(gemm_kernel<BM, BN, 2, 2, false, QUARTERS, true>, grid, dim3(256), stream, p)
+                 : launch(gemm_kernel<BM, BN, 2, 2, true, QUARTERS, true>, grid, dim3(256), stream, p);
+  return exact ? launch(gemm_kernel<BM, BN, 2, 2, false, QUARTERS, false>, grid, dim3(256), stream, p)
+               : launch(gemm_kernel<BM, BN, 2, 2, true, QUARTERS, false>, grid, dim3(256), stream, p);
+}
+
 size_t splitk_ws_bytes(const SplitPlan &sp) {
   return sp.ksplit <= 1 ? 0 : size_t(sp.tiles) * size_t(sp.ksplit) * 256 * 256 * sizeof(float);
 }
 
 hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
-                            void *ws, size_t ws_bytes, hipStream_t stream) {
+                            void *ws, size_t ws_bytes, hipStream_t stream, bool acc_c = false,
+                            float beta = 0.0f, unsigned *amax_bits = nullptr) {
   GemmParams p;
   p.a_codes = a->codes;
   p.a_scales = a->scales;
@@ -947,15 +1076,20 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
   p.ksplit = 1;
   p.split_first = 0;
   p.ws = nullptr;
+  p.acc_c = acc_c && !p.c_bf16;
+  p.beta = beta;
+  p.amax_bits = p.acc_c ? amax_bits : nullptr;
   if (p.M == 0 || p.N == 0) return hipSuccess;
   auto al = [](const void *q, uintptr_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
   // main path: whole 256-element K stages, 16-byte aligned codes and scale rows,
   // every DMA offset within 32 bits, and an output whose rows the 16-byte stores
-  // can write (16-byte aligned C and rows)
+  // can write (16-byte aligned C and rows; an accumulated C within the buffer
+  // offsets of its epilogue)
   const bool main_path = p.K >= 256 && p.K % 256 == 0 && al(a->codes, 16) && al(b->codes, 16) &&
                          al(a->scales, 16) && al(b->scales, 16) && (p.M + 256) * (p.K / 2) < (int64_t(1) << 32) &&
                          (p.N + 256) * (p.K / 2) < (int64_t(1) << 32) &&
-                         al(c, 16) && ldc % (p.c_bf16 ? 8 : 4) == 0 && p.N % 4 == 0;
+                         al(c, 16) && ldc % (p.c_bf16 ? 8 : 4) == 0 && p.N % 4 == 0 &&
+                         (!p.acc_c || ldc * 4 * 128 < (int64_t(1) << 31));
   if (main_path && ws) {
     const unsigned cus = compute_units();
     const SplitPlan sp = splitk_plan(p.M, p.N, p.K, cus);
@@ -966,8 +1100,7 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
       const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
       auto main = [&](const GemmParams &q, unsigned items) {
         const dim3 grid(items < cus ? items : cus);
-        return exact ? launch(gemm_kernel<256, 256, 2, 2, false, false>, grid, dim3(256), stream, q)
-                     : launch(gemm_kernel<256, 256, 2, 2, true, false>, grid, dim3(256), stream, q);
+        return launch_tiles<256, 256, false>(exact, grid, stream, q);
       };
       hipError_t e = hipSuccess;
       if (sp.first > 0) {
@@ -995,13 +1128,11 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
     p.tiles_main = int(split ? tiles - rest : tiles);
     const dim3 grid(tiles < cus ? tiles : cus);
     const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
-    hipError_t e = exact ? launch(gemm_kernel<256, 256, 2, 2, false, false>, grid, dim3(256), stream, p)
-                         : launch(gemm_kernel<256, 256, 2, 2, true, false>, grid, dim3(256), stream, p);
+    hipError_t e = launch_tiles<256, 256, false>(exact, grid, stream, p);
     if (e == hipSuccess && split) {
       p.tail_first = p.tiles_main;
       const dim3 qgrid(4 * rest < cus ? 4 * rest : cus);
-      e = exact ? launch(gemm_kernel<128, 128, 2, 2, false, true>, qgrid, dim3(256), stream, p)
-                : launch(gemm_kernel<128, 128, 2, 2, true, true>, qgrid, dim3(256), stream, p);
+      e = launch_tiles<128, 128, true>(exact, qgrid, stream, p);
     }
     return e;
   }
@@ -1045,6 +1176,16 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
 hipError_t launch_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc, void *ws,
                           size_t ws_bytes, hipStream_t stream) {
   return launch_gemm_impl(a, b, c, c_dtype, ldc, ws, ws_bytes, stream);
+}
+
+hipError_t launch_gemm_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, float beta,
+                              float *amax, void *ws, size_t ws_bytes, hipStream_t stream) {
+  unsigned *bits = reinterpret_cast<unsigned *>(amax);
+  if (bits && a->rows > 0 && b->rows > 0) {
+    const hipError_t e = launch(zero_word_kernel, dim3(1), dim3(64), stream, bits);
+    if (e != hipSuccess) return e;
+  }
+  return launch_gemm_impl(a, b, c, FP4_FP32, ldc, ws, ws_bytes, stream, true, beta, bits);
 }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {

@@ -497,18 +497,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 }
 
 
-// Raw buffer access from a wave-uniform base: the descriptor sits in scalar
-// registers, each row's byte offset in a scalar register, and only the lane's
-// column offset in a vector register, so 16 rows cost no vector address
-// arithmetic.  The base pointer is made explicitly uniform (its value is the same
-// in every lane of the wave); the range field is left at its maximum and every
-// access stays inside the tensor.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *p) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a)), hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((uint64_t(hi) << 32) | lo), short(0), 0x7FFFFFFF,
-                                           0x00020000);
-}
+// Raw buffer access from a wave-uniform base (wave_rsrc): the descriptor sits in
+// scalar registers, each row's byte offset in a scalar register, and only the
+// lane's column offset in a vector register, so 16 rows cost no vector address
+// arithmetic.
 
 // 16 rows x 4 adjacent columns of x (one 16-row slab), as loaded; row r negated
 // when bit r of `neg` is set.  Column j is widened to binary32 when it is used.

@@ -79,3 +79,36 @@ def test_newton_schulz_rejects_bad_arguments(fp4):
         fp4.fp4_newton_schulz(g, g, 1, bufs, flags=fp4.Q_SR)
     with pytest.raises(fp4.Fp4Error, match="MISMATCH"):
         fp4.fp4_newton_schulz(torch.zeros(64, 128, device="cuda"), torch.zeros(64, 128, device="cuda"), 1, bufs)
+
+
+@pytest.mark.parametrize("variant", ["rne", "rht_sr", "eden"])
+@pytest.mark.parametrize("shape", [(128, 256), (512, 400), (1024, 4096), (4096, 1024), (4400, 4000), (5120, 20480)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_newton_schulz_fused_epilogue_equals_the_axpby(fp4, variant, shape):
+    """Without B X, X' = a X + B X is taken in the B X GEMM's epilogue: the same
+    binary32 operations, so X and every quantized operand (amax included: with
+    nearest-even operands the epilogue's maximum gives the next X's) equal the call
+    that writes B X and runs the axpby.  The shapes reach the edge kernel (K = 128),
+    the partial-tile main kernel (N = 400), the whole-tile main kernel, its split-K
+    form (4096 x 1024: B X is 4096 x 1024 x 4096, 64 tiles split over K), partial
+    tiles with 128x128 quarters for the last 32 of 288 tiles (4400 x 4000), and the
+    12B weight-gradient shape (1600 whole tiles, the last 64 as quarters)."""
+    m, n = shape
+    if variant == "eden" and (m % 64 or n % 64):
+        pytest.skip("the 64-point transform needs multiples of 64")
+    g = dev(workloads.random_matrix((m, n), seed=m * 3 + n, dtype=torch.float32))
+    flags = variant_flags(fp4, variant)
+    out = {}
+    for keep in (True, False):
+        x = torch.empty_like(g)
+        bufs = fp4.NsBuffers(m, n, keep_bx=keep)
+        fp4.fp4_newton_schulz(g, x, 3, bufs, normalize=True, flags=flags, rht_signs=SIGNS, seed=5, offset=40)
+        torch.cuda.synchronize()
+        out[keep] = (x, bufs)
+    assert torch.equal(out[True][0], out[False][0]), f"{variant} {shape}: X"
+    names = ("x_left", "a_left", "b_q", "xt") if variant == "rne" else \
+        ("x_left", "x_right", "a_left", "a_right", "b_q", "xt")
+    for name in names:
+        c1, s1, a1 = host_q(getattr(out[True][1], name))
+        c2, s2, a2 = host_q(getattr(out[False][1], name))
+        assert a1 == a2 and np.array_equal(s1, s2) and np.array_equal(c1, c2), f"{variant} {shape}: {name}"
