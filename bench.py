@@ -768,15 +768,15 @@ def quantize_breakdown(layers, wl, reps=5):
         fprop, dgrad, wgrad = ("fprop" in wl.passes), ("dgrad" in wl.passes), ("wgrad" in wl.passes)
         if fprop and wgrad:
             xb = M * K * (in_b + 2 * one_d)
-            add(f"{lin.name} X dual call (amax pass + both layouts)", "amax_dual_kernel + quant_cols_kernel", xb,
+            add(f"{lin.name} X dual call (amax pass + both layouts)", "amax_dual4_kernel + quant_dual_ne_kernel", xb,
                 med_ms(lambda: Q.fp4_quantize_dual(x, Q.Q_RHT, inp.signs, 0, 0, 0, b.xq, b.xq_t)), "call")
-            add(f"{lin.name} X rowwise + X^T columnwise transformed, one kernel (amax given)", "quant_cols_kernel",
+            add(f"{lin.name} X rowwise + X^T columnwise transformed, one kernel (amax given)", "quant_dual_ne_kernel",
                 xb, med_ms(lambda: Q.fp4_quantize_dual(x, Q.Q_RHT | G, inp.signs, 0, 0, 0, b.xq, b.xq_t)), "hbm")
         elif fprop:
             add(f"{lin.name} X rowwise nearest-even (amax given)", "quant_rows_flat_kernel", M * K * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(x, G, 0, 0, 0, b.xq)), "hbm")
         elif wgrad:
-            add(f"{lin.name} X^T columnwise transformed (amax given)", "quant_cols_kernel", M * K * (in_b + one_d),
+            add(f"{lin.name} X^T columnwise transformed (amax given)", "quant_cols4_kernel", M * K * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(x, Q.Q_COLWISE | Q.Q_RHT | G, inp.signs, 0, 0, b.xq_t)), "hbm")
         if fprop or dgrad:
             wb = N * K * (in_b + two_d)
@@ -788,7 +788,7 @@ def quantize_breakdown(layers, wl, reps=5):
             add(f"{lin.name} W amax alone (fp4_amax: the same kernel, its atomic form)", "amax_flat_kernel",
                 N * K * in_b, med_ms(lambda: Q.fp4_amax(w, 0, 0, scratch)), "hbm")
         if dgrad and wgrad:
-            add(f"{lin.name} dY dual call (amax pass + two stochastic layouts)", "amax_dual_kernel + 2 kernels",
+            add(f"{lin.name} dY dual call (amax pass + two stochastic layouts)", "amax_dual4_kernel + quant_rows_flat_kernel + quant_cols4_kernel",
                 M * N * (in_b + 2 * one_d),
                 med_ms(lambda: Q.fp4_quantize_dual(dy, Q.Q_SR | Q.Q_RHT, inp.signs, sd, od, ow, b.dyq, b.dyq_t)),
                 "call")
@@ -796,7 +796,7 @@ def quantize_breakdown(layers, wl, reps=5):
             add(f"{lin.name} dY rowwise stochastic (amax given)", "quant_rows_flat_kernel", M * N * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(dy, Q.Q_SR | G, 0, sd, od, b.dyq)), "valu")
         if wgrad:
-            add(f"{lin.name} dY^T columnwise transformed stochastic (amax given)", "quant_cols_kernel",
+            add(f"{lin.name} dY^T columnwise transformed stochastic (amax given)", "quant_cols4_kernel",
                 M * N * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT | Q.Q_SR | G, inp.signs, sd, ow, b.dyq_t)),
                 "valu")
@@ -804,13 +804,13 @@ def quantize_breakdown(layers, wl, reps=5):
             # partner X^T with the same 64-point rotation (not in the timed step)
             key = 0x9E3779B9
             add(f"{lin.name} dY^T MS-EDEN call (64-point transform, amax pass + layout)",
-                "amax_rht64_cols_kernel + quant_cols64_kernel", M * N * (in_b + one_d),
+                "amax_rht64_cols4_kernel + quant_cols64q_kernel", M * N * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT64 | Q.Q_EDEN, key, sd, ow, b.dyq_t)), "call")
-            add(f"{lin.name} dY^T columnwise 64-point transform + MS-EDEN (amax given)", "quant_cols64_kernel",
+            add(f"{lin.name} dY^T columnwise 64-point transform + MS-EDEN (amax given)", "quant_cols64q_kernel",
                 M * N * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(dy, Q.Q_COLWISE | Q.Q_RHT64 | Q.Q_EDEN | G, key, sd, ow, b.dyq_t)),
                 "valu")
-            add(f"{lin.name} X^T columnwise 64-point transform nearest-even (amax given)", "quant_cols64_kernel",
+            add(f"{lin.name} X^T columnwise 64-point transform nearest-even (amax given)", "quant_cols64q_kernel",
                 M * K * (in_b + one_d),
                 med_ms(lambda: Q.fp4_quantize(x, Q.Q_COLWISE | Q.Q_RHT64 | G, key, 0, 0, b.xq_t)), "hbm")
     del flush
