@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (the known-size reference that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters into bytes) and exit")
+    ap.add_argument("--ns-calls-only", choices=["rne", "rht_sr", "eden"],
+                    help="with --workload newton_schulz: only run that operand variant's call (X' taken in the B X "
+                         "GEMM's epilogue), warmup + steps times, and print its time per call (a short run for "
+                         "kernel traces)")
     ap.add_argument("--stream-rates", action="store_true",
                     help="only measure streaming rates (the library's amax pass at 256 MiB to 2 GiB of bf16, and a "
                          "2 GiB device copy) and print one JSON line")
@@ -430,8 +434,41 @@ def newton_schulz_divergence(dev, m=1024, n=4096):
     return res
 
 
+def newton_schulz_calls(variant, steps, warmup, dev):
+    """Only the fused call of one operand variant on X 5120x20480: warmup + steps
+    calls, the last steps timed with HIP events (one JSON line)."""
+    import torch
+
+    import nvfp4_bit_microscaled_amd as fp4
+    import workloads
+
+    m, n = NS_SHAPE
+    g = workloads.random_matrix((m, n), seed=0, dtype=torch.float32).to(dev)
+    x = torch.empty_like(g)
+    bufs = fp4.NsBuffers(m, n, device=dev, keep_bx=False)
+    f = ns_flags(fp4, variant)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fp4.fp4_newton_schulz(g, x, NS_ITERS, bufs, flags=f, rht_signs=0x1234ACE1, seed=1, offset=0)
+    e0, e1 = HipTimingEvent(), HipTimingEvent()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fp4.fp4_newton_schulz(g, x, NS_ITERS, bufs, flags=f, rht_signs=0x1234ACE1, seed=1, offset=0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = NS_ITERS * (2.0 * m * m * n + 2.0 * m * m * m + 2.0 * m * n * m)
+    print(json.dumps({"workload": "newton_schulz", "variant": variant, "X": [m, n], "iters": NS_ITERS,
+                      "calls": warmup + steps, "timed_calls": steps, "ms_per_call": round(ms, 4),
+                      "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}), flush=True)
+
+
 def run_newton_schulz(args, dev):
     import torch
+    if args.ns_calls_only:
+        newton_schulz_calls(args.ns_calls_only, args.steps, args.warmup, dev)
+        return
     t = newton_schulz_timing(args.steps, args.warmup, dev)
     torch.cuda.empty_cache()
     d = newton_schulz_divergence(dev)
