@@ -319,6 +319,20 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
     auto q = [&](const float *src, int64_t r, int64_t c, uint32_t f, uint64_t off, const fp4_tensor *out) {
       return nvfp4::launch_quantize(src, FP4_FP32, r, c, c, f, key, cfg->seed, off, out, nullptr, stream);
     };
+    // The left and right rowwise layouts of one tensor [m][c] (RHT + SR, or MS-EDEN
+    // and the 64-point transform) transform it alike, so one amax pass serves both:
+    // the second quantization takes the first's amax (with MS-EDEN the stored amax
+    // is 7/4 of the transformed values', so the right layout goes first).
+    auto q_pair = [&](const float *src, int64_t c, uint64_t off_l, uint64_t off_r, const fp4_tensor *left,
+                      const fp4_tensor *right) {
+      const bool eden = fl & FP4_Q_EDEN;
+      const fp4_tensor *first = eden ? right : left, *second = eden ? left : right;
+      hipError_t r = q(src, m, c, eden ? fr : fl, eden ? off_r : off_l, first);
+      if (r == hipSuccess) r = nvfp4::launch_amax_copy(first->amax, second->amax, eden ? 1.75f : 1.0f, stream);
+      if (r == hipSuccess)
+        r = q(src, m, c, (eden ? fl : fr) | FP4_Q_AMAX_GIVEN, eden ? off_l : off_r, second);
+      return r;
+    };
     // Nearest-even: both operands of X X^T (and of A A^T) are the same quantization,
     // X's rowwise and columnwise layouts come from one read of X (the dual
     // quantization), and the amaxes of B and of the next X are taken by the axpby
@@ -342,13 +356,12 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
         e = nvfp4::launch_quantize_dual(x, FP4_FP32, m, n, n, given ? FP4_Q_AMAX_GIVEN : 0u, key, cfg->seed, o + 0,
                                         o + 5, &bufs->x_left, &bufs->xt, stream);
     } else {
-      e = q(x, m, n, fl, o + 0, &bufs->x_left);
-      if (e == hipSuccess) e = q(x, m, n, fr, o + 1, &bufs->x_right);
+      e = q_pair(x, n, o + 0, o + 1, &bufs->x_left, &bufs->x_right);
     }
     if (e == hipSuccess)
       e = nvfp4::launch_gemm_ws(&bufs->x_left, xr, bufs->a, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
-    if (e == hipSuccess) e = q(bufs->a, m, m, fl, o + 2, &bufs->a_left);
-    if (e == hipSuccess && !same) e = q(bufs->a, m, m, fr, o + 3, &bufs->a_right);
+    if (e == hipSuccess) e = same ? q(bufs->a, m, m, fl, o + 2, &bufs->a_left)
+                                  : q_pair(bufs->a, m, o + 2, o + 3, &bufs->a_left, &bufs->a_right);
     if (e == hipSuccess)
       e = nvfp4::launch_gemm_ws(&bufs->a_left, ar, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
     if (same) {

@@ -27,6 +27,10 @@ hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t strea
 hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                        uint32_t signs, float *out, hipStream_t stream);
 
+// *dst = fl(factor * *src), one thread: an amax taken by one quantization handed to
+// another of the same transformed values (factor 7/4 into an MS-EDEN one).
+hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream);
+
 hipError_t launch_quantize(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                            uint32_t signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
                            const fp4_tensor *out_t, hipStream_t stream);

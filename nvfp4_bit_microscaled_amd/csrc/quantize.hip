@@ -167,6 +167,7 @@ __global__ __launch_bounds__(kThreads) void amax_finish_kernel(const float *__re
 
 __global__ void zero_f32_kernel(float *p) { *p = 0.0f; }
 __global__ void scale_f32_kernel(float *p, float factor) { *p = factor * *p; }
+__global__ void copy_scale_f32_kernel(const float *src, float *dst, float factor) { *dst = factor * *src; }
 __global__ void zero2_f32_kernel(float *p, float *q) {
   *p = 0.0f;
   *q = 0.0f;
@@ -1461,6 +1462,10 @@ hipError_t launch_quantize_dual(const void *x, fp4_dtype dtype, int64_t R, int64
                      stream);
   return dual_impl(static_cast<const float *>(x), R, C, ld, flags, signs, seed, off_rows, off_cols, rows, cols,
                    stream);
+}
+
+hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream) {
+  return launch(copy_scale_f32_kernel, dim3(1), dim3(1), stream, src, dst, factor);
 }
 
 hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
