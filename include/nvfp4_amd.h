@@ -344,7 +344,8 @@ FP4_API fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype 
  *                            operands (X right, A right, X^T) the 64-point transform
  *                            (key rht_signs) nearest-even.
  * With either non-zero variant the left and right layouts of X (and of A) share
- * one amax pass: both transform the tensor alike.
+ * one amax pass: both transform the tensor alike; with FP4_Q_RHT | FP4_Q_SR they
+ * differ only in their random draws and come from one read of the tensor.
  * In iteration t the operands draw Philox offsets offset + 8 t + k, k = 0 (X left),
  * 1 (X right), 2 (A left), 3 (A right), 4 (B), 5 (X^T), all with key seed. */
 typedef struct fp4_ns_config {

@@ -323,8 +323,13 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
     // and the 64-point transform) transform it alike, so one amax pass serves both:
     // the second quantization takes the first's amax (with MS-EDEN the stored amax
     // is 7/4 of the transformed values', so the right layout goes first).
+    // With RHT + SR the two layouts differ only in their random draws: one kernel
+    // transforms and scales each block once and encodes it twice.
     auto q_pair = [&](const float *src, int64_t c, uint64_t off_l, uint64_t off_r, const fp4_tensor *left,
                       const fp4_tensor *right) {
+      if (fl == fr && (fl & FP4_Q_SR))
+        return nvfp4::launch_quantize_rows_pair(src, FP4_FP32, m, c, fl, key, cfg->seed, off_l, off_r, left, right,
+                                                stream);
       const bool eden = fl & FP4_Q_EDEN;
       const fp4_tensor *first = eden ? right : left, *second = eden ? left : right;
       hipError_t r = q(src, m, c, eden ? fr : fl, eden ? off_r : off_l, first);

@@ -31,6 +31,14 @@ hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int
 // another of the same transformed values (factor 7/4 into an MS-EDEN one).
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream);
 
+// Two rowwise stochastic layouts a, b of one contiguous tensor [R][C] (row stride C)
+// with Philox offsets off_a, off_b, from one read: flags FP4_Q_SR with optional
+// FP4_Q_RHT and FP4_Q_AMAX_GIVEN (then *a->amax holds the amax).  *b->amax
+// receives a's amax.  The same codes and scales as two launch_quantize calls.
+hipError_t launch_quantize_rows_pair(const void *x, fp4_dtype dtype, int64_t R, int64_t C, uint32_t flags,
+                                     uint32_t signs, uint64_t seed, uint64_t off_a, uint64_t off_b,
+                                     const fp4_tensor *a, const fp4_tensor *b, hipStream_t stream);
+
 hipError_t launch_quantize(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                            uint32_t signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
                            const fp4_tensor *out_t, hipStream_t stream);

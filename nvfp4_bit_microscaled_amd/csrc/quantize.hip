@@ -354,6 +354,48 @@ __global__ __launch_bounds__(kThreads) void quant_rows_flat_kernel(const T *__re
   }
 }
 
+// Two rowwise stochastic layouts of one contiguous tensor that differ only in
+// their random draws (offsets off_a and off_b): the transform, the block amax and
+// the scale are taken once, and each layout encodes with its own bits.  Both
+// layouts share the tensor amax *amax_p.  Bit-identical to two quant_rows_flat_kernel
+// launches.
+template <typename T, bool RHT>
+__global__ __launch_bounds__(kThreads) void quant_rows_flat_pair_kernel(
+    const T *__restrict__ x, int64_t nblocks, uint32_t signs, uint64_t seed, uint64_t off_a, uint64_t off_b,
+    const float *__restrict__ amax_p, uint8_t *__restrict__ codes_a, uint8_t *__restrict__ scales_a,
+    uint8_t *__restrict__ codes_b, uint8_t *__restrict__ scales_b) {
+  __shared__ float tab[kMultTable];
+  const float s_enc = encode_scale(*amax_p);
+  fill_mult_table(tab, s_enc);
+  __syncthreads();
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t b = int64_t(blockIdx.x) * kThreads + threadIdx.x; b < nblocks; b += stride) {
+    float v[16];
+    load8(x + b * 16, v);
+    load8(x + b * 16 + 8, v + 8);
+    float mult;
+    uint32_t sc;
+    if (RHT) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = ((signs >> j) & 1u) ? -v[j] : v[j];
+      hadamard16_unscaled(v);
+      block_scale_quarter(v, s_enc, tab, sc, mult);
+    } else {
+      float amax_b = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, __builtin_fabsf(v[j]));
+      block_scale(amax_b, s_enc, tab, sc, mult);
+    }
+    uint32_t rb[8];
+    sr_bits16(uint64_t(b) * 16u, seed, off_a, rb);
+    *reinterpret_cast<uint2 *>(codes_a + b * 8) = encode16_sr(v, mult, rb);
+    scales_a[b] = uint8_t(sc);
+    sr_bits16(uint64_t(b) * 16u, seed, off_b, rb);
+    *reinterpret_cast<uint2 *>(codes_b + b * 8) = encode16_sr(v, mult, rb);
+    scales_b[b] = uint8_t(sc);
+  }
+}
+
 // Rowwise 1D quantization of a strided tensor: one thread per 16-block.  grid.x
 // covers the blocks of a row, grid.y strides over rows.
 template <typename T, bool RHT, bool SR>
@@ -1462,6 +1504,30 @@ hipError_t launch_quantize_dual(const void *x, fp4_dtype dtype, int64_t R, int64
                      stream);
   return dual_impl(static_cast<const float *>(x), R, C, ld, flags, signs, seed, off_rows, off_cols, rows, cols,
                    stream);
+}
+
+template <typename T>
+hipError_t pair_impl(const T *x, int64_t R, int64_t C, uint32_t flags, uint32_t signs, uint64_t seed, uint64_t off_a,
+                     uint64_t off_b, const fp4_tensor *a, const fp4_tensor *b, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (!(flags & FP4_Q_AMAX_GIVEN)) e = amax_impl(x, R, C, C, flags, signs, a->amax, partial_room(a), stream);
+  if (e == hipSuccess) e = launch(copy_scale_f32_kernel, dim3(1), dim3(1), stream, a->amax, b->amax, 1.0f);
+  if (e != hipSuccess || R == 0 || C == 0) return e;
+  const int64_t nblocks = R * (C / 16);
+  const dim3 grid(grid_for(nblocks, kThreads, 1 << 20));
+  return (flags & FP4_Q_RHT)
+             ? launch(quant_rows_flat_pair_kernel<T, true>, grid, dim3(kThreads), stream, x, nblocks, signs, seed,
+                      off_a, off_b, a->amax, a->codes, a->scales, b->codes, b->scales)
+             : launch(quant_rows_flat_pair_kernel<T, false>, grid, dim3(kThreads), stream, x, nblocks, signs, seed,
+                      off_a, off_b, a->amax, a->codes, a->scales, b->codes, b->scales);
+}
+
+hipError_t launch_quantize_rows_pair(const void *x, fp4_dtype dtype, int64_t R, int64_t C, uint32_t flags,
+                                     uint32_t signs, uint64_t seed, uint64_t off_a, uint64_t off_b,
+                                     const fp4_tensor *a, const fp4_tensor *b, hipStream_t stream) {
+  if (dtype == FP4_BF16)
+    return pair_impl(static_cast<const uint16_t *>(x), R, C, flags, signs, seed, off_a, off_b, a, b, stream);
+  return pair_impl(static_cast<const float *>(x), R, C, flags, signs, seed, off_a, off_b, a, b, stream);
 }
 
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream) {
