@@ -320,23 +320,19 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
       return nvfp4::launch_quantize(src, FP4_FP32, r, c, c, f, key, cfg->seed, off, out, nullptr, stream);
     };
     // The left and right rowwise layouts of one tensor [m][c] (RHT + SR, or MS-EDEN
-    // and the 64-point transform) transform it alike, so one amax pass serves both:
-    // the second quantization takes the first's amax (with MS-EDEN the stored amax
-    // is 7/4 of the transformed values', so the right layout goes first).
-    // With RHT + SR the two layouts differ only in their random draws: one kernel
-    // transforms and scales each block once and encodes it twice.
+    // and the 64-point transform) transform it alike, so one amax pass serves both
+    // (MS-EDEN stores 7/4 of the transformed values' amax), and both layouts come
+    // from one read: with RHT + SR they differ only in their random draws (one
+    // kernel transforms and scales each block once and encodes it twice); with
+    // MS-EDEN and the 64-point transform each block is rotated once and quantized
+    // against each layout's tensor scale.
     auto q_pair = [&](const float *src, int64_t c, uint64_t off_l, uint64_t off_r, const fp4_tensor *left,
                       const fp4_tensor *right) {
-      if (fl == fr && (fl & FP4_Q_SR))
-        return nvfp4::launch_quantize_rows_pair(src, FP4_FP32, m, c, fl, key, cfg->seed, off_l, off_r, left, right,
-                                                stream);
-      const bool eden = fl & FP4_Q_EDEN;
-      const fp4_tensor *first = eden ? right : left, *second = eden ? left : right;
-      hipError_t r = q(src, m, c, eden ? fr : fl, eden ? off_r : off_l, first);
-      if (r == hipSuccess) r = nvfp4::launch_amax_copy(first->amax, second->amax, eden ? 1.75f : 1.0f, stream);
-      if (r == hipSuccess)
-        r = q(src, m, c, (eden ? fl : fr) | FP4_Q_AMAX_GIVEN, eden ? off_l : off_r, second);
-      return r;
+      (void)off_r;  // the right MS-EDEN partner is nearest-even: it draws no random bits
+      if (fl & FP4_Q_EDEN)
+        return nvfp4::launch_quantize_rows64_pair(src, FP4_FP32, m, c, key, cfg->seed, off_l, left, right, stream);
+      return nvfp4::launch_quantize_rows_pair(src, FP4_FP32, m, c, fl, key, cfg->seed, off_l, off_r, left, right,
+                                              stream);
     };
     // Nearest-even: both operands of X X^T (and of A A^T) are the same quantization,
     // X's rowwise and columnwise layouts come from one read of X (the dual

@@ -39,6 +39,14 @@ hipError_t launch_quantize_rows_pair(const void *x, fp4_dtype dtype, int64_t R, 
                                      uint32_t signs, uint64_t seed, uint64_t off_a, uint64_t off_b,
                                      const fp4_tensor *a, const fp4_tensor *b, hipStream_t stream);
 
+// The MS-EDEN layout `eden` (FP4_Q_RHT64 | FP4_Q_EDEN, Philox offset offset_e) and
+// the nearest-even layout `ne` (FP4_Q_RHT64) of one contiguous tensor [R][C], rowwise
+// with the 64-point transform of key `key`, from one read after one amax pass: the
+// same codes, scales and amaxes as two launch_quantize calls.
+hipError_t launch_quantize_rows64_pair(const void *x, fp4_dtype dtype, int64_t R, int64_t C, uint32_t key,
+                                       uint64_t seed, uint64_t offset_e, const fp4_tensor *eden, const fp4_tensor *ne,
+                                       hipStream_t stream);
+
 hipError_t launch_quantize(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                            uint32_t signs, uint64_t seed, uint64_t offset, const fp4_tensor *out,
                            const fp4_tensor *out_t, hipStream_t stream);

@@ -947,6 +947,41 @@ __global__ __launch_bounds__(kThreads) void quant_rows64_kernel(const T *__restr
   }
 }
 
+// MS-EDEN and nearest-even rowwise layouts of one tensor with the same 64-point
+// transform, from one read: each block is loaded and rotated once, then quantized
+// against each layout's tensor scale (MS-EDEN's amax *amax_e is 7/4 of the
+// nearest-even one's, *amax_n).  Bit-identical to two quant_rows64_kernel launches.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quant_rows64_pair_kernel(
+    const T *__restrict__ x, int64_t R, int64_t C, int64_t ld, uint32_t key, uint64_t seed, uint64_t offset_e,
+    const float *__restrict__ amax_e, uint8_t *__restrict__ codes_e, uint8_t *__restrict__ scales_e,
+    const float *__restrict__ amax_n, uint8_t *__restrict__ codes_n, uint8_t *__restrict__ scales_n) {
+  __shared__ float tab_e[kMultTable], tab_n[kMultTable];
+  const float s_enc_e = encode_scale(*amax_e), s_enc_n = encode_scale(*amax_n);
+  fill_mult_table(tab_e, s_enc_e);
+  fill_mult_table(tab_n, s_enc_n);
+  __syncthreads();
+  const int64_t nkb = C / 16, total = R * nkb;
+  for (int64_t q = int64_t(blockIdx.x) * kThreads + threadIdx.x; q < total; q += int64_t(gridDim.x) * kThreads) {
+    const int64_t r = q / nkb, kb = q - r * nkb;
+    float v[16];
+    load8(x + r * ld + kb * 16, v);
+    load8(x + r * ld + kb * 16 + 8, v + 8);
+    uint32_t w0, w1;
+    rht64_signs(uint64_t(kb >> 2), key, w0, w1);
+    rotate64_quad(v, rht64_quarter(w0, w1, int(kb & 3)), int(kb & 3));
+    const uint64_t i0 = uint64_t(r) * uint64_t(C) + uint64_t(kb) * 16u;
+    uint2 c;
+    uint32_t sc;
+    quant_block64<true, false>(v, s_enc_e, tab_e, uint64_t(q), i0, seed, offset_e, c, sc);
+    *reinterpret_cast<uint2 *>(codes_e + q * 8) = c;
+    scales_e[q] = uint8_t(sc);
+    quant_block64<false, false>(v, s_enc_n, tab_n, uint64_t(q), i0, seed, 0, c, sc);
+    *reinterpret_cast<uint2 *>(codes_n + q * 8) = c;
+    scales_n[q] = uint8_t(sc);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_rht64_rows_kernel(const T *__restrict__ x, int64_t R, int64_t C,
                                                                   int64_t ld, uint32_t key, float *out,
@@ -1528,6 +1563,25 @@ hipError_t launch_quantize_rows_pair(const void *x, fp4_dtype dtype, int64_t R, 
   if (dtype == FP4_BF16)
     return pair_impl(static_cast<const uint16_t *>(x), R, C, flags, signs, seed, off_a, off_b, a, b, stream);
   return pair_impl(static_cast<const float *>(x), R, C, flags, signs, seed, off_a, off_b, a, b, stream);
+}
+
+template <typename T>
+hipError_t pair64_impl(const T *x, int64_t R, int64_t C, uint32_t key, uint64_t seed, uint64_t offset_e,
+                       const fp4_tensor *eden, const fp4_tensor *ne, hipStream_t stream) {
+  hipError_t e = amax_impl(x, R, C, C, FP4_Q_RHT64, key, ne->amax, partial_room(ne), stream);
+  if (e == hipSuccess) e = launch(copy_scale_f32_kernel, dim3(1), dim3(1), stream, ne->amax, eden->amax, 1.75f);
+  if (e != hipSuccess || R == 0 || C == 0) return e;
+  const dim3 grid(grid_for(R * (C / 16), kThreads, 1 << 20));
+  return launch(quant_rows64_pair_kernel<T>, grid, dim3(kThreads), stream, x, R, C, C, key, seed, offset_e,
+                eden->amax, eden->codes, eden->scales, ne->amax, ne->codes, ne->scales);
+}
+
+hipError_t launch_quantize_rows64_pair(const void *x, fp4_dtype dtype, int64_t R, int64_t C, uint32_t key,
+                                       uint64_t seed, uint64_t offset_e, const fp4_tensor *eden, const fp4_tensor *ne,
+                                       hipStream_t stream) {
+  if (dtype == FP4_BF16)
+    return pair64_impl(static_cast<const uint16_t *>(x), R, C, key, seed, offset_e, eden, ne, stream);
+  return pair64_impl(static_cast<const float *>(x), R, C, key, seed, offset_e, eden, ne, stream);
 }
 
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream) {
