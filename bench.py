@@ -522,12 +522,18 @@ def setup_workload(name, dev):
     return wl, layers, ws, ws_need, t_gen
 
 
-def step(wl, layers, ws, stream, record):
+EDEN_KEY = 0x9E3779B9  # the 64-point rotation's key in the MS-EDEN backward
+
+
+def step(wl, layers, ws, stream, record, backward="recipe"):
     """One pass of the whole hot path through the linear-layer calls.  `record`
     collects (kind, bytes or flops, ev0, ev1) per phase: each call records the phase
     events it documents, and a phase's start event is the previous phase's end event
     (one record per boundary).  With fprop and wgrad, fp4_linear_fprop also writes
-    X^T transformed (one dual quantization of X) and the backward call reads it."""
+    X^T transformed (one dual quantization of X) and the backward call reads it.
+    backward="eden" (workloads with all three passes): fp4_linear_backward_eden, the
+    wgrad operands with the 64-point rotation and dY^T with MS-EDEN; X^T is then
+    quantized by the backward call from x."""
     import nvfp4_bit_microscaled_amd as Q
     import workloads
 
@@ -557,13 +563,21 @@ def step(wl, layers, ws, stream, record):
         one_d = 0.5 + 1 / 16           # code + scale bytes per element of a 1D layout
         two_d = 2 * (0.5 + 1 / 256)    # W and W^T of a 2D quantization
         gflop = 2.0 * M * N * K
+        eden = backward == "eden"
+        if eden:
+            assert fprop and dgrad and wgrad, "the MS-EDEN backward step needs all three passes"
         if fprop:
-            xt = b.xq_t if wgrad else None
-            call([("quant", M * K * (in_b + (2 if wgrad else 1) * one_d)), ("quant", N * K * (in_b + two_d)),
+            xt = b.xq_t if wgrad and not eden else None
+            call([("quant", M * K * (in_b + (2 if xt is not None else 1) * one_d)), ("quant", N * K * (in_b + two_d)),
                   ("gemm", gflop)],
                  lambda m: Q.fp4_linear_fprop(x, w, o["y"], b.xq, b.wq, b.wq_t, xq_t=xt, rht_signs=inp.signs, ws=ws,
                                               marks=m))
-        if dgrad and wgrad:
+        if eden:
+            call([("quant", M * N * (in_b + 2 * one_d)), ("quant", M * K * (in_b + one_d)), ("gemm", gflop),
+                  ("gemm", gflop)],
+                 lambda m: Q.fp4_linear_backward_eden(dy, x, b.wq_t, o["dx"], o["dw"], EDEN_KEY, sd, od, ow, b.dyq,
+                                                      b.dyq_t, b.xq_t, ws=ws, marks=m))
+        elif dgrad and wgrad:
             if fprop:  # X^T came with fprop's dual quantization: the X^T phase is empty
                 phases = [("quant", M * N * (in_b + 2 * one_d)), (None, 0), ("gemm", gflop), ("gemm", gflop)]
             else:
@@ -580,19 +594,19 @@ def step(wl, layers, ws, stream, record):
                  lambda m: Q.fp4_linear_wgrad(dy, x, o["dw"], inp.signs, sd, ow, b.dyq_t, b.xq_t, ws=ws, marks=m))
 
 
-def measure(wl, layers, ws, steps, warmup):
+def measure(wl, layers, ws, steps, warmup, backward="recipe"):
     """Warm up, then time `steps` steps (host clock between two device
     synchronizations) with the per-phase events; returns the step figures."""
     import torch
 
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        step(wl, layers, ws, stream, [])
+        step(wl, layers, ws, stream, [], backward)
     torch.cuda.synchronize()
     records = []
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(wl, layers, ws, stream, records)
+        step(wl, layers, ws, stream, records, backward)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
@@ -725,10 +739,23 @@ def main():
         "cpu_baseline": cpu,
         "input_generation_s": round(t_gen, 1),
     }
+    others = []
+    if not args.no_other_workloads and all(p_ in wl.passes for p_ in ("fprop", "dgrad", "wgrad")):
+        # the same layers with MS-EDEN in place of the 16-point transform + SR for dY^T
+        # (and the 64-point rotation on X^T): fp4_linear_backward_eden
+        o = measure(wl, layers, ws, args.other_steps, 2, backward="eden")
+        others.append({
+            "workload": wl.description + "; backward with MS-EDEN on dY^T and the 64-point rotation on both wgrad "
+                                         "operands (fp4_linear_backward_eden)",
+            "name": wl.name + "_eden_backward", "steps": args.other_steps,
+            "ms_per_step": round(o["ms_per_step"], 4), "value": round(o["value"], 2), "unit": "TFLOP/s",
+            "gemm_avg_call_ms": round(o["gemm_ms"] / o["n_gemm"], 4),
+            "gemm_tflops": round(o["gemm_tflops"], 2),
+            "quantize_ms_per_step": round(o["quant_ms"] / args.other_steps, 4),
+        })
     del layers, ws
     torch.cuda.empty_cache()
     if not args.no_other_workloads:
-        others = []
         for name in ("fprop_8k", "wgrad_8k", "block_3b"):
             if name == args.workload:
                 continue

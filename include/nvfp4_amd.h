@@ -321,6 +321,28 @@ FP4_API fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype 
                                        const fp4_tensor *xq_t, void *ws, size_t ws_bytes, const hipEvent_t *marks,
                                        hipStream_t stream);
 
+/* Backward pass with MS-EDEN on the weight gradient (Quartet II page, paragraph 1:
+ * MS-EDEN, the unbiased alternative to stochastic rounding for microscale formats,
+ * with lower quantization error; here the FP4_Q_RHT64 | FP4_Q_EDEN reading of
+ * fp4_quantize).  As fp4_linear_backward, except for the two wgrad operands: both
+ * take the 64-point rotation keyed by rht_key along the M tokens (M a multiple of
+ * 64), which cancels in the product over tokens -- dy^T with MS-EDEN (seed,
+ * offset_wgrad) into dyq_t ([N][M]), x^T nearest-even into xq_t ([K][M]).  dy for
+ * dgrad is quantized rowwise with stochastic rounding (seed, offset_dgrad) into dyq
+ * as in fp4_linear_backward.  dy's two amaxes (plain, and after the rotation) come
+ * from one read of dy.  x non-NULL: x^T is quantized
+ * from x; NULL: xq_t must already hold it (fp4_quantize of x with FP4_Q_COLWISE |
+ * FP4_Q_RHT64 and the same key).  The results equal fp4_quantize of each operand
+ * followed by fp4_gemm_ws.  marks (3): after dy's two quantizations, after x^T's,
+ * after the dgrad GEMM.  Errors: as fp4_linear_backward; FP4_ERR_SHAPE also for
+ * M not a multiple of 64. */
+FP4_API fp4_status fp4_linear_backward_eden(const void *dy, const void *x, fp4_dtype dtype, const fp4_tensor *wq_t,
+                                            void *dx, fp4_dtype dx_dtype, void *dw, fp4_dtype dw_dtype, int64_t M,
+                                            int64_t N, int64_t K, uint32_t rht_key, uint64_t seed,
+                                            uint64_t offset_dgrad, uint64_t offset_wgrad, const fp4_tensor *dyq,
+                                            const fp4_tensor *dyq_t, const fp4_tensor *xq_t, void *ws,
+                                            size_t ws_bytes, const hipEvent_t *marks, hipStream_t stream);
+
 /* NVFP4 Newton-Schulz: the Muon optimizer's orthogonalising iteration with every
  * GEMM operand in NVFP4 (Full-Stack FP4 pages, paragraph 1, the optimizer
  * sentence: Newton-Schulz iterations native in NVFP4; the pages give no

@@ -31,7 +31,7 @@ STATIC_SCRATCH_BYTES = 64 << 20
 # every symbol the header declares
 EXPORTS = ("fp4_tensor_bytes", "fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_gemm", "fp4_gemm_ws",
            "fp4_gemm_ws_bytes", "fp4_gemm_noalloc", "fp4_linear_ws_bytes", "fp4_linear_fprop", "fp4_linear_dgrad", "fp4_linear_wgrad",
-           "fp4_linear_backward", "fp4_newton_schulz", "fp4_newton_schulz_ws_bytes", "fp4_status_string")
+           "fp4_linear_backward", "fp4_linear_backward_eden", "fp4_newton_schulz", "fp4_newton_schulz_ws_bytes", "fp4_status_string")
 
 
 class Fp4Error(RuntimeError):
@@ -87,6 +87,8 @@ def load():
         "fp4_linear_wgrad": [vp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, tp, tp, vp, szv, vp, vp],
         "fp4_linear_backward": [vp, vp, i32, tp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, u64, tp, tp, tp, vp,
                                 szv, vp, vp],
+        "fp4_linear_backward_eden": [vp, vp, i32, tp, vp, i32, vp, i32, i64, i64, i64, u32, u64, u64, u64, tp, tp, tp,
+                                     vp, szv, vp, vp],
         "fp4_newton_schulz": [vp, vp, i64, i64, i32, i32, ctypes.POINTER(fp4_ns_config),
                               ctypes.POINTER(fp4_ns_buffers), vp],
         "fp4_newton_schulz_ws_bytes": [i64, i64, sz],
@@ -272,6 +274,24 @@ def fp4_linear_backward(dy, x, wq_t: QTensor, dx, dw, rht_signs: int, seed: int,
     _check("fp4_linear_backward", load().fp4_linear_backward(
         dy.data_ptr(), x.data_ptr() if x is not None else None, _dtype(dy), wq_t.desc, dx.data_ptr(), _dtype(dx),
         dw.data_ptr(), _dtype(dw), M, N, K, rht_signs, seed, offset_dgrad, offset_wgrad, dyq.desc, dyq_t.desc,
+        xq_t.desc, wp, wb, _marks(marks), _stream(stream)))
+
+
+def fp4_linear_backward_eden(dy, x, wq_t: QTensor, dx, dw, rht_key: int, seed: int, offset_dgrad: int,
+                             offset_wgrad: int, dyq: QTensor, dyq_t: QTensor, xq_t: QTensor, ws=None, marks=None,
+                             stream=None):
+    """As fp4_linear_backward with MS-EDEN on dy^T and the 64-point rotation (32-bit
+    key rht_key) on both wgrad operands.  x may be None when xq_t already holds x^T
+    with that rotation."""
+    M, N = dy.shape
+    K = dx.shape[1]
+    assert dy.is_contiguous() and dx.is_contiguous() and dw.is_contiguous()
+    if x is not None:
+        assert x.dtype == dy.dtype and x.is_contiguous()
+    wp, wb = _ws(ws)
+    _check("fp4_linear_backward_eden", load().fp4_linear_backward_eden(
+        dy.data_ptr(), x.data_ptr() if x is not None else None, _dtype(dy), wq_t.desc, dx.data_ptr(), _dtype(dx),
+        dw.data_ptr(), _dtype(dw), M, N, K, rht_key, seed, offset_dgrad, offset_wgrad, dyq.desc, dyq_t.desc,
         xq_t.desc, wp, wb, _marks(marks), _stream(stream)))
 
 

@@ -269,6 +269,39 @@ static size_t ns_max_slot(int64_t m, int64_t n) {
   return (w + 255) / 256 * 256;
 }
 
+fp4_status fp4_linear_backward_eden(const void *dy, const void *x, fp4_dtype dtype, const fp4_tensor *wq_t, void *dx,
+                                    fp4_dtype dx_dtype, void *dw, fp4_dtype dw_dtype, int64_t M, int64_t N, int64_t K,
+                                    uint32_t rht_key, uint64_t seed, uint64_t offset_dgrad, uint64_t offset_wgrad,
+                                    const fp4_tensor *dyq, const fp4_tensor *dyq_t, const fp4_tensor *xq_t, void *ws,
+                                    size_t ws_bytes, const hipEvent_t *marks, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M % 64 || N % 16 || K % 16) return FP4_ERR_SHAPE;
+  const uint32_t f_dyt = FP4_Q_COLWISE | FP4_Q_RHT64 | FP4_Q_EDEN, f_xt = FP4_Q_COLWISE | FP4_Q_RHT64;
+  fp4_status s;
+  if ((s = check_quantize(dy, dtype, M, N, N, FP4_Q_SR, dyq, nullptr)) != FP4_OK) return s;
+  if ((s = check_quantize(dy, dtype, M, N, N, f_dyt, dyq_t, nullptr)) != FP4_OK) return s;
+  if (x && (s = check_quantize(x, dtype, M, K, K, f_xt, xq_t, nullptr)) != FP4_OK) return s;
+  if ((s = check_tensor(xq_t, K, M, 0)) != FP4_OK) return s;
+  if ((s = check_tensor(wq_t, K, N, 1)) != FP4_OK) return s;
+  if ((s = check_gemm(dyq, wq_t, dx, dx_dtype, K)) != FP4_OK) return s;
+  if ((s = check_gemm(dyq_t, xq_t, dw, dw_dtype, K)) != FP4_OK) return s;
+  if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
+  // both of dy's amaxes from one read, then each layout with its amax given
+  hipError_t e = nvfp4::launch_amax_rows_cols64(dy, dtype, M, N, rht_key, dyq, dyq_t, stream);
+  if (e == hipSuccess)
+    e = nvfp4::launch_quantize(dy, dtype, M, N, N, FP4_Q_SR | FP4_Q_AMAX_GIVEN, 0, seed, offset_dgrad, dyq, nullptr,
+                               stream);
+  if (e == hipSuccess)
+    e = nvfp4::launch_quantize(dy, dtype, M, N, N, f_dyt | FP4_Q_AMAX_GIVEN, rht_key, seed, offset_wgrad, dyq_t,
+                               nullptr, stream);
+  if (e == hipSuccess) e = mark(marks, 0, stream);
+  if (e == hipSuccess && x) e = nvfp4::launch_quantize(x, dtype, M, K, K, f_xt, rht_key, 0, 0, xq_t, nullptr, stream);
+  if (e == hipSuccess) e = mark(marks, 1, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm_ws(dyq, wq_t, dx, dx_dtype, K, ws, ws_bytes, stream);
+  if (e == hipSuccess) e = mark(marks, 2, stream);
+  if (e == hipSuccess) e = nvfp4::launch_gemm_ws(dyq_t, xq_t, dw, dw_dtype, K, ws, ws_bytes, stream);
+  return from_hip(e);
+}
+
 fp4_status fp4_newton_schulz_ws_bytes(int64_t m, int64_t n, size_t *bytes) {
   if (!bytes) return FP4_ERR_NULL;
   if (m < 0 || n < 0 || m % 16 || n % 16) return FP4_ERR_SHAPE;

@@ -27,6 +27,14 @@ hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t strea
 hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int64_t ld, uint32_t flags,
                        uint32_t signs, float *out, hipStream_t stream);
 
+// The two amaxes of a contiguous x [R][C] (R a multiple of 64) that the MS-EDEN
+// backward quantizes twice, from one read: x's plain amax into *rows->amax (its
+// rowwise layout) and 7/4 of the amax of x^T after the 64-point rotation keyed by
+// `key` into *cols->amax (its columnwise MS-EDEN layout, FP4_Q_COLWISE |
+// FP4_Q_RHT64 | FP4_Q_EDEN).  Partial maxima go to rows' codes buffer.
+hipError_t launch_amax_rows_cols64(const void *x, fp4_dtype dtype, int64_t R, int64_t C, uint32_t key,
+                                   const fp4_tensor *rows, const fp4_tensor *cols, hipStream_t stream);
+
 // *dst = fl(factor * *src), one thread: an amax taken by one quantization handed to
 // another of the same transformed values (factor 7/4 into an MS-EDEN one).
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream);

@@ -1153,16 +1153,18 @@ __global__ __launch_bounds__(kThreads) void amax_rht64_cols_kernel(const T *__re
 
 // amax_rht64_cols_kernel with units of one group x 64 columns and 4 columns per
 // lane (lanes as in quant_cols64q_kernel, rows through buffer descriptors); the
-// launcher keeps 64 rows of x within 2^31 bytes.
-template <typename T>
+// launcher keeps 64 rows of x within 2^31 bytes.  With ROWS it also takes the plain
+// amax of x (every element passes through a lane) into *out_rows, partials of the
+// rows at [0, grid) and of the columns at [grid, 2 grid).
+template <typename T, bool ROWS = false>
 __global__ __launch_bounds__(kThreads) void amax_rht64_cols4_kernel(const T *__restrict__ x, int64_t R, int64_t C,
                                                                    int64_t ld, uint32_t key, float *out,
-                                                                   float *partial) {
+                                                                   float *partial, float *out_rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cg = lane & 15, sq = lane >> 4;
   const int64_t cblocks = (C + 63) / 64, units = (R / 64) * cblocks;
   const uint32_t ldb = uint32_t(ld * int64_t(sizeof(T)));
-  float m = 0.0f;
+  float m = 0.0f, mr = 0.0f;
   for (int64_t u = int64_t(blockIdx.x) * 4 + wave; u < units; u += int64_t(gridDim.x) * 4) {
     const int64_t g = u / cblocks, cw = (u - g * cblocks) * 64;
     if (cw + 4 * cg >= C) continue;  // lanes l ^ 16, l ^ 32 skip together
@@ -1175,13 +1177,21 @@ __global__ __launch_bounds__(kThreads) void amax_rht64_cols4_kernel(const T *__r
     for (int j = 0; j < 4; ++j) {
       float col[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) col[r] = slab.at(r, j);
+      for (int r = 0; r < 16; ++r) {
+        col[r] = slab.at(r, j);
+        if (ROWS) mr = fmaxf(mr, __builtin_fabsf(col[r]));  // the signs do not change |x|
+      }
       rotate64_cols(col, sq);
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, __builtin_fabsf(col[r]));
     }
   }
-  block_max_to(m, out, partial);
+  if (ROWS) {
+    block_max_to(mr, out_rows, partial);
+    block_max_to(m, out, partial ? partial + gridDim.x : nullptr);
+  } else {
+    block_max_to(m, out, partial);
+  }
 }
 
 // 2D (16x16 tile) nearest-even quantization of x [R][C] (R, C multiples of 16).
@@ -1345,7 +1355,8 @@ hipError_t amax_impl(const T *x, int64_t R, int64_t C, int64_t ld, uint32_t flag
   dim3 grid;
   if ((flags & FP4_Q_RHT64) && (flags & FP4_Q_COLWISE) && 64 * ld * int64_t(sizeof(T)) < (int64_t(1) << 31)) {
     grid = dim3(grid_for((R / 64) * ((C + 63) / 64), 4, cap));
-    e = launch(amax_rht64_cols4_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
+    e = launch(amax_rht64_cols4_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial,
+               static_cast<float *>(nullptr));
   } else if ((flags & FP4_Q_RHT64) && (flags & FP4_Q_COLWISE)) {
     grid = dim3(grid_for((R / 64) * ((C + 127) / 128), 4, cap));
     e = launch(amax_rht64_cols_kernel<T>, grid, dim3(kThreads), stream, x, R, C, ld, signs, out, partial);
@@ -1582,6 +1593,39 @@ hipError_t launch_quantize_rows64_pair(const void *x, fp4_dtype dtype, int64_t R
   if (dtype == FP4_BF16)
     return pair64_impl(static_cast<const uint16_t *>(x), R, C, key, seed, offset_e, eden, ne, stream);
   return pair64_impl(static_cast<const float *>(x), R, C, key, seed, offset_e, eden, ne, stream);
+}
+
+template <typename T>
+hipError_t amax_rows_cols64_impl(const T *x, int64_t R, int64_t C, uint32_t key, const fp4_tensor *rows,
+                                 const fp4_tensor *cols, hipStream_t stream) {
+  if (R == 0 || C == 0 || 64 * C * int64_t(sizeof(T)) >= (int64_t(1) << 31)) {
+    hipError_t e = amax_impl(x, R, C, C, 0u, 0u, rows->amax, partial_room(rows), stream);
+    return e == hipSuccess ? amax_impl(x, R, C, C, FP4_Q_COLWISE | FP4_Q_RHT64 | FP4_Q_EDEN, key, cols->amax,
+                                       partial_room(cols), stream)
+                           : e;
+  }
+  float *partial = partial_room(rows);
+  hipError_t e = hipSuccess;
+  if (!partial) e = launch(zero2_f32_kernel, dim3(1), dim3(1), stream, rows->amax, cols->amax);
+  const dim3 grid(grid_for((R / 64) * ((C + 63) / 64), 4, partial ? 512 : 256 * 16));
+  if (e == hipSuccess)
+    e = launch(amax_rht64_cols4_kernel<T, true>, grid, dim3(kThreads), stream, x, R, C, C, key, cols->amax, partial,
+               rows->amax);
+  if (e != hipSuccess) return e;
+  if (!partial) return launch(scale_f32_kernel, dim3(1), dim3(1), stream, cols->amax, 1.75f);
+  e = launch(amax_finish_kernel, dim3(1), dim3(kThreads), stream, static_cast<const float *>(partial), int(grid.x),
+             1, rows->amax, rows->amax, 1.0f);
+  return e == hipSuccess ? launch(amax_finish_kernel, dim3(1), dim3(kThreads), stream,
+                                  static_cast<const float *>(partial + grid.x), int(grid.x), 1, cols->amax, cols->amax,
+                                  1.75f)
+                         : e;
+}
+
+hipError_t launch_amax_rows_cols64(const void *x, fp4_dtype dtype, int64_t R, int64_t C, uint32_t key,
+                                   const fp4_tensor *rows, const fp4_tensor *cols, hipStream_t stream) {
+  if (dtype == FP4_BF16)
+    return amax_rows_cols64_impl(static_cast<const uint16_t *>(x), R, C, key, rows, cols, stream);
+  return amax_rows_cols64_impl(static_cast<const float *>(x), R, C, key, rows, cols, stream);
 }
 
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream) {

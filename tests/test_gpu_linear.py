@@ -332,3 +332,42 @@ def test_linear_calls_equal_the_primitive_composition(fp4, oracle):
                                     ("wgrad", dwa, odytq, oxtq, False)):
         ref, bound = oracle.gemm_ref(qa, qb)
         check_gemm(out.float().cpu().numpy(), ref, bound, bf16, name)
+
+
+@pytest.mark.parametrize("quantize_x", [True, False], ids=["x", "xq_t_given"])
+@pytest.mark.parametrize("shape", [(256, 128, 192), (1024, 272, 400), (2048, 768, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_linear_backward_eden(fp4, oracle, shape, quantize_x):
+    """fp4_linear_backward_eden: dY rowwise with stochastic rounding for dgrad, dY^T
+    with MS-EDEN and X^T nearest-even, both after the 64-point rotation along the
+    tokens, for wgrad.  Every quantized operand bit-exact against the oracle, both
+    outputs within the GEMM tolerance of the binary64 product of the oracle's
+    operands; the rotation cancels, so dW stays close to the unquantized product.
+    2048 x 768 x 1024 takes the split-K path for wgrad."""
+    M, N, K = shape
+    inp = workloads.make_linear_inputs(workloads.Linear("t", M, N, K), seed=M + 3 * N + K)
+    xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
+    x, w, dy = dev(inp.x), dev(inp.w), dev(inp.dy)
+    sr, od, ow = workloads.SR_SEED, workloads.SR_OFFSET_DGRAD, workloads.SR_OFFSET_WGRAD
+    key = 0x9E3779B9
+    b = fp4.LinearBuffers(M, N, K)
+    fp4.fp4_quantize(w, fp4.Q_2D, 0, 0, 0, b.wq, b.wq_t)
+    if not quantize_x:
+        fp4.fp4_quantize(x, fp4.Q_COLWISE | fp4.Q_RHT64, key, 0, 0, b.xq_t)
+    ws = torch.empty(max(fp4.fp4_linear_ws_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    fp4.fp4_linear_backward_eden(dy, x if quantize_x else None, b.wq_t, dx, dw, key, sr, od, ow, b.dyq, b.dyq_t,
+                                 b.xq_t, ws=ws)
+    torch.cuda.synchronize()
+    odyq, owtq = oracle.linear_dgrad(dyf, wf, sr, od)
+    odytq = oracle.quantize(dyf, colwise=True, rht64=True, eden=True, signs=key, seed=sr, offset=ow)
+    oxtq = oracle.quantize(xf, colwise=True, rht64=True, signs=key)
+    for name, o in (("dyq", odyq), ("wq_t", owtq), ("dyq_t", odytq), ("xq_t", oxtq)):
+        assert_q_equal(host_q(getattr(b, name)), o, name)
+    y_ref, bound = oracle.gemm_ref(odyq, owtq)
+    check_gemm(dx.float().cpu().numpy(), y_ref, bound, True, "eden backward dgrad")
+    y_ref, bound = oracle.gemm_ref(odytq, oxtq)
+    check_gemm(dw.cpu().numpy(), y_ref, bound, False, "eden backward wgrad")
+    exact = dyf.astype(np.float64).T @ xf.astype(np.float64)
+    assert np.linalg.norm(dw.cpu().numpy() - exact) / np.linalg.norm(exact) < 0.3

@@ -225,6 +225,22 @@ def test_linear_backward_rejects_bad_arguments(lib):
     assert f(dy, x, 0, *good[:15], None, 32, None, None) == 1  # workspace bytes without a pointer
 
 
+def test_linear_backward_eden_rejects_bad_arguments(lib):
+    Q = ctypes.byref
+    dy, x, dx, dw = (ctypes.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000))
+    M, N, K = 128, 32, 48
+    f = lib.fp4_linear_backward_eden
+    good = (Q(desc(K, N, 1)), dx, 1, dw, 0, M, N, K, 0x9E3779B9, 0, 1, 2, Q(desc(M, N)), Q(desc(N, M)),
+            Q(desc(K, M)), None, 0, None, None)
+    assert f(dy, x, 0, *good[:5], 96, N, K, *good[8:]) == 2  # M % 64: the rotation runs along the tokens
+    assert f(dy, x, 0, *good[:5], M, N, 40, *good[8:]) == 2  # K % 16
+    assert f(dy, x, 0, Q(desc(K, N, 0)), *good[1:]) == 6  # W^T must be 2D
+    assert f(dy, x, 0, *good[:13], Q(desc(M, N)), *good[14:]) == 6  # dY^T shape
+    assert f(dy, x, 0, *good[:14], Q(desc(M, K)), *good[15:]) == 6  # X^T shape
+    assert f(None, x, 0, *good) == 1
+    assert f(dy, x, 0, *good[:15], None, 32, None, None) == 1  # workspace bytes without a pointer
+
+
 def test_gemm_m0_is_only_written_by_the_lds_dma_statement(tmp_path):
     """The GEMM's LDS DMA sets M0 in inline assembly, which the compiler cannot see.
     That is sound only while no compiler-generated instruction of gemm.hip uses M0:
