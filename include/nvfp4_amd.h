@@ -277,6 +277,8 @@ FP4_API fp4_status fp4_linear_ws_bytes(int64_t M, int64_t N, int64_t K, size_t *
  *   w -> wq ([N][K]) 2D (16x16) nearest-even, and wq_t (nullable, [K][N]) w^T with
  *   the same tile scales, for dgrad;
  *   y = gemm(xq, wq).
+ * The amax passes of x (both of its amaxes with xq_t) and of w run as one launch,
+ * in x's phase.
  * marks (2): after x's quantization, after w's (before the GEMM). */
 FP4_API fp4_status fp4_linear_fprop(const void *x, const void *w, fp4_dtype dtype, void *y, fp4_dtype y_dtype, int64_t M,
                                     int64_t N, int64_t K, uint32_t rht_signs, const fp4_tensor *xq,

@@ -184,11 +184,17 @@ fp4_status fp4_linear_fprop(const void *x, const void *w, fp4_dtype dtype, void 
   if ((s = check_quantize(w, dtype, N, K, K, FP4_Q_2D, wq, wq_t)) != FP4_OK) return s;
   if ((s = check_gemm(xq, wq, y, y_dtype, N)) != FP4_OK) return s;
   if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
-  hipError_t e = xq_t ? nvfp4::launch_quantize_dual(x, dtype, M, K, K, FP4_Q_RHT, rht_signs & 0xFFFFu, 0, 0, 0, xq,
-                                                    xq_t, stream)
-                      : nvfp4::launch_quantize(x, dtype, M, K, K, 0, 0, 0, 0, xq, nullptr, stream);
+  // x's and w's amax passes in one launch (w's runs in x's phase), then the layouts
+  // with their amax given
+  bool merged = false;
+  const uint32_t signs = rht_signs & 0xFFFFu;
+  hipError_t e = nvfp4::launch_amax_fprop(x, w, dtype, M, N, K, signs, xq, xq_t, wq, &merged, stream);
+  const uint32_t given = merged ? FP4_Q_AMAX_GIVEN : 0u;
+  if (e == hipSuccess)
+    e = xq_t ? nvfp4::launch_quantize_dual(x, dtype, M, K, K, FP4_Q_RHT | given, signs, 0, 0, 0, xq, xq_t, stream)
+             : nvfp4::launch_quantize(x, dtype, M, K, K, given, 0, 0, 0, xq, nullptr, stream);
   if (e == hipSuccess) e = mark(marks, 0, stream);
-  if (e == hipSuccess) e = nvfp4::launch_quantize(w, dtype, N, K, K, FP4_Q_2D, 0, 0, 0, wq, wq_t, stream);
+  if (e == hipSuccess) e = nvfp4::launch_quantize(w, dtype, N, K, K, FP4_Q_2D | given, 0, 0, 0, wq, wq_t, stream);
   if (e == hipSuccess) e = mark(marks, 1, stream);
   if (e == hipSuccess) e = nvfp4::launch_gemm_ws(xq, wq, y, y_dtype, N, ws, ws_bytes, stream);
   return from_hip(e);

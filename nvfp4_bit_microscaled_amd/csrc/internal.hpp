@@ -35,6 +35,17 @@ hipError_t launch_amax(const void *x, fp4_dtype dtype, int64_t R, int64_t C, int
 hipError_t launch_amax_rows_cols64(const void *x, fp4_dtype dtype, int64_t R, int64_t C, uint32_t key,
                                    const fp4_tensor *rows, const fp4_tensor *cols, hipStream_t stream);
 
+// The forward call's amax passes in one launch plus one reduction launch: x [M][K]
+// (its plain amax into *xq->amax; with xq_t also the amax of x^T after the 16-point
+// transform with `signs` into *xq_t->amax) and w [N][K] (plain, into *wq->amax),
+// both contiguous.  *merged tells whether it ran: it does not when a tensor is
+// empty or too small to hold its partial maxima in its codes buffer, or when x's
+// rows exceed the 4-column kernel's offsets; the caller then lets the
+// quantizations take their own amax passes.
+hipError_t launch_amax_fprop(const void *x, const void *w, fp4_dtype dtype, int64_t M, int64_t N, int64_t K,
+                             uint32_t signs, const fp4_tensor *xq, const fp4_tensor *xq_t, const fp4_tensor *wq,
+                             bool *merged, hipStream_t stream);
+
 // *dst = fl(factor * *src), one thread: an amax taken by one quantization handed to
 // another of the same transformed values (factor 7/4 into an MS-EDEN one).
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream);

@@ -130,7 +130,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // *out with one atomic (its bit pattern orders like the value).  The atomics of
 // all workgroups serialise on one cache line, about 10 ns each on the MI355X, so
 // the partial form is used wherever the caller's output gives room for it.
-__device__ __forceinline__ void block_max_to(float v, float *out, float *partial) {
+__device__ __forceinline__ void block_max_to(float v, float *out, float *partial, unsigned slot = blockIdx.x) {
   __shared__ float part[kThreads / 64];
   v = wave_max(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -140,7 +140,7 @@ __device__ __forceinline__ void block_max_to(float v, float *out, float *partial
     float m = part[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, part[i]);
-    if (partial) partial[blockIdx.x] = m;
+    if (partial) partial[slot] = m;
     else atomicMax(reinterpret_cast<unsigned int *>(out), __float_as_uint(m));
   }
   __syncthreads();  // part[] is reused by a second reduction in the same kernel
@@ -191,12 +191,13 @@ __global__ __launch_bounds__(kThreads) void amax_plain_kernel(const T *__restric
 }
 
 // Plain |x| max of a contiguous tensor: four 16-byte loads in flight per thread.
+// The thread's maximum over its chunks of 8 when the tensor is spread over nblk
+// workgroups and this is workgroup blk.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict__ x, int64_t nchunks, float *out,
-                                                            float *partial) {
+__device__ __forceinline__ float flat_max(const T *__restrict__ x, int64_t nchunks, int64_t blk, int64_t nblk) {
   float m = 0.0f;
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nchunks; i += 4 * stride) {
+  const int64_t stride = nblk * kThreads;
+  for (int64_t i = blk * kThreads + threadIdx.x; i < nchunks; i += 4 * stride) {
     float v[4][8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf(v[u][e]));
   }
-  block_max_to(m, out, partial);
+  return m;
 }
 
 // bf16: the bit patterns of non-negative finite values order like the values, so
@@ -220,11 +221,11 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <>
-__global__ __launch_bounds__(kThreads) void amax_flat_kernel<uint16_t>(const uint16_t *__restrict__ x, int64_t nchunks,
-                                                                       float *out, float *partial) {
+__device__ __forceinline__ float flat_max<uint16_t>(const uint16_t *__restrict__ x, int64_t nchunks, int64_t blk,
+                                                    int64_t nblk) {
   u16x2 m = {0, 0};
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nchunks; i += 4 * stride) {
+  const int64_t stride = nblk * kThreads;
+  for (int64_t i = blk * kThreads + threadIdx.x; i < nchunks; i += 4 * stride) {
     uint4 q[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -239,7 +240,13 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel<uint16_t>(const uin
     }
   }
   const uint32_t top = m[0] > m[1] ? m[0] : m[1];
-  block_max_to(__uint_as_float(top << 16), out, partial);
+  return __uint_as_float(top << 16);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T *__restrict__ x, int64_t nchunks, float *out,
+                                                            float *partial) {
+  block_max_to(flat_max<T>(x, nchunks, blockIdx.x, gridDim.x), out, partial);
 }
 
 // amax after the Hadamard transform along rows (16 contiguous elements).
@@ -806,19 +813,18 @@ __global__ __launch_bounds__(kThreads) void amax_dual_kernel(const T *__restrict
                                                                                             // factor, once
 }
 
-// amax_dual_kernel with wave units of one 16-row slab x 256 columns, 4 columns per
-// lane and rows read through buffer descriptors (scalar row offsets); the launcher
-// keeps 16 rows of x within 2^31 bytes.  Without ROWS only the columnwise amax is
-// taken (out_rows unused; partials of the columns at [grid, 2 grid)).
-template <typename T, bool RHT, bool ROWS = true>
-__global__ __launch_bounds__(kThreads) void amax_dual4_kernel(const T *__restrict__ x, int64_t R, int64_t C,
-                                                             int64_t ld, uint32_t signs, float *out_rows,
-                                                             float *out_cols, float *partial) {
+// The thread's maxima for amax_dual4_kernel when the units are spread over nblk
+// workgroups and this is workgroup blk (mr: x, mc: x^T after the transform,
+// without its factor 1/4).
+template <typename T, bool RHT, bool ROWS>
+__device__ __forceinline__ void dual4_max(const T *__restrict__ x, int64_t R, int64_t C, int64_t ld, uint32_t signs,
+                                          int64_t blk, int64_t nblk, float &mr, float &mc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t cblocks = (C + 255) / 256, units = (R / 16) * cblocks;
   const uint32_t ldb = uint32_t(ld * int64_t(sizeof(T)));
-  float mr = 0.0f, mc = 0.0f;
-  for (int64_t u = int64_t(blockIdx.x) * 4 + wave; u < units; u += int64_t(gridDim.x) * 4) {
+  mr = 0.0f;
+  mc = 0.0f;
+  for (int64_t u = blk * 4 + wave; u < units; u += nblk * 4) {
     const int64_t sl = u / cblocks, cw = (u - sl * cblocks) * 256;
     if (cw + 4 * lane >= C) continue;  // a lane quad skips together (C % 16 == 0)
     Slab4<T> slab;
@@ -836,10 +842,69 @@ __global__ __launch_bounds__(kThreads) void amax_dual4_kernel(const T *__restric
       for (int r = 0; r < 16; ++r) mc = fmaxf(mc, __builtin_fabsf(col[r]));
     }
   }
+}
+
+// amax_dual_kernel with wave units of one 16-row slab x 256 columns, 4 columns per
+// lane and rows read through buffer descriptors (scalar row offsets); the launcher
+// keeps 16 rows of x within 2^31 bytes.  Without ROWS only the columnwise amax is
+// taken (out_rows unused; partials of the columns at [grid, 2 grid)).
+template <typename T, bool RHT, bool ROWS = true>
+__global__ __launch_bounds__(kThreads) void amax_dual4_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                             int64_t ld, uint32_t signs, float *out_rows,
+                                                             float *out_cols, float *partial) {
+  float mr, mc;
+  dual4_max<T, RHT, ROWS>(x, R, C, ld, signs, blockIdx.x, gridDim.x, mr, mc);
   // partials: rows at [0, grid), columns at [grid, 2 grid)
   if (ROWS) block_max_to(mr, out_rows, partial);
   block_max_to(RHT ? mc * 0.25f : mc, out_cols, partial ? partial + gridDim.x : nullptr);  // the transform's
                                                                                             // factor, once
+}
+
+// The forward call's amax passes in one launch: workgroups [0, gx) take x [R][C]
+// (contiguous; with XDUAL both of its amaxes as amax_dual4_kernel with the
+// transform, partials at xp[0, gx) and xp[gx, 2 gx); otherwise its plain amax as
+// amax_flat_kernel, partials at xp[0, gx)), the rest w's plain amax (wchunks
+// chunks of 8, partials at wp[0, grid - gx)).
+template <typename T, bool XDUAL>
+__global__ __launch_bounds__(kThreads) void amax_xw_kernel(const T *__restrict__ x, int64_t R, int64_t C,
+                                                          uint32_t signs, unsigned gx, float *xp,
+                                                          const T *__restrict__ w, int64_t wchunks, float *wp) {
+  if (blockIdx.x < gx) {
+    if (XDUAL) {
+      float mr, mc;
+      dual4_max<T, true, true>(x, R, C, C, signs, blockIdx.x, gx, mr, mc);
+      block_max_to(mr, nullptr, xp, blockIdx.x);
+      block_max_to(mc * 0.25f, nullptr, xp + gx, blockIdx.x);  // the transform's factor, once
+    } else {
+      block_max_to(flat_max<T>(x, R * (C / 8), blockIdx.x, gx), nullptr, xp, blockIdx.x);
+    }
+  } else {
+    const unsigned b = blockIdx.x - gx;
+    block_max_to(flat_max<T>(w, wchunks, b, gridDim.x - gx), nullptr, wp, b);
+  }
+}
+
+// Up to three partial-maximum sets reduced at once, one workgroup each: workgroup
+// b writes factor[b] times the maximum of p[b][0, n[b]) to *out[b].
+struct FinishSets {
+  const float *p[3];
+  int n[3];
+  float *out[3];
+  float factor[3];
+};
+
+__global__ __launch_bounds__(kThreads) void amax_finish_sets_kernel(FinishSets f) {
+  const int b = blockIdx.x;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < f.n[b]; i += kThreads) m = fmaxf(m, f.p[b][i]);
+  __shared__ float part[kThreads / 64];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, part[i]);
+    *f.out[b] = f.factor[b] * m;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1626,6 +1691,42 @@ hipError_t launch_amax_rows_cols64(const void *x, fp4_dtype dtype, int64_t R, in
   if (dtype == FP4_BF16)
     return amax_rows_cols64_impl(static_cast<const uint16_t *>(x), R, C, key, rows, cols, stream);
   return amax_rows_cols64_impl(static_cast<const float *>(x), R, C, key, rows, cols, stream);
+}
+
+template <typename T>
+hipError_t amax_fprop_impl(const T *x, const T *w, int64_t M, int64_t N, int64_t K, uint32_t signs,
+                           const fp4_tensor *xq, const fp4_tensor *xq_t, const fp4_tensor *wq, bool *merged,
+                           hipStream_t stream) {
+  *merged = false;
+  float *xp = partial_room(xq), *wp = partial_room(wq);
+  const bool dual = xq_t != nullptr;
+  if (M == 0 || N == 0 || K == 0 || !xp || !wp || (dual && 16 * K * int64_t(sizeof(T)) >= (int64_t(1) << 31)))
+    return hipSuccess;
+  const unsigned gx = dual ? grid_for((M / 16) * ((K + 255) / 256), 4, 512) : grid_for(M * (K / 8), kThreads * 4, 1024);
+  const unsigned gw = grid_for(N * (K / 8), kThreads * 4, 1024);
+  hipError_t e = dual ? launch(amax_xw_kernel<T, true>, dim3(gx + gw), dim3(kThreads), stream, x, M, K, signs, gx, xp,
+                               w, N * (K / 8), wp)
+                      : launch(amax_xw_kernel<T, false>, dim3(gx + gw), dim3(kThreads), stream, x, M, K, signs, gx,
+                               xp, w, N * (K / 8), wp);
+  if (e != hipSuccess) return e;
+  FinishSets f{};
+  int n = 0;
+  f.p[n] = xp, f.n[n] = int(gx), f.out[n] = xq->amax, f.factor[n++] = 1.0f;
+  if (dual) f.p[n] = xp + gx, f.n[n] = int(gx), f.out[n] = xq_t->amax, f.factor[n++] = 1.0f;
+  f.p[n] = wp, f.n[n] = int(gw), f.out[n] = wq->amax, f.factor[n++] = 1.0f;
+  e = launch(amax_finish_sets_kernel, dim3(n), dim3(kThreads), stream, f);
+  *merged = e == hipSuccess;
+  return e;
+}
+
+hipError_t launch_amax_fprop(const void *x, const void *w, fp4_dtype dtype, int64_t M, int64_t N, int64_t K,
+                             uint32_t signs, const fp4_tensor *xq, const fp4_tensor *xq_t, const fp4_tensor *wq,
+                             bool *merged, hipStream_t stream) {
+  if (dtype == FP4_BF16)
+    return amax_fprop_impl(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), M, N, K, signs, xq,
+                           xq_t, wq, merged, stream);
+  return amax_fprop_impl(static_cast<const float *>(x), static_cast<const float *>(w), M, N, K, signs, xq, xq_t, wq,
+                         merged, stream);
 }
 
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream) {
