@@ -298,6 +298,7 @@ FP4_API fp4_status fp4_linear_dgrad(const void *dy, fp4_dtype dtype, const fp4_t
  * both operands are quantized transposed (blocks along the M tokens) after the
  * random Hadamard transform with the same signs; dy with stochastic rounding (seed,
  * offset) into dyq_t ([N][M]), x nearest-even into xq_t ([K][M]).
+ * The amax passes of dy and x run as one launch, in dy's phase.
  * marks (2): after dy^T's quantization, after x^T's (before the GEMM). */
 FP4_API fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dtype, void *dw, fp4_dtype dw_dtype,
                                     int64_t M, int64_t N, int64_t K, uint32_t rht_signs, uint64_t seed,
@@ -314,6 +315,7 @@ FP4_API fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dty
  * if x is not NULL it is first quantized from x into xq_t, otherwise xq_t must
  * already hold it (fp4_linear_fprop with xq_t writes it).  The results equal
  * fp4_linear_dgrad and fp4_linear_wgrad with the same seeds, offsets and signs.
+ * With x, the amax passes of dy and x run as one launch, in dy's phase.
  * marks (3): after dy's quantization, after x^T's (at the same point when x is
  * NULL), after the dgrad GEMM (before the wgrad GEMM). */
 FP4_API fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, const fp4_tensor *wq_t,

@@ -227,9 +227,14 @@ fp4_status fp4_linear_wgrad(const void *dy, const void *x, fp4_dtype dtype, void
   if ((s = check_gemm(dyq_t, xq_t, dw, dw_dtype, K)) != FP4_OK) return s;
   if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
   const uint32_t signs = rht_signs & 0xFFFFu;
-  hipError_t e = nvfp4::launch_quantize(dy, dtype, M, N, N, fdy, signs, seed, offset, dyq_t, nullptr, stream);
+  // dy's and x's amax passes in one launch (x's runs in dy's phase), then the layouts
+  bool merged = false;
+  hipError_t e = nvfp4::launch_amax_wgrad(dy, x, dtype, M, N, K, signs, nullptr, dyq_t, xq_t, &merged, stream);
+  const uint32_t given = merged ? FP4_Q_AMAX_GIVEN : 0u;
+  if (e == hipSuccess)
+    e = nvfp4::launch_quantize(dy, dtype, M, N, N, fdy | given, signs, seed, offset, dyq_t, nullptr, stream);
   if (e == hipSuccess) e = mark(marks, 0, stream);
-  if (e == hipSuccess) e = nvfp4::launch_quantize(x, dtype, M, K, K, fx, signs, 0, 0, xq_t, nullptr, stream);
+  if (e == hipSuccess) e = nvfp4::launch_quantize(x, dtype, M, K, K, fx | given, signs, 0, 0, xq_t, nullptr, stream);
   if (e == hipSuccess) e = mark(marks, 1, stream);
   if (e == hipSuccess) e = nvfp4::launch_gemm_ws(dyq_t, xq_t, dw, dw_dtype, K, ws, ws_bytes, stream);
   return from_hip(e);
@@ -252,11 +257,18 @@ fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, c
   if ((s = check_gemm(dyq_t, xq_t, dw, dw_dtype, K)) != FP4_OK) return s;
   if ((s = check_ws(ws, ws_bytes)) != FP4_OK) return s;
   const uint32_t signs = rht_signs & 0xFFFFu;
-  hipError_t e = nvfp4::launch_quantize_dual(dy, dtype, M, N, N, FP4_Q_SR | FP4_Q_RHT, signs, seed, offset_dgrad,
-                                             offset_wgrad, dyq, dyq_t, stream);
+  // with x, dy's two amaxes and x^T's in one launch (x's runs in dy's phase)
+  bool merged = false;
+  hipError_t e = x ? nvfp4::launch_amax_wgrad(dy, x, dtype, M, N, K, signs, dyq, dyq_t, xq_t, &merged, stream)
+                   : hipSuccess;
+  const uint32_t given = merged ? FP4_Q_AMAX_GIVEN : 0u;
+  if (e == hipSuccess)
+    e = nvfp4::launch_quantize_dual(dy, dtype, M, N, N, FP4_Q_SR | FP4_Q_RHT | given, signs, seed, offset_dgrad,
+                                    offset_wgrad, dyq, dyq_t, stream);
   if (e == hipSuccess) e = mark(marks, 0, stream);
   if (e == hipSuccess && x)
-    e = nvfp4::launch_quantize(x, dtype, M, K, K, FP4_Q_COLWISE | FP4_Q_RHT, signs, 0, 0, xq_t, nullptr, stream);
+    e = nvfp4::launch_quantize(x, dtype, M, K, K, FP4_Q_COLWISE | FP4_Q_RHT | given, signs, 0, 0, xq_t, nullptr,
+                               stream);
   if (e == hipSuccess) e = mark(marks, 1, stream);
   if (e == hipSuccess) e = nvfp4::launch_gemm_ws(dyq, wq_t, dx, dx_dtype, K, ws, ws_bytes, stream);
   if (e == hipSuccess) e = mark(marks, 2, stream);

@@ -46,6 +46,15 @@ hipError_t launch_amax_fprop(const void *x, const void *w, fp4_dtype dtype, int6
                              uint32_t signs, const fp4_tensor *xq, const fp4_tensor *xq_t, const fp4_tensor *wq,
                              bool *merged, hipStream_t stream);
 
+// The weight gradient's amax passes in one launch plus one reduction launch: dy
+// [M][N] (the amax of dy^T after the 16-point transform with `signs` into
+// *dyq_t->amax, and with dyq non-NULL dy's plain amax into *dyq->amax) and x [M][K]
+// (x^T after the transform, into *xq_t->amax), both contiguous.  *merged as for
+// launch_amax_fprop.
+hipError_t launch_amax_wgrad(const void *dy, const void *x, fp4_dtype dtype, int64_t M, int64_t N, int64_t K,
+                             uint32_t signs, const fp4_tensor *dyq, const fp4_tensor *dyq_t, const fp4_tensor *xq_t,
+                             bool *merged, hipStream_t stream);
+
 // *dst = fl(factor * *src), one thread: an amax taken by one quantization handed to
 // another of the same transformed values (factor 7/4 into an MS-EDEN one).
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream);

@@ -884,6 +884,27 @@ __global__ __launch_bounds__(kThreads) void amax_xw_kernel(const T *__restrict__
   }
 }
 
+// The weight gradient's amax passes in one launch: workgroups [0, ga) take a [Ra][Ca]
+// (dY) as amax_dual4_kernel with the transform (with A_ROWS its plain amax too:
+// partials of the rows at ap[0, ga), of the columns at ap[ga, 2 ga); without, the
+// columns at ap[0, ga)), the rest the transformed columnwise amax of b [Rb][Cb] (x),
+// partials at bp[0, grid - ga).  Both contiguous.
+template <typename T, bool A_ROWS>
+__global__ __launch_bounds__(kThreads) void amax_wgrad_kernel(const T *__restrict__ a, int64_t Ra, int64_t Ca,
+                                                             unsigned ga, float *ap, const T *__restrict__ b,
+                                                             int64_t Rb, int64_t Cb, float *bp, uint32_t signs) {
+  float mr, mc;
+  if (blockIdx.x < ga) {
+    dual4_max<T, true, A_ROWS>(a, Ra, Ca, Ca, signs, blockIdx.x, ga, mr, mc);
+    if (A_ROWS) block_max_to(mr, nullptr, ap, blockIdx.x);
+    block_max_to(mc * 0.25f, nullptr, A_ROWS ? ap + ga : ap, blockIdx.x);  // the transform's factor, once
+  } else {
+    const unsigned k = blockIdx.x - ga;
+    dual4_max<T, true, false>(b, Rb, Cb, Cb, signs, k, gridDim.x - ga, mr, mc);
+    block_max_to(mc * 0.25f, nullptr, bp, k);
+  }
+}
+
 // Up to three partial-maximum sets reduced at once, one workgroup each: workgroup
 // b writes factor[b] times the maximum of p[b][0, n[b]) to *out[b].
 struct FinishSets {
@@ -1727,6 +1748,43 @@ hipError_t launch_amax_fprop(const void *x, const void *w, fp4_dtype dtype, int6
                            xq_t, wq, merged, stream);
   return amax_fprop_impl(static_cast<const float *>(x), static_cast<const float *>(w), M, N, K, signs, xq, xq_t, wq,
                          merged, stream);
+}
+
+template <typename T>
+hipError_t amax_wgrad_impl(const T *dy, const T *x, int64_t M, int64_t N, int64_t K, uint32_t signs,
+                           const fp4_tensor *dyq, const fp4_tensor *dyq_t, const fp4_tensor *xq_t, bool *merged,
+                           hipStream_t stream) {
+  *merged = false;
+  float *ap = partial_room(dyq_t), *bp = partial_room(xq_t);
+  const int64_t lim = int64_t(1) << 31;
+  if (M == 0 || N == 0 || K == 0 || !ap || !bp || 16 * N * int64_t(sizeof(T)) >= lim ||
+      16 * K * int64_t(sizeof(T)) >= lim)
+    return hipSuccess;
+  const unsigned ga = grid_for((M / 16) * ((N + 255) / 256), 4, 512);
+  const unsigned gb = grid_for((M / 16) * ((K + 255) / 256), 4, 1024);
+  hipError_t e = dyq ? launch(amax_wgrad_kernel<T, true>, dim3(ga + gb), dim3(kThreads), stream, dy, M, N, ga, ap, x,
+                              M, K, bp, signs)
+                     : launch(amax_wgrad_kernel<T, false>, dim3(ga + gb), dim3(kThreads), stream, dy, M, N, ga, ap, x,
+                              M, K, bp, signs);
+  if (e != hipSuccess) return e;
+  FinishSets f{};
+  int n = 0;
+  if (dyq) f.p[n] = ap, f.n[n] = int(ga), f.out[n] = dyq->amax, f.factor[n++] = 1.0f;
+  f.p[n] = dyq ? ap + ga : ap, f.n[n] = int(ga), f.out[n] = dyq_t->amax, f.factor[n++] = 1.0f;
+  f.p[n] = bp, f.n[n] = int(gb), f.out[n] = xq_t->amax, f.factor[n++] = 1.0f;
+  e = launch(amax_finish_sets_kernel, dim3(n), dim3(kThreads), stream, f);
+  *merged = e == hipSuccess;
+  return e;
+}
+
+hipError_t launch_amax_wgrad(const void *dy, const void *x, fp4_dtype dtype, int64_t M, int64_t N, int64_t K,
+                             uint32_t signs, const fp4_tensor *dyq, const fp4_tensor *dyq_t, const fp4_tensor *xq_t,
+                             bool *merged, hipStream_t stream) {
+  if (dtype == FP4_BF16)
+    return amax_wgrad_impl(static_cast<const uint16_t *>(dy), static_cast<const uint16_t *>(x), M, N, K, signs, dyq,
+                           dyq_t, xq_t, merged, stream);
+  return amax_wgrad_impl(static_cast<const float *>(dy), static_cast<const float *>(x), M, N, K, signs, dyq, dyq_t,
+                         xq_t, merged, stream);
 }
 
 hipError_t launch_amax_copy(const float *src, float *dst, float factor, hipStream_t stream) {
