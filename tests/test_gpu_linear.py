@@ -50,8 +50,11 @@ def check_rows(oracle, x_f32, gpu_q, rows, **kw):
     return oracle.QTensor(o_codes, o_scales, amax, len(rows), parts[0].K, False)
 
 
-@pytest.mark.parametrize("shape", [(256, 128, 512), (1008, 272, 400)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(32, 32, 64), (256, 128, 512), (1008, 272, 400)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_small_linear_all_passes(fp4, oracle, shape):
+    """32 x 32 x 64: codes buffers too small for partial maxima, so the calls take
+    their per-tensor amax passes (atomic form) instead of the merged launches."""
     M, N, K = shape
     inp = workloads.make_linear_inputs(workloads.Linear("t", M, N, K), seed=M + N + K)
     xf, wf, dyf = (workloads.widen(t) for t in (inp.x, inp.w, inp.dy))
