@@ -203,14 +203,15 @@ __device__ __forceinline__ void static_for(F &&f) {
 constexpr int kEpiBytes = 4096;
 
 // fp32 accumulating epilogue, C = fl(v + fl(beta * C)), block by block as the
-// plain fp32 path.  The old C of each block is loaded kAccAhead blocks ahead into
+// plain fp32 path.  The old C of each block is loaded kAccAhead blocks ahead
+// (kAccAheadCheck for partial tiles, whose bounds tests take registers) into
 // a ring of registers: a load issued only when its block is stored waits a whole
 // memory latency per block, with no other wave on the SIMD to cover it.  C is
 // addressed as a raw buffer from the wave's corner: the lane's offset in one
 // vector register, the block's row and column offsets in scalar ones (a wave's 128
 // rows of C span less than 2^31 bytes, else the launcher takes the edge kernel).  mx takes the maximum of |C|
 // over the lane's stored elements.
-constexpr int kAccAhead = 8, kAccAheadCheck = 8;
+constexpr int kAccAhead = 8, kAccAheadCheck = 4;
 
 template <int TM, int TN, bool CHECK>
 __device__ __forceinline__ void store_tiles_lds_acc(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
