@@ -82,6 +82,8 @@ struct GemmParams {
   float beta;
   unsigned *amax_bits;  // acc_c only, or null: atomic max of |C| over the stored elements, as the
                         // bits of a non-negative float (those order as unsigned integers)
+  int64_t sk_total;     // stream-K: stages of the stream-K tiles (tiles split_first .. + sk_tiles)
+  int sk_tiles;
 };
 
 // Wave-wide maximum of a non-negative lane value, merged into *bits by an atomic
@@ -409,8 +411,15 @@ __device__ __forceinline__ void dma16(const u32x4 &rsrc, void *dst, uint32_t vof
                : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP, bool QUARTERS, bool ACC>
+// SK: stream-K.  Workgroup r (in the order that gives each XCD a contiguous share)
+// takes stages [r T/G, (r+1) T/G) of the tile-by-stage sequence of the stream-K
+// tiles (T = sk_total, G = grid), as segments of at most one tile each.  A segment
+// that is a whole tile is stored as usual; any other is stored raw (no decode
+// scales) into workspace slot r + t (t: the tile's position among the stream-K
+// tiles), and streamk_reduce_kernel sums each split tile's segments in order.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP, bool QUARTERS, bool ACC, bool SK = false>
 __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams p) {
+  static_assert(!SK || (!QUARTERS && !ACC), "stream-K runs 256x256 tiles without an accumulated C");
   static_assert(!QUARTERS || (BM == 128 && BN == 128), "quarters of 256x256 tiles");
   constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -428,7 +437,8 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int64_t M = p.M, N = p.N;
   const uint32_t kbytes = uint32_t(p.K / 2), nkb = uint32_t(p.K / 16);
-  const int nst = int(p.K / 256) / (QUARTERS ? 1 : p.ksplit);  // K stages of one work item
+  const int zst = int(p.K / 256);                                 // K stages of a tile
+  int nst_new = zst / (QUARTERS ? 1 : p.ksplit);  // K stages of the work item set_tile last set
 
   // Persistent tiles.  The grid has at most one workgroup per CU; with a grid that
   // is a multiple of 8 and smaller than the tile count, workgroup w runs on XCD
@@ -440,7 +450,14 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   const int num_m = int((M + 255) / 256), num_n = int((N + 255) / 256);
   const int ntiles = QUARTERS ? 4 * (num_m * num_n - p.tail_first) : p.tiles_main;
   int L, Lend, Lstride;
-  if ((gridDim.x & 7) == 0 && int(gridDim.x) < ntiles) {
+  int sk_r = 0;  // stream-K: this workgroup's range
+  if constexpr (SK) {
+    const int G = gridDim.x;
+    sk_r = (G & 7) == 0 ? int(blockIdx.x & 7) * (G >> 3) + int(blockIdx.x >> 3) : int(blockIdx.x);
+    L = int(p.sk_total * sk_r / G);
+    Lend = int(p.sk_total * (sk_r + 1) / G);
+    Lstride = 0;
+  } else if ((gridDim.x & 7) == 0 && int(gridDim.x) < ntiles) {
     const int x = blockIdx.x & 7;
     L = int(int64_t(ntiles) * x / 8) + int(blockIdx.x >> 3);
     Lend = int(int64_t(ntiles) * (x + 1) / 8);
@@ -474,11 +491,21 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   const u32x4 rssa = make_rsrc(p.a_scales, uint32_t((M + (1 << p.a_shift) - 1) >> p.a_shift) * nkb);
   const u32x4 rssb = make_rsrc(p.b_scales, uint32_t((N + (1 << p.b_shift) - 1) >> p.b_shift) * nkb);
   uint32_t va[CLAMP ? JA : 1], vb[CLAMP ? JB : 1], vs[NSC];
-  int ks0 = 0;  // first K stage of the current item's split (0 without splits)
+  int ks0 = 0;   // first K stage of the current item's split (0 without splits)
+  int sk_t = 0;  // stream-K: the item's tile, as a position among the stream-K tiles
   // tile coordinates of sequence position l (groups of 8 tile-rows) and its DMA offsets
   auto set_tile = [&](int l) {
     int tm, tn;
-    if constexpr (QUARTERS) {
+    if constexpr (SK) {
+      // stream-K: l is a stage of the sequence; the segment runs to its tile's end or
+      // to the end of this workgroup's range
+      sk_t = l / zst;
+      ks0 = l - sk_t * zst;
+      nst_new = min(zst - ks0, Lend - l);
+      tile_at(p.split_first + sk_t, num_m, num_n, tm, tn);
+      m0 = int64_t(tm) * BM;
+      n0 = int64_t(tn) * BN;
+    } else if constexpr (QUARTERS) {
       tile_at(p.tail_first + (l >> 2), num_m, num_n, tm, tn);
       m0 = int64_t(tm) * 256 + BM * ((l >> 1) & 1);
       n0 = int64_t(tn) * 256 + BN * (l & 1);
@@ -486,7 +513,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       static_assert(QUARTERS || (BM == 256 && BN == 256), "tile grid of 256x256");
       // work item l: K split l % ksplit of tile l / ksplit, its first stage ks0
       const int t = l / p.ksplit;
-      ks0 = (l - t * p.ksplit) * nst;
+      ks0 = (l - t * p.ksplit) * nst_new;
       tile_at(p.split_first + t, num_m, num_n, tm, tn);
       m0 = int64_t(tm) * BM;
       n0 = int64_t(tn) * BN;
@@ -687,21 +714,23 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   // buffers alternate with par, the buffer of the tile's stage 0, when the stage
   // count is odd.
   set_tile(L);
+  int nst_cur = nst_new;  // K stages of the current item (the tile's, or the split's, or the segment's)
   int par = 0;
   bool first = true;  // no epilogue stores in flight yet
   float amx = 0.0f;   // with p.amax_bits: max |C| over this lane's stored elements
   issue(0, 0);
-  issue(min(1, nst - 1), 1);
+  issue(min(1, nst_cur - 1), 1);
   // the first stage's DMA has landed; the second stage's NDMA loads (issued last,
   // vector memory operations retire in order) stay in flight until quarter 3's wait
-  if (nst >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
+  if (nst_cur >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (;;) {
     // stage 0 of this tile is in buffer par and visible to every wave
     const int64_t mc = m0, nc = n0;
-    const int Lcur = L;
-    const int Lnext = L + Lstride;
+    const int Lcur = L, ks0c = ks0, tc = sk_t;
+    const int nst = nst_cur;
+    const int Lnext = SK ? L + nst : L + Lstride;
     const bool more = Lnext < Lend;
     // quarter 0 of stage 0 and the operands of its first substep
 #pragma unroll
@@ -739,14 +768,19 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       if (nst >= 2) {
         issue(1, par_next ^ 1);
       } else {
+        // a one-stage item loaded nothing ahead: the next item's first stage, and its
+        // second when it has one (a stream-K segment after a one-stage segment)
         set_tile(Lnext);
         issue(0, par_next);
+        if (nst_new >= 2) issue(1, par_next ^ 1);
       }
     }
-    if (!QUARTERS && p.ksplit > 1) {
+    const bool raw = SK ? !(ks0c == 0 && nst == zst) : (!QUARTERS && p.ksplit > 1);
+    if (raw) {
       // raw partial tile (no decode scales) into the item's 256x256 slot of the workspace
+      // (stream-K: slot r + t of this workgroup's range r and the segment's tile t)
       GemmParams pp = p;
-      pp.c = p.ws + int64_t(Lcur) * (256 * 256);
+      pp.c = p.ws + int64_t(SK ? sk_r + tc : Lcur) * (256 * 256);
       pp.ldc = 256;
       pp.c_bf16 = 0;
       pp.acc_c = 0;
@@ -758,14 +792,15 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
     }
     if (!more) break;
     if (nst == 1) {
-      // a one-stage tile's first stage was only just issued
+      // a one-stage tile's first stage (and second) was only just issued
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
     L = Lnext;
     par = par_next;
     first = false;
-    if (nst < 3) {
+    nst_cur = nst_new;
+    if (nst_cur < 3) {  // the next item's first stage does not start its accumulators
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -929,6 +964,53 @@ unsigned compute_units() {
   return n;
 }
 
+// Stream-K reduction: the workgroups of the stream-K launch (G = tiles_main of them)
+// own ranges [r T/G, (r+1) T/G) of the T = sk_total stages of the stream-K tiles;
+// tile t (stages [t Z, (t+1) Z)) whose stages one range holds was stored by that
+// workgroup, any other is the sum, in range order, of the raw segments in slots
+// r + t of the ranges r that share it, times the two tensor decode scales.
+// Workgroup b covers 16 rows of tile b / 16; each thread four groups of 4 columns.
+__global__ __launch_bounds__(256) void streamk_reduce_kernel(GemmParams p) {
+  const int t = blockIdx.x >> 4, r0 = (blockIdx.x & 15) * 16;
+  const int64_t G = p.tiles_main, Z = p.K / 256, total = p.sk_total;
+  auto start = [&](int64_t r) { return total * r / G; };
+  auto find = [&](int64_t u) {  // the range holding stage u
+    int64_t r = u * G / total;
+    while (r + 1 < G && start(r + 1) <= u) ++r;
+    while (start(r) > u) --r;
+    return r;
+  };
+  const int64_t lo = find(int64_t(t) * Z), hi = find(int64_t(t + 1) * Z - 1);
+  if (lo == hi) return;
+  const int num_m = int((p.M + 255) / 256), num_n = int((p.N + 255) / 256);
+  int tm, tn;
+  tile_at(p.split_first + t, num_m, num_n, tm, tn);
+  const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int f = threadIdx.x + 256 * i;  // float4 index within the 16 x 256 block
+    const int r = r0 + (f >> 6), c = (f & 63) * 4;
+    const int64_t m = int64_t(tm) * 256 + r, n = int64_t(tn) * 256 + c;
+    float4 v = *reinterpret_cast<const float4 *>(p.ws + (lo + t) * (256 * 256) + r * 256 + c);
+    for (int64_t rr = lo + 1; rr <= hi; ++rr) {
+      const float4 w = *reinterpret_cast<const float4 *>(p.ws + (rr + t) * (256 * 256) + r * 256 + c);
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    if (m >= p.M || n >= p.N) continue;  // N % 4 == 0: a group of 4 columns is inside or outside
+    if (p.c_bf16) {
+      const bf16x4 h = {(__bf16)(v.x * gscale), (__bf16)(v.y * gscale), (__bf16)(v.z * gscale),
+                        (__bf16)(v.w * gscale)};
+      *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = h;
+    } else {
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
+          make_float4(v.x * gscale, v.y * gscale, v.z * gscale, v.w * gscale);
+    }
+  }
+}
+
 // Split-K reduction: C tile split_first + t = (sum over s of partial tile
 // t * ksplit + s, in split order) times the two tensor decode scales, converted and
 // stored.  Workgroup b
@@ -996,12 +1078,14 @@ unsigned tiles_for(const GemmParams &p) {
 // K), or of the last round's tiles only, after the whole rounds (in place of the
 // quarters).  A split is taken when it saves at least 5% of the time it replaces.
 struct SplitPlan {
-  int ksplit = 1;     // S (1: no split)
-  int64_t first = 0;  // first split tile, in the grouped tile order
-  int64_t tiles = 0;  // split tiles
+  int ksplit = 1;        // S (1: no split)
+  int64_t first = 0;     // first split tile, in the grouped tile order
+  int64_t tiles = 0;     // split tiles
+  bool streamk = false;  // the split tiles run as stream-K instead (ksplit 1)
+  int64_t sk_grid = 0;   // stream-K: workgroups (ranges)
 };
 
-SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus) {
+SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus, bool allow_sk = true) {
   SplitPlan none;
   if (K < 256 || K % 256 != 0 || M <= 0 || N <= 0) return none;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256), z = K / 256;
@@ -1035,6 +1119,20 @@ SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus) {
       }
     }
   }
+  // Stream-K over the tiles after the whole rounds: every CU an equal run of their
+  // stages (at least 8), about 2.5 stages of restarts per run, and the partial tiles
+  // (at most one per run and tile boundary) written and read back.
+  if (allow_sk && rest > 0 && z >= 8 && rest * z >= 8 * int64_t(cus)) {
+    const int64_t total = rest * z, g = cus;
+    const double c = double((total + g - 1) / g) + 2.5 + double(g + rest) * tile_bytes * 2.0 / bw / stage_s;
+    if (double(full * z) + c < 0.95 * best_cost) {
+      best = SplitPlan{};
+      best.streamk = true;
+      best.first = full * cus;
+      best.tiles = rest;
+      best.sk_grid = g;
+    }
+  }
   return best;
 }
 
@@ -1051,6 +1149,7 @@ hipError_t launch_tiles(bool exact, const dim3 &grid, hipStream_t stream, const 
 }
 
 size_t splitk_ws_bytes(const SplitPlan &sp) {
+  if (sp.streamk) return size_t(sp.sk_grid + sp.tiles) * 256 * 256 * sizeof(float);  // slots r + t
   return sp.ksplit <= 1 ? 0 : size_t(sp.tiles) * size_t(sp.ksplit) * 256 * 256 * sizeof(float);
 }
 
@@ -1077,6 +1176,8 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
   p.ksplit = 1;
   p.split_first = 0;
   p.ws = nullptr;
+  p.sk_total = 0;
+  p.sk_tiles = 0;
   p.acc_c = acc_c && !p.c_bf16;
   p.beta = beta;
   p.amax_bits = p.acc_c ? amax_bits : nullptr;
@@ -1093,7 +1194,30 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
                          (!p.acc_c || ldc * 4 * 128 < (int64_t(1) << 31));
   if (main_path && ws) {
     const unsigned cus = compute_units();
-    const SplitPlan sp = splitk_plan(p.M, p.N, p.K, cus);
+    // stream-K stores raw segments and sums them afterwards; an accumulated C takes
+    // the split plan
+    const SplitPlan sp = splitk_plan(p.M, p.N, p.K, cus, !p.acc_c);
+    if (sp.streamk && ws_bytes >= splitk_ws_bytes(sp) && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
+      // whole rounds of tiles in the usual persistent launch, then the rest as
+      // stream-K, and one reduction launch for the tiles that runs share
+      const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
+      hipError_t e = hipSuccess;
+      if (sp.first > 0) {
+        p.tiles_main = int(sp.first);
+        e = launch_tiles<256, 256, false>(exact, dim3(cus), stream, p);
+      }
+      p.split_first = int(sp.first);
+      p.ws = static_cast<float *>(ws);
+      p.sk_tiles = int(sp.tiles);
+      p.sk_total = sp.tiles * (p.K / 256);
+      p.tiles_main = int(sp.sk_grid);
+      const dim3 grid(unsigned(sp.sk_grid));
+      if (e == hipSuccess)
+        e = exact ? launch(gemm_kernel<256, 256, 2, 2, false, false, false, true>, grid, dim3(256), stream, p)
+                  : launch(gemm_kernel<256, 256, 2, 2, true, false, false, true>, grid, dim3(256), stream, p);
+      if (e == hipSuccess) e = launch(streamk_reduce_kernel, dim3(unsigned(sp.tiles) * 16), dim3(256), stream, p);
+      return e;
+    }
     if (sp.ksplit > 1 && ws_bytes >= splitk_ws_bytes(sp) && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
       // whole tiles before the split ones (if any) in the usual persistent launch; then
       // every split tile as ksplit work items of K / ksplit writing partial tiles into

@@ -151,6 +151,48 @@ def test_ldc_larger_than_n(fp4, oracle):
     check_gemm(y[:, :60], y_ref, bound, False, "ldc")
 
 
+STREAMK_CASES = [
+    # (M, N, K, a2d, sampled rows or None, stream-K tiles, tiles before them):
+    (2560, 2560, 16384, False, None, 100, 0),     # 100 tiles, runs of 25 stages (some 1- and 2-stage segments)
+    (384, 4224, 16384, True, None, 34, 0),        # ragged rows, 2D-scaled A
+    (4224, 5760, 8192, False, 96, 135, 256),      # one whole round, then 135 tiles as stream-K
+]
+
+
+@pytest.mark.parametrize("case", STREAMK_CASES, ids=lambda c: "x".join(map(str, c[:3])))
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_gemm_stream_k(fp4, oracle, case, out_dtype):
+    """fp4_gemm_ws with a stream-K plan: 256 workgroups each take an equal run of
+    the stream-K tiles' stages, store the tiles they hold whole, and leave the rest
+    as raw segments that a reduction sums in order.  Against the oracle within the
+    GEMM tolerance (all rows, or sampled ones at the largest shape), twice on one
+    workspace, and unsplit with too small a workspace."""
+    M, N, K, a2d, nrows, sk_tiles, first = case
+    need = fp4.fp4_gemm_ws_bytes(M, N, K)
+    assert need == (256 + sk_tiles) * 256 * 256 * 4, need
+    assert ((M + 255) // 256) * ((N + 255) // 256) == first + sk_tiles
+    qa, qb = oracle_operands(oracle, M, N, K, seed=M + 2 * N + K, a2d=a2d, a_kind="laplace")
+    a, b = upload_q(fp4, qa), upload_q(fp4, qb)
+    rows = np.arange(M) if nrows is None else np.sort(np.random.default_rng(M).choice(M, nrows, replace=False))
+    if nrows is not None:
+        rows = np.union1d(rows, [0, M - 1])  # the first and last tile rows too
+    qa_rows = oracle.QTensor(qa.codes[rows], qa.scales[rows // 16] if a2d else qa.scales[rows], qa.amax,
+                             len(rows), qa.K, False)
+    y_ref, bound = oracle.gemm_ref(qa_rows, qb)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        c = torch.full((M, N), float("nan"), dtype=out_dtype, device="cuda")
+        fp4.fp4_gemm_ws(a, b, c, ws)
+        torch.cuda.synchronize()
+        check_gemm(c.float().cpu().numpy()[rows], y_ref, bound, out_dtype == torch.bfloat16,
+                   f"stream-K {case} rep {rep}")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=out_dtype, device="cuda")
+    fp4.fp4_gemm_ws(a, b, c, small)
+    torch.cuda.synchronize()
+    check_gemm(c.float().cpu().numpy()[rows], y_ref, bound, out_dtype == torch.bfloat16, f"small workspace {case}")
+
+
 SPLITK_CASES = [
     # (M, N, K, a2d, b2d, split tiles, splits): every tile split (few tiles, long K), or
     # only the tiles past the whole rounds of a 256-CU GPU (in place of quarters)

@@ -115,16 +115,18 @@ def test_gemm_ws_rejects_bad_arguments(lib):
 
 def test_gemm_ws_bytes_follows_the_split_plan(lib):
     """The split plan on a 256-CU GPU (the host query falls back to 256 without a
-    device): which products split, and the workspace = split tiles x splits x 256 KB."""
+    device): which products split, and the workspace = split tiles x splits x 256 KB;
+    under a round of long-K tiles takes stream-K instead, whose workspace holds a
+    256 KB slot per run (256) plus one per stream-K tile."""
     n = ctypes.c_size_t()
     tile = 256 * 256 * 4
 
     def need(M, N, K):
         assert lib.fp4_gemm_ws_bytes(M, N, K, ctypes.byref(n)) == 0
         return n.value
-    assert need(3072, 3072, 32768) == 144 * 8 * tile    # 144 tiles, every one in 8
-    assert need(8192, 3072, 32768) == 128 * 2 * tile    # 384 tiles: the last 128 in 2
-    assert need(9216, 3072, 32768) == 176 * 4 * tile    # 432 tiles: the last 176 in 4
+    assert need(3072, 3072, 32768) == (256 + 144) * tile  # 144 tiles: stream-K over all
+    assert need(8192, 3072, 32768) == 128 * 2 * tile      # 384 tiles: the last 128 in 2
+    assert need(9216, 3072, 32768) == (256 + 176) * tile  # 432 tiles: the last 176 as stream-K
     assert need(20480, 5120, 16384) == 64 * 4 * tile    # 1600 tiles: the last 64 in 4
     assert need(16384, 20480, 5120) == 0                # 20 whole rounds
     assert need(8192, 4096, 4096) == 0                  # 2 whole rounds
@@ -161,7 +163,8 @@ def test_linear_rejects_bad_arguments(lib):
 def test_gemm_noalloc_rejects_before_touching_the_device(lib):
     """fp4_gemm_noalloc checks its arguments and the static scratch limit on the
     host: a shape whose split plan needs more than 64 MiB (the 3B block's O-projection
-    wgrad, 144 tiles in 8 splits = 288 MiB) is rejected with FP4_ERR_WORKSPACE."""
+    wgrad, 144 tiles as stream-K over 256 runs = 100 MiB) is rejected with
+    FP4_ERR_WORKSPACE."""
     import nvfp4_bit_microscaled_amd as m
     Q = ctypes.byref
     c = ctypes.c_void_p(0x100000)
