@@ -218,9 +218,12 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, f
  * weight), each tile's K range is split into S parts that run as separate work
  * items writing raw fp32 partial tiles into ws, and a second kernel sums the S
  * partials of each tile in split order, applies the decode scales and writes C.
- * The split adds S-1 fp32 additions per output.  S comes from a fixed plan of
- * (M, N, K) on this GPU; fp4_gemm_ws_bytes gives the workspace the plan needs (0
- * when it takes no split).  With ws_bytes below that, or a shape off the 256-K main
+ * The split adds S-1 fp32 additions per output.  When under a round of tiles
+ * remains, the plan may run them as stream-K instead: each CU an equal run of the
+ * tiles' K stages, tiles held whole by one run stored directly, the others' raw
+ * segments (one 256 KB slot per run and tile it touches) summed in run order by
+ * the second kernel.  The plan is fixed for (M, N, K) on this GPU;
+ * fp4_gemm_ws_bytes gives the workspace it needs (0 when it takes no split).  With ws_bytes below that, or a shape off the 256-K main
  * path, this is fp4_gemm.
  * ws: device memory, 16-byte aligned, owned by the caller, overwritten; calls that
  * share a workspace must be ordered on one stream.  Errors: as fp4_gemm, plus
