@@ -223,8 +223,10 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, f
  * tiles' K stages, tiles held whole by one run stored directly, the others' raw
  * segments (one 256 KB slot per run and tile it touches) summed in run order by
  * the second kernel.  The plan is fixed for (M, N, K) on this GPU;
- * fp4_gemm_ws_bytes gives the workspace it needs (0 when it takes no split).  With ws_bytes below that, or a shape off the 256-K main
- * path, this is fp4_gemm.
+ * fp4_gemm_ws_bytes gives the workspace it needs (0 when it takes no split).  A
+ * stream-K plan given less workspace than that runs the shape's fixed split when it
+ * fits; with less than the plan needs, or a shape off the 256-K main path, this is
+ * fp4_gemm.
  * ws: device memory, 16-byte aligned, owned by the caller, overwritten; calls that
  * share a workspace must be ordered on one stream.  Errors: as fp4_gemm, plus
  * FP4_ERR_NULL / FP4_ERR_ALIGN for a non-empty workspace that is NULL / misaligned. */
@@ -238,10 +240,11 @@ FP4_API fp4_status fp4_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c
  * on that GPU until the process ends; this call allocates nothing.  Every call on
  * one GPU shares that GPU's array, so calls that overlap on one GPU (different
  * streams, or different host threads without ordering) race; calls ordered on one
- * stream do not.  A shape whose split-K plan needs more than the maximum (see
+ * stream do not.  A stream-K plan whose slots exceed the maximum gives way to the
+ * shape's fixed split; a shape whose plan still needs more than the maximum (see
  * fp4_gemm_ws_bytes) returns FP4_ERR_WORKSPACE and enqueues nothing (fp4_gemm runs
  * any shape without scratch).  Otherwise the result is that of fp4_gemm_ws with a
- * workspace of fp4_gemm_ws_bytes.  Errors: as fp4_gemm_ws, plus FP4_ERR_WORKSPACE. */
+ * workspace of the maximum.  Errors: as fp4_gemm_ws, plus FP4_ERR_WORKSPACE. */
 #define FP4_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 FP4_API fp4_status fp4_gemm_noalloc(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                                     hipStream_t stream);

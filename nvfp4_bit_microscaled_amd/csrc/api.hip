@@ -158,7 +158,9 @@ fp4_status fp4_gemm_noalloc(const fp4_tensor *a, const fp4_tensor *b, void *c, f
                             hipStream_t stream) {
   fp4_status s = check_gemm(a, b, c, c_dtype, ldc);
   if (s != FP4_OK) return s;
-  if (nvfp4::gemm_ws_bytes(a->rows, b->rows, a->cols) > nvfp4::kStaticScratchBytes) return FP4_ERR_WORKSPACE;
+  if (nvfp4::gemm_ws_bytes_within(a->rows, b->rows, a->cols, nvfp4::kStaticScratchBytes) >
+      nvfp4::kStaticScratchBytes)
+    return FP4_ERR_WORKSPACE;
   void *scratch = nullptr;
   hipError_t e = nvfp4::static_scratch(&scratch);
   if (e != hipSuccess) return FP4_ERR_HIP;

@@ -1196,8 +1196,9 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
     const unsigned cus = compute_units();
     // stream-K stores raw segments and sums them afterwards; an accumulated C takes
     // the split plan
-    const SplitPlan sp = splitk_plan(p.M, p.N, p.K, cus, !p.acc_c);
-    if (sp.streamk && ws_bytes >= splitk_ws_bytes(sp) && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
+    SplitPlan sp = splitk_plan(p.M, p.N, p.K, cus, !p.acc_c);
+    if (sp.streamk && ws_bytes < splitk_ws_bytes(sp)) sp = splitk_plan(p.M, p.N, p.K, cus, false);  // too small
+    if (sp.streamk && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
       // whole rounds of tiles in the usual persistent launch, then the rest as
       // stream-K, and one reduction launch for the tiles that runs share
       const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
@@ -1315,6 +1316,12 @@ hipError_t launch_gemm_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
   return splitk_ws_bytes(splitk_plan(M, N, K, compute_units()));
+}
+
+size_t gemm_ws_bytes_within(int64_t M, int64_t N, int64_t K, size_t limit) {
+  const unsigned cus = compute_units();
+  const size_t b = splitk_ws_bytes(splitk_plan(M, N, K, cus));
+  return b <= limit ? b : splitk_ws_bytes(splitk_plan(M, N, K, cus, false));
 }
 
 }  // namespace nvfp4

@@ -99,6 +99,9 @@ hipError_t launch_gemm_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c
                               float *amax, void *ws, size_t ws_bytes, hipStream_t stream);
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+// The workspace of the plan launch_gemm_ws runs with `limit` bytes: the stream-K
+// plan's when it fits, else the fixed split's (which may still exceed the limit).
+size_t gemm_ws_bytes_within(int64_t M, int64_t N, int64_t K, size_t limit);
 
 // Size of the library's static split-K scratch (fp4_gemm_noalloc), per GPU.
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;
