@@ -284,7 +284,8 @@ fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, c
 static size_t ns_max_slot(int64_t m, int64_t n) {
   size_t w = nvfp4::normalize_scratch_bytes();
   if (nvfp4::axpby_partial_bytes() > w) w = nvfp4::axpby_partial_bytes();
-  const size_t g[3] = {nvfp4::gemm_ws_bytes(m, m, n), nvfp4::gemm_ws_bytes(m, m, m), nvfp4::gemm_ws_bytes(m, n, m)};
+  const size_t g[5] = {nvfp4::gemm_ws_bytes(m, m, n), nvfp4::gemm_ws_bytes(m, m, m), nvfp4::gemm_ws_bytes(m, n, m),
+                       nvfp4::gemm_ws_bytes_sym(m, n), nvfp4::gemm_ws_bytes_sym(m, m)};
   for (size_t v : g) w = v > w ? v : w;
   return (w + 255) / 256 * 256;
 }
@@ -412,12 +413,16 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
     } else {
       e = q_pair(x, n, o + 0, o + 1, &bufs->x_left, &bufs->x_right);
     }
+    // with one quantization on both sides X X^T and A A^T are exactly symmetric: the
+    // GEMM computes the tiles on and above the diagonal and mirrors them
     if (e == hipSuccess)
-      e = nvfp4::launch_gemm_ws(&bufs->x_left, xr, bufs->a, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
+      e = same ? nvfp4::launch_gemm_sym_ws(&bufs->x_left, xr, bufs->a, m, bufs->ws, bufs->ws_bytes, stream)
+               : nvfp4::launch_gemm_ws(&bufs->x_left, xr, bufs->a, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
     if (e == hipSuccess) e = same ? q(bufs->a, m, m, fl, o + 2, &bufs->a_left)
                                   : q_pair(bufs->a, m, o + 2, o + 3, &bufs->a_left, &bufs->a_right);
     if (e == hipSuccess)
-      e = nvfp4::launch_gemm_ws(&bufs->a_left, ar, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
+      e = same ? nvfp4::launch_gemm_sym_ws(&bufs->a_left, ar, bufs->b, m, bufs->ws, bufs->ws_bytes, stream)
+               : nvfp4::launch_gemm_ws(&bufs->a_left, ar, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
     if (same) {
       if (e == hipSuccess) e = nvfp4::launch_axpby_amax(cfg->b, bufs->a, cfg->c, bufs->b, m * m, partial, stream);
       if (e == hipSuccess)

@@ -84,6 +84,8 @@ struct GemmParams {
                         // bits of a non-negative float (those order as unsigned integers)
   int64_t sk_total;     // stream-K: stages of the stream-K tiles (tiles split_first .. + sk_tiles)
   int sk_tiles;
+  int sym;              // C = A B^T is symmetric (M = N, the same operand on both sides): only the
+                        // tiles on and above the diagonal, in the triangle order of tri_at
 };
 
 // Wave-wide maximum of a non-negative lane value, merged into *bits by an atomic
@@ -113,6 +115,27 @@ __device__ __forceinline__ void tile_at(int l, int num_m, int num_n, int &tm, in
   const int gsz = min(num_m - first_m, kGroupM);
   tm = first_m + (l % per_group) % gsz;
   tn = (l % per_group) / gsz;
+}
+
+// Position l of the triangle order: (r, c) with c <= r, row by row (r = 0: (0, 0);
+// r = 1: (1, 0), (1, 1); ...).
+__device__ __forceinline__ void tri_at(int64_t l, int &r, int &c) {
+  int64_t i = int64_t((__builtin_sqrt(8.0 * double(l) + 1.0) - 1.0) * 0.5);
+  while ((i + 1) * (i + 2) / 2 <= l) ++i;
+  while (i * (i + 1) / 2 > l) --i;
+  r = int(i);
+  c = int(l - i * (i + 1) / 2);
+}
+
+// Tile (tm, tn) at position l of the launch's sequence: the grouped order, or for a
+// symmetric C the upper triangle column by column (tn = r, tm = c of tri_at:
+// neighbouring positions share B's tile).
+__device__ __forceinline__ void seq_tile(const GemmParams &p, int l, int num_m, int num_n, int &tm, int &tn) {
+  if (p.sym) {
+    tri_at(l, tn, tm);
+  } else {
+    tile_at(l, num_m, num_n, tm, tn);
+  }
 }
 
 // Tile coordinates of this workgroup (see the header comment).
@@ -448,7 +471,8 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
   // 256x256 tiles: a prefix of the grouped order.  Quarters: the four 128x128
   // quarters of each later 256x256 tile, in that order.
   const int num_m = int((M + 255) / 256), num_n = int((N + 255) / 256);
-  const int ntiles = QUARTERS ? 4 * (num_m * num_n - p.tail_first) : p.tiles_main;
+  const int all_tiles = p.sym ? num_m * (num_m + 1) / 2 : num_m * num_n;
+  const int ntiles = QUARTERS ? 4 * (all_tiles - p.tail_first) : p.tiles_main;
   int L, Lend, Lstride;
   int sk_r = 0;  // stream-K: this workgroup's range
   if constexpr (SK) {
@@ -502,11 +526,11 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       sk_t = l / zst;
       ks0 = l - sk_t * zst;
       nst_new = min(zst - ks0, Lend - l);
-      tile_at(p.split_first + sk_t, num_m, num_n, tm, tn);
+      seq_tile(p, p.split_first + sk_t, num_m, num_n, tm, tn);
       m0 = int64_t(tm) * BM;
       n0 = int64_t(tn) * BN;
     } else if constexpr (QUARTERS) {
-      tile_at(p.tail_first + (l >> 2), num_m, num_n, tm, tn);
+      seq_tile(p, p.tail_first + (l >> 2), num_m, num_n, tm, tn);
       m0 = int64_t(tm) * 256 + BM * ((l >> 1) & 1);
       n0 = int64_t(tn) * 256 + BN * (l & 1);
     } else {
@@ -514,7 +538,7 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       // work item l: K split l % ksplit of tile l / ksplit, its first stage ks0
       const int t = l / p.ksplit;
       ks0 = (l - t * p.ksplit) * nst_new;
-      tile_at(p.split_first + t, num_m, num_n, tm, tn);
+      seq_tile(p, p.split_first + t, num_m, num_n, tm, tn);
       m0 = int64_t(tm) * BM;
       n0 = int64_t(tn) * BN;
     }
@@ -984,7 +1008,7 @@ __global__ __launch_bounds__(256) void streamk_reduce_kernel(GemmParams p) {
   if (lo == hi) return;
   const int num_m = int((p.M + 255) / 256), num_n = int((p.N + 255) / 256);
   int tm, tn;
-  tile_at(p.split_first + t, num_m, num_n, tm, tn);
+  seq_tile(p, p.split_first + t, num_m, num_n, tm, tn);
   const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1011,6 +1035,30 @@ __global__ __launch_bounds__(256) void streamk_reduce_kernel(GemmParams p) {
   }
 }
 
+// C[i][j] = C[j][i] for i > j of an n x n fp32 C (row stride ldc): after a symmetric
+// product, whose tiles on and above the diagonal hold C, the lower triangle copied
+// from the upper one through LDS.  Workgroup b takes the 32x32 block (bi, bj) at
+// position b of tri_at (bj <= bi).
+__global__ __launch_bounds__(256) void mirror_lower_kernel(float *c, int64_t n, int64_t ldc) {
+  __shared__ float t[32][33];
+  int bi, bj;
+  tri_at(blockIdx.x, bi, bj);
+  const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;  // 8 rows per pass
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int y = y0 + 8 * k;
+    const int64_t r = int64_t(bj) * 32 + y, col = int64_t(bi) * 32 + x;  // the upper block (bj, bi)
+    if (r < n && col < n) t[y][x] = c[r * ldc + col];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int y = y0 + 8 * k;
+    const int64_t r = int64_t(bi) * 32 + y, col = int64_t(bj) * 32 + x;  // the lower block (bi, bj)
+    if (r < n && col < n && r > col) c[r * ldc + col] = t[x][y];
+  }
+}
+
 // Split-K reduction: C tile split_first + t = (sum over s of partial tile
 // t * ksplit + s, in split order) times the two tensor decode scales, converted and
 // stored.  Workgroup b
@@ -1019,7 +1067,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
   const int num_m = int((p.M + 255) / 256), num_n = int((p.N + 255) / 256);
   const int t = blockIdx.x >> 4, r0 = (blockIdx.x & 15) * 16;  // t: the t-th split tile
   int tm, tn;
-  tile_at(p.split_first + t, num_m, num_n, tm, tn);
+  seq_tile(p, p.split_first + t, num_m, num_n, tm, tn);
   const float gscale = decode_scale(*p.a_amax) * decode_scale(*p.b_amax);
   const float *part = p.ws + int64_t(t) * p.ksplit * (256 * 256);
   float mx = 0.0f;
@@ -1085,10 +1133,11 @@ struct SplitPlan {
   int64_t sk_grid = 0;   // stream-K: workgroups (ranges)
 };
 
-SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus, bool allow_sk = true) {
+SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus, bool allow_sk = true, bool sym = false) {
   SplitPlan none;
   if (K < 256 || K % 256 != 0 || M <= 0 || N <= 0) return none;
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256), z = K / 256;
+  const int64_t nm = (M + 255) / 256;
+  const int64_t tiles = sym ? nm * (nm + 1) / 2 : nm * ((N + 255) / 256), z = K / 256;
   const int64_t full = tiles / cus, rest = tiles % cus;
   const bool quarters = full > 0 && rest > 0 && rest <= int64_t(cus) / 2;
   const double tail = rest == 0 ? 0.0 : quarters ? double((4 * rest + cus - 1) / cus) * (double(z) / 4.0) / 0.6
@@ -1155,7 +1204,7 @@ size_t splitk_ws_bytes(const SplitPlan &sp) {
 
 hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                             void *ws, size_t ws_bytes, hipStream_t stream, bool acc_c = false,
-                            float beta = 0.0f, unsigned *amax_bits = nullptr) {
+                            float beta = 0.0f, unsigned *amax_bits = nullptr, bool *sym = nullptr) {
   GemmParams p;
   p.a_codes = a->codes;
   p.a_scales = a->scales;
@@ -1178,6 +1227,7 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
   p.ws = nullptr;
   p.sk_total = 0;
   p.sk_tiles = 0;
+  p.sym = 0;
   p.acc_c = acc_c && !p.c_bf16;
   p.beta = beta;
   p.amax_bits = p.acc_c ? amax_bits : nullptr;
@@ -1192,12 +1242,16 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
                          (p.N + 256) * (p.K / 2) < (int64_t(1) << 32) &&
                          al(c, 16) && ldc % (p.c_bf16 ? 8 : 4) == 0 && p.N % 4 == 0 &&
                          (!p.acc_c || ldc * 4 * 128 < (int64_t(1) << 31));
+  // a symmetric C: the main path computes the tiles on and above the diagonal (the
+  // caller mirrors the rest); elsewhere the whole product
+  p.sym = sym && *sym && main_path && p.M == p.N && !p.acc_c && !p.c_bf16;
+  if (sym) *sym = p.sym;
   if (main_path && ws) {
     const unsigned cus = compute_units();
     // stream-K stores raw segments and sums them afterwards; an accumulated C takes
     // the split plan
-    SplitPlan sp = splitk_plan(p.M, p.N, p.K, cus, !p.acc_c);
-    if (sp.streamk && ws_bytes < splitk_ws_bytes(sp)) sp = splitk_plan(p.M, p.N, p.K, cus, false);  // too small
+    SplitPlan sp = splitk_plan(p.M, p.N, p.K, cus, !p.acc_c, p.sym);
+    if (sp.streamk && ws_bytes < splitk_ws_bytes(sp)) sp = splitk_plan(p.M, p.N, p.K, cus, false, p.sym);  // too small
     if (sp.streamk && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
       // whole rounds of tiles in the usual persistent launch, then the rest as
       // stream-K, and one reduction launch for the tiles that runs share
@@ -1248,7 +1302,8 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
     // those last tiles would keep some CUs busy for a full tile time while the
     // rest idle; they go instead, as four 128x128 quarters each (one or two per
     // CU, a quarter of the time each), to a second persistent launch.
-    const unsigned tiles = tiles_for<256, 256>(p), cus = compute_units();
+    const int64_t nm = (p.M + 255) / 256;
+    const unsigned tiles = p.sym ? unsigned(nm * (nm + 1) / 2) : tiles_for<256, 256>(p), cus = compute_units();
     const unsigned rest = tiles % cus;
     const bool split = tiles > cus && rest > 0 && rest <= cus / 2;
     p.tiles_main = int(split ? tiles - rest : tiles);
@@ -1316,6 +1371,19 @@ hipError_t launch_gemm_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
   return splitk_ws_bytes(splitk_plan(M, N, K, compute_units()));
+}
+
+size_t gemm_ws_bytes_sym(int64_t M, int64_t K) {
+  return splitk_ws_bytes(splitk_plan(M, M, K, compute_units(), true, true));
+}
+
+hipError_t launch_gemm_sym_ws(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, void *ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  bool sym = true;
+  hipError_t e = launch_gemm_impl(a, b, c, FP4_FP32, ldc, ws, ws_bytes, stream, false, 0.0f, nullptr, &sym);
+  if (e != hipSuccess || !sym) return e;
+  const int64_t nb = (a->rows + 31) / 32;
+  return launch(mirror_lower_kernel, dim3(unsigned(nb * (nb + 1) / 2)), dim3(256), stream, c, a->rows, ldc);
 }
 
 size_t gemm_ws_bytes_within(int64_t M, int64_t N, int64_t K, size_t limit) {
