@@ -284,8 +284,15 @@ fp4_status fp4_linear_backward(const void *dy, const void *x, fp4_dtype dtype, c
 static size_t ns_max_slot(int64_t m, int64_t n) {
   size_t w = nvfp4::normalize_scratch_bytes();
   if (nvfp4::axpby_partial_bytes() > w) w = nvfp4::axpby_partial_bytes();
-  const size_t g[5] = {nvfp4::gemm_ws_bytes(m, m, n), nvfp4::gemm_ws_bytes(m, m, m), nvfp4::gemm_ws_bytes(m, n, m),
-                       nvfp4::gemm_ws_bytes_sym(m, n), nvfp4::gemm_ws_bytes_sym(m, m)};
+  // every product's plan: X X^T, A A^T and B X whole, X X^T symmetric, and the
+  // accumulated ones (no stream-K): A A^T symmetric into B, B X into X
+  const size_t g[7] = {nvfp4::gemm_ws_bytes(m, m, n),
+                       nvfp4::gemm_ws_bytes(m, m, m),
+                       nvfp4::gemm_ws_bytes(m, n, m),
+                       nvfp4::gemm_ws_bytes_sym(m, n),
+                       nvfp4::gemm_ws_bytes_sym(m, m),
+                       nvfp4::gemm_ws_bytes_plan(m, m, m, false, true),
+                       nvfp4::gemm_ws_bytes_plan(m, n, m, false, false)};
   for (size_t v : g) w = v > w ? v : w;
   return (w + 255) / 256 * 256;
 }
@@ -420,15 +427,16 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
                : nvfp4::launch_gemm_ws(&bufs->x_left, xr, bufs->a, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
     if (e == hipSuccess) e = same ? q(bufs->a, m, m, fl, o + 2, &bufs->a_left)
                                   : q_pair(bufs->a, m, o + 2, o + 3, &bufs->a_left, &bufs->a_right);
-    if (e == hipSuccess)
-      e = same ? nvfp4::launch_gemm_sym_ws(&bufs->a_left, ar, bufs->b, m, bufs->ws, bufs->ws_bytes, stream)
-               : nvfp4::launch_gemm_ws(&bufs->a_left, ar, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
     if (same) {
-      if (e == hipSuccess) e = nvfp4::launch_axpby_amax(cfg->b, bufs->a, cfg->c, bufs->b, m * m, partial, stream);
+      // B = fl(fl(c A2) + fl(b A)) in the symmetric A A^T's epilogue (A2 = A A^T is
+      // never stored; the sum is the axpby's, operands swapped), B's amax with it
       if (e == hipSuccess)
-        e = nvfp4::launch_max_finish(partial, nvfp4::axpby_parts(m * m), bufs->b_q.amax, nullptr, stream);
+        e = nvfp4::launch_gemm_sym_ws_acc(&bufs->a_left, ar, bufs->b, m, cfg->c, cfg->b, bufs->a, bufs->b_q.amax,
+                                          bufs->ws, bufs->ws_bytes, stream);
       if (e == hipSuccess) e = q(bufs->b, m, m, fl | FP4_Q_AMAX_GIVEN, o + 4, &bufs->b_q);
     } else {
+      if (e == hipSuccess)
+        e = nvfp4::launch_gemm_ws(&bufs->a_left, ar, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
       if (e == hipSuccess) e = nvfp4::launch_axpby(cfg->b, bufs->a, cfg->c, bufs->b, m * m, stream);
       if (e == hipSuccess) e = q(bufs->b, m, m, fl, o + 4, &bufs->b_q);
       if (e == hipSuccess) e = q(x, m, n, fr | FP4_Q_COLWISE, o + 5, &bufs->xt);

@@ -78,8 +78,10 @@ struct GemmParams {
   int ksplit;      // gemm_kernel, 256x256: K splits per tile (1: none)
   int split_first; // ksplit > 1: the first split tile (the tiles before it run unsplit)
   float *ws;       // ksplit > 1: raw partial tiles [tiles_main][256][256], item t * ksplit + s
-  int acc_c;       // fp32 output only: 0 stores the product v; 1 stores C = fl(v + fl(beta * C))
-  float beta;
+  int acc_c;       // fp32 output only: 0 stores the product v; 1 stores
+                   // C = fl(fl(alpha * v) + fl(beta * S)), S the addend (acc_src, or C itself)
+  float alpha, beta;
+  const float *acc_src;  // acc_c: the addend S, with C's row stride (null: C)
   unsigned *amax_bits;  // acc_c only, or null: atomic max of |C| over the stored elements, as the
                         // bits of a non-negative float (those order as unsigned integers)
   int64_t sk_total;     // stream-K: stages of the stream-K tiles (tiles split_first .. + sk_tiles)
@@ -171,7 +173,7 @@ __device__ __forceinline__ void store_tiles(const GemmParams &p, const f32x16 (&
             reinterpret_cast<uint16_t *>(p.c)[m * p.ldc + n] = f32_to_bf16(v);
           } else {
             float *dst = reinterpret_cast<float *>(p.c) + m * p.ldc + n;
-            const float y = p.acc_c ? v + p.beta * *dst : v;
+            const float y = p.acc_c ? p.alpha * v + p.beta * (p.acc_src ? p.acc_src[m * p.ldc + n] : *dst) : v;
             *dst = y;
             mx = fmaxf(mx, __builtin_fabsf(y));
           }
@@ -227,8 +229,9 @@ __device__ __forceinline__ void static_for(F &&f) {
 // the launcher guarantees N % 4 == 0, a 16-byte aligned C and ldc % 4 == 0).
 constexpr int kEpiBytes = 4096;
 
-// fp32 accumulating epilogue, C = fl(v + fl(beta * C)), block by block as the
-// plain fp32 path.  The old C of each block is loaded kAccAhead blocks ahead
+// fp32 accumulating epilogue, C = fl(fl(alpha * v) + fl(beta * S)) with S the addend
+// (C itself, or another array of C's shape and stride), block by block as the plain
+// fp32 path.  The addend of each block is loaded kAccAhead blocks ahead
 // (kAccAheadCheck for partial tiles, whose bounds tests take registers) into
 // a ring of registers: a load issued only when its block is stored waits a whole
 // memory latency per block, with no other wave on the SIMD to cover it.  C is
@@ -247,6 +250,8 @@ __device__ __forceinline__ void store_tiles_lds_acc(const GemmParams &p, const f
   const int rq = lane >> 3, ch = lane & 7;  // read-back: row 8k + rq of the block, columns 4 ch .. +3
   const uint32_t ldb = uint32_t(p.ldc) * 4u;
   const __amdgpu_buffer_rsrc_t rs = wave_rsrc(reinterpret_cast<float *>(p.c) + m0 * p.ldc + n0);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      p.acc_src ? wave_rsrc(const_cast<float *>(p.acc_src) + m0 * p.ldc + n0) : rs;
   const uint32_t voff = uint32_t(rq) * ldb + 16u * uint32_t(ch);
   const int64_t mlim = p.M - m0, nlim = p.N - n0;
   // block b = (i, j): rows 32 i + 8 k + rq, columns 32 j + 4 ch
@@ -257,7 +262,7 @@ __device__ __forceinline__ void store_tiles_lds_acc(const GemmParams &p, const f
     constexpr int b = decltype(bc)::value, i = b / TN, j = b % TN;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (inside(i, j, k)) old[b % D][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, int(voff), soff(i, j, k), 0);
+      if (inside(i, j, k)) old[b % D][k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, int(voff), soff(i, j, k), 0);
   };
   static_for<D>(fetch);
   static_for<NB>([&](auto bc) {
@@ -279,10 +284,10 @@ __device__ __forceinline__ void store_tiles_lds_acc(const GemmParams &p, const f
       const float4 x = *reinterpret_cast<const float4 *>(region + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
       if (inside(i, j, k)) {
         const u32x4 o = old[b % D][k];
-        const float y0 = x.x * gscale + p.beta * __uint_as_float(o[0]);
-        const float y1 = x.y * gscale + p.beta * __uint_as_float(o[1]);
-        const float y2 = x.z * gscale + p.beta * __uint_as_float(o[2]);
-        const float y3 = x.w * gscale + p.beta * __uint_as_float(o[3]);
+        const float y0 = p.alpha * (x.x * gscale) + p.beta * __uint_as_float(o[0]);
+        const float y1 = p.alpha * (x.y * gscale) + p.beta * __uint_as_float(o[1]);
+        const float y2 = p.alpha * (x.z * gscale) + p.beta * __uint_as_float(o[2]);
+        const float y3 = p.alpha * (x.w * gscale) + p.beta * __uint_as_float(o[3]);
         const u32x4 y = {__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
         __builtin_amdgcn_raw_buffer_store_b128(y, rs, int(voff), soff(i, j, k), kNontemporal);
         mx = fmaxf(fmaxf(mx, fmaxf(__builtin_fabsf(y0), __builtin_fabsf(y1))),
@@ -1035,27 +1040,44 @@ __global__ __launch_bounds__(256) void streamk_reduce_kernel(GemmParams p) {
   }
 }
 
-// C[i][j] = C[j][i] for i > j of an n x n fp32 C (row stride ldc): after a symmetric
-// product, whose tiles on and above the diagonal hold C, the lower triangle copied
-// from the upper one through LDS.  Workgroup b takes the 32x32 block (bi, bj) at
-// position b of tri_at (bj <= bi).
+// The lower triangle of an n x n symmetric product, whose tiles on and above the
+// diagonal hold C, copied from the upper one through LDS.  Workgroup b takes the
+// 64x64 block (bi, bj) at position b of tri_at (bj <= bi): it reads the upper block
+// (bj, bi) as rows of 16-byte vectors, and writes its transpose below the
+// diagonal, whole vectors off the diagonal.  Needs n, ldc multiples of 4 and c
+// 16-byte aligned (the launcher checks).
 __global__ __launch_bounds__(256) void mirror_lower_kernel(float *c, int64_t n, int64_t ldc) {
-  __shared__ float t[32][33];
+  __shared__ float t[64][65];
   int bi, bj;
   tri_at(blockIdx.x, bi, bj);
-  const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;  // 8 rows per pass
+  const int x = threadIdx.x & 15, y0 = threadIdx.x >> 4;  // 16 vectors per row, 16 rows per pass
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int y = y0 + 8 * k;
-    const int64_t r = int64_t(bj) * 32 + y, col = int64_t(bi) * 32 + x;  // the upper block (bj, bi)
-    if (r < n && col < n) t[y][x] = c[r * ldc + col];
+    const int y = y0 + 16 * k;
+    const int64_t r = int64_t(bj) * 64 + y, col = int64_t(bi) * 64 + 4 * x;  // the upper block (bj, bi)
+    if (r < n && col < n) {
+      const float4 v = *reinterpret_cast<const float4 *>(c + r * ldc + col);
+      t[y][4 * x] = v.x;
+      t[y][4 * x + 1] = v.y;
+      t[y][4 * x + 2] = v.z;
+      t[y][4 * x + 3] = v.w;
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int y = y0 + 8 * k;
-    const int64_t r = int64_t(bi) * 32 + y, col = int64_t(bj) * 32 + x;  // the lower block (bi, bj)
-    if (r < n && col < n && r > col) c[r * ldc + col] = t[x][y];
+    const int y = y0 + 16 * k;
+    const int64_t r = int64_t(bi) * 64 + y, col = int64_t(bj) * 64 + 4 * x;  // the lower block (bi, bj)
+    if (r >= n || col >= n) continue;
+    const float4 v = {t[4 * x][y], t[4 * x + 1][y], t[4 * x + 2][y], t[4 * x + 3][y]};
+    float *dst = c + r * ldc + col;
+    if (col + 3 < r) {
+      *reinterpret_cast<float4 *>(dst) = v;
+    } else {  // on the diagonal block: only the elements below it
+      if (col < r) dst[0] = v.x;
+      if (col + 1 < r) dst[1] = v.y;
+      if (col + 2 < r) dst[2] = v.z;
+    }
   }
 }
 
@@ -1093,9 +1115,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
       float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n);
       float4 y = make_float4(v.x * gscale, v.y * gscale, v.z * gscale, v.w * gscale);
       if (p.acc_c) {
-        const float4 old = *dst;
+        const float4 old = p.acc_src ? *reinterpret_cast<const float4 *>(p.acc_src + m * p.ldc + n) : *dst;
         const float4 q = make_float4(p.beta * old.x, p.beta * old.y, p.beta * old.z, p.beta * old.w);
-        y = make_float4(y.x + q.x, y.y + q.y, y.z + q.z, y.w + q.w);
+        y = make_float4(p.alpha * y.x + q.x, p.alpha * y.y + q.y, p.alpha * y.z + q.z, p.alpha * y.w + q.w);
       }
       *dst = y;
       mx = fmaxf(fmaxf(mx, fmaxf(__builtin_fabsf(y.x), __builtin_fabsf(y.y))),
@@ -1204,7 +1226,8 @@ size_t splitk_ws_bytes(const SplitPlan &sp) {
 
 hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                             void *ws, size_t ws_bytes, hipStream_t stream, bool acc_c = false,
-                            float beta = 0.0f, unsigned *amax_bits = nullptr, bool *sym = nullptr) {
+                            float beta = 0.0f, unsigned *amax_bits = nullptr, bool *sym = nullptr,
+                            float alpha = 1.0f, const float *acc_src = nullptr) {
   GemmParams p;
   p.a_codes = a->codes;
   p.a_scales = a->scales;
@@ -1229,7 +1252,9 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
   p.sk_tiles = 0;
   p.sym = 0;
   p.acc_c = acc_c && !p.c_bf16;
+  p.alpha = alpha;
   p.beta = beta;
+  p.acc_src = p.acc_c ? acc_src : nullptr;
   p.amax_bits = p.acc_c ? amax_bits : nullptr;
   if (p.M == 0 || p.N == 0) return hipSuccess;
   auto al = [](const void *q, uintptr_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
@@ -1241,10 +1266,10 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
                          al(a->scales, 16) && al(b->scales, 16) && (p.M + 256) * (p.K / 2) < (int64_t(1) << 32) &&
                          (p.N + 256) * (p.K / 2) < (int64_t(1) << 32) &&
                          al(c, 16) && ldc % (p.c_bf16 ? 8 : 4) == 0 && p.N % 4 == 0 &&
-                         (!p.acc_c || ldc * 4 * 128 < (int64_t(1) << 31));
+                         (!p.acc_c || ldc * 4 * 128 < (int64_t(1) << 31)) && al(p.acc_src, 16);
   // a symmetric C: the main path computes the tiles on and above the diagonal (the
   // caller mirrors the rest); elsewhere the whole product
-  p.sym = sym && *sym && main_path && p.M == p.N && !p.acc_c && !p.c_bf16;
+  p.sym = sym && *sym && main_path && p.M == p.N && !p.c_bf16;
   if (sym) *sym = p.sym;
   if (main_path && ws) {
     const unsigned cus = compute_units();
@@ -1379,11 +1404,31 @@ size_t gemm_ws_bytes_sym(int64_t M, int64_t K) {
 
 hipError_t launch_gemm_sym_ws(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, void *ws,
                               size_t ws_bytes, hipStream_t stream) {
-  bool sym = true;
+  // the mirror moves 16-byte vectors: a symmetric product only where they line up
+  bool sym = a->rows % 4 == 0 && ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0;
   hipError_t e = launch_gemm_impl(a, b, c, FP4_FP32, ldc, ws, ws_bytes, stream, false, 0.0f, nullptr, &sym);
   if (e != hipSuccess || !sym) return e;
-  const int64_t nb = (a->rows + 31) / 32;
+  const int64_t nb = (a->rows + 63) / 64;
   return launch(mirror_lower_kernel, dim3(unsigned(nb * (nb + 1) / 2)), dim3(256), stream, c, a->rows, ldc);
+}
+
+hipError_t launch_gemm_sym_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, float alpha,
+                                  float beta, const float *src, float *amax, void *ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  unsigned *bits = reinterpret_cast<unsigned *>(amax);
+  if (bits && a->rows > 0 && b->rows > 0) {
+    const hipError_t e = launch(zero_word_kernel, dim3(1), dim3(64), stream, bits);
+    if (e != hipSuccess) return e;
+  }
+  bool sym = a->rows % 4 == 0 && ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0;
+  hipError_t e = launch_gemm_impl(a, b, c, FP4_FP32, ldc, ws, ws_bytes, stream, true, beta, bits, &sym, alpha, src);
+  if (e != hipSuccess || !sym) return e;
+  const int64_t nb = (a->rows + 63) / 64;
+  return launch(mirror_lower_kernel, dim3(unsigned(nb * (nb + 1) / 2)), dim3(256), stream, c, a->rows, ldc);
+}
+
+size_t gemm_ws_bytes_plan(int64_t M, int64_t N, int64_t K, bool allow_sk, bool sym) {
+  return splitk_ws_bytes(splitk_plan(M, N, K, compute_units(), allow_sk, sym));
 }
 
 size_t gemm_ws_bytes_within(int64_t M, int64_t N, int64_t K, size_t limit) {

@@ -107,6 +107,16 @@ hipError_t launch_gemm_sym_ws(const fp4_tensor *a, const fp4_tensor *b, float *c
                               size_t ws_bytes, hipStream_t stream);
 // Workspace of launch_gemm_sym_ws's plan for an M x M x K product.
 size_t gemm_ws_bytes_sym(int64_t M, int64_t K);
+// The symmetric product accumulated into an fp32 C: C = fl(fl(alpha * v) + fl(beta * S))
+// with S = src (C's shape and stride, symmetric, not overlapping C unless src == c),
+// on and above the diagonal, then mirrored; *amax (if non-null) = max |C|, zeroed
+// first as in launch_gemm_ws_acc.
+hipError_t launch_gemm_sym_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, float alpha,
+                                  float beta, const float *src, float *amax, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+// Workspace of the plan for an M x N x K product: stream-K allowed or not (an
+// accumulated C takes no stream-K), symmetric or whole.
+size_t gemm_ws_bytes_plan(int64_t M, int64_t N, int64_t K, bool allow_sk, bool sym);
 // The workspace of the plan launch_gemm_ws runs with `limit` bytes: the stream-K
 // plan's when it fits, else the fixed split's (which may still exceed the limit).
 size_t gemm_ws_bytes_within(int64_t M, int64_t N, int64_t K, size_t limit);
