@@ -360,8 +360,8 @@ FP4_API fp4_status fp4_linear_backward_eden(const void *dy, const void *x, fp4_d
  * (3.4445, -4.7750, 2.0315)).  One iteration on X [m][n] (fp32, row-major):
  *   A = X X^T              fp4_gemm(X left, X right), fp32 [m][m]
  *   A2 = A A^T             fp4_gemm(A left, A right) (A is symmetric up to rounding)
- *   B = b A + c A2         fl(fl(b A) + fl(c A2)), in place of A2 (variant 0: in the
- *                          A A^T product's epilogue, A2 never stored)
+ *   B = b A + c A2         fl(fl(b A) + fl(c A2)), in the A A^T product's epilogue
+ *                          (A2 is never stored)
  *   BX = B X               fp4_gemm(B, X^T), X^T quantized columnwise
  *   X' = a X + BX          fl(fl(a X) + BX), in place of X
  * Operand quantization by variant (flags):
@@ -393,7 +393,7 @@ typedef struct fp4_ns_config {
  * x_left, x_right [m][n]; a_left, a_right, b_q [m][m]; xt [n][m]; none 2D. */
 typedef struct fp4_ns_buffers {
   float *a;  /* [m][m]: A */
-  float *b;  /* [m][m]: A A^T, then B (variant 0: B only) */
+  float *b;  /* [m][m]: B */
   float *bx; /* [m][n]: B X; or NULL: X' = a X + B X is then taken in the B X GEMM's epilogue
               * (C = fl(v + fl(a X)) for each product v, X updated in place; the same values;
               * with variant 0 that epilogue also takes the next X's amax) */

@@ -285,13 +285,14 @@ static size_t ns_max_slot(int64_t m, int64_t n) {
   size_t w = nvfp4::normalize_scratch_bytes();
   if (nvfp4::axpby_partial_bytes() > w) w = nvfp4::axpby_partial_bytes();
   // every product's plan: X X^T, A A^T and B X whole, X X^T symmetric, and the
-  // accumulated ones (no stream-K): A A^T symmetric into B, B X into X
-  const size_t g[7] = {nvfp4::gemm_ws_bytes(m, m, n),
+  // accumulated ones (no stream-K): A A^T into B (symmetric or whole), B X into X
+  const size_t g[8] = {nvfp4::gemm_ws_bytes(m, m, n),
                        nvfp4::gemm_ws_bytes(m, m, m),
                        nvfp4::gemm_ws_bytes(m, n, m),
                        nvfp4::gemm_ws_bytes_sym(m, n),
                        nvfp4::gemm_ws_bytes_sym(m, m),
                        nvfp4::gemm_ws_bytes_plan(m, m, m, false, true),
+                       nvfp4::gemm_ws_bytes_plan(m, m, m, false, false),
                        nvfp4::gemm_ws_bytes_plan(m, n, m, false, false)};
   for (size_t v : g) w = v > w ? v : w;
   return (w + 255) / 256 * 256;
@@ -429,15 +430,17 @@ fp4_status fp4_newton_schulz(const float *g, float *x, int64_t m, int64_t n, int
                                   : q_pair(bufs->a, m, o + 2, o + 3, &bufs->a_left, &bufs->a_right);
     if (same) {
       // B = fl(fl(c A2) + fl(b A)) in the symmetric A A^T's epilogue (A2 = A A^T is
-      // never stored; the sum is the axpby's, operands swapped), B's amax with it
+      // never stored; the sum is the axpby's, operands swapped), B's amax with it (with
+      // the other variants B's amax is that of its transformed values: an amax pass)
       if (e == hipSuccess)
         e = nvfp4::launch_gemm_sym_ws_acc(&bufs->a_left, ar, bufs->b, m, cfg->c, cfg->b, bufs->a, bufs->b_q.amax,
                                           bufs->ws, bufs->ws_bytes, stream);
       if (e == hipSuccess) e = q(bufs->b, m, m, fl | FP4_Q_AMAX_GIVEN, o + 4, &bufs->b_q);
     } else {
+      // B in A A^T's epilogue as above, the whole product (its two operands differ)
       if (e == hipSuccess)
-        e = nvfp4::launch_gemm_ws(&bufs->a_left, ar, bufs->b, FP4_FP32, m, bufs->ws, bufs->ws_bytes, stream);
-      if (e == hipSuccess) e = nvfp4::launch_axpby(cfg->b, bufs->a, cfg->c, bufs->b, m * m, stream);
+        e = nvfp4::launch_gemm_ws_acc(&bufs->a_left, ar, bufs->b, m, cfg->b, nullptr, bufs->ws, bufs->ws_bytes, stream,
+                                      cfg->c, bufs->a);
       if (e == hipSuccess) e = q(bufs->b, m, m, fl, o + 4, &bufs->b_q);
       if (e == hipSuccess) e = q(x, m, n, fr | FP4_Q_COLWISE, o + 5, &bufs->xt);
     }

@@ -1385,13 +1385,14 @@ hipError_t launch_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4
 }
 
 hipError_t launch_gemm_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, float beta,
-                              float *amax, void *ws, size_t ws_bytes, hipStream_t stream) {
+                              float *amax, void *ws, size_t ws_bytes, hipStream_t stream, float alpha,
+                              const float *src) {
   unsigned *bits = reinterpret_cast<unsigned *>(amax);
   if (bits && a->rows > 0 && b->rows > 0) {
     const hipError_t e = launch(zero_word_kernel, dim3(1), dim3(64), stream, bits);
     if (e != hipSuccess) return e;
   }
-  return launch_gemm_impl(a, b, c, FP4_FP32, ldc, ws, ws_bytes, stream, true, beta, bits);
+  return launch_gemm_impl(a, b, c, FP4_FP32, ldc, ws, ws_bytes, stream, true, beta, bits, nullptr, alpha, src);
 }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {

@@ -90,13 +90,15 @@ hipError_t launch_gemm(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dt
 // split plan for the shape wants one and ws holds gemm_ws_bytes of the shape)
 hipError_t launch_gemm_ws(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc, void *ws,
                           size_t ws_bytes, hipStream_t stream);
-// launch_gemm_ws into an fp32 C that also holds an addend: C = fl(v + fl(beta * C)),
-// v the product as launch_gemm_ws stores it (each element read and written by the
+// launch_gemm_ws into an fp32 C with an addend S: C = fl(fl(alpha * v) + fl(beta * S)),
+// v the product as launch_gemm_ws stores it; S = src (C's shape and stride, not
+// overlapping C), or C itself when src is null (each element read and written by the
 // same thread, so C may be updated in place).  With amax non-null, *amax is set to
 // max |C| over the new C (zeroed by a launch of its own first; it must not lie in
 // the split-K partial tiles of ws).
 hipError_t launch_gemm_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, float beta,
-                              float *amax, void *ws, size_t ws_bytes, hipStream_t stream);
+                              float *amax, void *ws, size_t ws_bytes, hipStream_t stream, float alpha = 1.0f,
+                              const float *src = nullptr);
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 // C = A B^T for a product known to be symmetric (M = N and the same quantized
