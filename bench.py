@@ -384,10 +384,14 @@ def newton_schulz_timing(steps, warmup, dev, variants=NS_VARIANTS):
         f = ns_flags(fp4, variant)
         ms_sep = per_call(bufs_bx, f)
         ms = per_call(bufs, f)
-        # the three GEMM shapes alone, on this call's last operands
+        # the three GEMM shapes alone (whole products through fp4_gemm_ws), on this call's
+        # last operands: with nearest-even X X^T and A A^T take the left layout on both
+        # sides (the right layouts are not written)
+        same = variant == "rne"
+        xr, ar = (bufs.x_left, bufs.a_left) if same else (bufs.x_right, bufs.a_right)
         gem = []
-        for name, qa, qb, c, flops in (("A = X X^T", bufs.x_left, bufs.x_right, bufs.a, 2.0 * m * m * n),
-                                       ("A A^T", bufs.a_left, bufs.a_right, bufs.b, 2.0 * m * m * m),
+        for name, qa, qb, c, flops in (("A = X X^T", bufs.x_left, xr, bufs.a, 2.0 * m * m * n),
+                                       ("A A^T", bufs.a_left, ar, bufs.b, 2.0 * m * m * m),
                                        ("B X", bufs.b_q, bufs.xt, bufs_bx.bx, 2.0 * m * n * m)):
             e0, e1 = HipTimingEvent(), HipTimingEvent()
             e0.record(stream)
