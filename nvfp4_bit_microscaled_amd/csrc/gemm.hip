@@ -88,6 +88,8 @@ struct GemmParams {
   int sk_tiles;
   int sym;              // C = A B^T is symmetric (M = N, the same operand on both sides): only the
                         // tiles on and above the diagonal, in the triangle order of tri_at
+  int mirror;           // sym, plain fp32 epilogue: each tile above the diagonal also stores its
+                        // transpose below it
 };
 
 // Wave-wide maximum of a non-negative lane value, merged into *bits by an atomic
@@ -302,7 +304,7 @@ __device__ __forceinline__ void store_tiles_lds_acc(const GemmParams &p, const f
 
 // ACC: the accumulating fp32 path (p.acc_c set), a kernel instantiation of its own
 // so that the plain kernels keep their registers.
-template <int TM, int TN, bool CHECK, bool ACC>
+template <int TM, int TN, bool CHECK, bool ACC, bool MIRROR = false>
 __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t m0,
                                                 int64_t n0, int lane, uint8_t *region, float gscale, float &mx) {
   static_assert(TN % 2 == 0, "bf16 blocks go in pairs");
@@ -371,15 +373,36 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
     store_tiles_lds_acc<TM, TN, CHECK>(p, acc, m0, n0, lane, region, gscale, mx);
     return;
   }
+  // MIRROR (a symmetric C in whole tiles): a tile above the diagonal (m0 and n0 in
+  // different 256-row tiles) also stores its transpose below the diagonal, straight
+  // from the accumulators.  Lane (lr, g) holds row m0 + 32 i + lr, columns
+  // 8q + 4g + t of block (i, j): column m0 + 32 i + lr of rows n0 + 32 j + 8q + 4g + t
+  // of the lower tile, so for each (q, t) the 32 lanes of a half store 128
+  // contiguous bytes of one row.  Addressed as a raw buffer from the wave's corner of
+  // the lower tile (the launcher keeps 128 rows of C within 2^31 bytes).  Ordinary
+  // stores: the amax pass that reads C next found them in the cache (84-93 us for
+  // 5120^2 against 124 us when every line was written non-temporally).
+  static_assert(!MIRROR || !CHECK, "the mirrored epilogue takes whole tiles");
+  const bool mirror = MIRROR && p.mirror && (m0 >> 8) != (n0 >> 8);
+  const uint32_t ldb = uint32_t(p.ldc) * 4u;
+  const __amdgpu_buffer_rsrc_t rt = wave_rsrc(reinterpret_cast<float *>(p.c) + n0 * p.ldc + m0);  // MIRROR only
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      // fp32: one block, raw from the accumulator registers
+      // fp32: one block, raw from the accumulator registers (explicit moves when the
+      // block is also mirrored: else the compiler moves every accumulator out at once)
+      float a[16];
+      if constexpr (MIRROR) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a[r]) : "a"(acc[i][j][r]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = acc[i][j][r];
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // columns 8q + 4g .. +3 of the block: chunk 2q + g
-        const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                     acc[i][j][4 * q + 3]);
+        const float4 v = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
         *reinterpret_cast<float4 *>(region + lr * 128 + (((2 * q + g) ^ wsw) << 4)) = v;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -394,6 +417,15 @@ __device__ __forceinline__ void store_tiles_lds(const GemmParams &p, const f32x1
           f32x4 *dst = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n);
           __builtin_nontemporal_store(y, dst);
         }
+      }
+      if (mirror) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a[4 * q + t] * gscale), rt,
+                                                  int(4u * uint32_t(32 * i + lr) + uint32_t(4 * g) * ldb),
+                                                  int(uint32_t(32 * j + 8 * q + t) * ldb), 0);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is rewritten by the next block
       __builtin_amdgcn_sched_barrier(0);
@@ -445,7 +477,8 @@ __device__ __forceinline__ void dma16(const u32x4 &rsrc, void *dst, uint32_t vof
 // that is a whole tile is stored as usual; any other is stored raw (no decode
 // scales) into workspace slot r + t (t: the tile's position among the stream-K
 // tiles), and streamk_reduce_kernel sums each split tile's segments in order.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP, bool QUARTERS, bool ACC, bool SK = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool CLAMP, bool QUARTERS, bool ACC, bool SK = false,
+          bool MIRROR = false>
 __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams p) {
   static_assert(!SK || (!QUARTERS && !ACC), "stream-K runs 256x256 tiles without an accumulated C");
   static_assert(!QUARTERS || (BM == 128 && BN == 128), "quarters of 256x256 tiles");
@@ -814,10 +847,11 @@ __global__ __launch_bounds__(64 * WAVES_M *WAVES_N) void gemm_kernel(GemmParams 
       pp.c_bf16 = 0;
       pp.acc_c = 0;
       pp.amax_bits = nullptr;
+      pp.mirror = 0;
       store_tiles_lds<TM, TN, false, false>(pp, acc, wm, wn, lane, lds + 2 * STAGE + wave * kEpiBytes, 1.0f, amx);
     } else {
-      store_tiles_lds<TM, TN, CLAMP, ACC>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes, gscale,
-                                          amx);
+      store_tiles_lds<TM, TN, CLAMP, ACC, MIRROR>(p, acc, mc + wm, nc + wn, lane, lds + 2 * STAGE + wave * kEpiBytes,
+                                                  gscale, amx);
     }
     if (!more) break;
     if (nst == 1) {
@@ -1212,6 +1246,7 @@ SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, unsigned cus, bool allow_
 // (split items store raw partial tiles; the reduction accumulates).
 template <int BM, int BN, bool QUARTERS>
 hipError_t launch_tiles(bool exact, const dim3 &grid, hipStream_t stream, const GemmParams &p) {
+  if (p.mirror) return launch(gemm_kernel<BM, BN, 2, 2, false, QUARTERS, false, false, true>, grid, dim3(256), stream, p);
   if (p.acc_c && (QUARTERS || p.ksplit == 1))
     return exact ? launch(gemm_kernel<BM, BN, 2, 2, false, QUARTERS, true>, grid, dim3(256), stream, p)
                  : launch(gemm_kernel<BM, BN, 2, 2, true, QUARTERS, true>, grid, dim3(256), stream, p);
@@ -1227,7 +1262,7 @@ size_t splitk_ws_bytes(const SplitPlan &sp) {
 hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, fp4_dtype c_dtype, int64_t ldc,
                             void *ws, size_t ws_bytes, hipStream_t stream, bool acc_c = false,
                             float beta = 0.0f, unsigned *amax_bits = nullptr, bool *sym = nullptr,
-                            float alpha = 1.0f, const float *acc_src = nullptr) {
+                            float alpha = 1.0f, const float *acc_src = nullptr, bool *mirrored = nullptr) {
   GemmParams p;
   p.a_codes = a->codes;
   p.a_scales = a->scales;
@@ -1251,6 +1286,8 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
   p.sk_total = 0;
   p.sk_tiles = 0;
   p.sym = 0;
+  p.mirror = 0;
+  if (mirrored) *mirrored = false;
   p.acc_c = acc_c && !p.c_bf16;
   p.alpha = alpha;
   p.beta = beta;
@@ -1334,6 +1371,10 @@ hipError_t launch_gemm_impl(const fp4_tensor *a, const fp4_tensor *b, void *c, f
     p.tiles_main = int(split ? tiles - rest : tiles);
     const dim3 grid(tiles < cus ? tiles : cus);
     const bool exact = p.M % 256 == 0 && p.N % 256 == 0;
+    // a symmetric plain fp32 C: every tile reaches its final store here, so the
+    // epilogue writes the lower triangle too
+    p.mirror = p.sym && !p.acc_c && exact && p.ldc * 4 * 128 < (int64_t(1) << 31);
+    if (mirrored) *mirrored = p.mirror != 0;
     hipError_t e = launch_tiles<256, 256, false>(exact, grid, stream, p);
     if (e == hipSuccess && split) {
       p.tail_first = p.tiles_main;
@@ -1405,10 +1446,13 @@ size_t gemm_ws_bytes_sym(int64_t M, int64_t K) {
 
 hipError_t launch_gemm_sym_ws(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, void *ws,
                               size_t ws_bytes, hipStream_t stream) {
-  // the mirror moves 16-byte vectors: a symmetric product only where they line up
-  bool sym = a->rows % 4 == 0 && ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0;
-  hipError_t e = launch_gemm_impl(a, b, c, FP4_FP32, ldc, ws, ws_bytes, stream, false, 0.0f, nullptr, &sym);
-  if (e != hipSuccess || !sym) return e;
+  // the mirror moves 16-byte vectors: a symmetric product only where they line up.
+  // The persistent launch stores the lower triangle itself; after split or stream-K
+  // plans a mirror kernel copies it.
+  bool sym = a->rows % 4 == 0 && ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0, mirrored = false;
+  hipError_t e = launch_gemm_impl(a, b, c, FP4_FP32, ldc, ws, ws_bytes, stream, false, 0.0f, nullptr, &sym, 1.0f,
+                                  nullptr, &mirrored);
+  if (e != hipSuccess || !sym || mirrored) return e;
   const int64_t nb = (a->rows + 63) / 64;
   return launch(mirror_lower_kernel, dim3(unsigned(nb * (nb + 1) / 2)), dim3(256), stream, c, a->rows, ldc);
 }

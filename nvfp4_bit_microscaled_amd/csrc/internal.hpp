@@ -103,8 +103,10 @@ hipError_t launch_gemm_ws_acc(const fp4_tensor *a, const fp4_tensor *b, float *c
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 // C = A B^T for a product known to be symmetric (M = N and the same quantized
 // operand on both sides, so exactly symmetric): on the main path only the 256x256
-// tiles on and above the diagonal are computed, and a second kernel copies the
-// upper triangle into the lower one; elsewhere the whole product.  fp32 C.
+// tiles on and above the diagonal are computed, each tile above the diagonal also
+// stored transposed below it by the persistent launch's epilogue (after a split or
+// stream-K plan a second kernel copies the upper triangle into the lower one instead);
+// elsewhere the whole product.  fp32 C.
 hipError_t launch_gemm_sym_ws(const fp4_tensor *a, const fp4_tensor *b, float *c, int64_t ldc, void *ws,
                               size_t ws_bytes, hipStream_t stream);
 // Workspace of launch_gemm_sym_ws's plan for an M x M x K product.

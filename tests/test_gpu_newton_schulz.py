@@ -21,16 +21,21 @@ def variant_flags(fp4, variant):
 
 
 @pytest.mark.parametrize("variant", ["rne", "rht_sr", "eden"])
-@pytest.mark.parametrize("shape", [(128, 256), (256, 768), (1024, 4096), (512, 128), (400, 512), (2560, 9984)],
+@pytest.mark.parametrize("shape", [(128, 256), (256, 768), (1024, 4096), (512, 128), (400, 512), (768, 512),
+                                   (2560, 9984), (5888, 256)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_newton_schulz_stagewise(fp4, oracle, variant, shape):
     """With nearest-even operands X X^T and A A^T take the symmetric GEMM (tiles on
     and above the diagonal, mirrored) when their K is whole 256-element stages: A and
     B come out exactly symmetric, each element within the GEMM tolerance; 400 x 512
     has ragged 256 x 256 tiles and a mirror whose 64 x 64 blocks overhang the edge.
-    The plans differ by shape: 1024 x 4096 splits X X^T over K; 2560 x 9984 runs it as
-    stream-K (55 upper tiles of 39 stages, 100 whole ones for the other variants) and
-    A A^T, with B in its epilogue, split over K in 2 (the reduction adds b A)."""
+    The plans differ by shape: 768 x 512 runs X X^T as one persistent launch whose
+    epilogue also stores each upper tile's transpose below the diagonal; 5888 x 256
+    does that for its first 256 of 276 upper tiles and the last 20 as 128 x 128
+    quarters; 1024 x 4096 splits X X^T over K; 2560 x 9984 runs it as stream-K (55
+    upper tiles of 39 stages, 100 whole ones for the other variants) and A A^T, with B
+    in its epilogue, split over K in 2 (the reduction adds b A); after a split or
+    stream-K, and after A A^T, the mirror kernel fills the lower triangle."""
     m, n = shape
     if variant == "eden" and (m % 64 or n % 64):
         pytest.skip("the 64-point transform needs multiples of 64")
