@@ -71,15 +71,20 @@ __global__ __launch_bounds__(kThreads) void max_finish_kernel(const float *__res
 }
 
 // Per-workgroup binary64 partial sums of g[i]^2 (each square exact in binary64),
-// in a fixed order: thread t of workgroup b sums i = b * T + t + k * G * T in k
-// order, then the workgroup sums its threads pairwise by a fixed tree.
-__global__ __launch_bounds__(kThreads) void sumsq_kernel(const float *__restrict__ g, int64_t n,
+// in a fixed order: thread t of workgroup b sums the 16-byte vectors
+// i = b * T + t + k * G * T in k order (their four squares in element order), then
+// the workgroup sums its threads pairwise by a fixed tree.
+__global__ __launch_bounds__(kThreads) void sumsq_kernel(const float4 *__restrict__ g, int64_t n4,
                                                          double *__restrict__ partial) {
   __shared__ double part[kThreads];
   double s = 0.0;
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads) {
-    const double v = double(g[i]);
-    s += v * v;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n4; i += int64_t(gridDim.x) * kThreads) {
+    const float4 v = g[i];
+    const double a = v.x, b = v.y, c = v.z, d = v.w;
+    s += a * a;
+    s += b * b;
+    s += c * c;
+    s += d * d;
   }
   part[threadIdx.x] = s;
   __syncthreads();
@@ -90,22 +95,26 @@ __global__ __launch_bounds__(kThreads) void sumsq_kernel(const float *__restrict
   if (threadIdx.x == 0) partial[blockIdx.x] = part[0];
 }
 
-// s = RN32(1 / (sqrt(sum of the partials) + eps)) into *scale (one workgroup; the
-// partials summed in index order by thread 0).
+// s = RN32(1 / (sqrt(sum of the partials) + eps)) into *scale (one wave, a fixed
+// order: lane l sums partials l, l + 64, ... in index order, then the lanes are
+// summed by a fixed butterfly).
 __global__ __launch_bounds__(64) void inv_norm_kernel(const double *__restrict__ partial, int nparts, float eps,
                                                       float *scale) {
-  if (threadIdx.x == 0) {
-    double ss = 0.0;
-    for (int i = 0; i < nparts; ++i) ss += partial[i];
-    *scale = float(1.0 / (sqrt(ss) + double(eps)));
-  }
+  double ss = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += 64) ss += partial[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if (threadIdx.x == 0) *scale = float(1.0 / (sqrt(ss) + double(eps)));
 }
 
-__global__ __launch_bounds__(kThreads) void scale_kernel(const float *__restrict__ g, const float *__restrict__ scale,
-                                                         float *__restrict__ x, int64_t n) {
+// x = g * s, 16-byte vectors (g and x may be the same array).
+__global__ __launch_bounds__(kThreads) void scale_kernel(const float4 *g, const float *__restrict__ scale, float4 *x,
+                                                         int64_t n4) {
   const float s = *scale;
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads)
-    x[i] = g[i] * s;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n4; i += int64_t(gridDim.x) * kThreads) {
+    const float4 v = g[i];
+    x[i] = make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
+  }
 }
 
 unsigned grid_of(int64_t n) {
@@ -139,17 +148,22 @@ size_t normalize_scratch_bytes() { return kSumBlocks * sizeof(double) + sizeof(f
 
 size_t axpby_partial_bytes() { return 4096 * sizeof(float); }  // grid_of's cap
 
-// x = g / (|g|_F + eps); scratch: normalize_scratch_bytes(), 8-byte aligned.
+// x = g / (|g|_F + eps); n % 4 == 0 and g, x 16-byte aligned (else hipErrorInvalidValue);
+// scratch: normalize_scratch_bytes(), 8-byte aligned.
 hipError_t launch_normalize(const float *g, float *x, int64_t n, float eps, void *scratch, hipStream_t stream) {
+  if (n % 4 != 0 || (reinterpret_cast<uintptr_t>(g) & 15) != 0 || (reinterpret_cast<uintptr_t>(x) & 15) != 0)
+    return hipErrorInvalidValue;
   double *partial = static_cast<double *>(scratch);
   float *scale = reinterpret_cast<float *>(partial + kSumBlocks);
-  const int64_t blocks64 = (n + kThreads - 1) / kThreads;
-  const int nparts = int(blocks64 < 1 ? 1 : (blocks64 > kSumBlocks ? kSumBlocks : blocks64));
-  hipError_t e = launch(sumsq_kernel, dim3(nparts), dim3(kThreads), stream, g, n, partial);
+  const int64_t n4 = n / 4, blocks = (n4 + kThreads - 1) / kThreads;
+  const int nparts = int(blocks < 1 ? 1 : (blocks > kSumBlocks ? kSumBlocks : blocks));
+  hipError_t e = launch(sumsq_kernel, dim3(nparts), dim3(kThreads), stream, reinterpret_cast<const float4 *>(g), n4,
+                        partial);
   if (e == hipSuccess) e = launch(inv_norm_kernel, dim3(1), dim3(64), stream, static_cast<const double *>(partial),
                                   nparts, eps, scale);
   if (e == hipSuccess && n > 0)
-    e = launch(scale_kernel, dim3(grid_of(n)), dim3(kThreads), stream, g, static_cast<const float *>(scale), x, n);
+    e = launch(scale_kernel, dim3(grid_of(n4)), dim3(kThreads), stream, reinterpret_cast<const float4 *>(g),
+               static_cast<const float *>(scale), reinterpret_cast<float4 *>(x), n4);
   return e;
 }
 
