@@ -633,6 +633,76 @@ def measure(wl, layers, ws, steps, warmup, backward="recipe"):
     }
 
 
+def sysfs_clock_dir():
+    """The sysfs directory of cuda:0's PCI device, which holds the driver's
+    pp_dpm_sclk / pp_dpm_mclk tables; None when it cannot be found."""
+    import glob
+
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    cand = []
+    bus = getattr(p, "pci_bus_id", None)
+    if bus is not None:
+        cand.append("/sys/bus/pci/devices/%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0) or 0, bus,
+                                                            getattr(p, "pci_device_id", 0) or 0))
+    found = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if len(found) == 1:
+        cand.append(os.path.dirname(found[0]))
+    for d in cand:
+        if os.access(os.path.join(d, "pp_dpm_sclk"), os.R_OK):
+            return d
+    return None
+
+
+def sample_clocks(run, period_s=0.002):
+    """Shader and memory clocks as the driver reports them while run() executes:
+    the level marked current in pp_dpm_sclk / pp_dpm_mclk (its frequency is the
+    measured one: it moves between the table's levels), read every period_s by a
+    host thread.  Median, min and max in MHz, or None when sysfs is not readable."""
+    import threading
+
+    d = sysfs_clock_dir()
+    if d is None:
+        run()
+        return None
+    samples = {"sclk": [], "mclk": []}
+    stop = threading.Event()
+
+    def current(name):
+        try:
+            with open(os.path.join(d, "pp_dpm_" + name)) as f:
+                for line in f:
+                    if "*" in line:
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def loop():
+        while not stop.is_set():
+            for k in samples:
+                v = current(k)
+                if v is not None:
+                    samples[k].append(v)
+            time.sleep(period_s)
+
+    t = threading.Thread(target=loop, daemon=True)
+    t.start()
+    try:
+        run()
+    finally:
+        stop.set()
+        t.join()
+    out = {"source": "sysfs " + os.path.join(d, "pp_dpm_{sclk,mclk}") + ", the level marked current, sampled every "
+                     f"{period_s * 1e3:g} ms"}
+    for k, v in samples.items():
+        if v:
+            v = sorted(v)
+            out[k + "_mhz"] = {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -663,6 +733,9 @@ def main():
 
     wl, layers, ws, ws_need, t_gen = setup_workload(args.workload, dev)
     r = measure(wl, layers, ws, args.steps, args.warmup)
+    # the clocks the driver reports over as many steps again, after the timed ones (a
+    # host thread reading sysfs stays out of the timed region)
+    clocks = sample_clocks(lambda: measure(wl, layers, ws, args.steps, 0))
     gemm_shapes = []
     for lin in wl.linears:
         if "fprop" in wl.passes:
@@ -741,6 +814,7 @@ def main():
         "gemm_ms_per_step": round(r["gemm_ms"] / args.steps, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "gpu_clocks": clocks,
         "input_generation_s": round(t_gen, 1),
     }
     others = []
