@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="measure only --workload (default: also the other full-size configurations, fewer steps)")
     ap.add_argument("--other-steps", type=int, default=10)
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the extra untimed steps that sample the driver's clocks (gpu_clocks: null)")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel quantize breakdown (profiler runs that look at the steps only)")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
@@ -735,7 +737,7 @@ def main():
     r = measure(wl, layers, ws, args.steps, args.warmup)
     # the clocks the driver reports over as many steps again, after the timed ones (a
     # host thread reading sysfs stays out of the timed region)
-    clocks = sample_clocks(lambda: measure(wl, layers, ws, args.steps, 0))
+    clocks = None if args.no_clocks else sample_clocks(lambda: measure(wl, layers, ws, args.steps, 0))
     gemm_shapes = []
     for lin in wl.linears:
         if "fprop" in wl.passes:
