@@ -37,7 +37,11 @@
 //                     matrix-core time.
 //                     A second instance with 128x128 tiles (four waves of 64x64)
 //                     takes, as quarters, the few 256x256 tiles that would
-//                     otherwise run as a mostly idle last round.
+//                     otherwise run as a mostly idle last round.  Other
+//                     instances, each with its own registers: CLAMP (tiles that
+//                     stick out of C), ACC (C = alpha v + beta S, an addend read in
+//                     the epilogue), SK (stream-K runs) and MIRROR (a symmetric
+//                     product's tiles above the diagonal also stored transposed).
 //   gemm_edge_kernel  any K multiple of 16, any 8-byte-aligned operands: 128x128
 //                     tile, register-staged loads with zero fill.
 // Workgroup -> tile order (both): consecutive workgroup ids go to different XCDs,
