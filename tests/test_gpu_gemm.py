@@ -229,3 +229,41 @@ def test_gemm_split_k(fp4, oracle, case, out_dtype):
     fp4.fp4_gemm_ws(a, b, c, small)
     torch.cuda.synchronize()
     check_gemm(c.float().cpu().numpy(), y_ref, bound, out_dtype == torch.bfloat16, f"small workspace {case}")
+
+
+def random_shapes(n=16, seed=20261203, max_work=2e10):
+    """Seeded (M, N, K, a2d, b2d) drawn across the paths: M, N from 1 to 4600 (each a
+    multiple of 16 half the time, which 2D scales need), K a multiple of 256 (the main
+    path) or of 16 (the edge kernel when K % 256 != 0) up to 8192, 2D scales on half
+    of the operands whose rows allow them; shapes whose M N K exceeds max_work are
+    drawn again (the binary64 reference stays within seconds)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M, N = (int(v) if rng.random() < 0.5 else 16 * max(1, int(v) // 16) for v in rng.integers(1, 4600, size=2))
+        K = 256 * int(rng.integers(1, 33)) if rng.random() < 0.5 else 16 * int(rng.integers(1, 513))
+        if float(M) * N * K > max_work:
+            continue
+        out.append((M, N, K, bool(M % 16 == 0 and rng.random() < 0.5), bool(N % 16 == 0 and rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("case", random_shapes(), ids=lambda c: "x".join(map(str, c[:3])))
+def test_gemm_random_shapes(fp4, oracle, case):
+    """fp4_gemm and fp4_gemm_ws (with the workspace its plan asks for) on seeded random
+    shapes, fp32 and bf16 outputs, against the oracle within the GEMM tolerance."""
+    M, N, K, a2d, b2d = case
+    qa, qb = oracle_operands(oracle, M, N, K, seed=M * 7 + N * 3 + K, a2d=a2d, b2d=b2d, a_kind="normal")
+    a, b = upload_q(fp4, qa), upload_q(fp4, qb)
+    y_ref, bound = oracle.gemm_ref(qa, qb)
+    ws = torch.empty(max(fp4.fp4_gemm_ws_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
+    for out_dtype in (torch.float32, torch.bfloat16):
+        for with_ws in (False, True):
+            c = torch.full((M, N), float("nan"), dtype=out_dtype, device="cuda")
+            if with_ws:
+                fp4.fp4_gemm_ws(a, b, c, ws)
+            else:
+                fp4.fp4_gemm(a, b, c)
+            torch.cuda.synchronize()
+            check_gemm(c.float().cpu().numpy(), y_ref, bound, out_dtype == torch.bfloat16,
+                       f"random {case} {out_dtype} ws={with_ws}")
