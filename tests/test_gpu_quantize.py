@@ -297,3 +297,55 @@ def test_dual_with_a_row_stride_beyond_the_fused_kernel(fp4, oracle, dtype):
     assert_q_equal(host_q(qc), oracle.quantize(xf, colwise=True, rht=True, signs=0x2C4B), "wide-stride dual cols")
     del full, x
     torch.cuda.empty_cache()
+
+
+QUANT_MODES = ["rne", "sr", "rht", "rht_sr", "2d", "rht64", "rht64_sr", "eden"]
+
+
+def random_quant_cases(n=24, seed=20261204, max_elems=6_000_000):
+    """Seeded (R, C, mode, colwise, dtype, kind) over every quantizer mode and layout:
+    the blocked dimension a multiple of 16 (64 for the 64-point transform and
+    MS-EDEN; both for 2D), the other dimension free but for the row stride's multiple
+    of 8 elements, ragged tiles in both, bf16 and fp32 inputs, Gaussian or Laplace
+    values."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        mode = QUANT_MODES[len(out) % len(QUANT_MODES)]
+        colwise = bool(rng.random() < 0.5)
+        blk = 64 if mode.startswith("rht64") or mode == "eden" else 16
+        nb = int(rng.integers(1, 4096 // blk + 1))
+        other = int(rng.integers(1, 3000))
+        if mode == "2d":
+            other = 16 * max(1, other // 16)
+        elif colwise:  # x's row stride: a multiple of 8 elements
+            other = 8 * max(1, other // 8)
+        R, C = (nb * blk, other) if colwise else (other, nb * blk)
+        if R * C > max_elems:
+            continue
+        out.append((R, C, mode, colwise, "bf16" if rng.random() < 0.5 else "fp32",
+                    "laplace" if rng.random() < 0.5 else "normal"))
+    return out
+
+
+@pytest.mark.parametrize("case", random_quant_cases(), ids=lambda c: f"{c[0]}x{c[1]}_{c[2]}_{'col' if c[3] else 'row'}_{c[4]}")
+def test_quantize_random_cases(fp4, oracle, case):
+    """fp4_quantize on seeded random shapes of every mode and layout, bit for bit
+    against the oracle (codes, scales, amax; 2D also its transposed layout)."""
+    R, C, mode, colwise, dtype, kind = case
+    x_cpu = make_x((R, C), seed=R * 5 + C, kind=kind, std=1.0 if kind == "normal" else 1e-3,
+                   dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    flags = {"rne": 0, "sr": fp4.Q_SR, "rht": fp4.Q_RHT, "rht_sr": fp4.Q_RHT | fp4.Q_SR, "2d": fp4.Q_2D,
+             "rht64": fp4.Q_RHT64, "rht64_sr": fp4.Q_RHT64 | fp4.Q_SR, "eden": fp4.Q_RHT64 | fp4.Q_EDEN}[mode]
+    if colwise:
+        flags |= fp4.Q_COLWISE
+    if mode in ("rne", "sr", "rht", "rht_sr", "2d"):
+        run_case(fp4, oracle, x_cpu, flags, signs=0x6B1D, seed=0xC0FFEE, offset=5)
+        return
+    key = 0x9E3779B9
+    lrows, lcols = (C, R) if colwise else (R, C)
+    q = fp4.QTensor(lrows, lcols)
+    fp4.fp4_quantize(dev(x_cpu), flags, key, 0xC0FFEE, 5, q)
+    ora = oracle.quantize(workloads.widen(x_cpu), colwise=colwise, rht64=True, sr=mode == "rht64_sr",
+                          eden=mode == "eden", signs=key, seed=0xC0FFEE, offset=5)
+    assert_q_equal(host_q(q), ora, f"{case}")
